@@ -1,0 +1,230 @@
+"""Thin Python binding of libmtp.so (include/mtp.h): ctypes structures and
+argument marshalling from torch tensors.  Every computation runs in the HIP
+library; this module only passes device pointers, sizes and the stream.
+
+Loading fails loudly when the library is missing: there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes as C
+import os
+from typing import Dict, List, Optional, Sequence
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmtp.so")
+
+MTP_F32, MTP_BF16 = 0, 1
+MTP_REDUCE_FIXED, MTP_REDUCE_VALID_MEAN = 0, 1
+STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEPTH",
+          -4: "MTP_ERR_DTYPE", -5: "MTP_ERR_WORKSPACE", -6: "MTP_ERR_ARG", -7: "MTP_ERR_HIP",
+          -8: "MTP_ERR_UNSUPPORTED"}
+EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_chain_workspace_size",
+           "mtp_ce_workspace_size", "mtp_verify_workspace_size", "mtp_strerror", "mtp_abi_version")
+
+vp = C.c_void_p
+fp = C.POINTER(C.c_float)
+
+
+class DepthWeights(C.Structure):
+    _fields_ = [("g_h", vp), ("g_e", vp), ("g_attn", vp), ("g_ffn", vp), ("M", vp), ("Wqkv", vp),
+                ("Wo", vp), ("Wgate", vp), ("Wup", vp), ("Wdown", vp)]
+
+
+class ChainArgs(C.Structure):
+    _fields_ = [("B", C.c_int), ("T", C.c_int), ("d", C.c_int), ("n_heads", C.c_int),
+                ("head_dim", C.c_int), ("ffn", C.c_int), ("V", C.c_int), ("D", C.c_int),
+                ("dtype", C.c_int), ("eps", C.c_float), ("rope_theta", C.c_float),
+                ("tokens", vp), ("segment_ids", vp), ("h0", vp), ("embed", vp),
+                ("w", C.POINTER(DepthWeights)), ("h_out", C.POINTER(vp)),
+                ("state_mask", vp), ("loss_mask", vp), ("labels", vp), ("counts", vp),
+                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+class CeArgs(C.Structure):
+    _fields_ = [("B", C.c_int), ("T", C.c_int), ("d", C.c_int), ("V", C.c_int), ("D", C.c_int),
+                ("dtype", C.c_int), ("eps", C.c_float), ("lambda_", C.c_float), ("reduce", C.c_int),
+                ("denom", C.c_double), ("h", C.POINTER(vp)), ("labels", vp), ("W_out", vp),
+                ("g_out", vp), ("loss_sum", vp), ("counts", vp), ("loss", vp), ("loss_mtp", vp),
+                ("lse", vp), ("dh", C.POINTER(vp)), ("dW_out", vp), ("dg_out", vp),
+                ("accumulate", C.c_int), ("device_error", vp), ("workspace", vp),
+                ("workspace_bytes", C.c_size_t)]
+
+
+class VerifyArgs(C.Structure):
+    _fields_ = [("R", C.c_int), ("gamma", C.c_int), ("V", C.c_int), ("temperature", C.c_float),
+                ("logits_dtype", C.c_int), ("target_logits", vp), ("draft_logits", vp),
+                ("draft_tokens", vp), ("u_accept", vp), ("u_sample", vp), ("accepted_len", vp),
+                ("next_token", vp), ("status", vp), ("margin", vp), ("workspace", vp),
+                ("workspace_bytes", C.c_size_t)]
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> C.CDLL:
+    """Load libmtp.so (once).  Raises if it is missing."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise RuntimeError(f"libmtp.so not found at {path}: build it with "
+                               "`python -m deepseek_sequential_mtp_amd.build`")
+        lib = C.CDLL(path)
+        lib.mtp_chain_forward.argtypes = [C.POINTER(ChainArgs), vp]
+        lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
+        lib.mtp_verify.argtypes = [C.POINTER(VerifyArgs), vp]
+        lib.mtp_chain_workspace_size.argtypes = [C.POINTER(ChainArgs)]
+        lib.mtp_chain_workspace_size.restype = C.c_size_t
+        lib.mtp_ce_workspace_size.argtypes = [C.POINTER(CeArgs)]
+        lib.mtp_ce_workspace_size.restype = C.c_size_t
+        lib.mtp_verify_workspace_size.argtypes = [C.POINTER(VerifyArgs)]
+        lib.mtp_verify_workspace_size.restype = C.c_size_t
+        lib.mtp_strerror.argtypes = [C.c_int]
+        lib.mtp_strerror.restype = C.c_char_p
+        lib.mtp_abi_version.restype = C.c_int
+        _lib = lib
+    return _lib
+
+
+class MtpError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {load().mtp_strerror(status).decode()}")
+
+
+def _check(status: int):
+    if status != 0:
+        raise MtpError(status)
+
+
+def _p(t: Optional[torch.Tensor]):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MTP_BF16
+    if t.dtype == torch.float32:
+        return MTP_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(stream) -> C.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return C.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes: int, device, cache: Optional[Dict] = None, key: str = "ws") -> torch.Tensor:
+    if cache is not None and key in cache and cache[key].numel() >= nbytes:
+        return cache[key]
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if cache is not None:
+        cache[key] = ws
+    return ws
+
+
+# ---------------------------------------------------------------------------
+def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Tensor,
+                  embed: torch.Tensor, depths: Sequence[Dict[str, torch.Tensor]], *, n_heads: int,
+                  head_dim: int, eps: float = 1e-6, rope_theta: float = 10000.0,
+                  out: Optional[Dict] = None, cache: Optional[Dict] = None, stream=None) -> Dict:
+    """mtp_chain_forward.  tokens/segment_ids int32 [B,T]; h0 [B*T,d]; embed [V,d];
+    depths: D dicts with g_h, g_e, M, g_a, Wqkv, Wo, g_f, Wgate, Wup, Wdown.
+    Returns dict(h=[D x [B*T,d]], state_mask, loss_mask, labels, counts, device_error)."""
+    B, T = tokens.shape
+    V, d = embed.shape
+    D = len(depths)
+    ffn = depths[0]["Wgate"].shape[0]
+    dev = h0.device
+    if out is None:
+        out = dict(h=[torch.empty_like(h0) for _ in range(D)],
+                   state_mask=torch.empty((D, B, T), dtype=torch.uint8, device=dev),
+                   loss_mask=torch.empty((D, B, T), dtype=torch.uint8, device=dev),
+                   labels=torch.empty((D, B, T), dtype=torch.int32, device=dev),
+                   counts=torch.empty((D,), dtype=torch.int32, device=dev),
+                   device_error=torch.empty((1,), dtype=torch.int32, device=dev))
+    ws_arr = (DepthWeights * D)()
+    for k, w in enumerate(depths):
+        ws_arr[k] = DepthWeights(_p(w["g_h"]), _p(w["g_e"]), _p(w["g_a"]), _p(w["g_f"]), _p(w["M"]),
+                                 _p(w["Wqkv"]), _p(w["Wo"]), _p(w["Wgate"]), _p(w["Wup"]),
+                                 _p(w["Wdown"]))
+    hout = (vp * D)(*[h.data_ptr() for h in out["h"]])
+    a = ChainArgs(B, T, d, n_heads, head_dim, ffn, V, D, _dtype_code(h0), eps, rope_theta,
+                  _p(tokens), _p(segment_ids), _p(h0), _p(embed), ws_arr, hout,
+                  _p(out["state_mask"]), _p(out["loss_mask"]), _p(out["labels"]), _p(out["counts"]),
+                  _p(out["device_error"]), None, 0)
+    lib = load()
+    nbytes = lib.mtp_chain_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_chain_forward(C.byref(a), _stream(stream)))   # raises the shape error
+    ws = _workspace(nbytes, dev, cache, "chain_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_chain_forward(C.byref(a), _stream(stream)))
+    out["_keep"] = (ws_arr, hout, ws)
+    return out
+
+
+def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: torch.Tensor,
+                    g_out: torch.Tensor, *, lam: float, eps: float = 1e-6, reduce: str = "fixed",
+                    denom: float = 0.0, accumulate: bool = False, want_lse: bool = False,
+                    out: Optional[Dict] = None, cache: Optional[Dict] = None, stream=None) -> Dict:
+    """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].
+    Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error)."""
+    D, B, T = labels.shape
+    V, d = W_out.shape
+    dev = W_out.device
+    if out is None:
+        out = dict(loss_sum=torch.empty(D, dtype=torch.float32, device=dev),
+                   counts=torch.empty(D, dtype=torch.int32, device=dev),
+                   loss=torch.empty(D, dtype=torch.float32, device=dev),
+                   loss_mtp=torch.empty(1, dtype=torch.float32, device=dev),
+                   lse=torch.empty((D, B * T), dtype=torch.float32, device=dev) if want_lse else None,
+                   dh=[torch.empty((B * T, d), dtype=torch.float32, device=dev) for _ in range(D)],
+                   dW_out=torch.zeros((V, d), dtype=torch.float32, device=dev),
+                   dg_out=torch.zeros((d,), dtype=torch.float32, device=dev),
+                   device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    hp = (vp * D)(*[h.data_ptr() for h in hs])
+    dhp = (vp * D)(*[x.data_ptr() for x in out["dh"]])
+    red = {"fixed": MTP_REDUCE_FIXED, "valid_mean": MTP_REDUCE_VALID_MEAN}[reduce]
+    a = CeArgs(B, T, d, V, D, _dtype_code(W_out), eps, lam, red, float(denom), hp, _p(labels),
+               _p(W_out), _p(g_out), _p(out["loss_sum"]), _p(out["counts"]), _p(out["loss"]),
+               _p(out["loss_mtp"]), _p(out["lse"]), dhp, _p(out["dW_out"]), _p(out["dg_out"]),
+               1 if accumulate else 0, _p(out["device_error"]), None, 0)
+    lib = load()
+    nbytes = lib.mtp_ce_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_head_ce_fwd_bwd(C.byref(a), _stream(stream)))
+    ws = _workspace(nbytes, dev, cache, "ce_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_head_ce_fwd_bwd(C.byref(a), _stream(stream)))
+    out["_keep"] = (hp, dhp, ws)
+    return out
+
+
+def verify(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+           u_accept: torch.Tensor, u_sample: torch.Tensor, *, temperature: float = 1.0,
+           want_margin: bool = True, out: Optional[Dict] = None, cache: Optional[Dict] = None,
+           stream=None) -> Dict:
+    """mtp_verify.  target [R, g+1, V], draft [R, g, V] (bf16 or f32), draft_tokens int32
+    [R, g], u_accept f32 [R, g], u_sample f32 [R, g+1]."""
+    R, G1, V = target_logits.shape
+    G = G1 - 1
+    dev = target_logits.device
+    if out is None:
+        out = dict(accepted_len=torch.empty(R, dtype=torch.int32, device=dev),
+                   next_token=torch.empty(R, dtype=torch.int32, device=dev),
+                   status=torch.empty(R, dtype=torch.int32, device=dev),
+                   margin=torch.empty(R, dtype=torch.float32, device=dev) if want_margin else None)
+    a = VerifyArgs(R, G, V, temperature, _dtype_code(target_logits), _p(target_logits),
+                   _p(draft_logits), _p(draft_tokens), _p(u_accept), _p(u_sample),
+                   _p(out["accepted_len"]), _p(out["next_token"]), _p(out["status"]),
+                   _p(out["margin"]), None, 0)
+    lib = load()
+    nbytes = lib.mtp_verify_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_verify(C.byref(a), _stream(stream)))
+    ws = _workspace(nbytes, dev, cache, "verify_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_verify(C.byref(a), _stream(stream)))
+    out["_keep"] = (ws,)
+    return out

@@ -1,0 +1,126 @@
+// Reductions of the fused linear cross-entropy (M7.6 0x05, 0x05A):
+// merging the per-tile online log-sum-exp partials of each row, the per-depth
+// loss sums and counts, the backward scale lambda / (D * denom_k), and the
+// final L^(k) and L_MTP.  The vocabulary GEMMs themselves live in
+// mtp_api.hip (GEMM core + CE epilogues).
+#include "kernels.hpp"
+
+namespace mtp {
+
+// One wave per row: lse = M + log(sum_t s_t exp(m_t - M)) over the nt tile
+// partials; row loss = lse - z[label] on labelled rows, else 0.
+__global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restrict__ part, int nt,
+                                                         const float *__restrict__ target,
+                                                         const int32_t *__restrict__ labels,
+                                                         float *__restrict__ lse, float *__restrict__ lse_out,
+                                                         float *__restrict__ row_loss, int N) {
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  if (row >= N) return;
+  const float2 *p = part + (long)row * nt;
+  float mx = -INFINITY;
+  for (int i = lane; i < nt; i += 64) mx = fmaxf(mx, p[i].x);
+  mx = warp_max(mx);
+  float s = 0.f;
+  for (int i = lane; i < nt; i += 64) {
+    const float2 v = p[i];
+    s += v.y * expf(v.x - mx);
+  }
+  s = warp_sum(s);
+  if (lane == 0) {
+    const float l = mx + logf(s);
+    lse[row] = l;
+    if (lse_out != nullptr) lse_out[row] = l;
+    const int lab = labels[row];
+    row_loss[row] = lab >= 0 ? l - target[row] : 0.f;
+  }
+}
+
+// One block: sum of the row losses of depth k (double, fixed order) and the
+// count of labelled rows; scale[k] = lambda / (D * denom_k) for the backward
+// (0 for an empty depth under the valid-row mean).
+__global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict__ row_loss,
+                                                         const int32_t *__restrict__ labels, int N, int k,
+                                                         int D, int valid_mean, double denom, float lambda,
+                                                         double *acc_sum, int32_t *acc_cnt, float *scale) {
+  __shared__ double shs[16];
+  __shared__ int shc[16];
+  const int t = threadIdx.x;
+  double s = 0.0;
+  int c = 0;
+  for (int i = t; i < N; i += 1024) {
+    s += (double)row_loss[i];
+    c += labels[i] >= 0 ? 1 : 0;
+  }
+  s = warp_sum(s);
+  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
+  if ((t & 63) == 0) { shs[t >> 6] = s; shc[t >> 6] = c; }
+  __syncthreads();
+  if (t == 0) {
+    double ts = 0.0;
+    int tc = 0;
+    for (int w = 0; w < 16; ++w) { ts += shs[w]; tc += shc[w]; }
+    acc_sum[k] = ts;
+    acc_cnt[k] = tc;
+    const double den = valid_mean ? (double)tc : denom;
+    scale[k] = den > 0.0 ? (float)((double)lambda / ((double)D * den)) : 0.f;
+  }
+}
+
+__global__ void ce_finalize_kernel(const double *acc_sum, const int32_t *acc_cnt, int D, int valid_mean,
+                                   double denom, float lambda, float *loss_sum, int32_t *counts,
+                                   float *loss, float *loss_mtp) {
+  if (threadIdx.x != 0) return;
+  double total = 0.0;
+  for (int k = 0; k < D; ++k) {
+    const double den = valid_mean ? (double)acc_cnt[k] : denom;
+    const double lk = den > 0.0 ? acc_sum[k] / den : 0.0;
+    loss_sum[k] = (float)acc_sum[k];
+    counts[k] = acc_cnt[k];
+    loss[k] = (float)lk;
+    total += lk;
+  }
+  loss_mtp[0] = (float)((double)lambda / D * total);
+}
+
+hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
+                             float *lse, float *lse_out, float *row_loss, int N, hipStream_t s) {
+  hipLaunchKernelGGL(ce_combine_kernel, dim3((N + 3) / 4), dim3(256), 0, s, part, nt, target, labels, lse,
+                     lse_out, row_loss, N);
+  return hipGetLastError();
+}
+hipError_t launch_ce_reduce(const float *row_loss, const int32_t *labels, int N, int k, int D,
+                            int valid_mean, double denom, float lambda, double *acc_sum, int32_t *acc_cnt,
+                            float *scale, hipStream_t s) {
+  hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, s, row_loss, labels, N, k, D, valid_mean,
+                     denom, lambda, acc_sum, acc_cnt, scale);
+  return hipGetLastError();
+}
+hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int D, int valid_mean,
+                              double denom, float lambda, float *loss_sum, int32_t *counts, float *loss,
+                              float *loss_mtp, hipStream_t s) {
+  hipLaunchKernelGGL(ce_finalize_kernel, dim3(1), dim3(64), 0, s, acc_sum, acc_cnt, D, valid_mean, denom,
+                     lambda, loss_sum, counts, loss, loss_mtp);
+  return hipGetLastError();
+}
+
+__global__ void fill_i32_kernel(int32_t *p, long n, int32_t v) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+__global__ void fill_f32_kernel(float *p, long n, float v) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+hipError_t fill_i32(int32_t *p, long n, int32_t v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+hipError_t fill_f32(float *p, long n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_f32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, n, v);
+  return hipGetLastError();
+}
+
+}  // namespace mtp

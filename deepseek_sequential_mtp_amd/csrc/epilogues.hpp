@@ -1,0 +1,249 @@
+// GEMM epilogues.  Each receives the wave's accumulators acc[MB][NB] in the
+// 32x32 MFMA result layout (lane l, register r -> row 8*(r/4)+4*(l/32)+r%4,
+// column l%32 of block (i, j)) plus the tile origin.
+#pragma once
+
+#include "gemm.hpp"
+
+namespace mtp {
+
+// ---------------------------------------------------------------------------
+// C = alpha * acc (+ residual) (+ C if accumulate).  One K-split writes its
+// own slab C + split * split_stride.
+// ---------------------------------------------------------------------------
+template <typename OutT, typename ResT>
+struct EpiStore {
+  OutT *C; long ldc; int M, N; float alpha;
+  const float *alpha_dev;       // if set, alpha is read from device memory
+  const ResT *R; long ldr;      // residual added after scaling (nullable)
+  int accumulate;               // add into existing C (f32 outputs)
+  long split_stride;
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int split, char *) const {
+    OutT *Cs = C + split * split_stride;
+    const float al = alpha_dev != nullptr ? *alpha_dev : alpha;
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::NB; ++j) {
+        const int col = n0 + acc_col<Cfg>(wn, j, lane);
+        if (col >= N) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
+          if (row >= M) continue;
+          float v = al * acc[i][j][r];
+          if (R != nullptr) v += load_elem(R, (long)row * ldr + col);
+          const long o = (long)row * ldc + col;
+          if (accumulate) v += load_elem(Cs, o);
+          store_elem(Cs, o, v);
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fused QKV + rotate-half RoPE.  Output [M, 3*A] with q = cols [0, A),
+// k = [A, 2A), v = [2A, 3A).  q and k are rotated at position pos[row]:
+// with jj = j mod HALF (j = column inside the head), (c, s) = rope[pos][jj],
+//   out_j = x_j c - x_(j+HALF) s      (j <  HALF)
+//   out_j = x_j c + x_(j-HALF) s      (j >= HALF)
+// The partner column sits in the same lane, HALF/32 blocks away (HALF >= 32:
+// the wave's column range covers whole heads), or HALF lanes away (HALF < 32).
+// ---------------------------------------------------------------------------
+template <typename OutT, int HALF>
+struct EpiRope {
+  OutT *C; long ldc; int M, N, A;
+  const int *pos;               // [M] position of each row inside its run
+  const float2 *rope;           // [max_pos][HALF] (cos, sin); nullptr = no RoPE
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *) const {
+    constexpr int HD = 2 * HALF;
+    static_assert(HALF < 32 || (Cfg::WN % HD) == 0, "wave columns must cover whole heads");
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < Cfg::NB; ++j) {
+        const int col = n0 + acc_col<Cfg>(wn, j, lane);
+        const int jh = col % HD;
+        const bool lo = jh < HALF;
+        const int jj = lo ? jh : jh - HALF;
+        const bool rot = rope != nullptr && col < 2 * A;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float x = acc[i][j][r];
+          float partner;
+          if constexpr (HALF >= 32) {
+            constexpr int PB = HALF / 32;
+            partner = acc[i][j ^ PB][r];
+          } else {
+            partner = __shfl_xor(x, HALF);
+          }
+          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
+          if (row >= M || col >= N) continue;
+          float v = x;
+          if (rot) {
+            const float2 cs = rope[(long)pos[row] * HALF + jj];
+            v = lo ? (x * cs.x - partner * cs.y) : (x * cs.x + partner * cs.y);
+          }
+          store_elem(C, (long)row * ldc + col, v);
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Fused gate/up + SwiGLU (pairs with RowsSwiGLU): block j < NB/2 holds gate
+// features, block j + NB/2 the up features of the same columns.
+// out[row, feat] = silu(gate) * up, feat = tn*(BN/2) + wn*(WN/2) + j*32 + lane.
+// ---------------------------------------------------------------------------
+template <typename OutT>
+struct EpiSwiGLU {
+  OutT *C; long ldc; int M, f;
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *) const {
+    constexpr int NBh = Cfg::NB / 2;
+    const int tile_n = n0 / Cfg::BN;
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBh; ++j) {
+        const int feat = tile_n * (Cfg::BN / 2) + wn * (Cfg::WN / 2) + j * 32 + (lane & 31);
+        if (feat >= f) continue;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
+          if (row >= M) continue;
+          const float g = acc[i][j][r], u = acc[i][j + NBh][r];
+          const float s = g / (1.f + __expf(-g));
+          store_elem(C, (long)row * ldc + feat, s * u);
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Linear-CE forward, one BM x BN tile of logits z = x_hat W^T: per row, the
+// tile's max m_t and s_t = sum exp(z - m_t) over its valid columns go to
+// part[row * nt + tile_n] (float2), and the target logit z[row, label[row]]
+// to target[row] when the label falls in this tile.  Reductions go through
+// LDS (the staging buffers are free after the main loop).
+// ---------------------------------------------------------------------------
+struct EpiCEFwd {
+  const int *labels; float2 *part; float *target; int M, V, nt;
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *lds) const {
+    constexpr int LD = 65;   // 64 partials per row + 1 pad
+    float *red = reinterpret_cast<float *>(lds);
+    float *mrow = red + Cfg::BM * LD;
+    const int c32 = lane & 31;
+    const int slot = wn * 32 + c32;
+    // 1) per-lane max over the lane's columns of each of its rows
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < Cfg::NB; ++j) {
+          const int col = n0 + acc_col<Cfg>(wn, j, lane);
+          mx = col < V ? fmaxf(mx, acc[i][j][r]) : mx;
+        }
+        red[acc_row<Cfg>(wm, i, r, lane) * LD + slot] = mx;
+      }
+    // Slots 32..63 are written only by the wn = 1 waves; with NB blocks per
+    // wave both halves always exist, so all 64 slots are defined.
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < Cfg::BM) {
+      float mx = -INFINITY;
+      for (int s = 0; s < 64; ++s) mx = fmaxf(mx, red[t * LD + s]);
+      mrow[t] = mx;
+    }
+    __syncthreads();
+    // 2) per-lane sums of exp(z - m_row); capture the target logit
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rl = acc_row<Cfg>(wm, i, r, lane);
+        const int row = m0 + rl;
+        const float m = mrow[rl];
+        const int lab = row < M ? labels[row] : -1;
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < Cfg::NB; ++j) {
+          const int col = n0 + acc_col<Cfg>(wn, j, lane);
+          const float z = acc[i][j][r];
+          if (col < V) s += exp2f((z - m) * kLog2e);
+          if (col == lab) target[row] = z;
+        }
+        red[rl * LD + slot] = s;
+      }
+    __syncthreads();
+    if (t < Cfg::BM && m0 + t < M) {
+      float s = 0.f;
+      for (int q = 0; q < 64; ++q) s += red[t * LD + q];
+      part[(long)(m0 + t) * nt + n0 / Cfg::BN] = make_float2(mrow[t], s);
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// Linear-CE backward, recompute pass: dz = softmax(z) - onehot(label) on
+// labelled rows, 0 on the others, stored (unscaled) in OutT [M, ldz].  The
+// depth's scale lambda / (D * denom) is applied by the consuming GEMMs.
+// ---------------------------------------------------------------------------
+template <typename OutT>
+struct EpiCEGrad {
+  const int *labels; const float *lse; OutT *dz; long ldz; int M, V;
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *) const {
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
+        if (row >= M) continue;
+        const int lab = labels[row];
+        const float l = lse[row];
+#pragma unroll
+        for (int j = 0; j < Cfg::NB; ++j) {
+          const int col = n0 + acc_col<Cfg>(wn, j, lane);
+          if (col >= V) continue;
+          float g = 0.f;
+          if (lab >= 0) g = exp2f((acc[i][j][r] - l) * kLog2e) - (col == lab ? 1.f : 0.f);
+          store_elem(dz, (long)row * ldz + col, g);
+        }
+      }
+  }
+};
+
+template <typename T, class Cfg, class LA, class LB, class Epi>
+__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
+  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
+  gemm_body<T, Cfg>(la, lb, epi, K, ts, lds);
+}
+
+// Host-side launch helper (grid = tiles * K splits, one block per tile).
+template <typename T, class Cfg, class LA, class LB, class Epi>
+inline hipError_t launch_gemm(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K,
+                              int group_m, int k_splits, hipStream_t stream) {
+  TileSched ts;
+  ts.mt = (M + Cfg::BM - 1) / Cfg::BM;
+  ts.nt = (N + Cfg::BN - 1) / Cfg::BN;
+  ts.group_m = group_m < 1 ? 1 : (group_m > ts.mt ? ts.mt : group_m);
+  ts.k_splits = k_splits < 1 ? 1 : k_splits;
+  const long tiles = (long)ts.mt * ts.nt * ts.k_splits;
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)tiles), dim3(kGemmThreads), 0,
+                     stream, la, lb, epi, K, ts);
+  return hipGetLastError();
+}
+
+}  // namespace mtp

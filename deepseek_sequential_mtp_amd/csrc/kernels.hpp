@@ -1,0 +1,61 @@
+// Internal launch interface of the kernels (host side).  Not part of the
+// public ABI; mtp_api.hip is the only caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace mtp {
+
+// K1 rows / masks / labels / counts
+hipError_t launch_rows(const int32_t *tokens, const int32_t *seg, int B, int T, int V, int D,
+                       int32_t *run_start, int32_t *pos, uint8_t *state_mask, uint8_t *loss_mask,
+                       int32_t *labels, int32_t *counts, int32_t *device_error, int32_t *cnt_part,
+                       int32_t *err_part, hipStream_t s);
+
+// norms
+template <typename T>
+hipError_t launch_dual_norm_concat(const T *h, const T *E, const int32_t *tokens, const float *g_h,
+                                   const float *g_e, T *c, int B, int T_len, int d, int V, int depth,
+                                   float eps, hipStream_t s);
+template <typename TI, typename TO>
+hipError_t launch_rmsnorm(const TI *z, const float *g, TO *out, float *r, long rows, int d, float eps,
+                          hipStream_t s);
+template <typename T>
+hipError_t launch_out_norm(const T *h, const float *g, T *xhat, float *r, const int32_t *labels_in,
+                           int32_t *labels_out, int32_t *err, long rows, int d, int V, float eps,
+                           hipStream_t s);
+template <typename T>
+hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *h, const float *r,
+                               const float *g, float *dh, float *dg_part, float *dg, int accumulate,
+                               int N, int d, hipStream_t s);
+inline int dg_row_blocks(int N) { int b = (N + 255) / 256; return b < 1 ? 1 : (b > 64 ? 64 : b); }
+
+// attention
+template <typename T>
+hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, int B, int T_len, int H,
+                            int hd, hipStream_t s);
+hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s);
+
+// CE reductions
+hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
+                             float *lse, float *lse_out, float *row_loss, int N, hipStream_t s);
+hipError_t launch_ce_reduce(const float *row_loss, const int32_t *labels, int N, int k, int D,
+                            int reduce_valid_mean, double denom, float lambda, double *acc_sum,
+                            int32_t *acc_cnt, float *scale, hipStream_t s);
+hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int D,
+                              int reduce_valid_mean, double denom, float lambda, float *loss_sum,
+                              int32_t *counts, float *loss, float *loss_mtp, hipStream_t s);
+
+// verify
+hipError_t launch_verify(const void *zt, const void *zd, int bf16, const int32_t *y, const float *ua,
+                         const float *us, int R, int G, int V, float tau, int32_t *A, int32_t *tok,
+                         int32_t *status, float *margin, double *ws, hipStream_t s);
+
+// small utilities
+hipError_t fill_i32(int32_t *p, long n, int32_t v, hipStream_t s);
+hipError_t fill_f32(float *p, long n, float v, hipStream_t s);
+
+}  // namespace mtp

@@ -1,0 +1,487 @@
+// C ABI of the library (declared in include/mtp.h): argument checks,
+// workspace layout and the launch sequence of each entry point.  All
+// launches go to the caller's stream; nothing here synchronises the host.
+#include <math.h>
+#include <string.h>
+
+#include "../../include/mtp.h"
+#include "epilogues.hpp"
+#include "kernels.hpp"
+
+using namespace mtp;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+struct Carve {
+  char *base;
+  size_t off = 0;
+  explicit Carve(void *b) : base(static_cast<char *>(b)) {}
+  template <typename P>
+  P *take(size_t count) {
+    off = (off + kAlign - 1) / kAlign * kAlign;
+    P *p = base ? reinterpret_cast<P *>(base + off) : nullptr;
+    off += count * sizeof(P);
+    return p;
+  }
+};
+
+inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
+
+#define MTP_TRY(expr)                        \
+  do {                                       \
+    hipError_t e_ = (expr);                  \
+    if (e_ != hipSuccess) return MTP_ERR_HIP; \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// GEMM dispatch.  The 256x256 tile is used when it still yields at least one
+// tile per compute unit; otherwise 128x128.
+// ---------------------------------------------------------------------------
+using Big = Tile<256, 256>;
+using Small = Tile<128, 128>;
+
+inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N, 256) >= 256; }
+
+template <typename T, typename OutT, typename ResT>
+int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc, const ResT *R, long ldr,
+                  int M, int N, int K, float alpha, const float *alpha_dev, int accumulate, hipStream_t s) {
+  EpiStore<OutT, ResT> epi{C, ldc, M, N, alpha, alpha_dev, R, ldr, accumulate, 0};
+  if constexpr (sizeof(T) == 2) {
+    if (use_big(M, N)) {
+      LoadKMajor<T, Big::BM, RowsDense<T>> la{{A, lda, M}, K};
+      LoadKMajor<T, Big::BN, RowsDense<T>> lb{{Bm, ldb, N}, K};
+      MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, N, K, 8, 1, s)));
+      return MTP_OK;
+    }
+  }
+  {
+    LoadKMajor<T, Small::BM, RowsDense<T>> la{{A, lda, M}, K};
+    LoadKMajor<T, Small::BN, RowsDense<T>> lb{{Bm, ldb, N}, K};
+    MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, N, K, 8, 1, s)));
+  }
+  return MTP_OK;
+}
+
+template <typename T, int HALF, class Cfg>
+int gemm_qkv_rope_cfg(const T *xa, const T *W, T *qkv, const int *pos, const float2 *rope, int M, int d,
+                      int A, hipStream_t s) {
+  const int N = 3 * A;
+  EpiRope<T, HALF> epi{qkv, (long)N, M, N, A, pos, rope};
+  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xa, (long)d, M}, d};
+  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, N}, d};
+  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, N, d, 8, 1, s)));
+  return MTP_OK;
+}
+
+template <typename T>
+int gemm_qkv_rope(const T *xa, const T *W, T *qkv, const int *pos, const float2 *rope, int M, int d, int A,
+                  int hd, hipStream_t s) {
+  // The wave's column range (WN) must cover whole heads for HALF >= 32.
+  if constexpr (sizeof(T) == 2) {
+    switch (hd) {
+      case 32: return gemm_qkv_rope_cfg<T, 16, Big>(xa, W, qkv, pos, rope, M, d, A, s);
+      case 64: return gemm_qkv_rope_cfg<T, 32, Big>(xa, W, qkv, pos, rope, M, d, A, s);
+      case 128: return gemm_qkv_rope_cfg<T, 64, Big>(xa, W, qkv, pos, rope, M, d, A, s);
+      default: return MTP_ERR_UNSUPPORTED;
+    }
+  } else switch (hd) {
+    case 16: return gemm_qkv_rope_cfg<T, 8, Small>(xa, W, qkv, pos, rope, M, d, A, s);
+    case 32: return gemm_qkv_rope_cfg<T, 16, Small>(xa, W, qkv, pos, rope, M, d, A, s);
+    case 64: return gemm_qkv_rope_cfg<T, 32, Small>(xa, W, qkv, pos, rope, M, d, A, s);
+    default: return MTP_ERR_UNSUPPORTED;
+  }
+}
+
+template <typename T>
+int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, hipStream_t s) {
+  if constexpr (sizeof(T) == 2) {
+    if (use_big(M, 2L * f)) {
+      EpiSwiGLU<T> epi{out, (long)f, M, f};
+      LoadKMajor<T, Big::BM, RowsDense<T>> la{{y, (long)d, M}, d};
+      LoadKMajor<T, Big::BN, RowsSwiGLU<T, Big::BN>> lb{{Wg, Wu, (long)d, f}, d};
+      MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, 1, s)));
+      return MTP_OK;
+    }
+  }
+  {
+    EpiSwiGLU<T> epi{out, (long)f, M, f};
+    LoadKMajor<T, Small::BM, RowsDense<T>> la{{y, (long)d, M}, d};
+    LoadKMajor<T, Small::BN, RowsSwiGLU<T, Small::BN>> lb{{Wg, Wu, (long)d, f}, d};
+    MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, 2 * ceil_div(f, Small::BN / 2) * (Small::BN / 2), d, 8,
+                                   1, s)));
+  }
+  return MTP_OK;
+}
+
+template <typename T, class Cfg>
+int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, int M, int V,
+                    int d, hipStream_t s) {
+  const int nt = ceil_div(V, Cfg::BN);
+  EpiCEFwd epi{lab, part, target, M, V, nt};
+  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xhat, (long)d, M}, d};
+  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, V}, d};
+  // all row tiles of one vocabulary tile run next to each other: W is read once
+  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
+  return MTP_OK;
+}
+
+template <typename T, class Cfg>
+int gemm_ce_grad_cfg(const T *xhat, const T *W, const int *lab, const float *lse, T *dz, int M, int V, int d,
+                     hipStream_t s) {
+  EpiCEGrad<T> epi{lab, lse, dz, (long)V, M, V};
+  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xhat, (long)d, M}, d};
+  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, V}, d};
+  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
+  return MTP_OK;
+}
+
+// dx[split] = scale * dz[:, split range] W_out[split range, :]  (B operand MN-major)
+template <typename T, class Cfg>
+int gemm_dx_cfg(const T *dz, const T *W, float *dxs, long slab, int M, int V, int d, const float *scale,
+                int splits, hipStream_t s) {
+  EpiStore<float, float> epi{dxs, (long)d, M, d, 1.f, scale, nullptr, 0, 0, slab};
+  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{dz, (long)V, M}, V};
+  LoadMNMajor<T, Cfg::BN> lb{W, (long)d, d, V};
+  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, d, V, 8, splits, s)));
+  return MTP_OK;
+}
+
+// dW (+)= scale * dz^T xhat  (both operands MN-major)
+template <typename T, class Cfg>
+int gemm_dw_cfg(const T *dz, const T *xhat, float *dW, int M, int V, int d, const float *scale, int accumulate,
+                hipStream_t s) {
+  EpiStore<float, float> epi{dW, (long)d, V, d, 1.f, scale, nullptr, 0, accumulate, 0};
+  LoadMNMajor<T, Cfg::BM> la{dz, (long)V, V, M};
+  LoadMNMajor<T, Cfg::BN> lb{xhat, (long)d, d, M};
+  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, V, d, M, 8, 1, s)));
+  return MTP_OK;
+}
+
+// Run f with the 256x256 tile (bf16 and `big`) or the 128x128 tile.
+template <typename T, class F>
+int pick(bool big, F &&f) {
+  if constexpr (sizeof(T) == 2) {
+    if (big) return f(Big{});
+  }
+  return f(Small{});
+}
+
+// K-split count for the dx GEMM: fill the 256 compute units with whole waves
+// of tiles while keeping each split long.
+inline int dx_splits(int M, int d, int V, bool big) {
+  const long tiles = (long)ceil_div(M, big ? 256 : 128) * ceil_div(d, big ? 256 : 128);
+  int best = 1;
+  double best_cost = 1e300;
+  for (int s = 1; s <= 8; s *= 2) {
+    const double waves = ceil((double)tiles * s / 256.0);
+    const double cost = waves * ((double)V / s) + 0.02 * V * s;   // + slab traffic
+    if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
+  }
+  return best;
+}
+
+// ---------------------------------------------------------------------------
+// argument checks
+// ---------------------------------------------------------------------------
+int check_chain(const mtp_chain_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->D < 1) return MTP_ERR_DEPTH;
+  if (a->dtype != MTP_F32 && a->dtype != MTP_BF16) return MTP_ERR_DTYPE;
+  if (a->B < 1 || a->T < 1 || a->d < 1 || a->n_heads < 1 || a->head_dim < 2 || a->ffn < 1 || a->V < 1)
+    return MTP_ERR_SHAPE;
+  if (a->head_dim % 2) return MTP_ERR_SHAPE;
+  const int E = a->dtype == MTP_BF16 ? 8 : 4;
+  const int A = a->n_heads * a->head_dim;
+  if (a->d % E || a->ffn % E || A % E) return MTP_ERR_SHAPE;
+  if ((long)a->B * a->T > (1L << 30) || (long)a->V * a->d > (1L << 40)) return MTP_ERR_SHAPE;
+  if (a->dtype == MTP_BF16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return MTP_ERR_UNSUPPORTED;
+  if (a->dtype == MTP_F32 && a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64)
+    return MTP_ERR_UNSUPPORTED;
+  if (!(a->eps >= 0.f) || !(a->rope_theta >= 0.f)) return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+int check_chain_ptrs(const mtp_chain_args *a) {
+  if (!a->tokens || !a->segment_ids || !a->h0 || !a->embed || !a->w || !a->h_out || !a->state_mask ||
+      !a->loss_mask || !a->labels || !a->counts || !a->device_error)
+    return MTP_ERR_NULL;
+  for (int k = 0; k < a->D; ++k) {
+    const mtp_depth_weights &w = a->w[k];
+    if (!w.g_h || !w.g_e || !w.g_attn || !w.g_ffn || !w.M || !w.Wqkv || !w.Wo || !w.Wgate || !w.Wup ||
+        !w.Wdown || !a->h_out[k])
+      return MTP_ERR_NULL;
+  }
+  return MTP_OK;
+}
+
+template <typename T>
+size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
+  const long N = (long)a->B * a->T;
+  const int d = a->d, A = a->n_heads * a->head_dim, f = a->ffn;
+  parts[0] = c.take<int32_t>(N);                              // run_start
+  parts[1] = c.take<int32_t>(N);                              // pos
+  parts[2] = c.take<int32_t>((size_t)a->D * a->B);             // cnt_part
+  parts[3] = c.take<int32_t>(a->B);                            // err_part
+  parts[4] = c.take<float2>((size_t)a->T * (a->head_dim / 2)); // rope table
+  parts[5] = c.take<T>(N * 2 * d);                             // c
+  parts[6] = c.take<float>(N * d);                             // u (residual stream, f32)
+  parts[7] = c.take<T>(N * d);                                 // x_a
+  parts[8] = c.take<T>(N * 3 * (long)A);                       // qkv
+  parts[9] = c.take<T>(N * (long)A);                           // o
+  parts[10] = c.take<float>(N * d);                            // a (residual stream, f32)
+  parts[11] = c.take<T>(N * d);                                // y
+  parts[12] = c.take<T>(N * (long)f);                          // silu(gate) * up
+  return c.off;
+}
+
+template <typename T>
+int chain_run(const mtp_chain_args *a, hipStream_t s) {
+  void *p[13];
+  Carve c(a->workspace);
+  chain_layout<T>(a, c, p);
+  const int B = a->B, Tl = a->T, d = a->d, H = a->n_heads, hd = a->head_dim, f = a->ffn, V = a->V;
+  const int A = H * hd;
+  const int N = B * Tl;
+  int32_t *run_start = (int32_t *)p[0], *pos = (int32_t *)p[1];
+  float2 *rope = (float2 *)p[4];
+  T *cbuf = (T *)p[5], *xa = (T *)p[7], *qkv = (T *)p[8], *o = (T *)p[9];
+  float *u = (float *)p[6];
+  float *abuf = (float *)p[10];
+  T *ybuf = (T *)p[11], *gsw = (T *)p[12];
+
+  MTP_TRY(launch_rows(a->tokens, a->segment_ids, B, Tl, V, a->D, run_start, pos, a->state_mask, a->loss_mask,
+                      a->labels, a->counts, a->device_error, (int32_t *)p[2], (int32_t *)p[3], s));
+  const bool use_rope = a->rope_theta > 0.f;
+  if (use_rope) MTP_TRY(rope_table(rope, Tl, hd / 2, a->rope_theta, s));
+
+  const T *h_prev = static_cast<const T *>(a->h0);
+  const T *E = static_cast<const T *>(a->embed);
+  for (int k = 1; k <= a->D; ++k) {
+    const mtp_depth_weights &w = a->w[k - 1];
+    T *h_out = static_cast<T *>(a->h_out[k - 1]);
+    MTP_TRY(launch_dual_norm_concat<T>(h_prev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
+    int st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d,
+                                            1.f, nullptr, 0, s);
+    if (st) return st;
+    MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
+    st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, s);
+    if (st) return st;
+    MTP_TRY(launch_attention<T>(qkv, o, run_start, B, Tl, H, hd, s));
+    st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0, s);
+    if (st) return st;
+    MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
+    st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, s);
+    if (st) return st;
+    st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
+                                    s);
+    if (st) return st;
+    h_prev = h_out;
+  }
+  return MTP_OK;
+}
+
+int check_ce(const mtp_ce_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->D < 1) return MTP_ERR_DEPTH;
+  if (a->dtype != MTP_F32 && a->dtype != MTP_BF16) return MTP_ERR_DTYPE;
+  if (a->B < 1 || a->T < 1 || a->d < 1 || a->V < 1) return MTP_ERR_SHAPE;
+  const int E = a->dtype == MTP_BF16 ? 8 : 4;
+  if (a->d % E || a->V % E) return MTP_ERR_SHAPE;
+  if ((long)a->B * a->T > (1L << 30)) return MTP_ERR_SHAPE;
+  if (a->reduce != MTP_REDUCE_FIXED && a->reduce != MTP_REDUCE_VALID_MEAN) return MTP_ERR_ARG;
+  if (a->reduce == MTP_REDUCE_FIXED && !(a->denom >= 0.0)) return MTP_ERR_ARG;
+  if (!(a->eps >= 0.f) || !isfinite(a->lambda)) return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+int check_ce_ptrs(const mtp_ce_args *a) {
+  if (!a->h || !a->labels || !a->W_out || !a->g_out || !a->loss_sum || !a->counts || !a->loss ||
+      !a->loss_mtp || !a->dh || !a->dW_out || !a->dg_out)
+    return MTP_ERR_NULL;
+  for (int k = 0; k < a->D; ++k)
+    if (!a->h[k] || !a->dh[k]) return MTP_ERR_NULL;
+  return MTP_OK;
+}
+
+struct CeDims {
+  long N; int d, V, nt, splits; bool big;
+};
+
+template <typename T>
+CeDims ce_dims(const mtp_ce_args *a) {
+  CeDims c;
+  c.N = (long)a->B * a->T;
+  c.d = a->d;
+  c.V = a->V;
+  c.big = sizeof(T) == 2 && use_big(c.N, c.V);
+  c.nt = ceil_div(c.V, c.big ? 256 : 128);
+  const bool big_dx = sizeof(T) == 2 && use_big(c.N, c.d);
+  c.splits = dx_splits((int)c.N, c.d, c.V, big_dx);
+  return c;
+}
+
+template <typename T>
+size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
+  const CeDims m = ce_dims<T>(a);
+  p[0] = c.take<T>(m.N * m.d);                   // x_hat
+  p[1] = c.take<float>(m.N);                     // r = 1 / rms
+  p[2] = c.take<int32_t>(m.N);                   // sanitised labels
+  p[3] = c.take<float2>(m.N * m.nt);             // (max, sumexp) per row and vocab tile
+  p[4] = c.take<float>(m.N);                     // target logit
+  p[5] = c.take<float>(m.N);                     // lse
+  p[6] = c.take<float>(m.N);                     // row loss
+  p[7] = c.take<double>(a->D);                   // loss sums
+  p[8] = c.take<int32_t>(a->D);                  // counts
+  p[9] = c.take<float>(a->D);                    // backward scales
+  p[10] = c.take<T>(m.N * m.V);                  // dz = softmax - onehot
+  p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
+  p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
+  return c.off;
+}
+
+template <typename T>
+int ce_run(const mtp_ce_args *a, hipStream_t s) {
+  void *p[13];
+  Carve c(a->workspace);
+  ce_layout<T>(a, c, p);
+  const CeDims m = ce_dims<T>(a);
+  const int N = (int)m.N, d = m.d, V = m.V, D = a->D;
+  T *xhat = (T *)p[0];
+  float *r = (float *)p[1];
+  int32_t *lab = (int32_t *)p[2];
+  float2 *part = (float2 *)p[3];
+  float *target = (float *)p[4], *lse = (float *)p[5], *row_loss = (float *)p[6];
+  double *acc_sum = (double *)p[7];
+  int32_t *acc_cnt = (int32_t *)p[8];
+  float *scale = (float *)p[9];
+  T *dz = (T *)p[10];
+  float *dxs = (float *)p[11];
+  float *dg_part = (float *)p[12];
+  const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
+  const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
+  const long slab = m.N * m.d;
+  if (a->device_error) MTP_TRY(fill_i32(a->device_error, 1, 0, s));
+
+  for (int k = 0; k < D; ++k) {
+    const T *h = static_cast<const T *>(a->h[k]);
+    MTP_TRY(launch_out_norm<T>(h, a->g_out, xhat, r, a->labels + (long)k * N, lab, a->device_error, N, d, V,
+                               a->eps, s));
+    int st = pick<T>(m.big, [&](auto cfg) {
+      return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, N, V, d, s);
+    });
+    if (st) return st;
+    MTP_TRY(launch_ce_combine(part, m.nt, target, lab, lse, a->lse ? a->lse + (long)k * N : nullptr, row_loss,
+                              N, s));
+    MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
+    st = pick<T>(m.big, [&](auto cfg) {
+      return gemm_ce_grad_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, lse, dz, N, V, d, s);
+    });
+    if (st) return st;
+    const bool big_dx = sizeof(T) == 2 && use_big(N, d);
+    st = pick<T>(big_dx, [&](auto cfg) {
+      return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs, slab, N, V, d, scale + k, m.splits, s);
+    });
+    if (st) return st;
+    const int acc = (k > 0 || a->accumulate) ? 1 : 0;
+    MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, slab, h, r, a->g_out, static_cast<float *>(a->dh[k]), dg_part,
+                                   a->dg_out, acc, N, d, s));
+    const bool big_dw = sizeof(T) == 2 && use_big(V, d);
+    st = pick<T>(big_dw, [&](auto cfg) {
+      return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat, a->dW_out, N, V, d, scale + k, acc, s);
+    });
+    if (st) return st;
+  }
+  MTP_TRY(launch_ce_finalize(acc_sum, acc_cnt, D, valid_mean, denom, a->lambda, a->loss_sum, a->counts, a->loss,
+                             a->loss_mtp, s));
+  return MTP_OK;
+}
+
+int check_verify(const mtp_verify_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->logits_dtype != MTP_F32 && a->logits_dtype != MTP_BF16) return MTP_ERR_DTYPE;
+  if (a->R < 1 || a->gamma < 1 || a->V < 1) return MTP_ERR_SHAPE;
+  if ((long)a->R * (2 * a->gamma + 1) > (1L << 31) - 1) return MTP_ERR_SHAPE;
+  if (!(a->temperature > 0.f) || !isfinite(a->temperature)) return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+size_t verify_bytes(const mtp_verify_args *a) {
+  return (size_t)a->R * (2 * a->gamma + 1) * 2 * sizeof(double);
+}
+
+}  // namespace
+
+extern "C" {
+
+int mtp_abi_version(void) { return 1; }
+
+const char *mtp_strerror(int status) {
+  switch (status) {
+    case MTP_OK: return "ok";
+    case MTP_ERR_NULL: return "a required pointer is NULL";
+    case MTP_ERR_SHAPE: return "invalid or unsupported shape";
+    case MTP_ERR_DEPTH: return "depth must be positive";
+    case MTP_ERR_DTYPE: return "unknown dtype";
+    case MTP_ERR_WORKSPACE: return "workspace missing or too small";
+    case MTP_ERR_ARG: return "invalid argument";
+    case MTP_ERR_HIP: return "HIP launch failed";
+    case MTP_ERR_UNSUPPORTED: return "configuration not supported by the kernels";
+    default: return "unknown status";
+  }
+}
+
+size_t mtp_chain_workspace_size(const mtp_chain_args *a) {
+  if (check_chain(a) != MTP_OK) return 0;
+  Carve c(nullptr);
+  void *p[13];
+  return a->dtype == MTP_BF16 ? chain_layout<bf16_t>(a, c, p) : chain_layout<float>(a, c, p);
+}
+
+int mtp_chain_forward(const mtp_chain_args *a, void *stream) {
+  int st = check_chain(a);
+  if (st) return st;
+  if ((st = check_chain_ptrs(a))) return st;
+  if (!a->workspace || a->workspace_bytes < mtp_chain_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return a->dtype == MTP_BF16 ? chain_run<bf16_t>(a, s) : chain_run<float>(a, s);
+}
+
+size_t mtp_ce_workspace_size(const mtp_ce_args *a) {
+  if (check_ce(a) != MTP_OK) return 0;
+  Carve c(nullptr);
+  void *p[13];
+  return a->dtype == MTP_BF16 ? ce_layout<bf16_t>(a, c, p) : ce_layout<float>(a, c, p);
+}
+
+int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream) {
+  int st = check_ce(a);
+  if (st) return st;
+  if ((st = check_ce_ptrs(a))) return st;
+  if (!a->workspace || a->workspace_bytes < mtp_ce_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return a->dtype == MTP_BF16 ? ce_run<bf16_t>(a, s) : ce_run<float>(a, s);
+}
+
+size_t mtp_verify_workspace_size(const mtp_verify_args *a) {
+  if (check_verify(a) != MTP_OK) return 0;
+  return verify_bytes(a);
+}
+
+int mtp_verify(const mtp_verify_args *a, void *stream) {
+  int st = check_verify(a);
+  if (st) return st;
+  if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->u_accept || !a->u_sample ||
+      !a->accepted_len || !a->next_token || !a->status)
+    return MTP_ERR_NULL;
+  if (!a->workspace || a->workspace_bytes < verify_bytes(a)) return MTP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  MTP_TRY(launch_verify(a->target_logits, a->draft_logits, a->logits_dtype == MTP_BF16 ? 1 : 0, a->draft_tokens,
+                        a->u_accept, a->u_sample, a->R, a->gamma, a->V, a->temperature, a->accepted_len,
+                        a->next_token, a->status, a->margin, static_cast<double *>(a->workspace), s));
+  return MTP_OK;
+}
+
+}  // extern "C"

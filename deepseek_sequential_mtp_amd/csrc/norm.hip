@@ -1,0 +1,228 @@
+// Bandwidth-bound row kernels: the dual RMSNorm + concat that feeds eh_proj
+// (K2), the block pre-norms, the shared output norm (K9) and its backward.
+//
+// RMSNorm_g(z) = g * z / sqrt(mean(z^2) + eps) (M7.6 0x03C); statistics in
+// float32.  One 256-thread block per row, 16-byte chunk accesses.
+#include "kernels.hpp"
+
+namespace mtp {
+
+namespace {
+constexpr int kNormThreads = 256;
+
+__device__ __forceinline__ float block_sum(float v, float *sh) {
+  v = warp_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  __syncthreads();
+  if (lane == 0) sh[w] = v;
+  __syncthreads();
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kNormThreads / 64; ++i) s += sh[i];
+  return s;
+}
+
+template <typename T>
+__device__ float row_sumsq(const T *row, int d) {
+  constexpr int E = Elem<T>::kPerChunk;
+  float acc = 0.f;
+  for (int c = threadIdx.x; c < d / E; c += kNormThreads) {
+    float v[E];
+    chunk_to_f32(reinterpret_cast<const uint4 *>(row)[c], v, T{});
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc += v[e] * v[e];
+  }
+  return acc;
+}
+
+template <typename TI, typename TO>
+__device__ void row_scale_store(const TI *row, const float *g, float s, TO *out, int d) {
+  constexpr int E = Elem<TI>::kPerChunk;
+  for (int c = threadIdx.x; c < d / E; c += kNormThreads) {
+    float v[E];
+    chunk_to_f32(reinterpret_cast<const uint4 *>(row)[c], v, TI{});
+#pragma unroll
+    for (int e = 0; e < E; ++e) store_elem(out, (long)c * E + e, g[c * E + e] * v[e] * s);
+  }
+}
+}  // namespace
+
+// c[n] = [ g_h * h[n] * s_h ; g_e * E[x(b, i+k)] * s_e ]  (he order)
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void dual_norm_concat_kernel(
+    const T *__restrict__ h, const T *__restrict__ E, const int32_t *__restrict__ tokens,
+    const float *__restrict__ g_h, const float *__restrict__ g_e, T *__restrict__ c, int T_len, int d,
+    int V, int depth, float eps) {
+  __shared__ float sh[kNormThreads / 64];
+  const long n = blockIdx.x;
+  const int b = (int)(n / T_len), i = (int)(n % T_len);
+  int ti = i + depth;
+  ti = ti < T_len ? ti : T_len - 1;              // rows with no x_(i+k): any valid id
+  int tok = tokens[(long)b * T_len + ti];
+  tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
+  const T *hr = h + n * d;
+  const T *er = E + (long)tok * d;
+  const float sh_h = block_sum(row_sumsq(hr, d), sh);
+  const float sh_e = block_sum(row_sumsq(er, d), sh);
+  const float s_h = rsqrtf(sh_h / d + eps);
+  const float s_e = rsqrtf(sh_e / d + eps);
+  T *cr = c + n * 2 * (long)d;
+  row_scale_store(hr, g_h, s_h, cr, d);
+  row_scale_store(er, g_e, s_e, cr + d, d);
+}
+
+// out[n] = g * z[n] / rms(z[n]); optionally r[n] = 1 / rms.
+template <typename TI, typename TO>
+__global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const TI *__restrict__ z,
+                                                              const float *__restrict__ g,
+                                                              TO *__restrict__ out, float *__restrict__ r,
+                                                              int d, float eps) {
+  __shared__ float sh[kNormThreads / 64];
+  const long n = blockIdx.x;
+  const TI *zr = z + n * d;
+  const float s = rsqrtf(block_sum(row_sumsq(zr, d), sh) / d + eps);
+  if (r != nullptr && threadIdx.x == 0) r[n] = s;
+  row_scale_store(zr, g, s, out + n * d, d);
+}
+
+// Shared output norm for one depth plus label sanitising: labels outside
+// [-1, V) become -1 and raise the error flag.
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void out_norm_kernel(
+    const T *__restrict__ h, const float *__restrict__ g, T *__restrict__ xhat, float *__restrict__ r,
+    const int32_t *__restrict__ labels_in, int32_t *__restrict__ labels_out, int32_t *__restrict__ err,
+    int d, int V, float eps) {
+  __shared__ float sh[kNormThreads / 64];
+  const long n = blockIdx.x;
+  const T *hr = h + n * d;
+  const float s = rsqrtf(block_sum(row_sumsq(hr, d), sh) / d + eps);
+  if (threadIdx.x == 0) {
+    r[n] = s;
+    int lab = labels_in[n];
+    if (lab < -1 || lab >= V) {
+      if (err != nullptr) atomicOr(err, 1);
+      lab = -1;
+    }
+    labels_out[n] = lab;
+  }
+  row_scale_store(hr, g, s, xhat + n * d, d);
+}
+
+// RMSNorm backward through the output norm:
+//   dh = r (g * dx - x_n * mean(x_n * g * dx)),  x_n = r h,
+// with dx = sum of `splits` partial slabs (stride slab).
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void out_norm_bwd_kernel(
+    const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h,
+    const float *__restrict__ r, const float *__restrict__ g, float *__restrict__ dh, int d) {
+  __shared__ float sh[kNormThreads / 64];
+  const long n = blockIdx.x;
+  const float rn = r[n];
+  const T *hr = h + n * d;
+  float acc = 0.f;
+  for (int j = threadIdx.x; j < d; j += kNormThreads) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += dx[s * slab + n * d + j];
+    acc += rn * load_elem(hr, j) * g[j] * v;
+  }
+  const float mean = block_sum(acc, sh) / d;
+  for (int j = threadIdx.x; j < d; j += kNormThreads) {
+    float v = 0.f;
+    for (int s = 0; s < splits; ++s) v += dx[s * slab + n * d + j];
+    const float xn = rn * load_elem(hr, j);
+    dh[n * d + j] = rn * (g[j] * v - xn * mean);
+  }
+}
+
+// dg partials: part[rb][j] = sum over rows in row block rb of dx[n][j] * x_n[n][j].
+template <typename T>
+__global__ __launch_bounds__(kNormThreads) void dg_partial_kernel(
+    const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h,
+    const float *__restrict__ r, float *__restrict__ part, int N, int d, int rows_per_block) {
+  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int rg = threadIdx.x >> 6;
+  const int n0 = blockIdx.y * rows_per_block;
+  const int n1 = min(N, n0 + rows_per_block);
+  __shared__ float sh[4][64];
+  float acc = 0.f;
+  if (j < d) {
+    for (int n = n0 + rg; n < n1; n += 4) {
+      float v = 0.f;
+      for (int s = 0; s < splits; ++s) v += dx[s * slab + (long)n * d + j];
+      acc += v * r[n] * load_elem(h, (long)n * d + j);
+    }
+  }
+  sh[rg][threadIdx.x & 63] = acc;
+  __syncthreads();
+  if (rg == 0 && j < d)
+    part[(long)blockIdx.y * d + j] = sh[0][threadIdx.x] + sh[1][threadIdx.x] + sh[2][threadIdx.x] +
+                                     sh[3][threadIdx.x];
+}
+
+// dg[j] (+)= sum_rb part[rb][j], in row-block order.
+__global__ void dg_reduce_kernel(const float *__restrict__ part, int nrb, int d, float *__restrict__ dg,
+                                 int accumulate) {
+  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+  if (j >= d) return;
+  float s = 0.f;
+  for (int b = 0; b < nrb; ++b) s += part[(long)b * d + j];
+  dg[j] = accumulate ? dg[j] + s : s;
+}
+
+// ---------------------------------------------------------------------------
+template <typename T>
+hipError_t launch_dual_norm_concat(const T *h, const T *E, const int32_t *tokens, const float *g_h,
+                                   const float *g_e, T *c, int B, int T_len, int d, int V, int depth,
+                                   float eps, hipStream_t s) {
+  hipLaunchKernelGGL(dual_norm_concat_kernel<T>, dim3(B * T_len), dim3(kNormThreads), 0, s, h, E, tokens,
+                     g_h, g_e, c, T_len, d, V, depth, eps);
+  return hipGetLastError();
+}
+template <typename TI, typename TO>
+hipError_t launch_rmsnorm(const TI *z, const float *g, TO *out, float *r, long rows, int d, float eps,
+                          hipStream_t s) {
+  hipLaunchKernelGGL((rmsnorm_kernel<TI, TO>), dim3(rows), dim3(kNormThreads), 0, s, z, g, out, r, d, eps);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t launch_out_norm(const T *h, const float *g, T *xhat, float *r, const int32_t *labels_in,
+                           int32_t *labels_out, int32_t *err, long rows, int d, int V, float eps,
+                           hipStream_t s) {
+  hipLaunchKernelGGL(out_norm_kernel<T>, dim3(rows), dim3(kNormThreads), 0, s, h, g, xhat, r, labels_in,
+                     labels_out, err, d, V, eps);
+  return hipGetLastError();
+}
+template <typename T>
+hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *h, const float *r,
+                               const float *g, float *dh, float *dg_part, float *dg, int accumulate,
+                               int N, int d, hipStream_t s) {
+  hipLaunchKernelGGL(out_norm_bwd_kernel<T>, dim3(N), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g,
+                     dh, d);
+  const int nrb = dg_row_blocks(N);
+  const int rpb = (N + nrb - 1) / nrb;
+  hipLaunchKernelGGL(dg_partial_kernel<T>, dim3((d + 63) / 64, nrb), dim3(kNormThreads), 0, s, dx, splits,
+                     slab, h, r, dg_part, N, d, rpb);
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3((d + 255) / 256), dim3(256), 0, s, dg_part, nrb, d, dg,
+                     accumulate);
+  return hipGetLastError();
+}
+
+#define MTP_NORM_INST(T)                                                                                  \
+  template hipError_t launch_dual_norm_concat<T>(const T *, const T *, const int32_t *, const float *,    \
+                                                 const float *, T *, int, int, int, int, int, float,      \
+                                                 hipStream_t);                                            \
+  template hipError_t launch_out_norm<T>(const T *, const float *, T *, float *, const int32_t *,         \
+                                         int32_t *, int32_t *, long, int, int, float, hipStream_t);       \
+  template hipError_t launch_out_norm_bwd<T>(const float *, int, long, const T *, const float *,          \
+                                             const float *, float *, float *, float *, int, int, int,     \
+                                             hipStream_t);
+MTP_NORM_INST(bf16_t)
+MTP_NORM_INST(float)
+template hipError_t launch_rmsnorm<bf16_t, bf16_t>(const bf16_t *, const float *, bf16_t *, float *, long,
+                                                   int, float, hipStream_t);
+template hipError_t launch_rmsnorm<float, bf16_t>(const float *, const float *, bf16_t *, float *, long,
+                                                  int, float, hipStream_t);
+template hipError_t launch_rmsnorm<float, float>(const float *, const float *, float *, float *, long, int,
+                                                 float, hipStream_t);
+
+}  // namespace mtp

@@ -1,0 +1,255 @@
+/*
+ * mtp.h -- C ABI of the MI355X (gfx950) library for the teacher-forced
+ * sequential multi-token-prediction (MTP) depth chain, its shared-head masked
+ * cross-entropy (forward and backward) and draft verification.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [M7.6] "M7.6 - DeepSeek MTP: Sequential Modules, Teacher Forcing, and
+ *          Speculative Runtime"
+ *   [SPEC] the speculative-decoding explainer page (ailearn,
+ *          "speculative-decoding"): gamma-token accept/correct/bonus rule
+ *   [M7.4] "M7.4 - Multi-Token Prediction Foundations"
+ *
+ * General conventions
+ *   - Every tensor pointer is a DEVICE pointer unless marked [host].  Tensors
+ *     are dense row-major.  "rows" means the B*T positions of the dense
+ *     [B, T] layout, row index b*T + i.
+ *   - Matrices follow the y = x W^T convention: a weight W of shape [out, in]
+ *     is stored row-major with `in` contiguous.
+ *   - The caller allocates and frees every buffer, including the workspace
+ *     (size from the matching *_workspace_size call).  The library keeps no
+ *     device memory of its own.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
+ *     stream).  No call synchronises the host.  Calls on different streams
+ *     with disjoint buffers may run concurrently.
+ *   - Errors: argument checks (null pointers, shapes, dtypes, depth,
+ *     workspace size) run on the host before any launch; on failure the call
+ *     returns a negative mtp_status and launches nothing, so outputs are left
+ *     untouched.  Data-dependent errors are reported on the device (see each
+ *     call) so that no host sync is needed.  MTP_ERR_HIP means a launch
+ *     failed; outputs are then undefined.
+ *   - dtype MTP_BF16: activations, embeddings and weight matrices are
+ *     bfloat16 (bit pattern in uint16); MTP_F32: float32.  RMSNorm gains are
+ *     always float32.  Matrix products run on MFMA with float32
+ *     accumulation; RMS statistics, softmax and loss sums are float32 or
+ *     wider.
+ */
+#ifndef MTP_H_
+#define MTP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MTP_OK = 0,
+  MTP_ERR_NULL = -1,         /* a required pointer is NULL                       */
+  MTP_ERR_SHAPE = -2,        /* a size is <= 0, inconsistent or not supported    */
+  MTP_ERR_DEPTH = -3,        /* D < 1 ([M7.6] 0x04C: depth must be positive)     */
+  MTP_ERR_DTYPE = -4,        /* unknown dtype                                    */
+  MTP_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than required          */
+  MTP_ERR_ARG = -6,          /* other invalid argument (reduce mode, denom, ...)  */
+  MTP_ERR_HIP = -7,          /* a HIP launch failed                              */
+  MTP_ERR_UNSUPPORTED = -8   /* valid request outside what the kernels handle    */
+} mtp_status;
+
+typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
+
+/* Per-depth loss reduction ([M7.6] 0x05).  FIXED divides depth k's summed
+ * token loss by a declared constant (the paper's fixed 1/T; default B*T);
+ * VALID_MEAN divides by |V_k| (the loss-valid rows of depth k).  An empty
+ * depth contributes a zero term that stays in the D-way mean. */
+typedef enum { MTP_REDUCE_FIXED = 0, MTP_REDUCE_VALID_MEAN = 1 } mtp_reduce;
+
+/* Per-request verify status codes (mtp_verify_args.status). */
+enum {
+  MTP_VERIFY_OK = 0,
+  MTP_VERIFY_BAD_UNIFORM = 1,      /* a uniform outside [0, 1) or NaN            */
+  MTP_VERIFY_BAD_TOKEN = 2,        /* a draft token outside [0, V)               */
+  MTP_VERIFY_ZERO_DRAFT_PROB = 3,  /* a tested draft token has q = 0             */
+  MTP_VERIFY_ZERO_RESIDUAL = 4,    /* rejection with zero residual mass          */
+  MTP_VERIFY_NONFINITE = 5         /* a used logit row has NaN/+inf or is all -inf */
+};
+
+/* ------------------------------------------------------------------------
+ * MTP module weights of one depth k ([M7.6] 0x03, 0x03C, 0x04B).
+ *   g_h, g_e  [d] f32   gains of RMSNorm_{h,k} (hnorm) and RMSNorm_{e,k} (enorm)
+ *   M         [d, 2d]   eh_proj; columns [0,d) multiply the normalised hidden
+ *                       state and [d,2d) the normalised embedding ("he" order,
+ *                       [M7.6] 0x07B).  No bias.
+ *   g_attn    [d] f32   gain of the block's attention pre-norm (Norm_a)
+ *   Wqkv      [3*H*hd, d]  rows [0,H*hd) = W_q, then W_k, then W_v
+ *   Wo        [d, H*hd]
+ *   g_ffn     [d] f32   gain of the block's FFN pre-norm (Norm_f)
+ *   Wgate, Wup [ffn, d]; Wdown [d, ffn]   SwiGLU: (silu(y Wg^T) * y Wu^T) Wd^T
+ * The block is pre-norm ([M7.6] 0x03C): a = u + Attn(Norm_a(u)),
+ * h = a + FFN(Norm_f(a)); attention is multi-head (H heads of width hd, no
+ * biases, scale 1/sqrt(hd)), segment-causal, with rotate-half RoPE at the
+ * position inside the segment run.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const float *g_h, *g_e, *g_attn, *g_ffn;
+  const void *M;
+  const void *Wqkv;
+  const void *Wo;
+  const void *Wgate, *Wup;
+  const void *Wdown;
+} mtp_depth_weights;
+
+/* ------------------------------------------------------------------------
+ * mtp_chain_forward: rows, masks and labels of every depth, then the
+ * teacher-forced depth chain h^(1..D) ([M7.6] 0x02, 0x03, 0x04, 0x04C, 0x06A).
+ *
+ * Depth k at row (b, i) reads h^(k-1)[b,i] and the ground-truth token
+ * x[b, i+k] and produces h^(k)[b,i]; its label is x[b, i+k+1].
+ * A run is a maximal stretch of one non-negative segment id inside a batch
+ * row (segment < 0 = padding).  For i in run [r0, r1]:
+ *   state_mask[k,b,i] = (i + k     <= r1)   the chain i..i+k is inside the run
+ *   loss_mask [k,b,i] = (i + k + 1 <= r1)   the label exists in the run
+ *   labels    [k,b,i] = loss ? x[b,i+k+1] : -1;  counts[k] = sum of loss_mask
+ * (padding rows: both masks 0).  h^(k) is defined on state rows; other rows
+ * hold unspecified finite values.  Attention of row i sees rows j of its own
+ * run with j <= i (a padding row sees only itself).
+ *
+ * Inputs : tokens, segment_ids int32 [B,T]; h0 [B*T, d]; embed [V, d] (the
+ *          main model's shared embedding); w [host] D entries.
+ * Outputs: h_out [host] D device pointers, each [B*T, d] in dtype;
+ *          state_mask, loss_mask uint8 [D,B,T]; labels int32 [D,B,T];
+ *          counts int32 [D]; device_error int32 [1]: set to 1 if an active
+ *          position (segment >= 0) holds a token outside [0, V) (such tokens
+ *          are clamped when gathered), else written 0.
+ * Requirements: B,T,d,n_heads,head_dim,ffn,V >= 1, D >= 1; head_dim even;
+ *   bf16: d, ffn, n_heads*head_dim multiples of 8 and head_dim % 32 == 0;
+ *   f32 : multiples of 4 and head_dim % 16 == 0; head_dim <= 256.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int B, T, d, n_heads, head_dim, ffn, V, D;
+  mtp_dtype dtype;
+  float eps;                /* RMSNorm epsilon ([M7.6] 0x03C)                    */
+  float rope_theta;         /* RoPE base; 0 disables RoPE                        */
+  const int32_t *tokens, *segment_ids;
+  const void *h0, *embed;
+  const mtp_depth_weights *w;        /* [host] D entries                       */
+  void *const *h_out;                /* [host] D device pointers               */
+  uint8_t *state_mask, *loss_mask;
+  int32_t *labels;
+  int32_t *counts;
+  int32_t *device_error;
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_chain_args;
+
+/* ------------------------------------------------------------------------
+ * mtp_head_ce_fwd_bwd: shared output head Norm_out + W_U, masked CE against
+ * the labels of every depth, and the gradients of
+ *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
+ * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  The logits [rows, V] are never
+ * written: the forward keeps an online log-sum-exp over vocabulary tiles.
+ *
+ * Inputs : h [host] D pointers [B*T, d] (dtype); labels int32 [D,B,T]
+ *          (-1 = no loss, as written by mtp_chain_forward); W_out [V, d]
+ *          (dtype); g_out [d] f32 (the shared final-norm gain).
+ * Outputs: loss_sum f32 [D] (sum of token losses of depth k), counts int32
+ *          [D] (labelled rows), loss f32 [D] (L^(k)), loss_mtp f32 [1];
+ *          lse f32 [D, B*T] (optional, may be NULL: log-sum-exp of every
+ *          row's logits; unlabelled rows included);
+ *          dh [host] D pointers, each f32 [B*T, d] = dL_MTP/dh^(k) through the
+ *          head (written, not accumulated; 0 on unlabelled rows);
+ *          dW_out f32 [V, d] and dg_out f32 [d]: the depths' contributions
+ *          summed; accumulate = 1 adds them to the existing values (e.g. the
+ *          main loss's), 0 overwrites.
+ * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
+ *          MTP_REDUCE_VALID_MEAN (denom ignored).
+ * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0.
+ * Labels outside [-1, V) are treated as -1 and set device_error (may be
+ * NULL).
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int B, T, d, V, D;
+  mtp_dtype dtype;
+  float eps, lambda;
+  mtp_reduce reduce;
+  double denom;
+  const void *const *h;              /* [host] D pointers                      */
+  const int32_t *labels;
+  const void *W_out;
+  const float *g_out;
+  float *loss_sum;
+  int32_t *counts;
+  float *loss, *loss_mtp;
+  float *lse;                        /* optional                               */
+  void *const *dh;                   /* [host] D pointers (f32)                */
+  float *dW_out, *dg_out;
+  int accumulate;
+  int32_t *device_error;             /* optional                               */
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_ce_args;
+
+/* ------------------------------------------------------------------------
+ * mtp_verify: one exact speculative round per request ([M7.6] 0x09 for one
+ * proposal; [SPEC] for gamma proposals).
+ *   p_j = softmax(target_logits[r,j,:] / temperature), j = 0..gamma
+ *   q_j = softmax(draft_logits [r,j,:] / temperature), j = 0..gamma-1
+ * Left to right, draft j is accepted iff u_accept[r,j] < p_j(y_j) / q_j(y_j)
+ * (strict; u in [0,1) makes min(1, .) redundant).  A = index of the first
+ * rejection, or gamma if none.  If A < gamma the emitted token is drawn from
+ * the normalised residual (p_A - q_A)+ ; otherwise from p_gamma (the bonus).
+ * A draw uses u_sample[r, A] by inverse CDF over ascending token ids: the
+ * smallest t with sum_{s<=t} w_s > u * sum_s w_s.  The round emits
+ * N_emit = A + 1 tokens: the accepted drafts and next_token.  EOS and output
+ * budget truncation are the caller's.
+ *
+ * Inputs : target_logits [R, gamma+1, V], draft_logits [R, gamma, V] in
+ *          logits_dtype; draft_tokens int32 [R, gamma] (each sampled from its
+ *          q); u_accept f32 [R, gamma]; u_sample f32 [R, gamma+1].
+ * Outputs: accepted_len int32 [R] (A), next_token int32 [R], status int32 [R]
+ *          (MTP_VERIFY_*; on a nonzero status A = 0 and next_token = -1);
+ *          margin f32 [R] optional (may be NULL): the smallest distance of a
+ *          decision from its threshold (|u - p/q| over the tests made, and the
+ *          sample's distance to the nearer CDF step relative to the mass).
+ * Checks in order: uniforms, token ids, then per used row: non-finite row,
+ * q_j(y_j) = 0, zero residual mass.  Rows after the first rejection are not
+ * read.
+ * Requirements: R >= 1, gamma >= 1, V >= 1, temperature > 0.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int R, gamma, V;
+  float temperature;
+  mtp_dtype logits_dtype;
+  const void *target_logits;
+  const void *draft_logits;
+  const int32_t *draft_tokens;
+  const float *u_accept;
+  const float *u_sample;
+  int32_t *accepted_len;
+  int32_t *next_token;
+  int32_t *status;
+  float *margin;                     /* optional                               */
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_verify_args;
+
+int mtp_chain_forward(const mtp_chain_args *a, void *stream);
+int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
+int mtp_verify(const mtp_verify_args *a, void *stream);
+
+/* Workspace bytes the call needs for these arguments (pointers are not
+ * inspected); 0 if the arguments are invalid. */
+size_t mtp_chain_workspace_size(const mtp_chain_args *a);
+size_t mtp_ce_workspace_size(const mtp_ce_args *a);
+size_t mtp_verify_workspace_size(const mtp_verify_args *a);
+
+/* Static string naming a status code. */
+const char *mtp_strerror(int status);
+
+/* ABI version of this header (incremented on incompatible changes). */
+int mtp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MTP_H_ */

@@ -129,7 +129,7 @@ def module_forward(h_prev: np.ndarray, tokens: np.ndarray, segment_ids: np.ndarr
     h_bar = rmsnorm(h_prev, w["g_h"], eps)
     e_bar = rmsnorm(e, w["g_e"], eps)
     c = st(np.concatenate([h_bar, e_bar], axis=1))                      # [N, 2d]
-    u = st(c @ np.asarray(w["M"], np.float64).T)                         # [N, d]
+    u = c @ np.asarray(w["M"], np.float64).T                             # [N, d], wide
 
     x_a = st(rmsnorm(u, w["g_a"], eps))
     qkv = x_a @ np.asarray(w["Wqkv"], np.float64).T                      # [N, 3A]

@@ -6,9 +6,10 @@ in bfloat16; everything between two stores is float64 here.  The "exact" model
 (used for the float32 tiny case) rounds nothing.
 
 The list of rounding points is a declared reading (the pages fix no storage
-precision): c (normalised concat), u, x_a (attention-norm output), q, k, v
+precision): c (normalised concat), x_a (attention-norm output), q, k, v
 (after RoPE), o, y (FFN-norm output), the SwiGLU product, h^k, and x_hat
-(output-norm output).  The residual stream a stays wide.
+(output-norm output).  The residual stream u -> a -> h stays wide until h^k
+is stored.
 """
 from __future__ import annotations
 

@@ -1,0 +1,144 @@
+"""GPU parity of mtp_head_ce_fwd_bwd against the oracle: per-depth loss sums
+to relative 2e-3 (float32: 1e-5); dh, dW_out, dg_out to max-abs 2e-2 plus a
+relative Frobenius gate (bf16: 1e-2, float32: 1e-4); counts exact."""
+import numpy as np
+import pytest
+import torch
+
+from deepseek_sequential_mtp_amd import _lib, synth
+from oracle import head as ohead, rows as orows
+from oracle.numerics import BF16, EXACT
+from tests.gpu_util import compare, rel_fro, tdev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, seed=0):
+    inp = synth.make_head_inputs(cfg, seed)
+    _, _, labels, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], cfg.D)
+    labels = labels.reshape(cfg.D, -1)
+    if label_rows is not None:            # keep labels only on these rows
+        keep = np.zeros(labels.shape[1], bool)
+        keep[label_rows] = True
+        labels = np.where(keep[None, :], labels, -1)
+    dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    hs = [tdev(h, dtype) for h in inp["h"]]
+    W = tdev(inp["W_out"], dtype)
+    g = tdev(inp["g_out"], torch.float32)
+    lab_t = tdev(labels.reshape(cfg.D, cfg.B, cfg.T).astype(np.int32), torch.int32)
+    print(f"[ce] {cfg.name} N={cfg.N} d={cfg.d} V={cfg.V} D={cfg.D} reduce={reduce} "
+          f"labelled={(labels >= 0).sum()}", flush=True)
+    out = None
+    if accumulate:
+        out = dict(loss_sum=torch.empty(cfg.D, device="cuda"), counts=torch.empty(cfg.D, dtype=torch.int32, device="cuda"),
+                   loss=torch.empty(cfg.D, device="cuda"), loss_mtp=torch.empty(1, device="cuda"),
+                   lse=torch.empty((cfg.D, cfg.N), device="cuda"),
+                   dh=[torch.empty((cfg.N, cfg.d), device="cuda") for _ in range(cfg.D)],
+                   dW_out=torch.full((cfg.V, cfg.d), 0.25, device="cuda"),
+                   dg_out=torch.full((cfg.d,), -0.5, device="cuda"),
+                   device_error=torch.empty(1, dtype=torch.int32, device="cuda"))
+    res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, reduce=reduce, denom=denom,
+                               accumulate=accumulate, want_lse=True, out=out)
+    torch.cuda.synchronize()
+    model = BF16 if cfg.dtype == "bf16" else EXACT
+    ref = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], cfg.eps, cfg.lam, reduce,
+                        denom if denom > 0 else None, model)
+    return res, ref, labels
+
+
+def _assert(cfg, res, ref, labels, accumulate=False):
+    f32 = cfg.dtype == "f32"
+    np.testing.assert_array_equal(to_np(res["counts"]), ref["counts"])
+    assert int(to_np(res["device_error"])[0]) == 0
+    ls = to_np(res["loss_sum"]).astype(np.float64)
+    np.testing.assert_allclose(ls, ref["loss_sum"], rtol=1e-5 if f32 else 2e-3, atol=1e-6)
+    np.testing.assert_allclose(to_np(res["loss"]), ref["loss"], rtol=1e-5 if f32 else 2e-3, atol=1e-9)
+    np.testing.assert_allclose(to_np(res["loss_mtp"])[0], ref["loss_mtp"], rtol=1e-5 if f32 else 2e-3)
+    lse = to_np(res["lse"])
+    m = labels >= 0
+    np.testing.assert_allclose(lse[m], ref["lse"][m], rtol=1e-5 if f32 else 2e-3)
+    gate = 1e-4 if f32 else 1e-2
+    for k in range(cfg.D):
+        g = to_np(res["dh"][k])
+        err, _, ok = compare(g, ref["dh"][k], 2e-2)
+        rf = rel_fro(g, ref["dh"][k])
+        print(f"  dh[{k}] max|err| {err:.3e} relF {rf:.2e}", flush=True)
+        assert ok and rf < gate
+    dW_ref = ref["dW_out"] + (0.25 if accumulate else 0.0)
+    dg_ref = ref["dg_out"] + (-0.5 if accumulate else 0.0)
+    dW = to_np(res["dW_out"])
+    err, _, ok = compare(dW, dW_ref, 2e-2)
+    rf = rel_fro(dW - (0.25 if accumulate else 0.0), ref["dW_out"])
+    print(f"  dW max|err| {err:.3e} relF {rf:.2e}", flush=True)
+    assert ok and rf < gate
+    dg = to_np(res["dg_out"])
+    err, _, ok = compare(dg, dg_ref, 2e-2)
+    rf = rel_fro(dg - (-0.5 if accumulate else 0.0), ref["dg_out"])
+    print(f"  dg max|err| {err:.3e} relF {rf:.2e}", flush=True)
+    assert ok and rf < gate
+
+
+def test_ce_tiny_f32():
+    cfg = synth.TINY
+    res, ref, labels = _case(cfg)
+    _assert(cfg, res, ref, labels)
+
+
+@pytest.mark.parametrize("reduce", ["fixed", "valid_mean"])
+def test_ce_bf16_ragged_two_depths(reduce):
+    cfg = synth.scaled(synth.D1, name="ce_ragged", B=2, T=300, d=256, V=1000, D=2, seg_lo=20,
+                       seg_hi=200, sigma_w=0.05)
+    res, ref, labels = _case(cfg, reduce=reduce)
+    _assert(cfg, res, ref, labels)
+
+
+def test_ce_bf16_accumulate_and_custom_denom():
+    cfg = synth.scaled(synth.D1, name="ce_acc", B=1, T=256, d=128, V=512, D=1, seg_lo=30,
+                       seg_hi=100, sigma_w=0.05)
+    res, ref, labels = _case(cfg, denom=1000.0, accumulate=True)
+    _assert(cfg, res, ref, labels, accumulate=True)
+
+
+def test_ce_bf16_big_tiles():
+    # 256x256 tiles in the forward, recompute and dW GEMMs (>= 256 tiles each)
+    cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=1024, V=16384, D=1, seg_lo=100,
+                       seg_hi=700, sigma_w=0.02)
+    res, ref, labels = _case(cfg)
+    _assert(cfg, res, ref, labels)
+
+
+def test_ce_bf16_big_dx_tiles_sparse_labels():
+    # 256x256 tiles with K splits in the dx GEMM (rows x d >= 256 tiles);
+    # labels on 64 sampled rows keep the oracle cheap, the GPU runs every row
+    cfg = synth.scaled(synth.D1, name="ce_bigdx", B=1, T=4096, d=4096, V=1024, D=1,
+                       seg_lo=4096, seg_hi=4096, sigma_w=0.01)
+    rows = np.random.default_rng(3).choice(4095, 64, replace=False)
+    res, ref, labels = _case(cfg, label_rows=rows)
+    _assert(cfg, res, ref, labels)
+
+
+def test_ce_empty_depth_and_bad_labels():
+    cfg = synth.scaled(synth.D1, name="ce_empty", B=1, T=64, d=128, V=256, D=2, seg_lo=64,
+                       seg_hi=64, sigma_w=0.05)
+    inp = synth.make_head_inputs(cfg)
+    _, _, labels, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], 2)
+    labels = labels.reshape(2, -1)
+    labels[1, :] = -1                          # depth 2 empty
+    hs = [tdev(h, torch.bfloat16) for h in inp["h"]]
+    W = tdev(inp["W_out"], torch.bfloat16)
+    g = tdev(inp["g_out"], torch.float32)
+    for reduce in ("fixed", "valid_mean"):
+        lab_t = tdev(labels.reshape(2, 1, 64).astype(np.int32), torch.int32)
+        res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=0.1, reduce=reduce)
+        torch.cuda.synchronize()
+        ref = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], 1e-6, 0.1, reduce, None, BF16)
+        assert to_np(res["loss"])[1] == 0.0 and to_np(res["counts"])[1] == 0
+        np.testing.assert_allclose(to_np(res["loss_mtp"])[0], ref["loss_mtp"], rtol=2e-3)
+        assert np.all(to_np(res["dh"][1]) == 0.0)
+    bad = labels.copy()
+    bad[0, 5] = 10 ** 6                        # out of range: ignored and flagged
+    lab_t = tdev(bad.reshape(2, 1, 64).astype(np.int32), torch.int32)
+    res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=0.1)
+    torch.cuda.synchronize()
+    assert int(to_np(res["device_error"])[0]) == 1
+    assert int(to_np(res["counts"])[0]) == int((labels[0] >= 0).sum()) - 1

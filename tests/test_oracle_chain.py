@@ -224,7 +224,7 @@ def test_bf16_model_rounds_only_at_declared_points():
     rng, seg, toks, h0, E, depths = _tiny_setup(6)
     h_ex = chain.module_forward(h0, toks, seg, 1, depths[0], E, 2, 8, 1e-6, 1e4, EXACT)
     h_bf, it = chain.module_forward(h0, toks, seg, 1, depths[0], E, 2, 8, 1e-6, 1e4, BF16, keep=True)
-    for name in ("c", "u", "x_a", "q", "k", "v", "o", "y", "gsw", "h"):
+    for name in ("c", "x_a", "q", "k", "v", "o", "y", "gsw", "h"):
         np.testing.assert_array_equal(bf16_round(it[name]), it[name])
     st = rows.dense_rows(toks, seg, 1)[0][0].reshape(-1).astype(bool)
     err = np.abs(h_ex[st] - h_bf[st]).max()
