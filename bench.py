@@ -1,0 +1,285 @@
+"""Benchmark of one MTP training step on one MI355X.
+
+A step is mtp_chain_forward (all D depths) followed by mtp_head_ce_fwd_bwd
+(all D depths) on one stream, inputs resident in HBM.  Default workload: the
+V3-width configuration (B=1, T=4096, d=7168, 128 heads x 128, ffn=18432,
+V=129280, D=1, bf16) with synthetic seeded inputs of the stated
+distributions, generated on the device.
+
+Prints one JSON line: tokens/s (B*T / step time), the step's fraction of the
+bf16 dense MFMA peak on algorithmic FLOPs, a roofline entry for the dominant
+kernel (its launches timed with HIP events over the timed region), and the
+CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload v3width_bf16]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3width_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=128)
+    ap.add_argument("--stages", action="store_true", help="print the per-stage time table to stderr")
+    return ap.parse_args()
+
+
+# ----------------------------------------------------------------------------
+# inputs (device-side generation with the synthetic recipe)
+# ----------------------------------------------------------------------------
+def device_inputs(cfg, torch):
+    from deepseek_sequential_mtp_amd import synth
+    ss = np.random.SeedSequence(synth.BASE_SEED + cfg.index)
+    g_tok, g_seg = [np.random.Generator(np.random.PCG64(k)) for k in ss.spawn(2)]
+    tokens = (synth.zipf_tokens(g_tok, cfg.V, (cfg.B, cfg.T)) if cfg.zipf
+              else g_tok.integers(0, cfg.V, (cfg.B, cfg.T)).astype(np.int32))
+    seg = synth.packed_segments(g_seg, cfg.B, cfg.T, cfg.seg_lo, cfg.seg_hi)
+    dev = "cuda:0"
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(synth.BASE_SEED + cfg.index)
+    bf = torch.bfloat16
+
+    def normal(shape, sigma, mean=0.0, dtype=bf):
+        t = torch.randn(shape, generator=gen, device=dev, dtype=torch.float32)
+        return (t * sigma + mean).to(dtype)
+
+    d, V, A, f = cfg.d, cfg.V, cfg.A_w, cfg.ffn
+    inp = dict(tokens=torch.from_numpy(tokens).to(dev), segment_ids=torch.from_numpy(seg).to(dev),
+               h0=normal((cfg.N, d), 1.0), E=normal((V, d), cfg.sigma_w),
+               W_out=normal((V, d), cfg.sigma_w), g_out=normal((d,), 0.1, 1.0, torch.float32))
+    inp["depths"] = [dict(g_h=normal((d,), 0.1, 1.0, torch.float32), g_e=normal((d,), 0.1, 1.0, torch.float32),
+                          M=normal((d, 2 * d), cfg.sigma_w), g_a=normal((d,), 0.1, 1.0, torch.float32),
+                          Wqkv=normal((3 * A, d), cfg.sigma_w), Wo=normal((d, A), cfg.sigma_w),
+                          g_f=normal((d,), 0.1, 1.0, torch.float32), Wgate=normal((f, d), cfg.sigma_w),
+                          Wup=normal((f, d), cfg.sigma_w), Wdown=normal((d, f), cfg.sigma_w))
+                     for _ in range(cfg.D)]
+    return inp
+
+
+# ----------------------------------------------------------------------------
+# algorithmic work from the realised packing
+# ----------------------------------------------------------------------------
+def algorithmic_flops(cfg, state_mask, counts, run_start_fn):
+    """Per depth: state rows S_k, loss rows L_k, attention pairs P_k (sum over
+    state rows of the causal window length).  FLOPs (multiply-add = 2):
+    eh_proj 4 d^2 S, QKV 6 d A S, attention 4 A P, O 2 A d S, SwiGLU 6 d f S,
+    head 6 d V L (2 forward + 4 backward)."""
+    d, A, f, V = cfg.d, cfg.A_w, cfg.ffn, cfg.V
+    per = []
+    rs = run_start_fn()
+    pos = np.arange(cfg.T)[None, :]
+    for k in range(cfg.D):
+        st = state_mask[k].astype(bool)
+        S = int(st.sum())
+        L = int(counts[k])
+        P = int(((pos - rs + 1) * st).sum())
+        per.append(dict(S=S, L=L, P=P,
+                        EH_PROJ=4.0 * d * d * S, QKV=6.0 * d * A * S, ATTN=4.0 * A * P,
+                        O_PROJ=2.0 * A * d * S, GATE_UP=4.0 * d * f * S, DOWN=2.0 * f * d * S,
+                        CE_FWD=2.0 * d * V * L, CE_DX=2.0 * d * V * L, CE_DW=2.0 * d * V * L,
+                        CE_GRAD=0.0))
+    return per
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
+              "sharding is a design only, see DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from deepseek_sequential_mtp_amd import _lib, synth
+    from oracle import rows as orows
+
+    cfg = synth.CHAIN_CONFIGS[args.workload]
+    assert cfg.dtype == "bf16"
+    print(f"[bench] workload {cfg.name}: B={cfg.B} T={cfg.T} d={cfg.d} H={cfg.n_heads}x{cfg.head_dim} "
+          f"ffn={cfg.ffn} V={cfg.V} D={cfg.D}", file=sys.stderr, flush=True)
+    inp = device_inputs(cfg, torch)
+    dev = inp["h0"].device
+    D, N = cfg.D, cfg.N
+    chain_out = dict(h=[torch.empty_like(inp["h0"]) for _ in range(D)],
+                     state_mask=torch.empty((D, cfg.B, cfg.T), dtype=torch.uint8, device=dev),
+                     loss_mask=torch.empty((D, cfg.B, cfg.T), dtype=torch.uint8, device=dev),
+                     labels=torch.empty((D, cfg.B, cfg.T), dtype=torch.int32, device=dev),
+                     counts=torch.empty((D,), dtype=torch.int32, device=dev),
+                     device_error=torch.empty((1,), dtype=torch.int32, device=dev))
+    ce_out = dict(loss_sum=torch.empty(D, device=dev), counts=torch.empty(D, dtype=torch.int32, device=dev),
+                  loss=torch.empty(D, device=dev), loss_mtp=torch.empty(1, device=dev), lse=None,
+                  dh=[torch.empty((N, cfg.d), device=dev) for _ in range(D)],
+                  dW_out=torch.empty((cfg.V, cfg.d), device=dev), dg_out=torch.empty((cfg.d,), device=dev),
+                  device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    cache = {}
+
+    def step():
+        _lib.chain_forward(inp["tokens"], inp["segment_ids"], inp["h0"], inp["E"], inp["depths"],
+                           n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps,
+                           rope_theta=cfg.rope_theta, out=chain_out, cache=cache)
+        _lib.head_ce_fwd_bwd(chain_out["h"], chain_out["labels"], inp["W_out"], inp["g_out"], lam=cfg.lam,
+                             eps=cfg.eps, out=ce_out, cache=cache)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert int(chain_out["device_error"][0]) == 0
+
+    # per-stage times (one profiled step per stage, outside the timed region)
+    stage_ms = {}
+    for name in _lib.STAGES:
+        if name == "VERIFY":
+            continue
+        with _lib.StageTimer(name, 64) as tm:
+            step()
+        ts = tm.times_ms()
+        if ts:
+            stage_ms[name] = sum(ts)
+    dominant = max((s for s in stage_ms if s in ("EH_PROJ", "QKV", "ATTN", "O_PROJ", "GATE_UP", "DOWN",
+                                                   "CE_FWD", "CE_GRAD", "CE_DX", "CE_DW")),
+                   key=lambda s: stage_ms[s])
+
+    # timed region; the dominant stage's launches carry HIP events
+    per_step_launches = D
+    timer = _lib.StageTimer(dominant, per_step_launches * args.steps)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    with timer:
+        e0.record()
+        for _ in range(args.steps):
+            step()
+        e1.record()
+        torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    dom_times = timer.times_ms()
+    dom_avg_ms = float(np.mean(dom_times))
+
+    # work accounting from the realised packing
+    sm = chain_out["state_mask"].cpu().numpy()
+    counts = chain_out["counts"].cpu().numpy()
+    seg = inp["segment_ids"].cpu().numpy()
+    per = algorithmic_flops(cfg, sm, counts, lambda: orows.run_bounds(seg)[0])
+    keys = ("EH_PROJ", "QKV", "ATTN", "O_PROJ", "GATE_UP", "DOWN", "CE_FWD", "CE_DX", "CE_DW")
+    alg_step = sum(p[k] for p in per for k in keys)
+    dom_alg_per_launch = float(np.mean([p[dominant] for p in per]))
+    if dom_alg_per_launch == 0.0:          # recompute pass: no algorithmic credit
+        dom_alg_per_launch = 2.0 * cfg.d * cfg.V * N
+        dom_note = "executed FLOPs (logit recompute carries no algorithmic FLOPs)"
+    else:
+        dom_note = "algorithmic FLOPs"
+    achieved = dom_alg_per_launch / (dom_avg_ms * 1e-3) / 1e12
+    tokens_s = cfg.N / (ms_step * 1e-3)
+    step_frac = alg_step / (ms_step * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", f"traffic_{dominant.lower()}_{cfg.name}.json")
+    if os.path.exists(tfile):
+        try:
+            with open(tfile) as fh:
+                tr = json.load(fh)
+            if tr.get("source_hash") == _kernel_hash():
+                traffic = tr.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+
+    if args.stages:
+        tot = sum(stage_ms.values())
+        for k, v in sorted(stage_ms.items(), key=lambda kv: -kv[1]):
+            print(f"  stage {k:12s} {v:9.3f} ms  {100 * v / tot:5.1f}%", file=sys.stderr)
+        print(f"  dominant {dominant}: {dom_avg_ms:.3f} ms/launch over {len(dom_times)} launches, "
+              f"{achieved:.1f} TFLOP/s ({dom_note})", file=sys.stderr)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(cfg, args.cpu_rows)
+
+    line = {
+        "metric": "MTP train tokens/s (chain fwd + head-CE fwd/bwd) and % bf16 MFMA peak, 1 GPU",
+        "value": round(tokens_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded, generated on device: Zipf(1.1) tokens, N(0,1) h0, N(0,sigma) weights)",
+        "config": {"workload": cfg.name, "B": cfg.B, "T": cfg.T, "d": cfg.d, "n_heads": cfg.n_heads,
+                   "head_dim": cfg.head_dim, "ffn": cfg.ffn, "V": cfg.V, "D": cfg.D, "lambda": cfg.lam,
+                   "reduce": "fixed (B*T)", "parallelism": "none (1 GPU)"},
+        "mfma_frac_step": round(step_frac, 4),
+        "algorithmic_tflop_per_step": round(alg_step / 1e12, 3),
+        "wall_s_timed": round(wall, 3),
+        "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": traffic, "launch_ms": round(dom_avg_ms, 4), "flops_basis": dom_note},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def _kernel_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "deepseek_sequential_mtp_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_baseline(cfg, P):
+    """The oracle as it stands, on the first P positions of the workload's first
+    batch row (the chain sees the same prefix context), plus its head CE with
+    the labels of those rows.  tokens/s = P / wall time."""
+    import threadpoolctl
+    from deepseek_sequential_mtp_amd import synth
+    from oracle import chain as ochain, head as ohead, rows as orows
+    from oracle.numerics import BF16
+
+    sub = synth.scaled(cfg, B=1, T=P + cfg.D + 1, seg_lo=P + cfg.D + 1, seg_hi=P + cfg.D + 1)
+    print(f"[bench] cpu baseline: generating {cfg.name} weights on the host", file=sys.stderr, flush=True)
+    inp = synth.make_chain_inputs(sub)
+    cores = len(os.sched_getaffinity(0))
+    info = threadpoolctl.threadpool_info()
+    blas_threads = max([i.get("num_threads", 1) for i in info] or [1])
+    t0 = time.perf_counter()
+    hs = ochain.chain_forward(inp["h0"], inp["tokens"], inp["segment_ids"], inp["depths"], inp["E"],
+                              sub.n_heads, sub.head_dim, sub.eps, sub.rope_theta, BF16)
+    _, _, labels, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], sub.D)
+    lab = labels.reshape(sub.D, -1).copy()
+    lab[:, P:] = -1
+    ohead.head_ce([h[:] for h in hs], lab, inp["W_out"], inp["g_out"], sub.eps, sub.lam, "fixed", float(cfg.N), BF16)
+    dt = time.perf_counter() - t0
+    rows = P
+    return {"value": round(rows / dt, 3), "unit": "tokens/s", "cores": int(min(cores, blas_threads)),
+            "kind": "oracle",
+            "sample": f"{cfg.name}: first {P} positions of one row (prefix attention context), "
+                      f"chain fwd + head CE fwd/bwd, float64 numpy; {dt:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

@@ -20,7 +20,11 @@ STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEP
           -4: "MTP_ERR_DTYPE", -5: "MTP_ERR_WORKSPACE", -6: "MTP_ERR_ARG", -7: "MTP_ERR_HIP",
           -8: "MTP_ERR_UNSUPPORTED"}
 EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_chain_workspace_size",
-           "mtp_ce_workspace_size", "mtp_verify_workspace_size", "mtp_strerror", "mtp_abi_version")
+           "mtp_ce_workspace_size", "mtp_verify_workspace_size", "mtp_strerror", "mtp_abi_version",
+           "mtp_profile_stage", "mtp_profile_count")
+STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
+          "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
+          "VERIFY")
 
 vp = C.c_void_p
 fp = C.POINTER(C.c_float)
@@ -82,6 +86,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_strerror.argtypes = [C.c_int]
         lib.mtp_strerror.restype = C.c_char_p
         lib.mtp_abi_version.restype = C.c_int
+        lib.mtp_profile_stage.argtypes = [C.c_int, C.POINTER(vp), C.POINTER(vp), C.c_int]
+        lib.mtp_profile_count.restype = C.c_int
         _lib = lib
     return _lib
 
@@ -228,3 +234,32 @@ def verify(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens
     _check(lib.mtp_verify(C.byref(a), _stream(stream)))
     out["_keep"] = (ws,)
     return out
+
+
+class StageTimer:
+    """Arms mtp_profile_stage with ``n`` hipEvent pairs (torch CUDA events on
+    the calling stream) around every launch of one stage."""
+
+    def __init__(self, stage: str, n: int):
+        self.stage = STAGES.index(stage)
+        self.start = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.stop = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.start + self.stop:
+            e.record()                       # materialise the hipEvent_t handles
+        torch.cuda.synchronize()
+        self._s = (vp * n)(*[e.cuda_event for e in self.start])
+        self._e = (vp * n)(*[e.cuda_event for e in self.stop])
+        self.n = n
+
+    def __enter__(self):
+        _check(load().mtp_profile_stage(self.stage, self._s, self._e, self.n))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = load().mtp_profile_count()
+        load().mtp_profile_stage(-1, None, None, 0)
+
+    def times_ms(self):
+        torch.cuda.synchronize()
+        k = min(self.count, self.n)
+        return [self.start[i].elapsed_time(self.stop[i]) for i in range(k)]

@@ -36,6 +36,36 @@ inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
   } while (0)
 
 // ---------------------------------------------------------------------------
+// Stage instrumentation (mtp_profile_stage): caller events recorded around
+// every launch of the armed stage.
+// ---------------------------------------------------------------------------
+struct Profile {
+  int stage = -1;
+  hipEvent_t *start = nullptr, *stop = nullptr;
+  int n = 0, count = 0;
+};
+Profile g_prof;
+
+struct StageScope {
+  hipStream_t s;
+  bool on;
+  int slot;
+  StageScope(int stage, hipStream_t st) : s(st), on(g_prof.stage == stage && g_prof.n > 0), slot(0) {
+    if (on) {
+      slot = g_prof.count % g_prof.n;
+      (void)hipEventRecord(g_prof.start[slot], s);
+    }
+  }
+  ~StageScope() {
+    if (on) {
+      (void)hipEventRecord(g_prof.stop[slot], s);
+      ++g_prof.count;
+    }
+  }
+};
+#define MTP_STAGE(id) StageScope stage_scope_##__LINE__((id), s)
+
+// ---------------------------------------------------------------------------
 // GEMM dispatch.  The 256x256 tile is used when it still yields at least one
 // tile per compute unit; otherwise 128x128.
 // ---------------------------------------------------------------------------
@@ -252,8 +282,11 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
   float *abuf = (float *)p[10];
   T *ybuf = (T *)p[11], *gsw = (T *)p[12];
 
+  {
+  MTP_STAGE(MTP_STAGE_ROWS);
   MTP_TRY(launch_rows(a->tokens, a->segment_ids, B, Tl, V, a->D, run_start, pos, a->state_mask, a->loss_mask,
                       a->labels, a->counts, a->device_error, (int32_t *)p[2], (int32_t *)p[3], s));
+  }
   const bool use_rope = a->rope_theta > 0.f;
   if (use_rope) MTP_TRY(rope_table(rope, Tl, hd / 2, a->rope_theta, s));
 
@@ -262,21 +295,49 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
   for (int k = 1; k <= a->D; ++k) {
     const mtp_depth_weights &w = a->w[k - 1];
     T *h_out = static_cast<T *>(a->h_out[k - 1]);
-    MTP_TRY(launch_dual_norm_concat<T>(h_prev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
-    int st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d,
-                                            1.f, nullptr, 0, s);
+    int st = 0;
+    {
+      MTP_STAGE(MTP_STAGE_DUAL_NORM);
+      MTP_TRY(launch_dual_norm_concat<T>(h_prev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_EH_PROJ);
+      st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d, 1.f,
+                                          nullptr, 0, s);
+    }
     if (st) return st;
-    MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
-    st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, s);
+    {
+      MTP_STAGE(MTP_STAGE_NORM_A);
+      MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_QKV);
+      st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, s);
+    }
     if (st) return st;
-    MTP_TRY(launch_attention<T>(qkv, o, run_start, B, Tl, H, hd, s));
-    st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0, s);
+    {
+      MTP_STAGE(MTP_STAGE_ATTN);
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, B, Tl, H, hd, s));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_O_PROJ);
+      st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0, s);
+    }
     if (st) return st;
-    MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
-    st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, s);
+    {
+      MTP_STAGE(MTP_STAGE_NORM_F);
+      MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_GATE_UP);
+      st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, s);
+    }
     if (st) return st;
-    st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
-                                    s);
+    {
+      MTP_STAGE(MTP_STAGE_DOWN);
+      st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
+                                      s);
+    }
     if (st) return st;
     h_prev = h_out;
   }
@@ -367,31 +428,53 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
 
   for (int k = 0; k < D; ++k) {
     const T *h = static_cast<const T *>(a->h[k]);
-    MTP_TRY(launch_out_norm<T>(h, a->g_out, xhat, r, a->labels + (long)k * N, lab, a->device_error, N, d, V,
-                               a->eps, s));
-    int st = pick<T>(m.big, [&](auto cfg) {
-      return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, N, V, d, s);
-    });
+    int st = 0;
+    {
+      MTP_STAGE(MTP_STAGE_OUT_NORM);
+      MTP_TRY(launch_out_norm<T>(h, a->g_out, xhat, r, a->labels + (long)k * N, lab, a->device_error, N, d, V,
+                                 a->eps, s));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_CE_FWD);
+      st = pick<T>(m.big, [&](auto cfg) {
+        return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, N, V, d, s);
+      });
+    }
     if (st) return st;
-    MTP_TRY(launch_ce_combine(part, m.nt, target, lab, lse, a->lse ? a->lse + (long)k * N : nullptr, row_loss,
-                              N, s));
-    MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
-    st = pick<T>(m.big, [&](auto cfg) {
-      return gemm_ce_grad_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, lse, dz, N, V, d, s);
-    });
+    {
+      MTP_STAGE(MTP_STAGE_CE_REDUCE);
+      MTP_TRY(launch_ce_combine(part, m.nt, target, lab, lse, a->lse ? a->lse + (long)k * N : nullptr, row_loss,
+                                N, s));
+      MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
+    }
+    {
+      MTP_STAGE(MTP_STAGE_CE_GRAD);
+      st = pick<T>(m.big, [&](auto cfg) {
+        return gemm_ce_grad_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, lse, dz, N, V, d, s);
+      });
+    }
     if (st) return st;
     const bool big_dx = sizeof(T) == 2 && use_big(N, d);
-    st = pick<T>(big_dx, [&](auto cfg) {
-      return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs, slab, N, V, d, scale + k, m.splits, s);
-    });
+    {
+      MTP_STAGE(MTP_STAGE_CE_DX);
+      st = pick<T>(big_dx, [&](auto cfg) {
+        return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs, slab, N, V, d, scale + k, m.splits, s);
+      });
+    }
     if (st) return st;
     const int acc = (k > 0 || a->accumulate) ? 1 : 0;
-    MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, slab, h, r, a->g_out, static_cast<float *>(a->dh[k]), dg_part,
-                                   a->dg_out, acc, N, d, s));
+    {
+      MTP_STAGE(MTP_STAGE_CE_NORM_BWD);
+      MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, slab, h, r, a->g_out, static_cast<float *>(a->dh[k]),
+                                     dg_part, a->dg_out, acc, N, d, s));
+    }
     const bool big_dw = sizeof(T) == 2 && use_big(V, d);
-    st = pick<T>(big_dw, [&](auto cfg) {
-      return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat, a->dW_out, N, V, d, scale + k, acc, s);
-    });
+    {
+      MTP_STAGE(MTP_STAGE_CE_DW);
+      st = pick<T>(big_dw, [&](auto cfg) {
+        return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat, a->dW_out, N, V, d, scale + k, acc, s);
+      });
+    }
     if (st) return st;
   }
   MTP_TRY(launch_ce_finalize(acc_sum, acc_cnt, D, valid_mean, denom, a->lambda, a->loss_sum, a->counts, a->loss,
@@ -417,6 +500,23 @@ size_t verify_bytes(const mtp_verify_args *a) {
 extern "C" {
 
 int mtp_abi_version(void) { return 1; }
+
+int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n) {
+  if (stage < 0) {
+    g_prof = Profile();
+    return MTP_OK;
+  }
+  if (stage >= MTP_STAGE_COUNT || n < 1) return MTP_ERR_ARG;
+  if (!start_events || !stop_events) return MTP_ERR_NULL;
+  g_prof.stage = stage;
+  g_prof.start = reinterpret_cast<hipEvent_t *>(const_cast<void **>(start_events));
+  g_prof.stop = reinterpret_cast<hipEvent_t *>(const_cast<void **>(stop_events));
+  g_prof.n = n;
+  g_prof.count = 0;
+  return MTP_OK;
+}
+
+int mtp_profile_count(void) { return g_prof.count; }
 
 const char *mtp_strerror(int status) {
   switch (status) {
@@ -478,6 +578,7 @@ int mtp_verify(const mtp_verify_args *a, void *stream) {
     return MTP_ERR_NULL;
   if (!a->workspace || a->workspace_bytes < verify_bytes(a)) return MTP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
+  MTP_STAGE(MTP_STAGE_VERIFY);
   MTP_TRY(launch_verify(a->target_logits, a->draft_logits, a->logits_dtype == MTP_BF16 ? 1 : 0, a->draft_tokens,
                         a->u_accept, a->u_sample, a->R, a->gamma, a->V, a->temperature, a->accepted_len,
                         a->next_token, a->status, a->margin, static_cast<double *>(a->workspace), s));

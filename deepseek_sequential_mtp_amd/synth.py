@@ -99,7 +99,17 @@ def from_bf16_bits(b: np.ndarray) -> np.ndarray:
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
-    return from_bf16_bits(to_bf16_bits(x))
+    """float32 array rounded to bfloat16 values (nearest even), in place for
+    finite float32 input (returned), else via a copy."""
+    if x.dtype != np.float32 or not x.flags.c_contiguous or not np.isfinite(x).all():
+        return from_bf16_bits(to_bf16_bits(x))
+    u = x.view(np.uint32)
+    t = u >> 16
+    t &= 1
+    t += 0x7FFF
+    u += t
+    u &= 0xFFFF0000
+    return x
 
 
 # ----------------------------------------------------------------------------
@@ -145,7 +155,12 @@ DEPTH_FIELDS = ("g_h", "g_e", "M", "g_a", "Wqkv", "Wo", "g_f", "Wgate", "Wup", "
 
 
 def _normal(rng, shape, sigma, mean=0.0):
-    return (mean + sigma * rng.standard_normal(shape, dtype=np.float32)).astype(np.float32)
+    x = rng.standard_normal(shape, dtype=np.float32)
+    if sigma != 1.0:
+        x *= np.float32(sigma)
+    if mean != 0.0:
+        x += np.float32(mean)
+    return x
 
 
 def make_chain_inputs(cfg: ChainConfig, seed_offset: int = 0) -> Dict[str, object]:
@@ -245,8 +260,9 @@ def make_verify_logits(vc: VerifyConfig, seed_offset: int = 0):
     R, G, V = vc.R, vc.gamma, vc.V
     zt32 = _normal(g[0], (R, G + 1, V), vc.target_sigma)
     noise = _normal(g[1], (R, G, V), vc.draft_noise)
-    zt = round_bf16(zt32)
-    zd = round_bf16(zt32[:, :G, :] + noise)
+    zt = round_bf16(zt32.copy())
+    noise += zt32[:, :G, :]
+    zd = round_bf16(noise)
     u_accept = g[2].random((R, G), dtype=np.float32)
     u_sample = g[3].random((R, G + 1), dtype=np.float32)
     return dict(vc=vc, zt=zt, zd=zd, u_accept=u_accept, u_sample=u_sample,

@@ -121,9 +121,10 @@ typedef struct {
  *          counts int32 [D]; device_error int32 [1]: set to 1 if an active
  *          position (segment >= 0) holds a token outside [0, V) (such tokens
  *          are clamped when gathered), else written 0.
- * Requirements: B,T,d,n_heads,head_dim,ffn,V >= 1, D >= 1; head_dim even;
- *   bf16: d, ffn, n_heads*head_dim multiples of 8 and head_dim % 32 == 0;
- *   f32 : multiples of 4 and head_dim % 16 == 0; head_dim <= 256.
+ * Requirements: B,T,d,n_heads,ffn,V >= 1, D >= 1;
+ *   bf16: d, ffn, n_heads*head_dim multiples of 8; head_dim in {32, 64, 128};
+ *   f32 : d, ffn, n_heads*head_dim multiples of 4; head_dim in {16, 32, 64}
+ *   (other widths return MTP_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, d, n_heads, head_dim, ffn, V, D;
@@ -242,6 +243,26 @@ int mtp_verify(const mtp_verify_args *a, void *stream);
 size_t mtp_chain_workspace_size(const mtp_chain_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);
 size_t mtp_verify_workspace_size(const mtp_verify_args *a);
+
+/* ------------------------------------------------------------------------
+ * Optional instrumentation.  mtp_profile_stage arms the library to record
+ * caller-created hipEvent_t pairs around every launch of one stage: launch
+ * number j (counted from the arming call) records start_events[j % n] before
+ * and stop_events[j % n] after the stage's kernel(s), on the call's stream.
+ * The caller reads the elapsed times once the stream is synchronised.
+ * stage < 0 disarms.  The setting is process-wide (not thread-safe); events
+ * stay owned by the caller and must outlive the armed period.
+ * mtp_profile_count returns the number of launches recorded since arming.
+ * ---------------------------------------------------------------------- */
+typedef enum {
+  MTP_STAGE_ROWS = 0, MTP_STAGE_DUAL_NORM = 1, MTP_STAGE_EH_PROJ = 2, MTP_STAGE_NORM_A = 3,
+  MTP_STAGE_QKV = 4, MTP_STAGE_ATTN = 5, MTP_STAGE_O_PROJ = 6, MTP_STAGE_NORM_F = 7,
+  MTP_STAGE_GATE_UP = 8, MTP_STAGE_DOWN = 9, MTP_STAGE_OUT_NORM = 10, MTP_STAGE_CE_FWD = 11,
+  MTP_STAGE_CE_REDUCE = 12, MTP_STAGE_CE_GRAD = 13, MTP_STAGE_CE_DX = 14,
+  MTP_STAGE_CE_NORM_BWD = 15, MTP_STAGE_CE_DW = 16, MTP_STAGE_VERIFY = 17, MTP_STAGE_COUNT = 18
+} mtp_stage;
+int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n);
+int mtp_profile_count(void);
 
 /* Static string naming a status code. */
 const char *mtp_strerror(int status);
