@@ -101,11 +101,13 @@ __device__ __forceinline__ void mma16(const uint4 &a, const uint4 &b, f32x4 &acc
   acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a.w), __uint_as_float(b.w), acc, 0, 0, 0);
 }
 
-// LDS operand tiles: rows of 128 bytes (8 chunks of 16 B); chunk c of row r
-// lives at physical chunk c ^ (r & 7), so eight lanes that read the same
-// logical chunk of eight consecutive rows hit eight different bank groups.
+// LDS operand tiles: rows of 128 bytes (8 chunks of 16 B).  gfx950's LDS
+// serves 256 bytes (64 banks) per cycle, i.e. a row pair; a 16-lane group
+// reading one logical chunk of 16 consecutive rows must therefore spread over
+// both halves and all eight chunk slots: chunk c of row r lives at physical
+// chunk c ^ ((r >> 1) & 7) of its row, and r's parity picks the half.
 __device__ __forceinline__ int lds_off128(int row, int chunk) {
-  return (row << 7) + (((chunk ^ row) & 7) << 4);
+  return (row << 7) + (((chunk ^ (row >> 1)) & 7) << 4);
 }
 
 // Transpose an E x E block held as E chunks (chunk i = row i, E elements)

@@ -20,7 +20,7 @@ struct EpiStore {
   long split_stride;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int split, char *) const {
+                                        int wn, int lane, int split, char *, char *) const {
     OutT *Cs = C + split * split_stride;
     const float al = alpha_dev != nullptr ? *alpha_dev : alpha;
 #pragma unroll
@@ -59,7 +59,7 @@ struct EpiRope {
   const float2 *rope;           // [max_pos][HALF] (cos, sin); nullptr = no RoPE
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *) const {
+                                        int wn, int lane, int, char *, char *) const {
     constexpr int HD = 2 * HALF;
     static_assert(HALF < 32 || (Cfg::WN % HD) == 0, "wave columns must cover whole heads");
 #pragma unroll
@@ -104,7 +104,7 @@ struct EpiSwiGLU {
   OutT *C; long ldc; int M, f;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *) const {
+                                        int wn, int lane, int, char *, char *) const {
     constexpr int NBh = Cfg::NB / 2;
     const int tile_n = n0 / Cfg::BN;
 #pragma unroll
@@ -136,10 +136,13 @@ struct EpiCEFwd {
   const int *labels; float2 *part; float *target; int M, V, nt;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *lds) const {
-    constexpr int LD = 65;   // 64 partials per row + 1 pad
-    float *red = reinterpret_cast<float *>(lds);
-    float *mrow = red + Cfg::BM * LD;
+                                        int wn, int lane, int, char *lds0, char *lds1) const {
+    // red[row][slot]: 64 per-lane partials per row, slot XOR-swizzled by the
+    // row so the per-row scans of the second phase hit 64 distinct banks.
+    float *red = reinterpret_cast<float *>(lds0);        // BM * 64 floats
+    float *mrow = reinterpret_cast<float *>(lds1);       // BM floats
+    static_assert(Cfg::BM * 64 * 4 <= Cfg::LDS_STAGE, "CE reduction fits one stage");
+    auto at = [](int row, int slot) { return row * 64 + (slot ^ (row & 63)); };
     const int c32 = lane & 31;
     const int slot = wn * 32 + c32;
     // 1) per-lane max over the lane's columns of each of its rows
@@ -153,15 +156,16 @@ struct EpiCEFwd {
           const int col = n0 + acc_col<Cfg>(wn, j, lane);
           mx = col < V ? fmaxf(mx, acc[i][j][r]) : mx;
         }
-        red[acc_row<Cfg>(wm, i, r, lane) * LD + slot] = mx;
+        red[at(acc_row<Cfg>(wm, i, r, lane), slot)] = mx;
       }
     // Slots 32..63 are written only by the wn = 1 waves; with NB blocks per
     // wave both halves always exist, so all 64 slots are defined.
+    static_assert(Cfg::WGN == 2, "64 partial slots per row");
     __syncthreads();
     const int t = threadIdx.x;
     if (t < Cfg::BM) {
       float mx = -INFINITY;
-      for (int s = 0; s < 64; ++s) mx = fmaxf(mx, red[t * LD + s]);
+      for (int q = 0; q < 64; ++q) mx = fmaxf(mx, red[at(t, q)]);
       mrow[t] = mx;
     }
     __syncthreads();
@@ -182,12 +186,12 @@ struct EpiCEFwd {
           if (col < V) s += exp2f((z - m) * kLog2e);
           if (col == lab) target[row] = z;
         }
-        red[rl * LD + slot] = s;
+        red[at(rl, slot)] = s;
       }
     __syncthreads();
     if (t < Cfg::BM && m0 + t < M) {
       float s = 0.f;
-      for (int q = 0; q < 64; ++q) s += red[t * LD + q];
+      for (int q = 0; q < 64; ++q) s += red[at(t, q)];
       part[(long)(m0 + t) * nt + n0 / Cfg::BN] = make_float2(mrow[t], s);
     }
   }
@@ -203,7 +207,7 @@ struct EpiCEGrad {
   const int *labels; const float *lse; OutT *dz; long ldz; int M, V;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *) const {
+                                        int wn, int lane, int, char *, char *) const {
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
@@ -225,9 +229,10 @@ struct EpiCEGrad {
 };
 
 template <typename T, class Cfg, class LA, class LB, class Epi>
-__global__ __launch_bounds__(kGemmThreads) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
-  __shared__ __attribute__((aligned(16))) char lds[Cfg::LDS_BYTES];
-  gemm_body<T, Cfg>(la, lb, epi, K, ts, lds);
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
+  __shared__ __attribute__((aligned(1024))) char lds0[Cfg::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char lds1[Cfg::LDS_STAGE];
+  gemm_body<T, Cfg>(la, lb, epi, K, ts, lds0, lds1);
 }
 
 // Host-side launch helper (grid = tiles * K splits, one block per tile).
@@ -241,7 +246,7 @@ inline hipError_t launch_gemm(const LA &la, const LB &lb, const Epi &epi, int M,
   ts.k_splits = k_splits < 1 ? 1 : k_splits;
   const long tiles = (long)ts.mt * ts.nt * ts.k_splits;
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)tiles), dim3(kGemmThreads), 0,
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)tiles), dim3(Cfg::NT), 0,
                      stream, la, lb, epi, K, ts);
   return hipGetLastError();
 }

@@ -1,13 +1,10 @@
 // MFMA GEMM core for gfx950: C[m, n] = sum_k A[m, k] * B[k, n] with fp32
-// accumulation, 256 threads (4 waves as 2 x 2), BM x BN output tile, K staged
+// accumulation, WGM x WGN waves per workgroup, BM x BN output tile, K staged
 // through LDS in slices of 128 bytes per row, double-buffered.
 //
-// Operands are described by loaders:
-//   * K-major  (K contiguous; A[m][k] = base[rowA(m) * ld + k]): direct 16-byte
-//     chunk copies, optional per-row source (gather / interleaved matrices);
-//   * MN-major (M or N contiguous; A[m][k] = base[k * ld + m]): 8x8 (bf16) or
-//     4x4 (f32) blocks transposed in registers on their way to LDS, so the LDS
-//     tile is always K-contiguous.
+// Operands are K-major (K contiguous; A[m][k] = base[row(m) * ld + k]) and
+// are described by loaders that copy them global -> LDS directly, optionally
+// with a per-row source (interleaved matrices).
 // Epilogues receive the accumulators in the MFMA result layout (see
 // common.hpp) and do the stores / reductions.
 #pragma once
@@ -16,118 +13,207 @@
 
 namespace mtp {
 
-constexpr int kGemmThreads = 256;
-
-template <int BM_, int BN_>
+template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
-  static constexpr int WM = BM / 2, WN = BN / 2;     // per-wave tile
-  static constexpr int MB = WM / 32, NB = WN / 32;   // 32x32 blocks per wave
-  static constexpr int LDS_STAGE = (BM + BN) * 128;  // bytes per stage
-  static constexpr int LDS_BYTES = 2 * LDS_STAGE;
+  static constexpr int WGM = WGM_, WGN = WGN_;       // waves along M and N
+  static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
+  static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
+  static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 blocks per wave
+  static constexpr int LDS_STAGE = (BM + BN) * 128;   // bytes per stage (two stages)
 };
 
 // ---------------------------------------------------------------------------
-// Row sources for K-major operands: pointer of source row r of the operand
-// (r in [0, rows)), or nullptr for a row past the end (zero fill).
+// Global loads go through raw buffer resources: one resource per tile (or
+// per K slice) in SGPRs, a 32-bit byte offset per lane, and the hardware
+// returns zeros for offsets at or past the resource's size.  Masked lanes get
+// kOOB.  No branches and no 64-bit address arithmetic per load.
 // ---------------------------------------------------------------------------
-template <typename T>
-struct RowsDense {
-  const T *base; long ld; int rows;
-  __device__ __forceinline__ const T *row(int r) const { return r < rows ? base + (long)r * ld : nullptr; }
-};
-template <typename T>
-struct RowsGather {   // row r reads base[idx[r]] (idx clamped into [0, nsrc))
-  const T *base; long ld; int rows; const int *idx; int nsrc;
-  __device__ __forceinline__ const T *row(int r) const {
-    if (r >= rows) return nullptr;
-    int s = idx[r];
-    s = s < 0 ? 0 : (s >= nsrc ? nsrc - 1 : s);
-    return base + (long)s * ld;
-  }
-};
-// SwiGLU pairing: a tile of BN columns holds BN/2 output features.  Within
-// each wave's WN columns, blocks [0, NB/2) read gate rows and [NB/2, NB) read
-// up rows of the same features, so one lane holds gate(j) and up(j).
-template <typename T, int BN>
-struct RowsSwiGLU {
-  const T *gate; const T *up; long ld; int f;
-  __device__ __forceinline__ const T *row(int r) const {  // r = tile_n * BN + c
-    const int tile = r / BN, c = r % BN;
-    constexpr int WN = BN / 2, NBh = WN / 64;
-    const int wn = c / WN, cc = c % WN, blk = cc / 32, lane = cc % 32;
-    const bool is_up = blk >= NBh;
-    const int feat = tile * (BN / 2) + wn * (WN / 2) + (is_up ? blk - NBh : blk) * 32 + lane;
-    if (feat >= f) return nullptr;
-    return (is_up ? up : gate) + (long)feat * ld;
-  }
-};
+constexpr unsigned kOOB = 0x80000000u;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, long bytes) {
+  const long cap = 0x7ffffff0L;
+  // The resource lives in SGPRs: make its inputs provably wave-uniform.
+  const int n = __builtin_amdgcn_readfirstlane((int)(bytes < 0 ? 0 : (bytes > cap ? cap : bytes)));
+  const unsigned long a = reinterpret_cast<unsigned long>(p);
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a);
+  const unsigned hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  void *pu = reinterpret_cast<void *>(((unsigned long)hi << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(pu, (short)0, n, 0x00020000);
+}
+__device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
 
 // ---------------------------------------------------------------------------
-// Loaders: global -> registers (load) and registers -> LDS (store).
-// ROWS = operand rows in the tile (BM for A, BN for B).
+// Direct global -> LDS loads (buffer_load_dwordx4 ... lds): one instruction
+// moves 64 lanes x 16 B into 1 KB of LDS at M0 + lane * 16, so operands never
+// pass through VGPRs and no ds_write is issued.  A 1 KB block holds 8 tile
+// rows of 128 B; lane L fills physical chunk L & 7 of row L >> 3 and fetches
+// the logical chunk that the LDS swizzle (lds_off128) places there.
 // ---------------------------------------------------------------------------
-template <typename T, int ROWS, class Rows>
-struct LoadKMajor {
+typedef __attribute__((address_space(3))) char lds_char;
+
+__device__ __forceinline__ lds_char *to_lds(char *p) { return (lds_char *)p; }
+
+// The lane's source is split into a per-lane byte offset (row rl = lane >> 3
+// inside the 8-row block, and the logical chunk) and a wave-uniform one (the
+// block's first row and the K slice) that rides in the instruction's SGPR
+// offset, so a tile's worth of loads costs two VGPRs of addresses.  The
+// swizzle term (row >> 1) & 7 = (4 * (q & 1) + (rl >> 1)) & 7 depends only on
+// the block parity.  Lanes past K get kOOB: with soffset below the resource
+// size, kOOB + soffset still lies past it and does not wrap.
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *lds_dst, unsigned voff, int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)to_lds(lds_dst), 16,
+                                           voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
+}
+
+// K-major dense operand, op[r][k] = base[r * ld + k].
+template <typename T, int ROWS, int NT>
+struct DmaKMajor {
   static constexpr int E = Elem<T>::kPerChunk;
-  static constexpr int NREG = ROWS * 8 / kGemmThreads;   // chunks per thread
-  Rows src; int K;
-  __device__ __forceinline__ void load(int row0, int k0, uint4 *reg) const {
-    const int t = threadIdx.x;
-    const int q = t & 7;
-    const int k = k0 + q * E;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int r = (t >> 3) + 32 * i;
-      const T *p = src.row(row0 + r);
-      reg[i] = (p != nullptr && k < K) ? *reinterpret_cast<const uint4 *>(p + k) : make_uint4(0, 0, 0, 0);
-    }
-  }
-  __device__ __forceinline__ void store(const uint4 *reg, char *lds) const {
-    const int t = threadIdx.x;
-    const int q = t & 7;
-#pragma unroll
-    for (int i = 0; i < NREG; ++i) {
-      const int r = (t >> 3) + 32 * i;
-      *reinterpret_cast<uint4 *>(lds + lds_off128(r, q)) = reg[i];
-    }
-  }
-};
-
-template <typename T, int ROWS>
-struct LoadMNMajor {   // operand[r][k] = base[k * ld + r], r < rows, k < K
-  static constexpr int E = Elem<T>::kPerChunk;
-  static constexpr int NBLK = 8 * (ROWS / E);                 // E x E blocks per tile
-  static constexpr int BPT = (NBLK + kGemmThreads - 1) / kGemmThreads;
-  static constexpr int NREG = BPT * E;
+  static constexpr int NBLK = ROWS / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static_assert(NBLK % WAVES == 0, "blocks per wave");
   const T *base; long ld; int rows; int K;
-  __device__ __forceinline__ void load(int row0, int k0, uint4 *reg) const {
-    const int t = threadIdx.x;
+  // Fragment of the 32-row block starting at tile row r0, K sub-step s
+  // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
+  __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
+    return *reinterpret_cast<const uint4 *>(region + lds_off128(r0 + (lane & 31), 2 * s + (lane >> 5)));
+  }
+  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const long nrow = rows - row0 < ROWS ? rows - row0 : ROWS;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (long)row0 * ld, nrow * ld * (long)sizeof(T));
+    const int rl = lane >> 3, pc = lane & 7;
+    const int ldb = (int)(ld * sizeof(T));
+    unsigned voff[2];
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = t + b * kGemmThreads;
-      const int kc = blk & 7, mb = blk >> 3;
-      const int m = row0 + mb * E;
-      const bool okm = blk < NBLK && m < rows;
+    for (int par = 0; par < 2; ++par) {
+      const int c = pc ^ ((4 * par + (rl >> 1)) & 7);
+      voff[par] = k0 + c * E < K ? (unsigned)(rl * ldb + c * 16) : kOOB;
+    }
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        const int k = k0 + kc * E + e;
-        reg[b * E + e] = (okm && k < K) ? *reinterpret_cast<const uint4 *>(base + (long)k * ld + m)
-                                        : make_uint4(0, 0, 0, 0);
-      }
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+      dma16(rs, stage + q * 1024, voff[q & 1], 8 * q * ldb + k0 * (int)sizeof(T));
     }
   }
-  __device__ __forceinline__ void store(uint4 *reg, char *lds) const {
-    const int t = threadIdx.x;
+};
+
+// SwiGLU-interleaved B operand: tile column c of wave column wn holds, for
+// block b = (c mod WN) / 32, gate features (b < NB/2) or up features
+// (b >= NB/2) of the same feature range, so the epilogue pairs them in-lane.
+// Every 8-row block lies in one 32-row block and hence reads one matrix.
+template <typename T, class Cfg>
+struct DmaKMajorSwiGLU {
+  static constexpr int E = Elem<T>::kPerChunk;
+  static constexpr int BN = Cfg::BN, NT = Cfg::NT, WN = Cfg::WN, NBh = WN / 64;
+  static constexpr int NBLK = BN / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  const T *gate; const T *up; long ld; int f; int K;
+  // Fragment of the 32-row block starting at tile row r0, K sub-step s
+  // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
+  __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
+    return *reinterpret_cast<const uint4 *>(region + lds_off128(r0 + (lane & 31), 2 * s + (lane >> 5)));
+  }
+  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int feat0 = (row0 / BN) * (BN / 2);
+    const long nfeat = f - feat0 < BN / 2 ? f - feat0 : BN / 2;
+    const long bytes = nfeat * ld * (long)sizeof(T);
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gate + (long)feat0 * ld, bytes);
+    const __amdgpu_buffer_rsrc_t ru = make_rsrc(up + (long)feat0 * ld, bytes);
+    const int rl = lane >> 3, pc = lane & 7;
+    const int ldb = (int)(ld * sizeof(T));
+    unsigned voff[2];
 #pragma unroll
-    for (int b = 0; b < BPT; ++b) {
-      const int blk = t + b * kGemmThreads;
-      if (blk >= NBLK) continue;
-      const int kc = blk & 7, mb = blk >> 3;
-      transpose_chunks(reg + b * E, T{});
+    for (int par = 0; par < 2; ++par) {
+      const int c = pc ^ ((4 * par + (rl >> 1)) & 7);
+      voff[par] = k0 + c * E < K ? (unsigned)(rl * ldb + c * 16) : kOOB;
+    }
 #pragma unroll
-      for (int j = 0; j < E; ++j)
-        *reinterpret_cast<uint4 *>(lds + lds_off128(mb * E + j, kc)) = reg[b * E + j];
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+      const int row = 8 * q;                                // first tile column of the block
+      const int wn = row / WN, blk = (row % WN) / 32;
+      const bool is_up = blk >= NBh;
+      const int fl = wn * (WN / 2) + (is_up ? blk - NBh : blk) * 32 + (row % 32);
+      dma16(is_up ? ru : rg, stage + q * 1024, voff[q & 1], fl * ldb + k0 * (int)sizeof(T));
+    }
+  }
+};
+
+// MN-major operand, op[r][k] = base[k * ld + r] (r < rows, k < K): the stage
+// region holds BK k-rows of ROWS elements each (CPR 16-byte chunks per k-row);
+// chunk c of k-row k sits at physical chunk c ^ (4 (k & 3)).  A 1 KB load
+// block covers RPB = 64 / CPR whole k-rows, so a lane's swizzle depends only
+// on its position and the block parity, as in the K-major case.
+//
+// Fragments (K-major from the MFMA's point of view) are read with gfx950's
+// transposing LDS read ds_read_b64_tr_b16: in each 16-lane group, lane j
+// addresses 4 consecutive elements (4 m values) of k-row K0 + j / 4 at
+// m = M0 + 4 (j % 4), and lane i receives the 4 values of column m = M0 + i
+// for k = K0 .. K0 + 3.  Two such reads (K0 and K0 + 4) give the 8 K-values a
+// 32x32x16 bf16 operand lane needs; with k-rows k .. k+3 in distinct 64-byte
+// bank groups (the swizzle above) each half-wave is conflict-free.  f32
+// operands (no transposing read) are read element by element.
+template <typename T, int ROWS, int NT>
+struct DmaMNMajor {
+  static constexpr int E = Elem<T>::kPerChunk;
+  static constexpr int BK = 8 * E;
+  static constexpr int ROWB = ROWS * (int)sizeof(T);
+  static constexpr int CPR = ROWB / 16;
+  static constexpr int RPB = 64 / CPR;
+  static_assert(CPR == 16 || CPR == 32, "k-row of 256 or 512 bytes");
+  static constexpr int NBLK = BK / RPB, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static_assert(NBLK % WAVES == 0, "blocks per wave");
+  const T *base; long ld; int rows; int K;
+
+  __device__ static __forceinline__ int off(int k, int m) {
+    return k * ROWB + ((((m / E) ^ (4 * (k & 3)))) << 4) + (m % E) * (int)sizeof(T);
+  }
+  __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
+    if constexpr (sizeof(T) == 2) {
+      typedef short v4s __attribute__((ext_vector_type(4)));
+      typedef __attribute__((address_space(3))) v4s lds_v4s;
+      const int g = lane >> 4, j = lane & 15;
+      const int k = 16 * s + 8 * (g >> 1) + (j >> 2);
+      const int m = r0 + 16 * (g & 1) + 4 * (j & 3);
+      const char *p = region + off(k, m);
+      const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)to_lds(const_cast<char *>(p)));
+      const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)to_lds(const_cast<char *>(p + 4 * ROWB)));
+      const uint2 a = __builtin_bit_cast(uint2, lo), b = __builtin_bit_cast(uint2, hi);
+      return make_uint4(a.x, a.y, b.x, b.y);
+    } else {
+      const int m = r0 + (lane & 31);
+      const int k = 8 * s + 4 * (lane >> 5);
+      uint4 v;
+      v.x = *reinterpret_cast<const unsigned *>(region + off(k, m));
+      v.y = *reinterpret_cast<const unsigned *>(region + off(k + 1, m));
+      v.z = *reinterpret_cast<const unsigned *>(region + off(k + 2, m));
+      v.w = *reinterpret_cast<const unsigned *>(region + off(k + 3, m));
+      return v;
+    }
+  }
+  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const long nk = K - k0 < BK ? K - k0 : BK;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (long)k0 * ld, nk * ld * (long)sizeof(T));
+    const int kl = lane / CPR, pc = lane % CPR;
+    const int ldb = (int)(ld * sizeof(T));
+    unsigned voff[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int c = pc ^ (4 * ((RPB * par + kl) & 3));
+      voff[par] = row0 + c * E < rows ? (unsigned)(kl * ldb + c * 16) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+      dma16(rs, stage + q * 1024, voff[q & 1], RPB * q * ldb + row0 * (int)sizeof(T));
     }
   }
 };
@@ -151,11 +237,20 @@ struct TileSched { int mt, nt, group_m, k_splits; };
 
 // ---------------------------------------------------------------------------
 // The kernel body.  Each block computes one BM x BN tile (optionally one K
-// split of it) and hands the accumulators to the epilogue.
+// split of it) and hands the accumulators to the epilogue.  Operands arrive
+// by direct global -> LDS loads into two stages.
 // ---------------------------------------------------------------------------
+// Waits for this wave's direct loads and LDS operations, then barriers: after
+// it every wave's loads into LDS have landed and every earlier LDS read of
+// the workgroup has retired.
+__device__ __forceinline__ void vm_lds_barrier() {
+  __builtin_amdgcn_s_waitcnt(0);     // vmcnt = expcnt = lgkmcnt = 0
+  __builtin_amdgcn_s_barrier();
+}
+
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi &epi, int K,
-                                          const TileSched &ts, char *lds) {
+                                          const TileSched &ts, char *lds0, char *lds1) {
   constexpr int E = Elem<T>::kPerChunk;
   constexpr int BK = 8 * E;                    // K elements per LDS slice
   constexpr int MB = Cfg::MB, NB = Cfg::NB;
@@ -173,7 +268,7 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
 
   f32x16 acc[MB][NB];
 #pragma unroll
@@ -183,50 +278,63 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  uint4 ra[LA::NREG], rb[LB::NREG];
-  if (kt0 < kt1) {
-    la.load(m0, kt0 * BK, ra);
-    lb.load(n0, kt0 * BK, rb);
-    la.store(ra, lds);
-    lb.store(rb, lds + Cfg::BM * 128);
-  }
-  __syncthreads();
-
-  const int arow = wm * Cfg::WM + (lane & 31);
-  const int brow = wn * Cfg::WN + (lane & 31);
-  const int hsel = lane >> 5;
-  for (int kt = kt0; kt < kt1; ++kt) {
-    const int cur = (kt - kt0) & 1;
-    char *sa = lds + cur * Cfg::LDS_STAGE;
-    char *sb = sa + Cfg::BM * 128;
-    const bool more = kt + 1 < kt1;
-    if (more) {
-      la.load(m0, (kt + 1) * BK, ra);
-      lb.load(n0, (kt + 1) * BK, rb);
-    }
+  uint4 fa[2][MB], fb[2][NB];
+  const int ar0 = wm * Cfg::WM, br0 = wn * Cfg::WN;
+  auto read_frags = [&](const char *stage, int s, uint4 *a, uint4 *b) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) a[i] = LA::frag(stage, ar0 + 32 * i, s, lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = LB::frag(stage + Cfg::BM * 128, br0 + 32 * j, s, lane);
+  };
+  auto issue = [&](int kt, char *stage) {
+    la.issue(m0, kt * BK, stage);
+    lb.issue(n0, kt * BK, stage + Cfg::BM * 128);
+  };
+  const int nk = kt1 - kt0;
+  if (nk > 0) issue(kt0, lds0);
+  vm_lds_barrier();
+  if (nk > 0) read_frags(lds0, 0, fa[0], fb[0]);
+  if (nk > 1) issue(kt0 + 1, lds1);
+  // One K tile on stage sc (the other stage is sn): each sub-step's MFMAs
+  // run while the next sub-step's fragments are read.  Before sub-step 3:
+  // wait for the next tile's loads, barrier (which also retires every read
+  // of sc), issue tile it+2 into sc and read sub-step 0 of the next tile.
+  // The two stages are distinct LDS objects and the loop is unrolled by two,
+  // so the compiler can tell that reads of one stage do not wait for the
+  // direct loads still in flight into the other.
+  constexpr int NM = MB * NB;                  // MFMAs per sub-step
+  constexpr int NR = MB + NB;                  // fragment reads per sub-step
+  auto ktile = [&](int it, char *sc, const char *sn) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const int ch = 2 * s + hsel;
-      uint4 fa[MB], fb[NB];
+      if (s < 3) read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
+      if (s == 3) {
+        vm_lds_barrier();
+        if (it + 2 < nk) issue(kt0 + it + 2, sc);
+        if (it + 1 < nk) read_frags(sn, 0, fa[0], fb[0]);
+      }
 #pragma unroll
       for (int i = 0; i < MB; ++i)
-        fa[i] = *reinterpret_cast<const uint4 *>(sa + lds_off128(arow + 32 * i, ch));
 #pragma unroll
-      for (int j = 0; j < NB; ++j)
-        fb[j] = *reinterpret_cast<const uint4 *>(sb + lds_off128(brow + 32 * j, ch));
+        for (int j = 0; j < NB; ++j) mma32(fa[s & 1][i], fb[s & 1][j], acc[i][j], T{});
+      if constexpr (sizeof(T) == 2) {
+        if (s < 3) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) mma32(fa[i], fb[j], acc[i][j], T{});
+          for (int q = 0; q < NM; ++q) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
+          }
+        }
+      }
     }
-    if (more) {
-      char *na = lds + (cur ^ 1) * Cfg::LDS_STAGE;
-      la.store(ra, na);
-      lb.store(rb, na + Cfg::BM * 128);
-    }
-    __syncthreads();
+  };
+  int it = 0;
+  for (; it + 1 < nk; it += 2) {
+    ktile(it, lds0, lds1);
+    ktile(it + 1, lds1, lds0);
   }
-  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, lds);
+  if (it < nk) ktile(it, lds0, lds1);
+  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, lds0, lds1);
 }
 
 // Result-layout helpers: row / column of accumulator register r of block

@@ -69,8 +69,14 @@ struct StageScope {
 // GEMM dispatch.  The 256x256 tile is used when it still yields at least one
 // tile per compute unit; otherwise 128x128.
 // ---------------------------------------------------------------------------
-using Big = Tile<256, 256>;
+using Big = Tile<256, 256, 4, 2>;
 using Small = Tile<128, 128>;
+
+// Operand loaders for a tile shape: K-major / MN-major A (BM rows) and B (BN rows).
+template <typename T, class Cfg> using KA = DmaKMajor<T, Cfg::BM, Cfg::NT>;
+template <typename T, class Cfg> using KB = DmaKMajor<T, Cfg::BN, Cfg::NT>;
+template <typename T, class Cfg> using MA = DmaMNMajor<T, Cfg::BM, Cfg::NT>;
+template <typename T, class Cfg> using MB_ = DmaMNMajor<T, Cfg::BN, Cfg::NT>;
 
 inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N, 256) >= 256; }
 
@@ -80,15 +86,15 @@ int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc
   EpiStore<OutT, ResT> epi{C, ldc, M, N, alpha, alpha_dev, R, ldr, accumulate, 0};
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, N)) {
-      LoadKMajor<T, Big::BM, RowsDense<T>> la{{A, lda, M}, K};
-      LoadKMajor<T, Big::BN, RowsDense<T>> lb{{Bm, ldb, N}, K};
+      KA<T, Big> la{A, lda, M, K};
+      KB<T, Big> lb{Bm, ldb, N, K};
       MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, N, K, 8, 1, s)));
       return MTP_OK;
     }
   }
   {
-    LoadKMajor<T, Small::BM, RowsDense<T>> la{{A, lda, M}, K};
-    LoadKMajor<T, Small::BN, RowsDense<T>> lb{{Bm, ldb, N}, K};
+    KA<T, Small> la{A, lda, M, K};
+    KB<T, Small> lb{Bm, ldb, N, K};
     MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, N, K, 8, 1, s)));
   }
   return MTP_OK;
@@ -99,8 +105,8 @@ int gemm_qkv_rope_cfg(const T *xa, const T *W, T *qkv, const int *pos, const flo
                       int A, hipStream_t s) {
   const int N = 3 * A;
   EpiRope<T, HALF> epi{qkv, (long)N, M, N, A, pos, rope};
-  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xa, (long)d, M}, d};
-  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, N}, d};
+  KA<T, Cfg> la{xa, (long)d, M, d};
+  KB<T, Cfg> lb{W, (long)d, N, d};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, N, d, 8, 1, s)));
   return MTP_OK;
 }
@@ -129,16 +135,16 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, 2L * f)) {
       EpiSwiGLU<T> epi{out, (long)f, M, f};
-      LoadKMajor<T, Big::BM, RowsDense<T>> la{{y, (long)d, M}, d};
-      LoadKMajor<T, Big::BN, RowsSwiGLU<T, Big::BN>> lb{{Wg, Wu, (long)d, f}, d};
+      KA<T, Big> la{y, (long)d, M, d};
+      DmaKMajorSwiGLU<T, Big> lb{Wg, Wu, (long)d, f, d};
       MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, 1, s)));
       return MTP_OK;
     }
   }
   {
     EpiSwiGLU<T> epi{out, (long)f, M, f};
-    LoadKMajor<T, Small::BM, RowsDense<T>> la{{y, (long)d, M}, d};
-    LoadKMajor<T, Small::BN, RowsSwiGLU<T, Small::BN>> lb{{Wg, Wu, (long)d, f}, d};
+    KA<T, Small> la{y, (long)d, M, d};
+    DmaKMajorSwiGLU<T, Small> lb{Wg, Wu, (long)d, f, d};
     MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, 2 * ceil_div(f, Small::BN / 2) * (Small::BN / 2), d, 8,
                                    1, s)));
   }
@@ -150,8 +156,8 @@ int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, flo
                     int d, hipStream_t s) {
   const int nt = ceil_div(V, Cfg::BN);
   EpiCEFwd epi{lab, part, target, M, V, nt};
-  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xhat, (long)d, M}, d};
-  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, V}, d};
+  KA<T, Cfg> la{xhat, (long)d, M, d};
+  KB<T, Cfg> lb{W, (long)d, V, d};
   // all row tiles of one vocabulary tile run next to each other: W is read once
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
   return MTP_OK;
@@ -161,8 +167,8 @@ template <typename T, class Cfg>
 int gemm_ce_grad_cfg(const T *xhat, const T *W, const int *lab, const float *lse, T *dz, int M, int V, int d,
                      hipStream_t s) {
   EpiCEGrad<T> epi{lab, lse, dz, (long)V, M, V};
-  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{xhat, (long)d, M}, d};
-  LoadKMajor<T, Cfg::BN, RowsDense<T>> lb{{W, (long)d, V}, d};
+  KA<T, Cfg> la{xhat, (long)d, M, d};
+  KB<T, Cfg> lb{W, (long)d, V, d};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
   return MTP_OK;
 }
@@ -172,8 +178,8 @@ template <typename T, class Cfg>
 int gemm_dx_cfg(const T *dz, const T *W, float *dxs, long slab, int M, int V, int d, const float *scale,
                 int splits, hipStream_t s) {
   EpiStore<float, float> epi{dxs, (long)d, M, d, 1.f, scale, nullptr, 0, 0, slab};
-  LoadKMajor<T, Cfg::BM, RowsDense<T>> la{{dz, (long)V, M}, V};
-  LoadMNMajor<T, Cfg::BN> lb{W, (long)d, d, V};
+  KA<T, Cfg> la{dz, (long)V, M, V};
+  MB_<T, Cfg> lb{W, (long)d, d, V};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, d, V, 8, splits, s)));
   return MTP_OK;
 }
@@ -183,8 +189,8 @@ template <typename T, class Cfg>
 int gemm_dw_cfg(const T *dz, const T *xhat, float *dW, int M, int V, int d, const float *scale, int accumulate,
                 hipStream_t s) {
   EpiStore<float, float> epi{dW, (long)d, V, d, 1.f, scale, nullptr, 0, accumulate, 0};
-  LoadMNMajor<T, Cfg::BM> la{dz, (long)V, V, M};
-  LoadMNMajor<T, Cfg::BN> lb{xhat, (long)d, d, M};
+  MA<T, Cfg> la{dz, (long)V, V, M};
+  MB_<T, Cfg> lb{xhat, (long)d, d, M};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, V, d, M, 8, 1, s)));
   return MTP_OK;
 }
