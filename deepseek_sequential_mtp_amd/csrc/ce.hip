@@ -36,6 +36,44 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restric
   }
 }
 
+// dz = softmax(z) - onehot(label) on labelled rows, 0 on the others, from the
+// stored fp32 logits and the row's log-sum-exp; stored unscaled in T (the
+// depth's scale lambda / (D * denom) is applied by the consuming GEMMs).
+// V is a multiple of 4: each thread handles 4 consecutive columns.
+template <typename T>
+__global__ __launch_bounds__(256) void ce_dz_kernel(const float *__restrict__ z, const float *__restrict__ lse,
+                                                    const int32_t *__restrict__ labels, T *__restrict__ dz,
+                                                    int V) {
+  const long row = blockIdx.y;
+  const int lab = labels[row];
+  const float l = lse[row];
+  const float4 *zr = reinterpret_cast<const float4 *>(z + row * V);
+  T *dr = dz + row * V;
+  for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
+    float g[4] = {0.f, 0.f, 0.f, 0.f};
+    if (lab >= 0) {
+      const float4 v = zr[c4];
+      const float zz[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) g[e] = exp2f((zz[e] - l) * kLog2e) - (4 * c4 + e == lab ? 1.f : 0.f);
+    }
+    store4(dr + 4 * c4, g);
+  }
+}
+
+template <typename T>
+hipError_t launch_ce_dz(const float *z, const float *lse, const int32_t *labels, T *dz, int N, int V,
+                        hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  const int bx = min((V / 4 + 1023) / 1024, 65535);
+  hipLaunchKernelGGL(ce_dz_kernel<T>, dim3(bx, N), dim3(256), 0, s, z, lse, labels, dz, V);
+  return hipGetLastError();
+}
+template hipError_t launch_ce_dz<bf16_t>(const float *, const float *, const int32_t *, bf16_t *, int, int,
+                                         hipStream_t);
+template hipError_t launch_ce_dz<float>(const float *, const float *, const int32_t *, float *, int, int,
+                                        hipStream_t);
+
 // One block: sum of the row losses of depth k (double, fixed order) and the
 // count of labelled rows; scale[k] = lambda / (D * denom_k) for the backward
 // (0 for an empty depth under the valid-row mean).

@@ -38,6 +38,16 @@ __device__ __forceinline__ float load_elem(const bf16_t *p, long i) { return bf1
 __device__ __forceinline__ float load_elem(const float *p, long i) { return p[i]; }
 __device__ __forceinline__ void store_elem(bf16_t *p, long i, float v) { p[i].bits = f32_to_bf16(v); }
 __device__ __forceinline__ void store_elem(float *p, long i, float v) { p[i] = v; }
+// 4 consecutive values in one store (p 8-byte aligned for bf16, 16 for f32).
+__device__ __forceinline__ void store4(bf16_t *p, const float (&v)[4]) {
+  uint2 w;
+  w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+  w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+  *reinterpret_cast<uint2 *>(p) = w;
+}
+__device__ __forceinline__ void store4(float *p, const float (&v)[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
 
 // Unpack / pack one 16-byte chunk to / from floats.
 __device__ __forceinline__ void chunk_to_f32(const uint4 &c, float *o, bf16_t) {

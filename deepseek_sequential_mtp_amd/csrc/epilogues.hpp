@@ -129,11 +129,13 @@ struct EpiSwiGLU {
 // Linear-CE forward, one BM x BN tile of logits z = x_hat W^T: per row, the
 // tile's max m_t and s_t = sum exp(z - m_t) over its valid columns go to
 // part[row * nt + tile_n] (float2), and the target logit z[row, label[row]]
-// to target[row] when the label falls in this tile.  Reductions go through
-// LDS (the staging buffers are free after the main loop).
+// to target[row] when the label falls in this tile.  The fp32 logits are also
+// stored to zout [M, V] for the backward (softmax - onehot needs the row's
+// final log-sum-exp, known only after every vocabulary tile).  Reductions go
+// through LDS (the staging buffers are free after the main loop).
 // ---------------------------------------------------------------------------
 struct EpiCEFwd {
-  const int *labels; float2 *part; float *target; int M, V, nt;
+  const int *labels; float2 *part; float *target; float *zout; int M, V, nt;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
                                         int wn, int lane, int, char *lds0, char *lds1) const {
@@ -183,7 +185,10 @@ struct EpiCEFwd {
         for (int j = 0; j < Cfg::NB; ++j) {
           const int col = n0 + acc_col<Cfg>(wn, j, lane);
           const float z = acc[i][j][r];
-          if (col < V) s += exp2f((z - m) * kLog2e);
+          if (col < V) {
+            s += exp2f((z - m) * kLog2e);
+            if (row < M) zout[(long)row * V + col] = z;
+          }
           if (col == lab) target[row] = z;
         }
         red[at(rl, slot)] = s;
@@ -194,37 +199,6 @@ struct EpiCEFwd {
       for (int q = 0; q < 64; ++q) s += red[at(t, q)];
       part[(long)(m0 + t) * nt + n0 / Cfg::BN] = make_float2(mrow[t], s);
     }
-  }
-};
-
-// ---------------------------------------------------------------------------
-// Linear-CE backward, recompute pass: dz = softmax(z) - onehot(label) on
-// labelled rows, 0 on the others, stored (unscaled) in OutT [M, ldz].  The
-// depth's scale lambda / (D * denom) is applied by the consuming GEMMs.
-// ---------------------------------------------------------------------------
-template <typename OutT>
-struct EpiCEGrad {
-  const int *labels; const float *lse; OutT *dz; long ldz; int M, V;
-  template <class Cfg>
-  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *, char *) const {
-#pragma unroll
-    for (int i = 0; i < Cfg::MB; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
-        if (row >= M) continue;
-        const int lab = labels[row];
-        const float l = lse[row];
-#pragma unroll
-        for (int j = 0; j < Cfg::NB; ++j) {
-          const int col = n0 + acc_col<Cfg>(wn, j, lane);
-          if (col >= V) continue;
-          float g = 0.f;
-          if (lab >= 0) g = exp2f((acc[i][j][r] - l) * kLog2e) - (col == lab ? 1.f : 0.f);
-          store_elem(dz, (long)row * ldz + col, g);
-        }
-      }
   }
 };
 

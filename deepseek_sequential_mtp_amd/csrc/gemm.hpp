@@ -75,6 +75,7 @@ struct DmaKMajor {
   static constexpr int E = Elem<T>::kPerChunk;
   static constexpr int NBLK = ROWS / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
   static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kReads = 1;          // LDS read instructions per fragment
   const T *base; long ld; int rows; int K;
   // Fragment of the 32-row block starting at tile row r0, K sub-step s
   // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
@@ -111,6 +112,7 @@ struct DmaKMajorSwiGLU {
   static constexpr int E = Elem<T>::kPerChunk;
   static constexpr int BN = Cfg::BN, NT = Cfg::NT, WN = Cfg::WN, NBh = WN / 64;
   static constexpr int NBLK = BN / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static constexpr int kReads = 1;
   const T *gate; const T *up; long ld; int f; int K;
   // Fragment of the 32-row block starting at tile row r0, K sub-step s
   // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
@@ -169,6 +171,7 @@ struct DmaMNMajor {
   static_assert(CPR == 16 || CPR == 32, "k-row of 256 or 512 bytes");
   static constexpr int NBLK = BK / RPB, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
   static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kReads = sizeof(T) == 2 ? 2 : 4;
   const T *base; long ld; int rows; int K;
 
   __device__ static __forceinline__ int off(int k, int m) {
@@ -248,6 +251,18 @@ __device__ __forceinline__ void vm_lds_barrier() {
   __builtin_amdgcn_s_barrier();
 }
 
+// Scheduling pattern of one sub-step: NM slots of one MFMA followed by the
+// slot's share of the NR LDS reads of the next sub-step.
+template <int NM, int NR, int Q = 0>
+__device__ __forceinline__ void sched_interleave() {
+  if constexpr (Q < NM) {
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
+    constexpr int nr = (Q + 1) * NR / NM - Q * NR / NM;
+    if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // DS read
+    sched_interleave<NM, NR, Q + 1>();
+  }
+}
+
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi &epi, int K,
                                           const TileSched &ts, char *lds0, char *lds1) {
@@ -302,8 +317,8 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
   // The two stages are distinct LDS objects and the loop is unrolled by two,
   // so the compiler can tell that reads of one stage do not wait for the
   // direct loads still in flight into the other.
-  constexpr int NM = MB * NB;                  // MFMAs per sub-step
-  constexpr int NR = MB + NB;                  // fragment reads per sub-step
+  constexpr int NM = MB * NB;                                  // MFMAs per sub-step
+  constexpr int NR = MB * LA::kReads + NB * LB::kReads;        // LDS reads per sub-step
   auto ktile = [&](int it, char *sc, const char *sn) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -319,11 +334,7 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
         for (int j = 0; j < NB; ++j) mma32(fa[s & 1][i], fb[s & 1][j], acc[i][j], T{});
       if constexpr (sizeof(T) == 2) {
         if (s < 3) {
-#pragma unroll
-          for (int q = 0; q < NM; ++q) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
-            if (q < NR) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // DS read
-          }
+          sched_interleave<NM, NR>();
         }
       }
     }

@@ -152,23 +152,13 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
 }
 
 template <typename T, class Cfg>
-int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, int M, int V,
-                    int d, hipStream_t s) {
+int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, float *z, int M,
+                    int V, int d, hipStream_t s) {
   const int nt = ceil_div(V, Cfg::BN);
-  EpiCEFwd epi{lab, part, target, M, V, nt};
+  EpiCEFwd epi{lab, part, target, z, M, V, nt};
   KA<T, Cfg> la{xhat, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, V, d};
   // all row tiles of one vocabulary tile run next to each other: W is read once
-  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
-  return MTP_OK;
-}
-
-template <typename T, class Cfg>
-int gemm_ce_grad_cfg(const T *xhat, const T *W, const int *lab, const float *lse, T *dz, int M, int V, int d,
-                     hipStream_t s) {
-  EpiCEGrad<T> epi{lab, lse, dz, (long)V, M, V};
-  KA<T, Cfg> la{xhat, (long)d, M, d};
-  KB<T, Cfg> lb{W, (long)d, V, d};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
   return MTP_OK;
 }
@@ -253,6 +243,8 @@ int check_chain_ptrs(const mtp_chain_args *a) {
   return MTP_OK;
 }
 
+constexpr int kChainParts = 13;  // workspace regions of the chain call
+
 template <typename T>
 size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
   const long N = (long)a->B * a->T;
@@ -275,7 +267,7 @@ size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
 
 template <typename T>
 int chain_run(const mtp_chain_args *a, hipStream_t s) {
-  void *p[13];
+  void *p[kChainParts];
   Carve c(a->workspace);
   chain_layout<T>(a, c, p);
   const int B = a->B, Tl = a->T, d = a->d, H = a->n_heads, hd = a->head_dim, f = a->ffn, V = a->V;
@@ -390,6 +382,8 @@ CeDims ce_dims(const mtp_ce_args *a) {
   return c;
 }
 
+constexpr int kCeParts = 14;     // workspace regions of the CE call
+
 template <typename T>
 size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   const CeDims m = ce_dims<T>(a);
@@ -404,6 +398,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[8] = c.take<int32_t>(a->D);                  // counts
   p[9] = c.take<float>(a->D);                    // backward scales
   p[10] = c.take<T>(m.N * m.V);                  // dz = softmax - onehot
+  p[13] = c.take<float>(m.N * m.V);              // fp32 logits of the current depth
   p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
   return c.off;
@@ -411,7 +406,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
 
 template <typename T>
 int ce_run(const mtp_ce_args *a, hipStream_t s) {
-  void *p[13];
+  void *p[kCeParts];
   Carve c(a->workspace);
   ce_layout<T>(a, c, p);
   const CeDims m = ce_dims<T>(a);
@@ -427,6 +422,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   T *dz = (T *)p[10];
   float *dxs = (float *)p[11];
   float *dg_part = (float *)p[12];
+  float *zbuf = (float *)p[13];
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
   const long slab = m.N * m.d;
@@ -443,7 +439,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     {
       MTP_STAGE(MTP_STAGE_CE_FWD);
       st = pick<T>(m.big, [&](auto cfg) {
-        return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, N, V, d, s);
+        return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, zbuf, N, V, d,
+                                                  s);
       });
     }
     if (st) return st;
@@ -455,11 +452,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_CE_GRAD);
-      st = pick<T>(m.big, [&](auto cfg) {
-        return gemm_ce_grad_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, lse, dz, N, V, d, s);
-      });
+      MTP_TRY(launch_ce_dz<T>(zbuf, lse, lab, dz, N, V, s));
     }
-    if (st) return st;
     const bool big_dx = sizeof(T) == 2 && use_big(N, d);
     {
       MTP_STAGE(MTP_STAGE_CE_DX);
@@ -542,7 +536,7 @@ const char *mtp_strerror(int status) {
 size_t mtp_chain_workspace_size(const mtp_chain_args *a) {
   if (check_chain(a) != MTP_OK) return 0;
   Carve c(nullptr);
-  void *p[13];
+  void *p[kChainParts];
   return a->dtype == MTP_BF16 ? chain_layout<bf16_t>(a, c, p) : chain_layout<float>(a, c, p);
 }
 
@@ -558,7 +552,7 @@ int mtp_chain_forward(const mtp_chain_args *a, void *stream) {
 size_t mtp_ce_workspace_size(const mtp_ce_args *a) {
   if (check_ce(a) != MTP_OK) return 0;
   Carve c(nullptr);
-  void *p[13];
+  void *p[kCeParts];
   return a->dtype == MTP_BF16 ? ce_layout<bf16_t>(a, c, p) : ce_layout<float>(a, c, p);
 }
 
