@@ -51,8 +51,8 @@ class CeArgs(C.Structure):
                 ("denom", C.c_double), ("h", C.POINTER(vp)), ("labels", vp), ("W_out", vp),
                 ("g_out", vp), ("loss_sum", vp), ("counts", vp), ("loss", vp), ("loss_mtp", vp),
                 ("lse", vp), ("dh", C.POINTER(vp)), ("dW_out", vp), ("dg_out", vp),
-                ("accumulate", C.c_int), ("device_error", vp), ("workspace", vp),
-                ("workspace_bytes", C.c_size_t)]
+                ("accumulate", C.c_int), ("device_error", vp), ("logit_slab_bytes", C.c_size_t),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
 class VerifyArgs(C.Structure):
@@ -173,8 +173,10 @@ def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Ten
 def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: torch.Tensor,
                     g_out: torch.Tensor, *, lam: float, eps: float = 1e-6, reduce: str = "fixed",
                     denom: float = 0.0, accumulate: bool = False, want_lse: bool = False,
-                    out: Optional[Dict] = None, cache: Optional[Dict] = None, stream=None) -> Dict:
-    """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].
+                    logit_slab_bytes: int = 0, out: Optional[Dict] = None, cache: Optional[Dict] = None,
+                    stream=None) -> Dict:
+    """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].  logit_slab_bytes
+    bounds the fp32 logit slab (0: the library default).
     Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error)."""
     D, B, T = labels.shape
     V, d = W_out.shape
@@ -195,7 +197,7 @@ def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: tor
     a = CeArgs(B, T, d, V, D, _dtype_code(W_out), eps, lam, red, float(denom), hp, _p(labels),
                _p(W_out), _p(g_out), _p(out["loss_sum"]), _p(out["counts"]), _p(out["loss"]),
                _p(out["loss_mtp"]), _p(out["lse"]), dhp, _p(out["dW_out"]), _p(out["dg_out"]),
-               1 if accumulate else 0, _p(out["device_error"]), None, 0)
+               1 if accumulate else 0, _p(out["device_error"]), int(logit_slab_bytes), None, 0)
     lib = load()
     nbytes = lib.mtp_ce_workspace_size(C.byref(a))
     if nbytes == 0:

@@ -1,4 +1,4 @@
-// K5: segment-causal multi-head attention of the MTP block (M7.6 0x03C: the
+// Segment-causal multi-head attention of the MTP block (M7.6 0x03C: the
 // block attends under a causal mask; 0x04C: the segment rule shapes the
 // attention graph, not only the loss).  Query row i of a batch row sees keys
 // j with run_start(i) <= j <= i (a padding row: itself only); scores are

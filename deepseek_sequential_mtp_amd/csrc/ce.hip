@@ -76,7 +76,8 @@ template hipError_t launch_ce_dz<float>(const float *, const float *, const int3
 
 // One block: sum of the row losses of depth k (double, fixed order) and the
 // count of labelled rows; scale[k] = lambda / (D * denom_k) for the backward
-// (0 for an empty depth under the valid-row mean).
+// (0 for an empty depth under the valid-row mean).  With row_loss = nullptr
+// only the count and the scale are produced (they depend on the labels alone).
 __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict__ row_loss,
                                                          const int32_t *__restrict__ labels, int N, int k,
                                                          int D, int valid_mean, double denom, float lambda,
@@ -87,7 +88,7 @@ __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict
   double s = 0.0;
   int c = 0;
   for (int i = t; i < N; i += 1024) {
-    s += (double)row_loss[i];
+    if (row_loss != nullptr) s += (double)row_loss[i];
     c += labels[i] >= 0 ? 1 : 0;
   }
   s = warp_sum(s);
@@ -98,7 +99,7 @@ __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict
     double ts = 0.0;
     int tc = 0;
     for (int w = 0; w < 16; ++w) { ts += shs[w]; tc += shc[w]; }
-    acc_sum[k] = ts;
+    if (row_loss != nullptr) acc_sum[k] = ts;
     acc_cnt[k] = tc;
     const double den = valid_mean ? (double)tc : denom;
     scale[k] = den > 0.0 ? (float)((double)lambda / ((double)D * den)) : 0.f;

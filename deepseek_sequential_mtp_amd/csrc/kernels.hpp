@@ -9,7 +9,7 @@
 
 namespace mtp {
 
-// K1 rows / masks / labels / counts
+// rows / masks / labels / counts
 hipError_t launch_rows(const int32_t *tokens, const int32_t *seg, int B, int T, int V, int D,
                        int32_t *run_start, int32_t *pos, uint8_t *state_mask, uint8_t *loss_mask,
                        int32_t *labels, int32_t *counts, int32_t *device_error, int32_t *cnt_part,

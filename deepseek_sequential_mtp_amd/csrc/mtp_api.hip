@@ -367,7 +367,10 @@ int check_ce_ptrs(const mtp_ce_args *a) {
 
 struct CeDims {
   long N; int d, V, nt, splits; bool big;
+  long slab;          // rows per logit slab
 };
+
+constexpr size_t kDefaultLogitSlab = size_t(1) << 30;
 
 template <typename T>
 CeDims ce_dims(const mtp_ce_args *a) {
@@ -375,10 +378,14 @@ CeDims ce_dims(const mtp_ce_args *a) {
   c.N = (long)a->B * a->T;
   c.d = a->d;
   c.V = a->V;
-  c.big = sizeof(T) == 2 && use_big(c.N, c.V);
+  const size_t budget = a->logit_slab_bytes ? a->logit_slab_bytes : kDefaultLogitSlab;
+  long r = (long)(budget / ((size_t)c.V * sizeof(float)));
+  if (r >= 256) r -= r % 256;
+  c.slab = r < 1 ? 1 : (r > c.N ? c.N : r);
+  c.big = sizeof(T) == 2 && use_big(c.slab, c.V);
   c.nt = ceil_div(c.V, c.big ? 256 : 128);
-  const bool big_dx = sizeof(T) == 2 && use_big(c.N, c.d);
-  c.splits = dx_splits((int)c.N, c.d, c.V, big_dx);
+  const bool big_dx = sizeof(T) == 2 && use_big(c.slab, c.d);
+  c.splits = dx_splits((int)c.slab, c.d, c.V, big_dx);
   return c;
 }
 
@@ -390,17 +397,17 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[0] = c.take<T>(m.N * m.d);                   // x_hat
   p[1] = c.take<float>(m.N);                     // r = 1 / rms
   p[2] = c.take<int32_t>(m.N);                   // sanitised labels
-  p[3] = c.take<float2>(m.N * m.nt);             // (max, sumexp) per row and vocab tile
+  p[3] = c.take<float2>(m.slab * m.nt);          // (max, sumexp) per slab row and vocab tile
   p[4] = c.take<float>(m.N);                     // target logit
   p[5] = c.take<float>(m.N);                     // lse
   p[6] = c.take<float>(m.N);                     // row loss
   p[7] = c.take<double>(a->D);                   // loss sums
   p[8] = c.take<int32_t>(a->D);                  // counts
   p[9] = c.take<float>(a->D);                    // backward scales
-  p[10] = c.take<T>(m.N * m.V);                  // dz = softmax - onehot
-  p[13] = c.take<float>(m.N * m.V);              // fp32 logits of the current depth
+  p[10] = c.take<T>(m.slab * m.V);               // dz = softmax - onehot of the slab
   p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
+  p[13] = c.take<float>(m.slab * m.V);           // fp32 logits of the slab
   return c.off;
 }
 
@@ -425,11 +432,12 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   float *zbuf = (float *)p[13];
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
-  const long slab = m.N * m.d;
+  const long slab = m.N * m.d;                   // stride of the dx_hat split partials
   if (a->device_error) MTP_TRY(fill_i32(a->device_error, 1, 0, s));
 
   for (int k = 0; k < D; ++k) {
     const T *h = static_cast<const T *>(a->h[k]);
+    const int dw_acc0 = (k > 0 || a->accumulate) ? 1 : 0;
     int st = 0;
     {
       MTP_STAGE(MTP_STAGE_OUT_NORM);
@@ -437,45 +445,58 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
                                  a->eps, s));
     }
     {
-      MTP_STAGE(MTP_STAGE_CE_FWD);
-      st = pick<T>(m.big, [&](auto cfg) {
-        return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat, (const T *)a->W_out, lab, part, target, zbuf, N, V, d,
-                                                  s);
-      });
+      // the backward scale depends on the labels only: known before any slab
+      MTP_STAGE(MTP_STAGE_CE_REDUCE);
+      MTP_TRY(launch_ce_reduce(nullptr, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
     }
-    if (st) return st;
+    for (long r0 = 0; r0 < m.N; r0 += m.slab) {
+      const int nr = (int)(m.N - r0 < m.slab ? m.N - r0 : m.slab);
+      const T *xs = xhat + r0 * d;
+      const int32_t *ls = lab + r0;
+      {
+        MTP_STAGE(MTP_STAGE_CE_FWD);
+        st = pick<T>(m.big, [&](auto cfg) {
+          return gemm_ce_fwd_cfg<T, decltype(cfg)>(xs, (const T *)a->W_out, ls, part, target + r0, zbuf, nr, V, d,
+                                                    s);
+        });
+      }
+      if (st) return st;
+      {
+        MTP_STAGE(MTP_STAGE_CE_REDUCE);
+        MTP_TRY(launch_ce_combine(part, m.nt, target + r0, ls, lse + r0,
+                                  a->lse ? a->lse + (long)k * N + r0 : nullptr, row_loss + r0, nr, s));
+      }
+      {
+        MTP_STAGE(MTP_STAGE_CE_GRAD);
+        MTP_TRY(launch_ce_dz<T>(zbuf, lse + r0, ls, dz, nr, V, s));
+      }
+      const bool big_dx = sizeof(T) == 2 && use_big(nr, d);
+      {
+        MTP_STAGE(MTP_STAGE_CE_DX);
+        st = pick<T>(big_dx, [&](auto cfg) {
+          return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs + r0 * d, slab, nr, V, d, scale + k,
+                                               m.splits, s);
+        });
+      }
+      if (st) return st;
+      const bool big_dw = sizeof(T) == 2 && use_big(V, d);
+      {
+        MTP_STAGE(MTP_STAGE_CE_DW);
+        st = pick<T>(big_dw, [&](auto cfg) {
+          return gemm_dw_cfg<T, decltype(cfg)>(dz, xs, a->dW_out, nr, V, d, scale + k, dw_acc0 || r0 > 0, s);
+        });
+      }
+      if (st) return st;
+    }
     {
       MTP_STAGE(MTP_STAGE_CE_REDUCE);
-      MTP_TRY(launch_ce_combine(part, m.nt, target, lab, lse, a->lse ? a->lse + (long)k * N : nullptr, row_loss,
-                                N, s));
       MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
     }
     {
-      MTP_STAGE(MTP_STAGE_CE_GRAD);
-      MTP_TRY(launch_ce_dz<T>(zbuf, lse, lab, dz, N, V, s));
-    }
-    const bool big_dx = sizeof(T) == 2 && use_big(N, d);
-    {
-      MTP_STAGE(MTP_STAGE_CE_DX);
-      st = pick<T>(big_dx, [&](auto cfg) {
-        return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs, slab, N, V, d, scale + k, m.splits, s);
-      });
-    }
-    if (st) return st;
-    const int acc = (k > 0 || a->accumulate) ? 1 : 0;
-    {
       MTP_STAGE(MTP_STAGE_CE_NORM_BWD);
       MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, slab, h, r, a->g_out, static_cast<float *>(a->dh[k]),
-                                     dg_part, a->dg_out, acc, N, d, s));
+                                     dg_part, a->dg_out, dw_acc0, N, d, s));
     }
-    const bool big_dw = sizeof(T) == 2 && use_big(V, d);
-    {
-      MTP_STAGE(MTP_STAGE_CE_DW);
-      st = pick<T>(big_dw, [&](auto cfg) {
-        return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat, a->dW_out, N, V, d, scale + k, acc, s);
-      });
-    }
-    if (st) return st;
   }
   MTP_TRY(launch_ce_finalize(acc_sum, acc_cnt, D, valid_mean, denom, a->lambda, a->loss_sum, a->counts, a->loss,
                              a->loss_mtp, s));
@@ -499,7 +520,7 @@ size_t verify_bytes(const mtp_verify_args *a) {
 
 extern "C" {
 
-int mtp_abi_version(void) { return 1; }
+int mtp_abi_version(void) { return 2; }
 
 int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n) {
   if (stage < 0) {

@@ -1,5 +1,5 @@
-// Bandwidth-bound row kernels: the dual RMSNorm + concat that feeds eh_proj
-// (K2), the block pre-norms, the shared output norm (K9) and its backward.
+// Bandwidth-bound row kernels: the dual RMSNorm + concat that feeds eh_proj,
+// the block pre-norms, the shared output norm and its backward.
 //
 // RMSNorm_g(z) = g * z / sqrt(mean(z^2) + eps) (M7.6 0x03C); statistics in
 // float32.  One 256-thread block per row, 16-byte chunk accesses.

@@ -1,4 +1,4 @@
-// K1: runs, state/loss masks, labels and counts of every depth
+// Runs, state/loss masks, labels and counts of every depth
 // (M7.6 0x02 depth contract, 0x04 alignment, 0x04C row compiler restated on
 // the dense [B, T] layout).
 //

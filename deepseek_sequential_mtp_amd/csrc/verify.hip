@@ -1,4 +1,4 @@
-// K12: exact speculative verification (M7.6 0x09 for one proposal; the
+// Exact speculative verification (M7.6 0x09 for one proposal; the
 // speculative-decoding explainer page for gamma proposals).
 //
 // Pass 1 (one block per logit row, all rows of all requests): log-sum-exp of

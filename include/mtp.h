@@ -147,8 +147,14 @@ typedef struct {
  * mtp_head_ce_fwd_bwd: shared output head Norm_out + W_U, masked CE against
  * the labels of every depth, and the gradients of
  *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
- * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  The logits [rows, V] are never
- * written: the forward keeps an online log-sum-exp over vocabulary tiles.
+ * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  The logits are never held for
+ * the whole batch: rows are processed in slabs of R rows with
+ * R * V * 4 <= logit_slab_bytes (R rounded down to a multiple of 256 when it
+ * is at least 256, and at least 1).  Per slab the forward GEMM reduces each
+ * vocabulary tile to an online (max, sum-exp) partial per row and keeps the
+ * slab's fp32 logits; the partials give the row's log-sum-exp, softmax -
+ * onehot is formed from the kept logits and consumed by the dx_hat and dW_out
+ * GEMMs of the same slab.  Workspace grows with the slab, not with B*T.
  *
  * Inputs : h [host] D pointers [B*T, d] (dtype); labels int32 [D,B,T]
  *          (-1 = no loss, as written by mtp_chain_forward); W_out [V, d]
@@ -164,6 +170,7 @@ typedef struct {
  *          main loss's), 0 overwrites.
  * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
  *          MTP_REDUCE_VALID_MEAN (denom ignored).
+ * logit_slab_bytes: bound on the fp32 logit slab (0 selects 1 GiB).
  * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0.
  * Labels outside [-1, V) are treated as -1 and set device_error (may be
  * NULL).
@@ -186,6 +193,7 @@ typedef struct {
   float *dW_out, *dg_out;
   int accumulate;
   int32_t *device_error;             /* optional                               */
+  size_t logit_slab_bytes;           /* 0 = 1 GiB                              */
   void *workspace;
   size_t workspace_bytes;
 } mtp_ce_args;

@@ -36,7 +36,7 @@ def test_header_declares_the_three_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mtp_abi_version() == 1
+    assert lib.mtp_abi_version() == 2
     assert lib.mtp_strerror(0) == b"ok"
     assert lib.mtp_strerror(-3) == b"depth must be positive"
 

@@ -13,7 +13,7 @@ from tests.gpu_util import compare, rel_fro, tdev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, seed=0):
+def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, seed=0, slab_rows=0):
     inp = synth.make_head_inputs(cfg, seed)
     _, _, labels, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], cfg.D)
     labels = labels.reshape(cfg.D, -1)
@@ -27,7 +27,7 @@ def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, see
     g = tdev(inp["g_out"], torch.float32)
     lab_t = tdev(labels.reshape(cfg.D, cfg.B, cfg.T).astype(np.int32), torch.int32)
     print(f"[ce] {cfg.name} N={cfg.N} d={cfg.d} V={cfg.V} D={cfg.D} reduce={reduce} "
-          f"labelled={(labels >= 0).sum()}", flush=True)
+          f"labelled={(labels >= 0).sum()} slab_rows={slab_rows or 'default'}", flush=True)
     out = None
     if accumulate:
         out = dict(loss_sum=torch.empty(cfg.D, device="cuda"), counts=torch.empty(cfg.D, dtype=torch.int32, device="cuda"),
@@ -38,7 +38,8 @@ def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, see
                    dg_out=torch.full((cfg.d,), -0.5, device="cuda"),
                    device_error=torch.empty(1, dtype=torch.int32, device="cuda"))
     res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, reduce=reduce, denom=denom,
-                               accumulate=accumulate, want_lse=True, out=out)
+                               accumulate=accumulate, want_lse=True, out=out,
+                               logit_slab_bytes=slab_rows * cfg.V * 4)
     torch.cuda.synchronize()
     model = BF16 if cfg.dtype == "bf16" else EXACT
     ref = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], cfg.eps, cfg.lam, reduce,
@@ -78,32 +79,39 @@ def _assert(cfg, res, ref, labels, accumulate=False):
     assert ok and rf < gate
 
 
-def test_ce_tiny_f32():
+@pytest.mark.parametrize("slab_rows", [0, 5])
+def test_ce_tiny_f32(slab_rows):
+    # slab_rows=5: 32 rows in 7 logit slabs, the last one ragged
     cfg = synth.TINY
-    res, ref, labels = _case(cfg)
+    res, ref, labels = _case(cfg, slab_rows=slab_rows)
     _assert(cfg, res, ref, labels)
 
 
-@pytest.mark.parametrize("reduce", ["fixed", "valid_mean"])
-def test_ce_bf16_ragged_two_depths(reduce):
+@pytest.mark.parametrize("reduce,slab_rows", [("fixed", 0), ("valid_mean", 0), ("fixed", 128),
+                                              ("valid_mean", 128)])
+def test_ce_bf16_ragged_two_depths(reduce, slab_rows):
+    # slab_rows=128: 600 rows in 5 slabs (88 in the last), two depths
     cfg = synth.scaled(synth.D1, name="ce_ragged", B=2, T=300, d=256, V=1000, D=2, seg_lo=20,
                        seg_hi=200, sigma_w=0.05)
-    res, ref, labels = _case(cfg, reduce=reduce)
+    res, ref, labels = _case(cfg, reduce=reduce, slab_rows=slab_rows)
     _assert(cfg, res, ref, labels)
 
 
-def test_ce_bf16_accumulate_and_custom_denom():
+@pytest.mark.parametrize("slab_rows", [0, 100])
+def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
     cfg = synth.scaled(synth.D1, name="ce_acc", B=1, T=256, d=128, V=512, D=1, seg_lo=30,
                        seg_hi=100, sigma_w=0.05)
-    res, ref, labels = _case(cfg, denom=1000.0, accumulate=True)
+    res, ref, labels = _case(cfg, denom=1000.0, accumulate=True, slab_rows=slab_rows)
     _assert(cfg, res, ref, labels, accumulate=True)
 
 
-def test_ce_bf16_big_tiles():
-    # 256x256 tiles in the forward, recompute and dW GEMMs (>= 256 tiles each)
+@pytest.mark.parametrize("slab_rows", [0, 256])
+def test_ce_bf16_big_tiles(slab_rows):
+    # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each); slab_rows=256
+    # runs the 1024 rows as four slabs
     cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=1024, V=16384, D=1, seg_lo=100,
                        seg_hi=700, sigma_w=0.02)
-    res, ref, labels = _case(cfg)
+    res, ref, labels = _case(cfg, slab_rows=slab_rows)
     _assert(cfg, res, ref, labels)
 
 
