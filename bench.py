@@ -40,7 +40,59 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--stages", action="store_true", help="print the per-stage time table to stderr")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the timed region, run a plain 256 MiB fp32 copy kernel 3 times (the "
+                         "reference dispatch that scales FETCH_SIZE / WRITE_SIZE counters)")
+    ap.add_argument("--ingest-pmc", nargs=3, metavar=("STAGE", "FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
+                         "--copy-calibration run into profiles/traffic_<stage>_<workload>.json")
     return ap.parse_args()
+
+
+# Kernel-name patterns of each stage (demangled names as rocprofv3 prints them).
+STAGE_KERNELS = {
+    "CE_DW": r"gemm_kernel<.*DmaMNMajor<[^>]*>, mtp::DmaMNMajor",
+    "CE_DX": r"gemm_kernel<.*DmaKMajor<[^>]*>, mtp::DmaMNMajor",
+    "CE_FWD": r"gemm_kernel<.*EpiCEFwd",
+    "QKV": r"gemm_kernel<.*EpiRope",
+    "GATE_UP": r"gemm_kernel<.*EpiSwiGLU",
+    "ATTN": r"attention_kernel",
+}
+COPY_BYTES = 256 << 20          # one direction of the calibration copy
+COPY_KERNEL = r"neg_kernel"
+
+
+def ingest_pmc(stage, fetch_csv, write_csv, workload):
+    """Per-launch HBM bytes of `stage`'s kernel from the two counter passes,
+    each scaled by the same counter's reading for the plain copy kernel."""
+    import csv
+    import re
+
+    def per_dispatch(path, counter):
+        rows = {}
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (r["Dispatch_Id"], r["Kernel_Name"])
+                rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
+        kern = [v for (_, n), v in rows.items() if re.search(STAGE_KERNELS[stage], n)]
+        copy = [v for (_, n), v in rows.items() if re.search(COPY_KERNEL, n)]
+        if not kern or not copy:
+            raise SystemExit(f"{path}: no {counter} rows for the stage kernel or the copy kernel")
+        factor = float(np.median(copy)) * 1024.0 / COPY_BYTES     # counter KiB -> bytes, per byte copied
+        return float(np.mean(kern)) * 1024.0 / factor, factor, len(kern)
+
+    fetch, ff, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
+    write, fw, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    out = {"stage": stage, "workload": workload, "kernel_regex": STAGE_KERNELS[stage],
+           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+           "bytes_per_launch": fetch + write, "copy_factor_fetch": ff, "copy_factor_write": fw,
+           "launches_counted": [nf, nw], "source_hash": _kernel_hash()}
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage.lower()}_{workload}.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out))
 
 
 # ----------------------------------------------------------------------------
@@ -102,6 +154,9 @@ def algorithmic_flops(cfg, state_mask, counts, run_start_fn):
 
 def main():
     args = parse()
+    if args.ingest_pmc:
+        ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.ingest_pmc[2], args.workload)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
               "sharding is a design only, see DESIGN.md)", file=sys.stderr)
@@ -210,6 +265,13 @@ def main():
             print(f"  stage {k:12s} {v:9.3f} ms  {100 * v / tot:5.1f}%", file=sys.stderr)
         print(f"  dominant {dominant}: {dom_avg_ms:.3f} ms/launch over {len(dom_times)} launches, "
               f"{dom_step_ms:.3f} ms/step, {achieved:.1f} TFLOP/s ({dom_note})", file=sys.stderr)
+
+    if args.copy_calibration:
+        src = torch.randn(COPY_BYTES // 4, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
