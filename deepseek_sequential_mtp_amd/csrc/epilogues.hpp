@@ -9,36 +9,52 @@ namespace mtp {
 
 // ---------------------------------------------------------------------------
 // C = alpha * acc (+ residual) (+ C if accumulate).  One K-split writes its
-// own slab C + split * split_stride.
+// own slab C + split * split_stride.  Branch-free: C and R are addressed
+// through buffer resources that start at the tile's first row and end at
+// row M, columns past N get an out-of-range offset, so a block's loads are
+// issued back to back and masked lanes neither read nor write.
 // ---------------------------------------------------------------------------
 template <typename OutT, typename ResT>
 struct EpiStore {
   OutT *C; long ldc; int M, N; float alpha;
   const float *alpha_dev;       // if set, alpha is read from device memory
   const ResT *R; long ldr;      // residual added after scaling (nullable)
-  int accumulate;               // add into existing C (f32 outputs)
+  int accumulate;               // add into existing C
   long split_stride;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
                                         int wn, int lane, int split, char *, char *) const {
     OutT *Cs = C + split * split_stride;
     const float al = alpha_dev != nullptr ? *alpha_dev : alpha;
+    const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(Cs + (long)m0 * ldc, rows * ldc * (long)sizeof(OutT));
+    const __amdgpu_buffer_rsrc_t rr =
+        make_rsrc(R != nullptr ? R + (long)m0 * ldr : nullptr, R != nullptr ? rows * ldr * (long)sizeof(ResT) : 0);
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
       for (int j = 0; j < Cfg::NB; ++j) {
         const int col = n0 + acc_col<Cfg>(wn, j, lane);
-        if (col >= N) continue;
+        const bool cok = col < N;
+        unsigned oc[16], orr[16];
+        float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
-          if (row >= M) continue;
-          float v = al * acc[i][j][r];
-          if (R != nullptr) v += load_elem(R, (long)row * ldr + col);
-          const long o = (long)row * ldc + col;
-          if (accumulate) v += load_elem(Cs, o);
-          store_elem(Cs, o, v);
+          const int row = acc_row<Cfg>(wm, i, r, lane);
+          oc[r] = cok ? (unsigned)(((long)row * ldc + col) * sizeof(OutT)) : kOOB;
+          orr[r] = cok ? (unsigned)(((long)row * ldr + col) * sizeof(ResT)) : kOOB;
+          v[r] = al * acc[i][j][r];
         }
+        if (R != nullptr) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] += buf_load_elem(rr, orr[r], ResT{});
+        }
+        if (accumulate) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) v[r] += buf_load_elem(rc, oc[r], OutT{});
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) buf_store_elem(rc, oc[r], v[r], OutT{});
       }
   }
 };

@@ -45,6 +45,20 @@ __device__ __forceinline__ uint4 buf_load16(__amdgpu_buffer_rsrc_t r, unsigned o
   const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
   return make_uint4(v[0], v[1], v[2], v[3]);
 }
+// Scalar element access through a buffer resource: loads past the resource
+// return 0, stores past it are dropped (used for masked epilogue lanes).
+__device__ __forceinline__ float buf_load_elem(__amdgpu_buffer_rsrc_t r, unsigned off, float) {
+  return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+__device__ __forceinline__ float buf_load_elem(__amdgpu_buffer_rsrc_t r, unsigned off, bf16_t) {
+  return bf16_to_f32(__builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0));
+}
+__device__ __forceinline__ void buf_store_elem(__amdgpu_buffer_rsrc_t r, unsigned off, float v, float) {
+  __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), r, off, 0, 0);
+}
+__device__ __forceinline__ void buf_store_elem(__amdgpu_buffer_rsrc_t r, unsigned off, float v, bf16_t) {
+  __builtin_amdgcn_raw_buffer_store_b16(f32_to_bf16(v), r, off, 0, 0);
+}
 
 // ---------------------------------------------------------------------------
 // Direct global -> LDS loads (buffer_load_dwordx4 ... lds): one instruction

@@ -366,7 +366,7 @@ int check_ce_ptrs(const mtp_ce_args *a) {
 }
 
 struct CeDims {
-  long N; int d, V, nt, splits; bool big;
+  long N; int d, V, nt, splits; bool big, big_dx;
   long slab;          // rows per logit slab
 };
 
@@ -384,8 +384,9 @@ CeDims ce_dims(const mtp_ce_args *a) {
   c.slab = r < 1 ? 1 : (r > c.N ? c.N : r);
   c.big = sizeof(T) == 2 && use_big(c.slab, c.V);
   c.nt = ceil_div(c.V, c.big ? 256 : 128);
-  const bool big_dx = sizeof(T) == 2 && use_big(c.slab, c.d);
-  c.splits = dx_splits((int)c.slab, c.d, c.V, big_dx);
+  // the dx_hat GEMM (slab rows x d, K = V) may also fill the chip with K splits
+  c.big_dx = sizeof(T) == 2 && (long)ceil_div(c.slab, 256) * ceil_div(c.d, 256) * 8 >= 256;
+  c.splits = dx_splits((int)c.slab, c.d, c.V, c.big_dx);
   return c;
 }
 
@@ -470,10 +471,9 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         MTP_STAGE(MTP_STAGE_CE_GRAD);
         MTP_TRY(launch_ce_dz<T>(zbuf, lse + r0, ls, dz, nr, V, s));
       }
-      const bool big_dx = sizeof(T) == 2 && use_big(nr, d);
       {
         MTP_STAGE(MTP_STAGE_CE_DX);
-        st = pick<T>(big_dx, [&](auto cfg) {
+        st = pick<T>(m.big_dx, [&](auto cfg) {
           return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs + r0 * d, slab, nr, V, d, scale + k,
                                                m.splits, s);
         });
