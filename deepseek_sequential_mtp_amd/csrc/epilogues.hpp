@@ -154,16 +154,15 @@ struct EpiCEFwd {
   const int *labels; float2 *part; float *target; float *zout; int M, V, nt;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
-                                        int wn, int lane, int, char *lds0, char *lds1) const {
-    // red[row][slot]: 64 per-lane partials per row, slot XOR-swizzled by the
-    // row so the per-row scans of the second phase hit 64 distinct banks.
-    float *red = reinterpret_cast<float *>(lds0);        // BM * 64 floats
-    float *mrow = reinterpret_cast<float *>(lds1);       // BM floats
-    static_assert(Cfg::BM * 64 * 4 <= Cfg::LDS_STAGE, "CE reduction fits one stage");
-    auto at = [](int row, int slot) { return row * 64 + (slot ^ (row & 63)); };
-    const int c32 = lane & 31;
-    const int slot = wn * 32 + c32;
-    // 1) per-lane max over the lane's columns of each of its rows
+                                        int wn, int lane, int, char *lds, char *) const {
+    // The 32 lanes of a half-wave hold one row (per accumulator register) in
+    // 32 different columns: reduce across them with lane shuffles, then over
+    // the WGN = 2 column waves through LDS ([WGN][BM] floats per quantity).
+    static_assert(Cfg::WGN == 2, "two column waves per row");
+    float *redm = reinterpret_cast<float *>(lds);          // [2][BM] row max per column wave
+    float *reds = redm + 2 * Cfg::BM;                        // [2][BM] row sum-exp per column wave
+    const bool writer = (lane & 31) == 0;
+    // 1) row max over this wave's columns
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
@@ -174,27 +173,19 @@ struct EpiCEFwd {
           const int col = n0 + acc_col<Cfg>(wn, j, lane);
           mx = col < V ? fmaxf(mx, acc[i][j][r]) : mx;
         }
-        red[at(acc_row<Cfg>(wm, i, r, lane), slot)] = mx;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        if (writer) redm[wn * Cfg::BM + acc_row<Cfg>(wm, i, r, lane)] = mx;
       }
-    // Slots 32..63 are written only by the wn = 1 waves; with NB blocks per
-    // wave both halves always exist, so all 64 slots are defined.
-    static_assert(Cfg::WGN == 2, "64 partial slots per row");
     __syncthreads();
-    const int t = threadIdx.x;
-    if (t < Cfg::BM) {
-      float mx = -INFINITY;
-      for (int q = 0; q < 64; ++q) mx = fmaxf(mx, red[at(t, q)]);
-      mrow[t] = mx;
-    }
-    __syncthreads();
-    // 2) per-lane sums of exp(z - m_row); capture the target logit
+    // 2) sum of exp(z - m_row) over this wave's columns; target logit; logits
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rl = acc_row<Cfg>(wm, i, r, lane);
         const int row = m0 + rl;
-        const float m = mrow[rl];
+        const float m = fmaxf(redm[rl], redm[Cfg::BM + rl]);
         const int lab = row < M ? labels[row] : -1;
         float s = 0.f;
 #pragma unroll
@@ -207,22 +198,25 @@ struct EpiCEFwd {
           }
           if (col == lab) target[row] = z;
         }
-        red[at(rl, slot)] = s;
+#pragma unroll
+        for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o);
+        if (writer) reds[wn * Cfg::BM + rl] = s;
       }
     __syncthreads();
-    if (t < Cfg::BM && m0 + t < M) {
-      float s = 0.f;
-      for (int q = 0; q < 64; ++q) s += red[at(t, q)];
-      part[(long)(m0 + t) * nt + n0 / Cfg::BN] = make_float2(mrow[t], s);
-    }
+    const int t = threadIdx.x;
+    if (t < Cfg::BM && m0 + t < M)
+      part[(long)(m0 + t) * nt + n0 / Cfg::BN] =
+          make_float2(fmaxf(redm[t], redm[Cfg::BM + t]), reds[t] + reds[Cfg::BM + t]);
   }
 };
 
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
-  __shared__ __attribute__((aligned(1024))) char lds0[Cfg::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char lds1[Cfg::LDS_STAGE];
-  gemm_body<T, Cfg>(la, lb, epi, K, ts, lds0, lds1);
+  __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[Cfg::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st2[Cfg::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) char st3[Cfg::LDS_STAGE];
+  gemm_body<T, Cfg>(la, lb, epi, K, ts, st0, st1, st2, st3);
 }
 
 // Host-side launch helper (grid = tiles * K splits, one block per tile).

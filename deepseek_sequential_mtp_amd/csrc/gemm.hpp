@@ -1,12 +1,19 @@
 // MFMA GEMM core for gfx950: C[m, n] = sum_k A[m, k] * B[k, n] with fp32
-// accumulation, WGM x WGN waves per workgroup, BM x BN output tile, K staged
-// through LDS in slices of 128 bytes per row, double-buffered.
+// accumulation, WGM x WGN waves per workgroup, BM x BN output tile.
 //
-// Operands are K-major (K contiguous; A[m][k] = base[row(m) * ld + k]) and
-// are described by loaders that copy them global -> LDS directly, optionally
-// with a per-row source (interleaved matrices).
-// Epilogues receive the accumulators in the MFMA result layout (see
-// common.hpp) and do the stores / reductions.
+// K is staged through LDS in slices of 64 bytes per operand row (32 bf16 or
+// 16 f32 elements) in NS = 4 stages: the loads of slice kt + 4 are issued as
+// soon as slice kt has been consumed, so every load has three slices of MFMA
+// work to land.  Operands go global -> LDS directly (buffer_load ... lds): no
+// staging registers and no ds_write.  The stages are four distinct LDS
+// objects and the K loop is unrolled by four, so the compiler can tell that a
+// fragment read of one stage does not depend on the loads in flight into the
+// others.
+//
+// Operands are described by loaders: K-major (K contiguous), optionally with
+// interleaved row sources, or MN-major (M or N contiguous), read back with
+// the transposing LDS read.  Epilogues receive the accumulators in the MFMA
+// result layout (see common.hpp) and do the stores / reductions.
 #pragma once
 
 #include "common.hpp"
@@ -20,7 +27,9 @@ struct Tile {
   static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 blocks per wave
-  static constexpr int LDS_STAGE = (BM + BN) * 128;   // bytes per stage (two stages)
+  static constexpr int ROWB = 64;                     // bytes per operand row and stage
+  static constexpr int NS = 4;                        // LDS stages
+  static constexpr int LDS_STAGE = (BM + BN) * ROWB;  // bytes per stage
 };
 
 // ---------------------------------------------------------------------------
@@ -61,58 +70,60 @@ __device__ __forceinline__ void buf_store_elem(__amdgpu_buffer_rsrc_t r, unsigne
 }
 
 // ---------------------------------------------------------------------------
-// Direct global -> LDS loads (buffer_load_dwordx4 ... lds): one instruction
-// moves 64 lanes x 16 B into 1 KB of LDS at M0 + lane * 16, so operands never
-// pass through VGPRs and no ds_write is issued.  A 1 KB block holds 8 tile
-// rows of 128 B; lane L fills physical chunk L & 7 of row L >> 3 and fetches
-// the logical chunk that the LDS swizzle (lds_off128) places there.
+// LDS operand tiles (K-major): rows of 64 bytes (4 chunks of 16 B).  The LDS
+// serves 256 bytes (64 banks) per cycle, i.e. 4 rows; a 16-lane group reading
+// one logical chunk of 16 consecutive rows must hit 16 distinct 16-byte bank
+// groups: chunk c of row r lives at physical chunk c ^ ((r >> 2) & 3).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int lds_off64(int row, int chunk) {
+  return (row << 6) + (((chunk ^ (row >> 2)) & 3) << 4);
+}
+
+// ---------------------------------------------------------------------------
+// Direct global -> LDS loads: one instruction moves 64 lanes x 16 B into 1 KB
+// of LDS at M0 + lane * 16.  The lane's source is split into a per-lane byte
+// offset and a wave-uniform one carried in the instruction's SGPR offset.
+// Lanes past K get kOOB; with the SGPR offset below the resource size,
+// kOOB + offset still lies past it and does not wrap.
 // ---------------------------------------------------------------------------
 typedef __attribute__((address_space(3))) char lds_char;
 
 __device__ __forceinline__ lds_char *to_lds(char *p) { return (lds_char *)p; }
 
-// The lane's source is split into a per-lane byte offset (row rl = lane >> 3
-// inside the 8-row block, and the logical chunk) and a wave-uniform one (the
-// block's first row and the K slice) that rides in the instruction's SGPR
-// offset, so a tile's worth of loads costs two VGPRs of addresses.  The
-// swizzle term (row >> 1) & 7 = (4 * (q & 1) + (rl >> 1)) & 7 depends only on
-// the block parity.  Lanes past K get kOOB: with soffset below the resource
-// size, kOOB + soffset still lies past it and does not wrap.
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *lds_dst, unsigned voff, int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void *)to_lds(lds_dst), 16,
                                            voff, __builtin_amdgcn_readfirstlane(soff), 0, 0);
 }
 
-// K-major dense operand, op[r][k] = base[r * ld + k].
+// K-major dense operand, op[r][k] = base[r * ld + k].  A 1 KB load block holds
+// 16 tile rows; lane L fills physical chunk L & 3 of row L >> 2 and fetches
+// the logical chunk the swizzle places there, (L & 3) ^ (L >> 4) (the block's
+// first row is a multiple of 16, so the swizzle term depends on L only).
 template <typename T, int ROWS, int NT>
 struct DmaKMajor {
   static constexpr int E = Elem<T>::kPerChunk;
-  static constexpr int NBLK = ROWS / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static constexpr int NBLK = ROWS / 16, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
   static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kLoads = PER_WAVE;   // load instructions per wave and slice
   static constexpr int kReads = 1;          // LDS read instructions per fragment
   const T *base; long ld; int rows; int K;
   // Fragment of the 32-row block starting at tile row r0, K sub-step s
   // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
   __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
-    return *reinterpret_cast<const uint4 *>(region + lds_off128(r0 + (lane & 31), 2 * s + (lane >> 5)));
+    return *reinterpret_cast<const uint4 *>(region + lds_off64(r0 + (lane & 31), 2 * s + (lane >> 5)));
   }
-  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+  __device__ __forceinline__ void issue(int row0, int k0, char *region) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long nrow = rows - row0 < ROWS ? rows - row0 : ROWS;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (long)row0 * ld, nrow * ld * (long)sizeof(T));
-    const int rl = lane >> 3, pc = lane & 7;
     const int ldb = (int)(ld * sizeof(T));
-    unsigned voff[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int c = pc ^ ((4 * par + (rl >> 1)) & 7);
-      voff[par] = k0 + c * E < K ? (unsigned)(rl * ldb + c * 16) : kOOB;
-    }
+    const int c = (lane & 3) ^ (lane >> 4);
+    const unsigned voff = k0 + c * E < K ? (unsigned)((lane >> 2) * ldb + c * 16) : kOOB;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
-      dma16(rs, stage + q * 1024, voff[q & 1], 8 * q * ldb + k0 * (int)sizeof(T));
+      dma16(rs, region + q * 1024, voff, 16 * q * ldb + k0 * (int)sizeof(T));
     }
   }
 };
@@ -120,20 +131,20 @@ struct DmaKMajor {
 // SwiGLU-interleaved B operand: tile column c of wave column wn holds, for
 // block b = (c mod WN) / 32, gate features (b < NB/2) or up features
 // (b >= NB/2) of the same feature range, so the epilogue pairs them in-lane.
-// Every 8-row block lies in one 32-row block and hence reads one matrix.
+// Every 16-row load block lies in one 32-row block and hence reads one matrix.
 template <typename T, class Cfg>
 struct DmaKMajorSwiGLU {
   static constexpr int E = Elem<T>::kPerChunk;
   static constexpr int BN = Cfg::BN, NT = Cfg::NT, WN = Cfg::WN, NBh = WN / 64;
-  static constexpr int NBLK = BN / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static constexpr int NBLK = BN / 16, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kLoads = PER_WAVE;
   static constexpr int kReads = 1;
   const T *gate; const T *up; long ld; int f; int K;
-  // Fragment of the 32-row block starting at tile row r0, K sub-step s
-  // (32 bytes of K): lane l holds row r0 + l % 32, chunk 2 s + l / 32.
   __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
-    return *reinterpret_cast<const uint4 *>(region + lds_off128(r0 + (lane & 31), 2 * s + (lane >> 5)));
+    return *reinterpret_cast<const uint4 *>(region + lds_off64(r0 + (lane & 31), 2 * s + (lane >> 5)));
   }
-  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+  __device__ __forceinline__ void issue(int row0, int k0, char *region) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int feat0 = (row0 / BN) * (BN / 2);
@@ -141,22 +152,17 @@ struct DmaKMajorSwiGLU {
     const long bytes = nfeat * ld * (long)sizeof(T);
     const __amdgpu_buffer_rsrc_t rg = make_rsrc(gate + (long)feat0 * ld, bytes);
     const __amdgpu_buffer_rsrc_t ru = make_rsrc(up + (long)feat0 * ld, bytes);
-    const int rl = lane >> 3, pc = lane & 7;
     const int ldb = (int)(ld * sizeof(T));
-    unsigned voff[2];
-#pragma unroll
-    for (int par = 0; par < 2; ++par) {
-      const int c = pc ^ ((4 * par + (rl >> 1)) & 7);
-      voff[par] = k0 + c * E < K ? (unsigned)(rl * ldb + c * 16) : kOOB;
-    }
+    const int c = (lane & 3) ^ (lane >> 4);
+    const unsigned voff = k0 + c * E < K ? (unsigned)((lane >> 2) * ldb + c * 16) : kOOB;
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
-      const int row = 8 * q;                                // first tile column of the block
+      const int row = 16 * q;                               // first tile column of the block
       const int wn = row / WN, blk = (row % WN) / 32;
       const bool is_up = blk >= NBh;
       const int fl = wn * (WN / 2) + (is_up ? blk - NBh : blk) * 32 + (row % 32);
-      dma16(is_up ? ru : rg, stage + q * 1024, voff[q & 1], fl * ldb + k0 * (int)sizeof(T));
+      dma16(is_up ? ru : rg, region + q * 1024, voff, fl * ldb + k0 * (int)sizeof(T));
     }
   }
 };
@@ -165,7 +171,7 @@ struct DmaKMajorSwiGLU {
 // region holds BK k-rows of ROWS elements each (CPR 16-byte chunks per k-row);
 // chunk c of k-row k sits at physical chunk c ^ (4 (k & 3)).  A 1 KB load
 // block covers RPB = 64 / CPR whole k-rows, so a lane's swizzle depends only
-// on its position and the block parity, as in the K-major case.
+// on its position and the block parity.
 //
 // Fragments (K-major from the MFMA's point of view) are read with gfx950's
 // transposing LDS read ds_read_b64_tr_b16: in each 16-lane group, lane j
@@ -178,13 +184,14 @@ struct DmaKMajorSwiGLU {
 template <typename T, int ROWS, int NT>
 struct DmaMNMajor {
   static constexpr int E = Elem<T>::kPerChunk;
-  static constexpr int BK = 8 * E;
+  static constexpr int BK = 4 * E;                     // K elements per 64-byte slice
   static constexpr int ROWB = ROWS * (int)sizeof(T);
   static constexpr int CPR = ROWB / 16;
   static constexpr int RPB = 64 / CPR;
   static_assert(CPR == 16 || CPR == 32, "k-row of 256 or 512 bytes");
   static constexpr int NBLK = BK / RPB, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
   static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kLoads = PER_WAVE;
   static constexpr int kReads = sizeof(T) == 2 ? 2 : 4;
   const T *base; long ld; int rows; int K;
 
@@ -214,7 +221,7 @@ struct DmaMNMajor {
       return v;
     }
   }
-  __device__ __forceinline__ void issue(int row0, int k0, char *stage) const {
+  __device__ __forceinline__ void issue(int row0, int k0, char *region) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const long nk = K - k0 < BK ? K - k0 : BK;
@@ -230,7 +237,7 @@ struct DmaMNMajor {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
-      dma16(rs, stage + q * 1024, voff[q & 1], RPB * q * ldb + row0 * (int)sizeof(T));
+      dma16(rs, region + q * 1024, voff[q & 1], RPB * q * ldb + row0 * (int)sizeof(T));
     }
   }
 };
@@ -252,16 +259,13 @@ __device__ __forceinline__ void tile_coords(int logical, int mt, int nt, int gro
 
 struct TileSched { int mt, nt, group_m, k_splits; };
 
-// ---------------------------------------------------------------------------
-// The kernel body.  Each block computes one BM x BN tile (optionally one K
-// split of it) and hands the accumulators to the epilogue.  Operands arrive
-// by direct global -> LDS loads into two stages.
-// ---------------------------------------------------------------------------
-// Waits for this wave's direct loads and LDS operations, then barriers: after
-// it every wave's loads into LDS have landed and every earlier LDS read of
-// the workgroup has retired.
-__device__ __forceinline__ void vm_lds_barrier() {
-  __builtin_amdgcn_s_waitcnt(0);     // vmcnt = expcnt = lgkmcnt = 0
+// Waits until at most VM of this wave's vector-memory operations are
+// outstanding and all its LDS operations are done, then barriers.  s_waitcnt
+// layout on gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
+template <int VM>
+__device__ __forceinline__ void wait_vm_lds_barrier() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -277,12 +281,25 @@ __device__ __forceinline__ void sched_interleave() {
   }
 }
 
+// ---------------------------------------------------------------------------
+// The kernel body.  Each block computes one BM x BN tile (optionally one K
+// split of it) and hands the accumulators to the epilogue.
+//
+// Slice kt lives in stage kt % 4.  At the end of slice kt (before its second
+// sub-step's MFMAs) every wave waits for its loads of slice kt + 1 -- the
+// loads of slices kt + 2 and kt + 3 may stay in flight -- and the block
+// barriers, which also retires every read of stage kt % 4; the loads of
+// slice kt + 4 then go into that stage.  Slices past the block's K range are
+// issued as all-out-of-range loads (no memory traffic), so the number of
+// loads in flight, and with it the wait count, is the same for every slice.
+// ---------------------------------------------------------------------------
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi &epi, int K,
-                                          const TileSched &ts, char *lds0, char *lds1) {
+                                          const TileSched &ts, char *st0, char *st1, char *st2, char *st3) {
   constexpr int E = Elem<T>::kPerChunk;
-  constexpr int BK = 8 * E;                    // K elements per LDS slice
+  constexpr int BK = 4 * E;                    // K elements per 64-byte slice
   constexpr int MB = Cfg::MB, NB = Cfg::NB;
+  constexpr int LOADS = LA::kLoads + LB::kLoads;   // load instructions per wave and slice
   const int ntiles = ts.mt * ts.nt * ts.k_splits;
   const int logical = xcd_remap(blockIdx.x, ntiles);
   const int split = logical % ts.k_splits;
@@ -294,6 +311,7 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
   const int per = (nk_total + ts.k_splits - 1) / ts.k_splits;
   const int kt0 = split * per;
   const int kt1 = min(nk_total, kt0 + per);
+  const int nk = kt1 > kt0 ? kt1 - kt0 : 0;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -313,53 +331,51 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
 #pragma unroll
     for (int i = 0; i < MB; ++i) a[i] = LA::frag(stage, ar0 + 32 * i, s, lane);
 #pragma unroll
-    for (int j = 0; j < NB; ++j) b[j] = LB::frag(stage + Cfg::BM * 128, br0 + 32 * j, s, lane);
+    for (int j = 0; j < NB; ++j) b[j] = LB::frag(stage + Cfg::BM * Cfg::ROWB, br0 + 32 * j, s, lane);
   };
-  auto issue = [&](int kt, char *stage) {
-    la.issue(m0, kt * BK, stage);
-    lb.issue(n0, kt * BK, stage + Cfg::BM * 128);
+  // slice it (relative to kt0) into a stage; past the range: out-of-range loads
+  auto issue = [&](int it, char *stage) {
+    const int k0 = it < nk ? (kt0 + it) * BK : K;
+    la.issue(m0, k0, stage);
+    lb.issue(n0, k0, stage + Cfg::BM * Cfg::ROWB);
   };
-  const int nk = kt1 - kt0;
-  if (nk > 0) issue(kt0, lds0);
-  vm_lds_barrier();
-  if (nk > 0) read_frags(lds0, 0, fa[0], fb[0]);
-  if (nk > 1) issue(kt0 + 1, lds1);
-  // One K tile on stage sc (the other stage is sn): each sub-step's MFMAs
-  // run while the next sub-step's fragments are read.  Before sub-step 3:
-  // wait for the next tile's loads, barrier (which also retires every read
-  // of sc), issue tile it+2 into sc and read sub-step 0 of the next tile.
-  // The two stages are distinct LDS objects and the loop is unrolled by two,
-  // so the compiler can tell that reads of one stage do not wait for the
-  // direct loads still in flight into the other.
   constexpr int NM = MB * NB;                                  // MFMAs per sub-step
   constexpr int NR = MB * LA::kReads + NB * LB::kReads;        // LDS reads per sub-step
-  auto ktile = [&](int it, char *sc, const char *sn) {
+  auto mfmas = [&](int s) {
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      if (s < 3) read_frags(sc, s + 1, fa[(s + 1) & 1], fb[(s + 1) & 1]);
-      if (s == 3) {
-        vm_lds_barrier();
-        if (it + 2 < nk) issue(kt0 + it + 2, sc);
-        if (it + 1 < nk) read_frags(sn, 0, fa[0], fb[0]);
-      }
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int i = 0; i < MB; ++i)
-#pragma unroll
-        for (int j = 0; j < NB; ++j) mma32(fa[s & 1][i], fb[s & 1][j], acc[i][j], T{});
-      if constexpr (sizeof(T) == 2) {
-        if (s < 3) {
-          sched_interleave<NM, NR>();
-        }
-      }
-    }
+      for (int j = 0; j < NB; ++j) mma32(fa[s][i], fb[s][j], acc[i][j], T{});
+    if constexpr (sizeof(T) == 2) sched_interleave<NM, NR>();
   };
+  // one slice on stage sc; sn is the next slice's stage
+  auto slice = [&](int it, char *sc, const char *sn) {
+    read_frags(sc, 1, fa[1], fb[1]);
+    mfmas(0);
+    wait_vm_lds_barrier<2 * LOADS>();          // slice it+1 landed, stage sc retired
+    issue(it + 4, sc);
+    read_frags(sn, 0, fa[0], fb[0]);
+    mfmas(1);
+  };
+
+  issue(0, st0);
+  issue(1, st1);
+  issue(2, st2);
+  issue(3, st3);
+  wait_vm_lds_barrier<3 * LOADS>();            // slice 0 landed
+  read_frags(st0, 0, fa[0], fb[0]);
   int it = 0;
-  for (; it + 1 < nk; it += 2) {
-    ktile(it, lds0, lds1);
-    ktile(it + 1, lds1, lds0);
+  for (; it + 3 < nk; it += 4) {
+    slice(it, st0, st1);
+    slice(it + 1, st1, st2);
+    slice(it + 2, st2, st3);
+    slice(it + 3, st3, st0);
   }
-  if (it < nk) ktile(it, lds0, lds1);
-  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, lds0, lds1);
+  if (it < nk) slice(it, st0, st1);
+  if (it + 1 < nk) slice(it + 1, st1, st2);
+  if (it + 2 < nk) slice(it + 2, st2, st3);
+  wait_vm_lds_barrier<0>();                    // no load in flight into the stages
+  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, st0, st1);
 }
 
 // Result-layout helpers: row / column of accumulator register r of block
