@@ -46,9 +46,20 @@ __device__ __forceinline__ int swz(int row, int chunk) {
   return row * (CPR * 16) + ((chunk ^ (row & m)) << 4);
 }
 
-__device__ __forceinline__ uint4 pack_p(const f32x4 &a, const f32x4 &b, bf16_t) {
+// P in bf16 for the O^T MFMA as hi + lo: hi = bf16(p), lo = bf16(p - hi), so
+// the product carries ~16 mantissa bits of p instead of 8 (the probabilities
+// are not a stored tensor of the method and get no bf16 rounding point).
+__device__ __forceinline__ void pack_p2(const f32x4 &a, const f32x4 &b, uint4 &hi, uint4 &lo) {
   const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  return f32_to_chunk(v, bf16_t{});
+  hi = f32_to_chunk(v, bf16_t{});
+  float r[8];
+  const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    r[2 * i] = v[2 * i] - bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffff));
+    r[2 * i + 1] = v[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+  }
+  lo = f32_to_chunk(r, bf16_t{});
 }
 __device__ __forceinline__ uint4 pack_p(const f32x4 &a, const f32x4 &, float) {
   return make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
@@ -202,17 +213,20 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
       // ---- O^T += V^T P^T
 #pragma unroll
       for (int sv = 0; sv < SV; ++sv) {
-        uint4 pb[2];
+        uint4 pb[2], pl[2];
 #pragma unroll
         for (int qb = 0; qb < 2; ++qb) {
-          if constexpr (E == 8) pb[qb] = pack_p(s[2 * sv][qb], s[2 * sv + 1][qb], T{});
+          if constexpr (E == 8) pack_p2(s[2 * sv][qb], s[2 * sv + 1][qb], pb[qb], pl[qb]);
           else pb[qb] = pack_p(s[sv][qb], s[sv][qb], T{});
         }
 #pragma unroll
         for (int db = 0; db < MBD; ++db) {
           const uint4 a = *reinterpret_cast<const uint4 *>(ldsV + lds_off128(db * 16 + c16, 4 * sv + g));
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) mma16(a, pb[qb], o[db][qb], T{});
+          for (int qb = 0; qb < 2; ++qb) {
+            mma16(a, pb[qb], o[db][qb], T{});
+            if constexpr (E == 8) mma16(a, pl[qb], o[db][qb], T{});
+          }
         }
       }
     }

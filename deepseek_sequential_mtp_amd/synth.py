@@ -163,12 +163,14 @@ def _normal(rng, shape, sigma, mean=0.0):
     return x
 
 
-def make_chain_inputs(cfg: ChainConfig, seed_offset: int = 0) -> Dict[str, object]:
+def make_chain_inputs(cfg: ChainConfig, seed_offset: int = 0, with_head: bool = True) -> Dict[str, object]:
     """All inputs of one step of ``cfg``.
 
     Floating arrays are float32 numpy arrays whose values are exactly
     representable in the config's dtype (bf16-rounded for bf16 cases).
-    Per-depth weights are a list of dicts (``DEPTH_FIELDS``)."""
+    Per-depth weights are a list of dicts (``DEPTH_FIELDS``).  With
+    ``with_head=False`` W_out is not drawn (None); every other array is the
+    same, since each tensor has its own child stream."""
     ss = np.random.SeedSequence(BASE_SEED + cfg.index + 1000 * seed_offset)
     n_children = 6 + len(DEPTH_FIELDS) * cfg.D
     kids = ss.spawn(n_children)
@@ -189,7 +191,8 @@ def make_chain_inputs(cfg: ChainConfig, seed_offset: int = 0) -> Dict[str, objec
         segment_ids = packed_segments(g_seg, B, T, cfg.seg_lo, cfg.seg_hi)
     h0 = rnd(_normal(next(it), (B * T, d), 1.0))
     E = rnd(_normal(next(it), (V, d), cfg.sigma_w))
-    W_out = rnd(_normal(next(it), (V, d), cfg.sigma_w))
+    g_w = next(it)
+    W_out = rnd(_normal(g_w, (V, d), cfg.sigma_w)) if with_head else None
     g_out = _normal(next(it), (d,), 0.1, 1.0)
     depths: List[Dict[str, np.ndarray]] = []
     for _ in range(cfg.D):

@@ -1,7 +1,9 @@
 """GPU parity of mtp_chain_forward against the oracle: masks, labels and
 counts bit-exact; h^(k) on state rows within tolerance (float32: 1e-4
-max-abs; bf16: 2e-2 max-abs, a one-ulp rounding flip at the final bf16 store
-admitted)."""
+max-abs; bf16: 2e-2 max-abs with 4k bf16 ulps of the reference admitted at
+depth k -- rounding flips at the block's bf16 stores, amplified by attention
+and SwiGLU and inherited by the next depth; both: relative Frobenius error
+below 4e-3 k)."""
 import numpy as np
 import pytest
 import torch
@@ -9,7 +11,7 @@ import torch
 from deepseek_sequential_mtp_amd import _lib, synth
 from oracle import chain as ochain, rows as orows
 from oracle.numerics import BF16, EXACT
-from tests.gpu_util import chain_tensors, compare, to_np
+from tests.gpu_util import chain_tensors, compare, rel_fro, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +44,11 @@ def _check(cfg, inp, out, model, atol):
         rows_k = st[k].reshape(-1).astype(bool)
         g = to_np(out["h"][k])
         assert np.isfinite(g).all()
-        err, n_over, ok = compare(g[rows_k], hs[k][rows_k], atol, bf16_store=(model is BF16))
+        err, n_over, ok = compare(g[rows_k], hs[k][rows_k], atol, bf16_store=(model is BF16), ulps=4 * (k + 1))
+        rf = rel_fro(g[rows_k], hs[k][rows_k])
         print(f"  depth {k + 1}: state rows {rows_k.sum()}, max|err| {err:.3e}, "
-              f"over atol {n_over}", flush=True)
-        assert ok, (k, err, n_over)
+              f"over atol {n_over}, relF {rf:.2e}", flush=True)
+        assert ok and rf < 4e-3 * (k + 1), (k, err, n_over, rf)
 
 
 def test_chain_tiny_f32():

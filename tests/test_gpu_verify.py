@@ -56,7 +56,7 @@ def test_verify_small_vocab(gamma):
     assert (g["status"] == 0).all()
 
 
-@pytest.mark.parametrize("gamma", [1, 4])
+@pytest.mark.parametrize("gamma", [1, 2, 3, 4])
 def test_verify_full_vocab_sampled_requests(gamma):
     # the full launch (R = 256, V = 129280); the oracle checks 48 requests
     vc, d, y = _inputs(gamma, R=256, V=129280)
