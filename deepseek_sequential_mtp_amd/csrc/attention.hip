@@ -5,65 +5,59 @@
 // scaled by 1/sqrt(hd), softmax in float32 with an online max.
 //
 // Layout: qkv [B*T, 3*A] (q | k | v, head h at columns h*hd), out [B*T, A].
-// One block = 4 waves = 128 queries of one (batch row, head); each wave owns
-// 32 queries (two 16-query MFMA blocks).  Per key tile the wave computes
-// S^T = K Q^T (keys on MFMA rows, queries on columns), so every softmax
-// statistic of a query lives in one lane column: 16 values in-lane plus a
-// reduction over the 4 lane groups.  P^T goes straight from the result
-// registers into the B operand of O^T = V^T P^T; V is staged transposed in
-// LDS with the key order permuted to match the result layout.
+//
+// One block = 4 waves = 256 queries of one (batch row, head); each wave owns
+// 64 queries (two 32-query MFMA column blocks) held in registers.  Key tiles
+// of 64 keys (K and V, row-major as stored) move global -> LDS by direct
+// loads into two stages; the loads of tile t+1 are issued as soon as tile
+// t-1 has been consumed.  Per tile each wave computes
+//   S^T = K Q^T     (keys on MFMA rows, queries on columns: every softmax
+//                    statistic of a query lives in one lane column, 16 values
+//                    in-lane plus the partner lane 32 away),
+//   O^T += V^T P^T  (P^T taken straight from the S^T result registers: the
+//                    MFMA's K-slots are mapped to the keys those registers
+//                    hold, and V^T is read with the transposing LDS read at
+//                    the same key order).
+// P enters the bf16 product as hi + lo (two MFMAs), carrying ~16 mantissa
+// bits of the probabilities (they are no stored tensor of the method).
+#include "gemm.hpp"
 #include "kernels.hpp"
 
 namespace mtp {
 
 namespace {
 constexpr int kAttnThreads = 256;
-constexpr int kQW = 32;                       // queries per wave
+constexpr int kQW = 64;                       // queries per wave
 constexpr int kQT = 4 * kQW;                  // queries per block
+constexpr int kKT = 64;                       // keys per tile
 
-template <typename T> struct AttnCfg {
+template <typename T, int HD>
+struct AttnCfg {
   static constexpr int E = Elem<T>::kPerChunk;
-  static constexpr int KT = 128 / Elem<T>::kBytes;   // keys per tile (V^T rows = 128 B)
+  static constexpr int ROWB = HD * (int)sizeof(T);     // bytes per K / V row
+  static constexpr int CPR = ROWB / 16;                // 16-byte chunks per row
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "row of 64, 128 or 256 bytes");
+  static constexpr int RPL = 1024 / ROWB;              // rows per 1 KB load block
+  static constexpr int TILE_BYTES = kKT * ROWB;        // K (or V) tile
+  static constexpr int STAGE = 2 * TILE_BYTES;         // K then V
+  static_assert((2 * kKT / RPL) % 4 == 0, "load blocks per wave");
+  static constexpr int LOADS = 2 * kKT / RPL / 4;      // load instructions per wave and tile
+  static constexpr int SK = HD / (2 * E);              // S^T MFMA steps over the head dim
+  static constexpr int MD = HD >= 32 ? HD / 32 : 1;    // O^T row blocks (head dim)
+  static constexpr int KPS = 2 * E;                    // keys per O^T MFMA step
 };
 
-// Physical position of key k (0 <= k < KT) inside a V^T row.  The O^T MFMA
-// consumes, in lane group g and chunk element e, key 16*(e/4) + 4*g + e%4 of a
-// 32-key step (bf16) or key 4*g + e of a 16-key step (f32); those keys are
-// placed contiguously.
-__device__ __forceinline__ int vt_pos(int k, bf16_t) {
-  return (k & ~31) | (((k >> 2) & 3) << 3) | (((k >> 4) & 1) << 2) | (k & 3);
-}
-__device__ __forceinline__ int vt_pos(int k, float) { return k; }
-// The key held by element e of physical chunk c (inverse of vt_pos).
-__device__ __forceinline__ int vt_key(int c, int e, bf16_t) {
-  return 32 * (c >> 2) + 16 * (e >> 2) + 4 * (c & 3) + (e & 3);
-}
-__device__ __forceinline__ int vt_key(int c, int e, float) { return 4 * c + e; }
-
+// K tile: chunk c of key row r at physical chunk c ^ kswz(r) -- a 16-lane
+// fragment read (16 consecutive rows, one logical chunk) covers all banks.
 template <int CPR>
-__device__ __forceinline__ int swz(int row, int chunk) {
-  constexpr int m = (CPR < 8 ? CPR : 8) - 1;
-  return row * (CPR * 16) + ((chunk ^ (row & m)) << 4);
+__device__ __forceinline__ int kswz(int r) {
+  return (r / (16 / CPR)) & (CPR - 1);
 }
-
-// P in bf16 for the O^T MFMA as hi + lo: hi = bf16(p), lo = bf16(p - hi), so
-// the product carries ~16 mantissa bits of p instead of 8 (the probabilities
-// are not a stored tensor of the method and get no bf16 rounding point).
-__device__ __forceinline__ void pack_p2(const f32x4 &a, const f32x4 &b, uint4 &hi, uint4 &lo) {
-  const float v[8] = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-  hi = f32_to_chunk(v, bf16_t{});
-  float r[8];
-  const uint32_t w[4] = {hi.x, hi.y, hi.z, hi.w};
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    r[2 * i] = v[2 * i] - bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffff));
-    r[2 * i + 1] = v[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
-  }
-  lo = f32_to_chunk(r, bf16_t{});
-}
-__device__ __forceinline__ uint4 pack_p(const f32x4 &a, const f32x4 &, float) {
-  return make_uint4(__float_as_uint(a[0]), __float_as_uint(a[1]), __float_as_uint(a[2]),
-                    __float_as_uint(a[3]));
+// V tile: chunk c of key row k at physical chunk c ^ vswz(k) -- the four
+// consecutive rows of a transposing read land in distinct 64-byte groups.
+template <int CPR>
+__device__ __forceinline__ int vswz(int k) {
+  return CPR == 16 ? 4 * (k & 3) : (CPR == 8 ? 4 * ((k >> 1) & 1) : 0);
 }
 }  // namespace
 
@@ -72,23 +66,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
                                                                 T *__restrict__ out,
                                                                 const int32_t *__restrict__ run_start,
                                                                 int B, int T_len, int H, float scale_log2) {
-  using C = AttnCfg<T>;
-  constexpr int E = C::E, KT = C::KT;
-  constexpr int CPR_K = HD * Elem<T>::kBytes / 16;   // chunks per K row
-  constexpr int SK = HD / (4 * E);                   // MFMA steps over head dim
-  constexpr int MBK = KT / 16;                       // key blocks per tile
-  constexpr int MBD = HD / 16;                       // head-dim blocks
-  constexpr int SV = KT / (4 * E);                   // MFMA steps over keys
-  constexpr int K_BYTES = KT * HD * Elem<T>::kBytes;
-  constexpr int V_BYTES = HD * 128;
-  constexpr int O_BYTES = kQT * HD * Elem<T>::kBytes;
-  constexpr int LDS = (K_BYTES + V_BYTES) > O_BYTES ? (K_BYTES + V_BYTES) : O_BYTES;
-  __shared__ __attribute__((aligned(16))) char lds[LDS];
-  char *ldsK = lds;
-  char *ldsV = lds + K_BYTES;
+  using C = AttnCfg<T, HD>;
+  constexpr int E = C::E, CPR = C::CPR, ROWB = C::ROWB, SK = C::SK, MD = C::MD, KPS = C::KPS;
+  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
 
   const int A = H * HD;
   const long ld = 3L * A;
+  const int ldb = (int)(ld * sizeof(T));
   const int nqt = (T_len + kQT - 1) / kQT;
   const int total = nqt * H * B;
   const int logical = xcd_remap(blockIdx.x, total);
@@ -98,154 +83,218 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
   const int q0 = qt * kQT;
   const long rowbase = (long)b * T_len;
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int g = lane >> 4, c16 = lane & 15;
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int hl = lane >> 5, c32 = lane & 31;
 
-  // this lane's queries and their windows
+  // ---- this lane's queries (two column blocks) and their Q fragments
+  const int qw0 = q0 + wave * kQW;
   int qi[2], rsq[2];
   uint4 qreg[2][SK];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    qi[qb] = q0 + wave * kQW + qb * 16 + c16;
-    const bool ok = qi[qb] < T_len;
-    rsq[qb] = ok ? run_start[rowbase + qi[qb]] : 0;
-    const T *qp = qkv + (rowbase + (ok ? qi[qb] : 0)) * ld + (long)h * HD;
+  for (int nb = 0; nb < 2; ++nb) {
+    qi[nb] = qw0 + 32 * nb + c32;
+    const bool ok = qi[nb] < T_len;
+    rsq[nb] = ok ? run_start[rowbase + qi[nb]] : 0;
+    const T *qp = qkv + (rowbase + (ok ? qi[nb] : 0)) * ld + (long)h * HD;
 #pragma unroll
     for (int s = 0; s < SK; ++s)
-      qreg[qb][s] = ok ? reinterpret_cast<const uint4 *>(qp)[4 * s + g] : make_uint4(0, 0, 0, 0);
+      qreg[nb][s] = ok ? reinterpret_cast<const uint4 *>(qp)[2 * s + hl] : make_uint4(0, 0, 0, 0);
   }
+  // block key range: windows start no earlier than the first query's
   const int qlast = min(q0 + kQT, T_len) - 1;
-  const int kbeg = run_start[rowbase + q0] / KT * KT;
+  const int kbeg = run_start[rowbase + q0] / kKT * kKT;
+  const int ntiles = (qlast - kbeg) / kKT + 1;
   // wave bounds: smallest window start and largest query of the wave
-  const int wq_lo = q0 + wave * kQW;
-  const int wq_hi = min(wq_lo + kQW, T_len) - 1;
-  const int w_rs = wq_lo < T_len ? run_start[rowbase + wq_lo] : 0;
+  const int wq_hi = min(qw0 + kQW, T_len) - 1;
+  const int w_rs = qw0 < T_len ? run_start[rowbase + qw0] : 0;
 
-  f32x4 o[MBD][2];
+  // ---- direct loads of key tile `it` (relative to kbeg) into a stage; tiles
+  // past the range become all-out-of-range loads (no traffic)
+  const long kv_bytes = (long)(T_len - 1) * ldb + ROWB;
+  const __amdgpu_buffer_rsrc_t rk = make_rsrc(qkv + rowbase * ld + A + (long)h * HD, kv_bytes);
+  const __amdgpu_buffer_rsrc_t rv = make_rsrc(qkv + rowbase * ld + 2L * A + (long)h * HD, kv_bytes);
+  const int rl = lane / CPR, pc = lane % CPR;
+  auto issue = [&](int it, char *stage) {
+    const bool valid = it < ntiles;
+    const int k0 = kbeg + it * kKT;
 #pragma unroll
-  for (int i = 0; i < MBD; ++i)
+    for (int i = 0; i < C::LOADS; ++i) {
+      const int q = wave * C::LOADS + i;               // load block: K blocks first, then V
+      const bool isv = q >= kKT / C::RPL;
+      const int qb = isv ? q - kKT / C::RPL : q;
+      const int row = qb * C::RPL + rl;                // key row inside the tile
+      const int c = pc ^ (isv ? vswz<CPR>(row) : kswz<CPR>(row));
+      const unsigned voff = valid ? (unsigned)(rl * ldb + c * 16) : kOOB;
+      dma16(isv ? rv : rk, stage + (isv ? C::TILE_BYTES : 0) + qb * 1024, voff,
+            valid ? (k0 + qb * C::RPL) * ldb : 0);
+    }
+  };
+
+  f32x16 o[MD][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) o[i][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < MD; ++i)
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[i][nb][r] = 0.f;
   float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
 
-  const T *kbase = qkv + rowbase * ld + A + (long)h * HD;
-  const T *vbase = qkv + rowbase * ld + 2L * A + (long)h * HD;
-
-  for (int k0 = kbeg; k0 <= qlast; k0 += KT) {
-    // ---- stage K (row-major, swizzled) and V^T (permuted keys) in LDS
-    for (int cidx = t; cidx < KT * CPR_K; cidx += kAttnThreads) {
-      const int kr = cidx / CPR_K, ch = cidx % CPR_K;
-      const int key = k0 + kr;
-      uint4 v = make_uint4(0, 0, 0, 0);
-      if (key < T_len) v = reinterpret_cast<const uint4 *>(kbase + (long)key * ld)[ch];
-      *reinterpret_cast<uint4 *>(ldsK + swz<CPR_K>(kr, ch)) = v;
-    }
-    {
-      constexpr int NCH = KT / E;                     // physical chunks per V^T row
-      constexpr int NBLK = NCH * (HD / E);
-      for (int blk = t; blk < NBLK; blk += kAttnThreads) {
-        const int c = blk % NCH, db = blk / NCH;
-        uint4 r[E];
+  // one key tile on stage sk (K at sk, V at sk + TILE_BYTES)
+  auto tile = [&](int it, const char *sk) {
+    const int k0 = kbeg + it * kKT;
+    const bool active = qw0 < T_len && k0 <= wq_hi && k0 + kKT - 1 >= w_rs;
+    if (!active) return;
+    const char *sv = sk + C::TILE_BYTES;
+    // ---- S^T = K Q^T: two 32-key row blocks x two 32-query column blocks
+    f32x16 s[2][2];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int key = k0 + vt_key(c, e, T{});
-          r[e] = key < T_len ? reinterpret_cast<const uint4 *>(vbase + (long)key * ld)[db]
-                             : make_uint4(0, 0, 0, 0);
-        }
-        transpose_chunks(r, T{});
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int j = 0; j < E; ++j) *reinterpret_cast<uint4 *>(ldsV + lds_off128(db * E + j, c)) = r[j];
+      for (int nb = 0; nb < 2; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[mb][nb][r] = 0.f;
+#pragma unroll
+    for (int st = 0; st < SK; ++st) {
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        const int row = 32 * mb + c32, ch = 2 * st + hl;
+        const uint4 a = *reinterpret_cast<const uint4 *>(sk + row * ROWB + ((ch ^ kswz<CPR>(row)) << 4));
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) mma32(a, qreg[nb][st], s[mb][nb], T{});
       }
     }
-    __syncthreads();
-
-    const bool active = wq_lo < T_len && k0 <= wq_hi && k0 + KT - 1 >= w_rs;
-    if (active) {
-      // ---- S^T = K Q^T
-      f32x4 s[MBK][2];
+    // ---- mask, online softmax (base 2)
 #pragma unroll
-      for (int mb = 0; mb < MBK; ++mb)
+    for (int nb = 0; nb < 2; ++nb) {
+      float mx = -INFINITY;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) s[mb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int st = 0; st < SK; ++st) {
-#pragma unroll
-        for (int mb = 0; mb < MBK; ++mb) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(ldsK + swz<CPR_K>(mb * 16 + c16, 4 * st + g));
-#pragma unroll
-          for (int qb = 0; qb < 2; ++qb) mma16(a, qreg[qb][st], s[mb][qb], T{});
+        for (int r = 0; r < 16; ++r) {
+          const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool ok = qi[nb] < T_len && key <= qi[nb] && key >= rsq[nb];
+          const float x = ok ? s[mb][nb][r] * scale_log2 : -INFINITY;
+          s[mb][nb][r] = x;
+          mx = fmaxf(mx, x);
         }
-      }
-      // ---- mask, online softmax
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float mnew = fmaxf(m[nb], mx);
+      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m[nb] - mnew);
+      float ls = 0.f;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        float mx = -INFINITY;
+      for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int mb = 0; mb < MBK; ++mb)
+        for (int r = 0; r < 16; ++r) {
+          const float p = (mnew == -INFINITY) ? 0.f : exp2f(s[mb][nb][r] - mnew);
+          s[mb][nb][r] = p;
+          ls += p;
+        }
+      l[nb] = l[nb] * alpha + ls;
+      m[nb] = mnew;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int key = k0 + mb * 16 + 4 * g + r;
-            const bool ok = qi[qb] < T_len && key <= qi[qb] && key >= rsq[qb];
-            const float x = ok ? s[mb][qb][r] * scale_log2 : -INFINITY;
-            s[mb][qb][r] = x;
-            mx = fmaxf(mx, x);
-          }
-        mx = fmaxf(mx, __shfl_xor(mx, 16));
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        const float mnew = fmaxf(m[qb], mx);
-        const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m[qb] - mnew);
-        float ls = 0.f;
+      for (int md = 0; md < MD; ++md)
 #pragma unroll
-        for (int mb = 0; mb < MBK; ++mb)
+        for (int r = 0; r < 16; ++r) o[md][nb][r] *= alpha;
+    }
+    // ---- O^T += V^T P^T.  Step j of 32-key block mb covers KPS keys; lane
+    // half hl supplies the E registers E*j .. E*j+E-1 of s[mb], i.e. keys
+    // 32 mb + 8 c + 4 hl + (0..3) for the register groups c of the step.
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float p = (mnew == -INFINITY) ? 0.f : exp2f(s[mb][qb][r] - mnew);
-            s[mb][qb][r] = p;
-            ls += p;
-          }
-        l[qb] = l[qb] * alpha + ls;
-        m[qb] = mnew;
+    for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int db = 0; db < MBD; ++db)
-#pragma unroll
-          for (int r = 0; r < 4; ++r) o[db][qb][r] *= alpha;
-      }
-      // ---- O^T += V^T P^T
-#pragma unroll
-      for (int sv = 0; sv < SV; ++sv) {
+      for (int j = 0; j < 32 / KPS; ++j) {
         uint4 pb[2], pl[2];
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb) {
-          if constexpr (E == 8) pack_p2(s[2 * sv][qb], s[2 * sv + 1][qb], pb[qb], pl[qb]);
-          else pb[qb] = pack_p(s[sv][qb], s[sv][qb], T{});
+        for (int nb = 0; nb < 2; ++nb) {
+          float v[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) v[e] = s[mb][nb][E * j + e];
+          pb[nb] = f32_to_chunk(v, T{});
+          if constexpr (sizeof(T) == 2) {
+            const uint32_t w[4] = {pb[nb].x, pb[nb].y, pb[nb].z, pb[nb].w};
+            float rr[8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              rr[2 * i] = v[2 * i] - bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffff));
+              rr[2 * i + 1] = v[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+            }
+            pl[nb] = f32_to_chunk(rr, T{});
+          }
         }
 #pragma unroll
-        for (int db = 0; db < MBD; ++db) {
-          const uint4 a = *reinterpret_cast<const uint4 *>(ldsV + lds_off128(db * 16 + c16, 4 * sv + g));
+        for (int md = 0; md < MD; ++md) {
+          uint4 a;
+          if constexpr (sizeof(T) == 2) {
+            // transposing reads: 16-lane group g reads head-dim rows M0 .. M0+15
+            // at keys K0 .. K0+3 (first read) and K0+8 .. K0+11 (second read)
+            typedef short v4s __attribute__((ext_vector_type(4)));
+            typedef __attribute__((address_space(3))) v4s lds_v4s;
+            const int g = lane >> 4, jj = lane & 15;
+            const int kr = 32 * mb + 16 * j + 4 * (g >> 1) + (jj >> 2);      // key row of this lane's address
+            const int dm = 32 * md + 16 * (g & 1) + 4 * (jj & 3);           // first head-dim element
+            const int ch = dm / E, within = (dm % E) * (int)sizeof(T);
+            const char *p0 = sv + kr * ROWB + ((ch ^ vswz<CPR>(kr)) << 4) + within;
+            const char *p1 = sv + (kr + 8) * ROWB + ((ch ^ vswz<CPR>(kr + 8)) << 4) + within;
+            const v4s x0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)to_lds(const_cast<char *>(p0)));
+            const v4s x1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s *)to_lds(const_cast<char *>(p1)));
+            const uint2 ua = __builtin_bit_cast(uint2, x0), ub = __builtin_bit_cast(uint2, x1);
+            a = make_uint4(ua.x, ua.y, ub.x, ub.y);
+          } else {
+            // f32: element e of the chunk is key 32 mb + 8 j + 4 hl + e, head-dim row 32 md + c32
+            const int dm = 32 * md + c32;
+            uint32_t w[4];
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb) {
-            mma16(a, pb[qb], o[db][qb], T{});
-            if constexpr (E == 8) mma16(a, pl[qb], o[db][qb], T{});
+            for (int e = 0; e < 4; ++e) {
+              const int kr = 32 * mb + 8 * j + 4 * hl + e;
+              w[e] = dm < HD ? *reinterpret_cast<const uint32_t *>(
+                                   sv + kr * ROWB + (((dm / E) ^ vswz<CPR>(kr)) << 4) + (dm % E) * 4)
+                             : 0u;
+            }
+            a = make_uint4(w[0], w[1], w[2], w[3]);
+          }
+#pragma unroll
+          for (int nb = 0; nb < 2; ++nb) {
+            mma32(a, pb[nb], o[md][nb], T{});
+            if constexpr (sizeof(T) == 2) mma32(a, pl[nb], o[md][nb], T{});
           }
         }
       }
-    }
-    __syncthreads();
-  }
+  };
 
-  // ---- normalise, stage [query][dh] in LDS, coalesced stores
+  // ---- pipeline over the key tiles: tile it lives in stage it & 1; after a
+  // tile is consumed, wait for the next one and refill the consumed stage
+  issue(0, st0);
+  issue(1, st1);
+  wait_vm_lds_barrier<C::LOADS>();             // tile 0 landed (tile 1 may be in flight)
+  int it = 0;
+  for (; it + 1 < ntiles; it += 2) {
+    tile(it, st0);
+    wait_vm_lds_barrier<0>();                  // tile it+1 landed, stage 0 retired
+    issue(it + 2, st0);
+    tile(it + 1, st1);
+    wait_vm_lds_barrier<0>();                  // tile it+2 landed, stage 1 retired
+    issue(it + 3, st1);
+  }
+  if (it < ntiles) tile(it, st0);
+  wait_vm_lds_barrier<0>();                    // no load in flight into the stages
+
+  // ---- normalise, stage [query][hd] in LDS (waves 0-1: stage 0, 2-3: stage 1),
+  // coalesced stores
+  char *ostage = wave < 2 ? st0 : st1;
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    float lt = l[qb];
-    lt += __shfl_xor(lt, 16);
-    lt += __shfl_xor(lt, 32);
+  for (int nb = 0; nb < 2; ++nb) {
+    const float lt = l[nb] + __shfl_xor(l[nb], 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int ql = wave * kQW + qb * 16 + c16;
-    T *orow = reinterpret_cast<T *>(lds) + (long)ql * HD;
+    const int ql = (wave & 1) * kQW + 32 * nb + c32;      // query inside the stage half
+    T *orow = reinterpret_cast<T *>(ostage) + (long)ql * HD;
 #pragma unroll
-    for (int db = 0; db < MBD; ++db)
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) store_elem(orow, db * 16 + 4 * g + r, o[db][qb][r] * inv);
+      for (int r = 0; r < 16; ++r) {
+        const int dd = 32 * md + 8 * (r >> 2) + 4 * hl + (r & 3);
+        if (dd < HD) store_elem(orow, dd, o[md][nb][r] * inv);
+      }
   }
   __syncthreads();
   constexpr int OCH = HD / E;   // chunks per output row
@@ -253,7 +302,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     const int ql = cidx / OCH, ch = cidx % OCH;
     const int q = q0 + ql;
     if (q >= T_len) continue;
-    const uint4 v = reinterpret_cast<const uint4 *>(lds + (long)ql * HD * Elem<T>::kBytes)[ch];
+    const char *src = (ql < 2 * kQW ? st0 : st1) + (long)(ql % (2 * kQW)) * HD * sizeof(T);
+    const uint4 v = reinterpret_cast<const uint4 *>(src)[ch];
     reinterpret_cast<uint4 *>(out + (rowbase + q) * (long)A + (long)h * HD)[ch] = v;
   }
 }
@@ -276,7 +326,6 @@ hipError_t launch_attention<bf16_t>(const bf16_t *qkv, bf16_t *out, const int32_
     case 32: return attn_launch<bf16_t, 32>(qkv, out, rs, B, T_len, H, s);
     case 64: return attn_launch<bf16_t, 64>(qkv, out, rs, B, T_len, H, s);
     case 128: return attn_launch<bf16_t, 128>(qkv, out, rs, B, T_len, H, s);
-    case 256: return attn_launch<bf16_t, 256>(qkv, out, rs, B, T_len, H, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -287,7 +336,6 @@ hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *
     case 16: return attn_launch<float, 16>(qkv, out, rs, B, T_len, H, s);
     case 32: return attn_launch<float, 32>(qkv, out, rs, B, T_len, H, s);
     case 64: return attn_launch<float, 64>(qkv, out, rs, B, T_len, H, s);
-    case 128: return attn_launch<float, 128>(qkv, out, rs, B, T_len, H, s);
     default: return hipErrorInvalidValue;
   }
 }
