@@ -6,8 +6,8 @@
 //
 // Layout: qkv [B*T, 3*A] (q | k | v, head h at columns h*hd), out [B*T, A].
 //
-// One block = 4 waves = 256 queries of one (batch row, head); each wave owns
-// 64 queries (two 32-query MFMA column blocks) held in registers.  Key tiles
+// One block = 256 queries of one (batch row, head); each wave owns 32 kNBQ
+// queries (kNBQ 32-query MFMA column blocks) held in registers.  Key tiles
 // of 64 keys (K and V, row-major as stored) move global -> LDS by direct
 // loads into two stages; the loads of tile t+1 are issued as soon as tile
 // t-1 has been consumed.  Per tile each wave computes
@@ -26,10 +26,15 @@
 namespace mtp {
 
 namespace {
-constexpr int kAttnThreads = 256;
-constexpr int kQW = 64;                       // queries per wave
-constexpr int kQT = 4 * kQW;                  // queries per block
+constexpr int kQT = 256;                      // queries per block
 constexpr int kKT = 64;                       // keys per tile
+constexpr int kNBQ = 1;                       // 32-query column blocks per wave
+constexpr int kQW = 32 * kNBQ;                // queries per wave
+constexpr int kWaves = kQT / kQW;             // waves per block
+constexpr int kAttnThreads = 64 * kWaves;
+// The running max is raised (and the accumulators rescaled) only when a tile's
+// max exceeds it by more than this (log2 units): probabilities stay <= 2^8.
+constexpr float kRescale = 8.f;
 
 template <typename T, int HD>
 struct AttnCfg {
@@ -40,8 +45,8 @@ struct AttnCfg {
   static constexpr int RPL = 1024 / ROWB;              // rows per 1 KB load block
   static constexpr int TILE_BYTES = kKT * ROWB;        // K (or V) tile
   static constexpr int STAGE = 2 * TILE_BYTES;         // K then V
-  static_assert((2 * kKT / RPL) % 4 == 0, "load blocks per wave");
-  static constexpr int LOADS = 2 * kKT / RPL / 4;      // load instructions per wave and tile
+  static_assert((2 * kKT / RPL) % kWaves == 0, "load blocks per wave");
+  static constexpr int LOADS = 2 * kKT / RPL / kWaves; // load instructions per wave and tile
   static constexpr int SK = HD / (2 * E);              // S^T MFMA steps over the head dim
   static constexpr int MD = HD >= 32 ? HD / 32 : 1;    // O^T row blocks (head dim)
   static constexpr int KPS = 2 * E;                    // keys per O^T MFMA step
@@ -87,12 +92,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int hl = lane >> 5, c32 = lane & 31;
 
-  // ---- this lane's queries (two column blocks) and their Q fragments
+  // ---- this lane's queries (NBQ column blocks) and their Q fragments
   const int qw0 = q0 + wave * kQW;
-  int qi[2], rsq[2];
-  uint4 qreg[2][SK];
+  constexpr int NBQ = kNBQ;
+  int qi[NBQ], rsq[NBQ];
+  uint4 qreg[NBQ][SK];
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NBQ; ++nb) {
     qi[nb] = qw0 + 32 * nb + c32;
     const bool ok = qi[nb] < T_len;
     rsq[nb] = ok ? run_start[rowbase + qi[nb]] : 0;
@@ -105,9 +111,11 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
   const int qlast = min(q0 + kQT, T_len) - 1;
   const int kbeg = run_start[rowbase + q0] / kKT * kKT;
   const int ntiles = (qlast - kbeg) / kKT + 1;
-  // wave bounds: smallest window start and largest query of the wave
+  // wave bounds: smallest window start and largest query of the wave; the
+  // latest window start (window starts never decrease along a row)
   const int wq_hi = min(qw0 + kQW, T_len) - 1;
   const int w_rs = qw0 < T_len ? run_start[rowbase + qw0] : 0;
+  const int w_rs_hi = qw0 < T_len ? run_start[rowbase + wq_hi] : 0;
 
   // ---- direct loads of key tile `it` (relative to kbeg) into a stage; tiles
   // past the range become all-out-of-range loads (no traffic)
@@ -131,14 +139,17 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     }
   };
 
-  f32x16 o[MD][2];
+  f32x16 o[MD][NBQ];
+  float m[NBQ], l[NBQ];
 #pragma unroll
-  for (int i = 0; i < MD; ++i)
+  for (int nb = 0; nb < NBQ; ++nb) {
+    m[nb] = -INFINITY;
+    l[nb] = 0.f;
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb)
+    for (int i = 0; i < MD; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) o[i][nb][r] = 0.f;
-  float m[2] = {-INFINITY, -INFINITY}, l[2] = {0.f, 0.f};
+  }
 
   // one key tile on stage sk (K at sk, V at sk + TILE_BYTES)
   auto tile = [&](int it, const char *sk) {
@@ -146,12 +157,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     const bool active = qw0 < T_len && k0 <= wq_hi && k0 + kKT - 1 >= w_rs;
     if (!active) return;
     const char *sv = sk + C::TILE_BYTES;
-    // ---- S^T = K Q^T: two 32-key row blocks x two 32-query column blocks
-    f32x16 s[2][2];
+    // every key of the tile visible to every query of the wave: no masking
+    const bool full = k0 + kKT - 1 <= qw0 && k0 >= w_rs_hi && wq_hi == qw0 + kQW - 1;
+    // ---- S^T = K Q^T: two 32-key row blocks x NBQ 32-query column blocks
+    f32x16 s[2][NBQ];
 #pragma unroll
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-      for (int nb = 0; nb < 2; ++nb)
+      for (int nb = 0; nb < NBQ; ++nb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) s[mb][nb][r] = 0.f;
 #pragma unroll
@@ -161,26 +174,35 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
         const int row = 32 * mb + c32, ch = 2 * st + hl;
         const uint4 a = *reinterpret_cast<const uint4 *>(sk + row * ROWB + ((ch ^ kswz<CPR>(row)) << 4));
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) mma32(a, qreg[nb][st], s[mb][nb], T{});
+        for (int nb = 0; nb < NBQ; ++nb) mma32(a, qreg[nb][st], s[mb][nb], T{});
       }
     }
-    // ---- mask, online softmax (base 2)
+    // ---- mask, online softmax (base 2) with a lazily raised running max
 #pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
+    for (int nb = 0; nb < NBQ; ++nb) {
       float mx = -INFINITY;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool ok = qi[nb] < T_len && key <= qi[nb] && key >= rsq[nb];
+          const bool ok = full | ((qi[nb] < T_len) & (key <= qi[nb]) & (key >= rsq[nb]));
           const float x = ok ? s[mb][nb][r] * scale_log2 : -INFINITY;
           s[mb][nb][r] = x;
           mx = fmaxf(mx, x);
         }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float mnew = fmaxf(m[nb], mx);
-      const float alpha = (mnew == -INFINITY) ? 1.f : exp2f(m[nb] - mnew);
+      const bool raise = mx > m[nb] + kRescale;          // same in both lanes of a query
+      const float mnew = raise ? mx : m[nb];
+      if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
+        const float alpha = raise ? exp2f(m[nb] - mnew) : 1.f;   // m = -inf: alpha = 0
+        l[nb] *= alpha;
+#pragma unroll
+        for (int md = 0; md < MD; ++md)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[md][nb][r] *= alpha;
+      }
+      m[nb] = mnew;
       float ls = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
@@ -190,12 +212,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
           s[mb][nb][r] = p;
           ls += p;
         }
-      l[nb] = l[nb] * alpha + ls;
-      m[nb] = mnew;
-#pragma unroll
-      for (int md = 0; md < MD; ++md)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[md][nb][r] *= alpha;
+      l[nb] += ls;
     }
     // ---- O^T += V^T P^T.  Step j of 32-key block mb covers KPS keys; lane
     // half hl supplies the E registers E*j .. E*j+E-1 of s[mb], i.e. keys
@@ -204,9 +221,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 32 / KPS; ++j) {
-        uint4 pb[2], pl[2];
+        uint4 pb[NBQ], pl[NBQ];
 #pragma unroll
-        for (int nb = 0; nb < 2; ++nb) {
+        for (int nb = 0; nb < NBQ; ++nb) {
           float v[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) v[e] = s[mb][nb][E * j + e];
@@ -254,7 +271,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
             a = make_uint4(w[0], w[1], w[2], w[3]);
           }
 #pragma unroll
-          for (int nb = 0; nb < 2; ++nb) {
+          for (int nb = 0; nb < NBQ; ++nb) {
             mma32(a, pb[nb], o[md][nb], T{});
             if constexpr (sizeof(T) == 2) mma32(a, pl[nb], o[md][nb], T{});
           }
@@ -279,15 +296,15 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
   if (it < ntiles) tile(it, st0);
   wait_vm_lds_barrier<0>();                    // no load in flight into the stages
 
-  // ---- normalise, stage [query][hd] in LDS (waves 0-1: stage 0, 2-3: stage 1),
-  // coalesced stores
-  char *ostage = wave < 2 ? st0 : st1;
+  // ---- normalise, stage [query][hd] in LDS (queries 0-127: stage 0,
+  // 128-255: stage 1), coalesced stores
 #pragma unroll
-  for (int nb = 0; nb < 2; ++nb) {
+  for (int nb = 0; nb < NBQ; ++nb) {
     const float lt = l[nb] + __shfl_xor(l[nb], 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
-    const int ql = (wave & 1) * kQW + 32 * nb + c32;      // query inside the stage half
-    T *orow = reinterpret_cast<T *>(ostage) + (long)ql * HD;
+    const int qb = wave * kQW + 32 * nb + c32;            // query inside the block
+    char *ostage = qb < kQT / 2 ? st0 : st1;
+    T *orow = reinterpret_cast<T *>(ostage) + (long)(qb % (kQT / 2)) * HD;
 #pragma unroll
     for (int md = 0; md < MD; ++md)
 #pragma unroll
@@ -302,7 +319,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     const int ql = cidx / OCH, ch = cidx % OCH;
     const int q = q0 + ql;
     if (q >= T_len) continue;
-    const char *src = (ql < 2 * kQW ? st0 : st1) + (long)(ql % (2 * kQW)) * HD * sizeof(T);
+    const char *src = (ql < kQT / 2 ? st0 : st1) + (long)(ql % (kQT / 2)) * HD * sizeof(T);
     const uint4 v = reinterpret_cast<const uint4 *>(src)[ch];
     reinterpret_cast<uint4 *>(out + (rowbase + q) * (long)A + (long)h * HD)[ch] = v;
   }
