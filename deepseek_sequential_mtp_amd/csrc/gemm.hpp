@@ -270,14 +270,18 @@ __device__ __forceinline__ void wait_vm_lds_barrier() {
 }
 
 // Scheduling pattern of one sub-step: NM slots of one MFMA followed by the
-// slot's share of the NR LDS reads of the next sub-step.
-template <int NM, int NR, int Q = 0>
+// slot's share of the NR LDS reads of the next sub-step and of NV global
+// loads (spread out so that a wave never stalls on a burst of loads queued
+// in front of its MFMAs).
+template <int NM, int NR, int NV = 0, int Q = 0>
 __device__ __forceinline__ void sched_interleave() {
   if constexpr (Q < NM) {
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);               // MFMA
     constexpr int nr = (Q + 1) * NR / NM - Q * NR / NM;
     if constexpr (nr > 0) __builtin_amdgcn_sched_group_barrier(0x100, nr, 0);  // DS read
-    sched_interleave<NM, NR, Q + 1>();
+    constexpr int nv = (Q + 1) * NV / NM - Q * NV / NM;
+    if constexpr (nv > 0) __builtin_amdgcn_sched_group_barrier(0x020, nv, 0);  // VMEM read
+    sched_interleave<NM, NR, NV, Q + 1>();
   }
 }
 
@@ -346,16 +350,17 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
     for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int j = 0; j < NB; ++j) mma32(fa[s][i], fb[s][j], acc[i][j], T{});
-    if constexpr (sizeof(T) == 2) sched_interleave<NM, NR>();
   };
   // one slice on stage sc; sn is the next slice's stage
   auto slice = [&](int it, char *sc, const char *sn) {
     read_frags(sc, 1, fa[1], fb[1]);
     mfmas(0);
+    if constexpr (sizeof(T) == 2) sched_interleave<NM, NR>();
     wait_vm_lds_barrier<2 * LOADS>();          // slice it+1 landed, stage sc retired
     issue(it + 4, sc);
     read_frags(sn, 0, fa[0], fb[0]);
     mfmas(1);
+    if constexpr (sizeof(T) == 2) sched_interleave<NM, NR, LOADS>();
   };
 
   issue(0, st0);
