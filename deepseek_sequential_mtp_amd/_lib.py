@@ -176,7 +176,7 @@ def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: tor
                     logit_slab_bytes: int = 0, out: Optional[Dict] = None, cache: Optional[Dict] = None,
                     stream=None) -> Dict:
     """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].  logit_slab_bytes
-    bounds the fp32 logit slab (0: the library default).
+    bounds the fp32 logit slab and the dz row group (0: the library default).
     Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error)."""
     D, B, T = labels.shape
     V, d = W_out.shape

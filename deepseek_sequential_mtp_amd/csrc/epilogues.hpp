@@ -67,6 +67,8 @@ struct EpiStore {
 //   out_j = x_j c + x_(j-HALF) s      (j >= HALF)
 // The partner column sits in the same lane, HALF/32 blocks away (HALF >= 32:
 // the wave's column range covers whole heads), or HALF lanes away (HALF < 32).
+// Stores go through a buffer resource ending at row M (branch-free, as in
+// EpiStore); whether a 32-column block is rotated is decided per wave.
 // ---------------------------------------------------------------------------
 template <typename OutT, int HALF>
 struct EpiRope {
@@ -78,15 +80,25 @@ struct EpiRope {
                                         int wn, int lane, int, char *, char *) const {
     constexpr int HD = 2 * HALF;
     static_assert(HALF < 32 || (Cfg::WN % HD) == 0, "wave columns must cover whole heads");
+    const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (long)m0 * ldc, rows * ldc * (long)sizeof(OutT));
+    const __amdgpu_buffer_rsrc_t rp = make_rsrc(pos + m0, rows * (long)sizeof(int));
 #pragma unroll
-    for (int i = 0; i < Cfg::MB; ++i)
+    for (int i = 0; i < Cfg::MB; ++i) {
+      int p[16];
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        p[r] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, (unsigned)(acc_row<Cfg>(wm, i, r, lane) * 4), 0, 0);
 #pragma unroll
       for (int j = 0; j < Cfg::NB; ++j) {
         const int col = n0 + acc_col<Cfg>(wn, j, lane);
         const int jh = col % HD;
         const bool lo = jh < HALF;
         const int jj = lo ? jh : jh - HALF;
-        const bool rot = rope != nullptr && col < 2 * A;
+        // 2A is a multiple of 32: the whole block column is q/k or v
+        const int col0 = n0 + acc_col<Cfg>(wn, j, 0);
+        const bool rot = rope != nullptr && __builtin_amdgcn_readfirstlane(col0) < 2 * A;
+        float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const float x = acc[i][j][r];
@@ -97,16 +109,20 @@ struct EpiRope {
           } else {
             partner = __shfl_xor(x, HALF);
           }
-          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
-          if (row >= M || col >= N) continue;
-          float v = x;
+          v[r] = x;
           if (rot) {
-            const float2 cs = rope[(long)pos[row] * HALF + jj];
-            v = lo ? (x * cs.x - partner * cs.y) : (x * cs.x + partner * cs.y);
+            const float2 cs = rope[(long)p[r] * HALF + jj];
+            v[r] = lo ? (x * cs.x - partner * cs.y) : (x * cs.x + partner * cs.y);
           }
-          store_elem(C, (long)row * ldc + col, v);
+        }
+        const bool cok = col < N;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rl = acc_row<Cfg>(wm, i, r, lane);
+          buf_store_elem(rc, cok ? (unsigned)(((long)rl * ldc + col) * sizeof(OutT)) : kOOB, v[r], OutT{});
         }
       }
+    }
   }
 };
 
@@ -114,6 +130,7 @@ struct EpiRope {
 // Fused gate/up + SwiGLU (pairs with RowsSwiGLU): block j < NB/2 holds gate
 // features, block j + NB/2 the up features of the same columns.
 // out[row, feat] = silu(gate) * up, feat = tn*(BN/2) + wn*(WN/2) + j*32 + lane.
+// Branch-free stores through a buffer resource ending at row M.
 // ---------------------------------------------------------------------------
 template <typename OutT>
 struct EpiSwiGLU {
@@ -123,19 +140,20 @@ struct EpiSwiGLU {
                                         int wn, int lane, int, char *, char *) const {
     constexpr int NBh = Cfg::NB / 2;
     const int tile_n = n0 / Cfg::BN;
+    const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (long)m0 * ldc, rows * ldc * (long)sizeof(OutT));
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
       for (int j = 0; j < NBh; ++j) {
         const int feat = tile_n * (Cfg::BN / 2) + wn * (Cfg::WN / 2) + j * 32 + (lane & 31);
-        if (feat >= f) continue;
+        const bool fok = feat < f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = m0 + acc_row<Cfg>(wm, i, r, lane);
-          if (row >= M) continue;
+          const int rl = acc_row<Cfg>(wm, i, r, lane);
           const float g = acc[i][j][r], u = acc[i][j + NBh][r];
-          const float s = g / (1.f + __expf(-g));
-          store_elem(C, (long)row * ldc + feat, s * u);
+          const float sw = g / (1.f + __expf(-g));
+          buf_store_elem(rc, fok ? (unsigned)(((long)rl * ldc + feat) * sizeof(OutT)) : kOOB, sw * u, OutT{});
         }
       }
   }
@@ -148,7 +166,10 @@ struct EpiSwiGLU {
 // to target[row] when the label falls in this tile.  The fp32 logits are also
 // stored to zout [M, V] for the backward (softmax - onehot needs the row's
 // final log-sum-exp, known only after every vocabulary tile).  Reductions go
-// through LDS (the staging buffers are free after the main loop).
+// through LDS (the staging buffers are free after the main loop).  Logit and
+// label accesses go through buffer resources ending at row M (branch-free);
+// the target store is skipped by the whole wave when no lane holds a label
+// column.  Requires BM * V * 4 < 2^31 (checked by the caller).
 // ---------------------------------------------------------------------------
 struct EpiCEFwd {
   const int *labels; float2 *part; float *target; float *zout; int M, V, nt;
@@ -162,6 +183,17 @@ struct EpiCEFwd {
     float *redm = reinterpret_cast<float *>(lds);          // [2][BM] row max per column wave
     float *reds = redm + 2 * Cfg::BM;                        // [2][BM] row sum-exp per column wave
     const bool writer = (lane & 31) == 0;
+    const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + (long)m0 * V, rows * V * 4L);
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(labels + m0, rows * 4L);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(target + m0, rows * 4L);
+    int col[Cfg::NB];
+    bool cok[Cfg::NB];
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j) {
+      col[j] = n0 + acc_col<Cfg>(wn, j, lane);
+      cok[j] = col[j] < V;
+    }
     // 1) row max over this wave's columns
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
@@ -169,10 +201,7 @@ struct EpiCEFwd {
       for (int r = 0; r < 16; ++r) {
         float mx = -INFINITY;
 #pragma unroll
-        for (int j = 0; j < Cfg::NB; ++j) {
-          const int col = n0 + acc_col<Cfg>(wn, j, lane);
-          mx = col < V ? fmaxf(mx, acc[i][j][r]) : mx;
-        }
+        for (int j = 0; j < Cfg::NB; ++j) mx = cok[j] ? fmaxf(mx, acc[i][j][r]) : mx;
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
         if (writer) redm[wn * Cfg::BM + acc_row<Cfg>(wm, i, r, lane)] = mx;
@@ -183,24 +212,26 @@ struct EpiCEFwd {
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int rl = acc_row<Cfg>(wm, i, r, lane);
-        const int row = m0 + rl;
-        const float m = fmaxf(redm[rl], redm[Cfg::BM + rl]);
-        const int lab = row < M ? labels[row] : -1;
-        float s = 0.f;
+        const int rr = acc_row<Cfg>(wm, i, r, lane);
+        const float m = fmaxf(redm[rr], redm[Cfg::BM + rr]);
+        const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(rr * 4), 0, 0);
+        const int lab = rr < rows ? lab0 : -1;
+        float s = 0.f, tv = 0.f;
+        bool has = false;
 #pragma unroll
         for (int j = 0; j < Cfg::NB; ++j) {
-          const int col = n0 + acc_col<Cfg>(wn, j, lane);
           const float z = acc[i][j][r];
-          if (col < V) {
-            s += exp2f((z - m) * kLog2e);
-            if (row < M) zout[(long)row * V + col] = z;
-          }
-          if (col == lab) target[row] = z;
+          s += cok[j] ? exp2f((z - m) * kLog2e) : 0.f;
+          buf_store_elem(rz, cok[j] ? (unsigned)(((long)rr * V + col[j]) * 4) : kOOB, z, float{});
+          const bool hit = col[j] == lab;
+          tv = hit ? z : tv;
+          has = has || hit;
         }
+        if (__builtin_amdgcn_ballot_w64(has) != 0)
+          buf_store_elem(rt, has ? (unsigned)(rr * 4) : kOOB, tv, float{});
 #pragma unroll
         for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (writer) reds[wn * Cfg::BM + rl] = s;
+        if (writer) reds[wn * Cfg::BM + rr] = s;
       }
     __syncthreads();
     const int t = threadIdx.x;
@@ -216,7 +247,14 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, in
   __shared__ __attribute__((aligned(1024))) char st1[Cfg::LDS_STAGE];
   __shared__ __attribute__((aligned(1024))) char st2[Cfg::LDS_STAGE];
   __shared__ __attribute__((aligned(1024))) char st3[Cfg::LDS_STAGE];
-  gemm_body<T, Cfg>(la, lb, epi, K, ts, st0, st1, st2, st3);
+  if constexpr (Cfg::NS == 5) {
+    __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];
+    char *const st[5] = {st0, st1, st2, st3, st4};
+    gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+  } else {
+    char *const st[4] = {st0, st1, st2, st3};
+    gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+  }
 }
 
 // Host-side launch helper (grid = tiles * K splits, one block per tile).

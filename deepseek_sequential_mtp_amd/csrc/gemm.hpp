@@ -2,13 +2,14 @@
 // accumulation, WGM x WGN waves per workgroup, BM x BN output tile.
 //
 // K is staged through LDS in slices of 64 bytes per operand row (32 bf16 or
-// 16 f32 elements) in NS = 4 stages: the loads of slice kt + 4 are issued as
-// soon as slice kt has been consumed, so every load has three slices of MFMA
-// work to land.  Operands go global -> LDS directly (buffer_load ... lds): no
-// staging registers and no ds_write.  The stages are four distinct LDS
-// objects and the K loop is unrolled by four, so the compiler can tell that a
-// fragment read of one stage does not depend on the loads in flight into the
-// others.
+// 16 f32 elements) in NS stages.  Operands go global -> LDS directly
+// (buffer_load ... lds): no staging registers and no ds_write.  The loads of
+// slice kt + NS - 1 go into the stage that slice kt - 1 used, so the one
+// barrier of each slice only needs the reads of the slice before it retired
+// and the MFMA pipe never drains behind a wait for reads just issued.  The
+// stages are distinct LDS objects and the K loop is unrolled by NS, so the
+// compiler can tell that a fragment read of one stage does not depend on the
+// loads in flight into the others.
 //
 // Operands are described by loaders: K-major (K contiguous), optionally with
 // interleaved row sources, or MN-major (M or N contiguous), read back with
@@ -20,7 +21,7 @@
 
 namespace mtp {
 
-template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2>
+template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2, int NS_ = 4>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
   static constexpr int WGM = WGM_, WGN = WGN_;       // waves along M and N
@@ -28,7 +29,8 @@ struct Tile {
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 blocks per wave
   static constexpr int ROWB = 64;                     // bytes per operand row and stage
-  static constexpr int NS = 4;                        // LDS stages
+  static constexpr int NS = NS_;                      // LDS stages
+  static_assert(NS == 4 || NS == 5, "stage count");
   static constexpr int LDS_STAGE = (BM + BN) * ROWB;  // bytes per stage
 };
 
@@ -259,13 +261,17 @@ __device__ __forceinline__ void tile_coords(int logical, int mt, int nt, int gro
 
 struct TileSched { int mt, nt, group_m, k_splits; };
 
-// Waits until at most VM of this wave's vector-memory operations are
-// outstanding and all its LDS operations are done, then barriers.  s_waitcnt
-// layout on gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8].
-template <int VM>
+// Waits until at most VM of this wave's vector-memory operations and at most
+// LGKM of its LDS operations are outstanding, then barriers.  s_waitcnt
+// layout on gfx9: vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt
+// [11:8].  LDS operations complete in order, so "at most LGKM outstanding"
+// means every LDS operation issued before the last LGKM has completed; a
+// count above the field's maximum is clamped (a stricter wait).
+template <int VM, int LGKM = 0>
 __device__ __forceinline__ void wait_vm_lds_barrier() {
   static_assert(VM >= 0 && VM < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4));
+  constexpr int L = LGKM > 15 ? 15 : LGKM;
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (L << 8));
   __builtin_amdgcn_s_barrier();
 }
 
@@ -289,20 +295,24 @@ __device__ __forceinline__ void sched_interleave() {
 // The kernel body.  Each block computes one BM x BN tile (optionally one K
 // split of it) and hands the accumulators to the epilogue.
 //
-// Slice kt lives in stage kt % 4.  At the end of slice kt (before its second
-// sub-step's MFMAs) every wave waits for its loads of slice kt + 1 -- the
-// loads of slices kt + 2 and kt + 3 may stay in flight -- and the block
-// barriers, which also retires every read of stage kt % 4; the loads of
-// slice kt + 4 then go into that stage.  Slices past the block's K range are
-// issued as all-out-of-range loads (no memory traffic), so the number of
-// loads in flight, and with it the wait count, is the same for every slice.
+// Slice kt lives in stage kt % NS and is consumed in two sub-steps of 32
+// bytes of K each.  In the middle of slice kt (after the first
+// sub-step's MFMAs, whose shadow hides the second sub-step's fragment reads)
+// every wave waits until its loads of slice kt + 1 have landed -- the loads
+// of slices kt + 2 .. kt + NS - 2 may stay in flight -- and until every LDS
+// read it issued before this slice's second sub-step has completed; the
+// block barrier then makes both true for all waves.  Stage (kt - 1) % NS is
+// thereby retired and receives the loads of slice kt + NS - 1.  Slices past
+// the block's K range are issued as all-out-of-range loads (no memory
+// traffic), so the number of loads in flight, and with it the wait count, is
+// the same for every slice.
 // ---------------------------------------------------------------------------
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi &epi, int K,
-                                          const TileSched &ts, char *st0, char *st1, char *st2, char *st3) {
+                                          const TileSched &ts, char *const *st) {
   constexpr int E = Elem<T>::kPerChunk;
   constexpr int BK = 4 * E;                    // K elements per 64-byte slice
-  constexpr int MB = Cfg::MB, NB = Cfg::NB;
+  constexpr int MB = Cfg::MB, NB = Cfg::NB, NS = Cfg::NS;
   constexpr int LOADS = LA::kLoads + LB::kLoads;   // load instructions per wave and slice
   const int ntiles = ts.mt * ts.nt * ts.k_splits;
   const int logical = xcd_remap(blockIdx.x, ntiles);
@@ -351,36 +361,32 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
 #pragma unroll
       for (int j = 0; j < NB; ++j) mma32(fa[s][i], fb[s][j], acc[i][j], T{});
   };
-  // one slice on stage sc; sn is the next slice's stage
-  auto slice = [&](int it, char *sc, const char *sn) {
+  // one slice on stage sc; sn is the next slice's stage, sp the previous one's
+  auto slice = [&](int it, char *sc, const char *sn, char *sp) {
     read_frags(sc, 1, fa[1], fb[1]);
     mfmas(0);
     if constexpr (sizeof(T) == 2) sched_interleave<NM, NR>();
-    wait_vm_lds_barrier<2 * LOADS>();          // slice it+1 landed, stage sc retired
-    issue(it + 4, sc);
+    wait_vm_lds_barrier<(NS - 3) * LOADS, NR>();   // slice it+1 landed, stage sp retired
+    issue(it + NS - 1, sp);
     read_frags(sn, 0, fa[0], fb[0]);
     mfmas(1);
     if constexpr (sizeof(T) == 2) sched_interleave<NM, NR, LOADS>();
   };
 
-  issue(0, st0);
-  issue(1, st1);
-  issue(2, st2);
-  issue(3, st3);
-  wait_vm_lds_barrier<3 * LOADS>();            // slice 0 landed
-  read_frags(st0, 0, fa[0], fb[0]);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j) issue(j, st[j]);
+  wait_vm_lds_barrier<(NS - 2) * LOADS>();     // slice 0 landed
+  read_frags(st[0], 0, fa[0], fb[0]);
   int it = 0;
-  for (; it + 3 < nk; it += 4) {
-    slice(it, st0, st1);
-    slice(it + 1, st1, st2);
-    slice(it + 2, st2, st3);
-    slice(it + 3, st3, st0);
+  for (; it + NS - 1 < nk; it += NS) {
+#pragma unroll
+    for (int j = 0; j < NS; ++j) slice(it + j, st[j], st[(j + 1) % NS], st[(j + NS - 1) % NS]);
   }
-  if (it < nk) slice(it, st0, st1);
-  if (it + 1 < nk) slice(it + 1, st1, st2);
-  if (it + 2 < nk) slice(it + 2, st2, st3);
+#pragma unroll
+  for (int j = 0; j < NS - 1; ++j)
+    if (it + j < nk) slice(it + j, st[j], st[j + 1], st[(j + NS - 1) % NS]);
   wait_vm_lds_barrier<0>();                    // no load in flight into the stages
-  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, st0, st1);
+  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, st[0], st[1]);
 }
 
 // Result-layout helpers: row / column of accumulator register r of block

@@ -195,14 +195,18 @@ int pick(bool big, F &&f) {
 }
 
 // K-split count for the dx GEMM: fill the 256 compute units with whole waves
-// of tiles while keeping each split long.
+// of tiles while keeping each split long.  Cost in units of one K step: a
+// wave of tiles takes its K range plus a fixed ~10^4 for the tile's start,
+// epilogue and partial-sum traffic (measured on the 256x256 tile: one
+// unsplit pass over K = 129280 beats 2 or 4 splits even when it leaves the
+// second wave of tiles a quarter empty).
 inline int dx_splits(int M, int d, int V, bool big) {
   const long tiles = (long)ceil_div(M, big ? 256 : 128) * ceil_div(d, big ? 256 : 128);
   int best = 1;
   double best_cost = 1e300;
   for (int s = 1; s <= 8; s *= 2) {
     const double waves = ceil((double)tiles * s / 256.0);
-    const double cost = waves * ((double)V / s) + 0.02 * V * s;   // + slab traffic
+    const double cost = waves * ((double)V / s + 1e4) + 0.02 * V * s;   // + split-sum traffic
     if (cost < best_cost - 1e-9) { best_cost = cost; best = s; }
   }
   return best;
@@ -350,6 +354,7 @@ int check_ce(const mtp_ce_args *a) {
   const int E = a->dtype == MTP_BF16 ? 8 : 4;
   if (a->d % E || a->V % E) return MTP_ERR_SHAPE;
   if ((long)a->B * a->T > (1L << 30)) return MTP_ERR_SHAPE;
+  if (a->V >= (1 << 21)) return MTP_ERR_SHAPE;   // a 256-row logit tile spans < 2 GiB
   if (a->reduce != MTP_REDUCE_FIXED && a->reduce != MTP_REDUCE_VALID_MEAN) return MTP_ERR_ARG;
   if (a->reduce == MTP_REDUCE_FIXED && !(a->denom >= 0.0)) return MTP_ERR_ARG;
   if (!(a->eps >= 0.f) || !isfinite(a->lambda)) return MTP_ERR_ARG;
@@ -367,7 +372,8 @@ int check_ce_ptrs(const mtp_ce_args *a) {
 
 struct CeDims {
   long N; int d, V, nt, splits; bool big, big_dx;
-  long slab;          // rows per logit slab
+  long slab;          // rows per fp32 logit slab
+  long group;         // rows per dz buffer: a whole number of slabs (or all N rows)
 };
 
 constexpr size_t kDefaultLogitSlab = size_t(1) << 30;
@@ -382,11 +388,16 @@ CeDims ce_dims(const mtp_ce_args *a) {
   long r = (long)(budget / ((size_t)c.V * sizeof(float)));
   if (r >= 256) r -= r % 256;
   c.slab = r < 1 ? 1 : (r > c.N ? c.N : r);
+  // dz is stored in T: the same byte budget holds sizeof(float) / sizeof(T)
+  // slabs of it, and the dx_hat / dW_out GEMMs run once per group of slabs
+  long g = (long)(budget / ((size_t)c.V * sizeof(T)));
+  g -= g % c.slab;
+  c.group = g < c.slab ? c.slab : (g > c.N ? c.N : g);
   c.big = sizeof(T) == 2 && use_big(c.slab, c.V);
   c.nt = ceil_div(c.V, c.big ? 256 : 128);
-  // the dx_hat GEMM (slab rows x d, K = V) may also fill the chip with K splits
-  c.big_dx = sizeof(T) == 2 && (long)ceil_div(c.slab, 256) * ceil_div(c.d, 256) * 8 >= 256;
-  c.splits = dx_splits((int)c.slab, c.d, c.V, c.big_dx);
+  // the dx_hat GEMM (group rows x d, K = V) may also fill the chip with K splits
+  c.big_dx = sizeof(T) == 2 && (long)ceil_div(c.group, 256) * ceil_div(c.d, 256) * 8 >= 256;
+  c.splits = dx_splits((int)c.group, c.d, c.V, c.big_dx);
   return c;
 }
 
@@ -405,7 +416,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[7] = c.take<double>(a->D);                   // loss sums
   p[8] = c.take<int32_t>(a->D);                  // counts
   p[9] = c.take<float>(a->D);                    // backward scales
-  p[10] = c.take<T>(m.slab * m.V);               // dz = softmax - onehot of the slab
+  p[10] = c.take<T>(m.group * m.V);              // dz = softmax - onehot of the row group
   p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
   p[13] = c.take<float>(m.slab * m.V);           // fp32 logits of the slab
@@ -433,8 +444,9 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   float *zbuf = (float *)p[13];
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
-  const long slab = m.N * m.d;                   // stride of the dx_hat split partials
+  const long sstride = m.N * m.d;                // stride of the dx_hat split partials
   if (a->device_error) MTP_TRY(fill_i32(a->device_error, 1, 0, s));
+  const bool big_dw = sizeof(T) == 2 && use_big(V, d);
 
   for (int k = 0; k < D; ++k) {
     const T *h = static_cast<const T *>(a->h[k]);
@@ -450,40 +462,42 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
       MTP_STAGE(MTP_STAGE_CE_REDUCE);
       MTP_TRY(launch_ce_reduce(nullptr, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
     }
-    for (long r0 = 0; r0 < m.N; r0 += m.slab) {
-      const int nr = (int)(m.N - r0 < m.slab ? m.N - r0 : m.slab);
-      const T *xs = xhat + r0 * d;
-      const int32_t *ls = lab + r0;
-      {
-        MTP_STAGE(MTP_STAGE_CE_FWD);
-        st = pick<T>(m.big, [&](auto cfg) {
-          return gemm_ce_fwd_cfg<T, decltype(cfg)>(xs, (const T *)a->W_out, ls, part, target + r0, zbuf, nr, V, d,
-                                                    s);
-        });
-      }
-      if (st) return st;
-      {
-        MTP_STAGE(MTP_STAGE_CE_REDUCE);
-        MTP_TRY(launch_ce_combine(part, m.nt, target + r0, ls, lse + r0,
-                                  a->lse ? a->lse + (long)k * N + r0 : nullptr, row_loss + r0, nr, s));
-      }
-      {
-        MTP_STAGE(MTP_STAGE_CE_GRAD);
-        MTP_TRY(launch_ce_dz<T>(zbuf, lse + r0, ls, dz, nr, V, s));
+    for (long g0 = 0; g0 < m.N; g0 += m.group) {
+      const int gn = (int)(m.N - g0 < m.group ? m.N - g0 : m.group);
+      for (long r0 = g0; r0 < g0 + gn; r0 += m.slab) {
+        const int nr = (int)(g0 + gn - r0 < m.slab ? g0 + gn - r0 : m.slab);
+        const int32_t *ls = lab + r0;
+        {
+          MTP_STAGE(MTP_STAGE_CE_FWD);
+          st = pick<T>(m.big, [&](auto cfg) {
+            return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat + r0 * d, (const T *)a->W_out, ls, part, target + r0,
+                                                      zbuf, nr, V, d, s);
+          });
+        }
+        if (st) return st;
+        {
+          MTP_STAGE(MTP_STAGE_CE_REDUCE);
+          MTP_TRY(launch_ce_combine(part, m.nt, target + r0, ls, lse + r0,
+                                    a->lse ? a->lse + (long)k * N + r0 : nullptr, row_loss + r0, nr, s));
+        }
+        {
+          MTP_STAGE(MTP_STAGE_CE_GRAD);
+          MTP_TRY(launch_ce_dz<T>(zbuf, lse + r0, ls, dz + (r0 - g0) * V, nr, V, s));
+        }
       }
       {
         MTP_STAGE(MTP_STAGE_CE_DX);
         st = pick<T>(m.big_dx, [&](auto cfg) {
-          return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs + r0 * d, slab, nr, V, d, scale + k,
+          return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs + g0 * d, sstride, gn, V, d, scale + k,
                                                m.splits, s);
         });
       }
       if (st) return st;
-      const bool big_dw = sizeof(T) == 2 && use_big(V, d);
       {
         MTP_STAGE(MTP_STAGE_CE_DW);
         st = pick<T>(big_dw, [&](auto cfg) {
-          return gemm_dw_cfg<T, decltype(cfg)>(dz, xs, a->dW_out, nr, V, d, scale + k, dw_acc0 || r0 > 0, s);
+          return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat + g0 * d, a->dW_out, gn, V, d, scale + k,
+                                               dw_acc0 || g0 > 0, s);
         });
       }
       if (st) return st;
@@ -494,7 +508,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_CE_NORM_BWD);
-      MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, slab, h, r, a->g_out, static_cast<float *>(a->dh[k]),
+      MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, sstride, h, r, a->g_out, static_cast<float *>(a->dh[k]),
                                      dg_part, a->dg_out, dw_acc0, N, d, s));
     }
   }

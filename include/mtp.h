@@ -152,9 +152,12 @@ typedef struct {
  * R * V * 4 <= logit_slab_bytes (R rounded down to a multiple of 256 when it
  * is at least 256, and at least 1).  Per slab the forward GEMM reduces each
  * vocabulary tile to an online (max, sum-exp) partial per row and keeps the
- * slab's fp32 logits; the partials give the row's log-sum-exp, softmax -
- * onehot is formed from the kept logits and consumed by the dx_hat and dW_out
- * GEMMs of the same slab.  Workspace grows with the slab, not with B*T.
+ * slab's fp32 logits; the partials give the row's log-sum-exp and softmax -
+ * onehot is formed from the kept logits, stored in dtype.  That gradient is
+ * kept for a group of G rows, G * V * sizeof(dtype) <= logit_slab_bytes (a
+ * whole number of slabs, at least one; two for bf16), and the dx_hat and
+ * dW_out GEMMs run once per group.  Workspace grows with the slab, not with
+ * B*T.
  *
  * Inputs : h [host] D pointers [B*T, d] (dtype); labels int32 [D,B,T]
  *          (-1 = no loss, as written by mtp_chain_forward); W_out [V, d]
@@ -170,10 +173,11 @@ typedef struct {
  *          main loss's), 0 overwrites.
  * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
  *          MTP_REDUCE_VALID_MEAN (denom ignored).
- * logit_slab_bytes: bound on the fp32 logit slab (0 selects 1 GiB).
- * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0.
- * Labels outside [-1, V) are treated as -1 and set device_error (may be
- * NULL).
+ * logit_slab_bytes: bound on the fp32 logit slab and on the gradient group
+ *          (0 selects 1 GiB).
+ * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0;
+ * V < 2^21.  Labels outside [-1, V) are treated as -1 and set device_error
+ * (may be NULL).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, d, V, D;

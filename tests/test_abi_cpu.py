@@ -83,6 +83,8 @@ def test_ce_host_errors(lib):
     assert run(args(reduce=5)) == -6
     assert run(args(denom=-1.0)) == -6
     assert run(args(V=510)) == -2
+    assert run(args(V=1 << 21)) == -2       # a 256-row logit tile must span < 2 GiB
+    assert run(args(V=(1 << 21) - 4)) == -1  # shape accepted; fails on the null pointers
     assert run(args()) == -1
     assert lib.mtp_ce_workspace_size(C.byref(args())) > 0
 

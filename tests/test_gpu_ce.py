@@ -87,10 +87,12 @@ def test_ce_tiny_f32(slab_rows):
     _assert(cfg, res, ref, labels)
 
 
-@pytest.mark.parametrize("reduce,slab_rows", [("fixed", 0), ("valid_mean", 0), ("fixed", 128),
+@pytest.mark.parametrize("reduce,slab_rows", [("fixed", 0), ("valid_mean", 0), ("fixed", 80),
                                               ("valid_mean", 128)])
 def test_ce_bf16_ragged_two_depths(reduce, slab_rows):
-    # slab_rows=128: 600 rows in 5 slabs (88 in the last), two depths
+    # bf16 dz holds two logit slabs of rows, so the dx / dW GEMMs run per
+    # group of two slabs.  slab_rows=128: 600 rows in groups 256, 256, 88;
+    # slab_rows=80: groups 160 x 3 and 120 (slabs 80 + 40); two depths
     cfg = synth.scaled(synth.D1, name="ce_ragged", B=2, T=300, d=256, V=1000, D=2, seg_lo=20,
                        seg_hi=200, sigma_w=0.05)
     res, ref, labels = _case(cfg, reduce=reduce, slab_rows=slab_rows)
@@ -108,7 +110,7 @@ def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
 @pytest.mark.parametrize("slab_rows", [0, 256])
 def test_ce_bf16_big_tiles(slab_rows):
     # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each); slab_rows=256
-    # runs the 1024 rows as four slabs
+    # runs the 1024 rows as four slabs in two dz groups
     cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=1024, V=16384, D=1, seg_lo=100,
                        seg_hi=700, sigma_w=0.02)
     res, ref, labels = _case(cfg, slab_rows=slab_rows)
@@ -116,9 +118,9 @@ def test_ce_bf16_big_tiles(slab_rows):
 
 
 def test_ce_bf16_big_dx_tiles_sparse_labels():
-    # 256x256 tiles with K splits in the dx GEMM (rows x d >= 256 tiles);
+    # 256x256 tiles in the dx GEMM, 64 of them, split 4 ways over K = V;
     # labels on 64 sampled rows keep the oracle cheap, the GPU runs every row
-    cfg = synth.scaled(synth.D1, name="ce_bigdx", B=1, T=4096, d=4096, V=1024, D=1,
+    cfg = synth.scaled(synth.D1, name="ce_bigdx", B=1, T=4096, d=1024, V=4096, D=1,
                        seg_lo=4096, seg_hi=4096, sigma_w=0.01)
     rows = np.random.default_rng(3).choice(4095, 64, replace=False)
     res, ref, labels = _case(cfg, label_rows=rows)
