@@ -3,6 +3,8 @@
 // column l%32 of block (i, j)) plus the tile origin.
 #pragma once
 
+#include <type_traits>
+
 #include "gemm.hpp"
 
 namespace mtp {
@@ -241,19 +243,38 @@ struct EpiCEFwd {
   }
 };
 
+// Whether a loader stages its operand in 128-byte pair rows.
+template <class L, class = void>
+struct PairRows : std::false_type {};
+template <class L>
+struct PairRows<L, std::void_t<decltype(L::kPairRows)>> : std::bool_constant<L::kPairRows> {};
+
 template <typename T, class Cfg, class LA, class LB, class Epi>
 __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
-  __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[Cfg::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char st2[Cfg::LDS_STAGE];
-  __shared__ __attribute__((aligned(1024))) char st3[Cfg::LDS_STAGE];
-  if constexpr (Cfg::NS == 5) {
-    __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];
-    char *const st[5] = {st0, st1, st2, st3, st4};
-    gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+  if constexpr (PairRows<LA>::value) {
+    __shared__ __attribute__((aligned(1024))) char a0[Cfg::BM * 128];
+    __shared__ __attribute__((aligned(1024))) char a1[Cfg::BM * 128];
+    __shared__ __attribute__((aligned(1024))) char a2[Cfg::BM * 128];
+    __shared__ __attribute__((aligned(1024))) char b0[Cfg::BN * 64];
+    __shared__ __attribute__((aligned(1024))) char b1[Cfg::BN * 64];
+    __shared__ __attribute__((aligned(1024))) char b2[Cfg::BN * 64];
+    __shared__ __attribute__((aligned(1024))) char b3[Cfg::BN * 64];
+    char *const sa[3] = {a0, a1, a2};
+    char *const sb[4] = {b0, b1, b2, b3};
+    gemm_body_pairs<T, Cfg>(la, lb, epi, K, ts, sa, sb);
   } else {
-    char *const st[4] = {st0, st1, st2, st3};
-    gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+    __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE];
+    __shared__ __attribute__((aligned(1024))) char st1[Cfg::LDS_STAGE];
+    __shared__ __attribute__((aligned(1024))) char st2[Cfg::LDS_STAGE];
+    __shared__ __attribute__((aligned(1024))) char st3[Cfg::LDS_STAGE];
+    if constexpr (Cfg::NS == 5) {
+      __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];
+      char *const st[5] = {st0, st1, st2, st3, st4};
+      gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+    } else {
+      char *const st[4] = {st0, st1, st2, st3};
+      gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
+    }
   }
 }
 

@@ -17,6 +17,8 @@
 // result layout (see common.hpp) and do the stores / reductions.
 #pragma once
 
+#include <utility>
+
 #include "common.hpp"
 
 namespace mtp {
@@ -126,6 +128,51 @@ struct DmaKMajor {
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
       dma16(rs, region + q * 1024, voff, 16 * q * ldb + k0 * (int)sizeof(T));
+    }
+  }
+};
+
+// K-major A operand in 128-byte rows: one row holds two consecutive 64-byte
+// slices (a "pair"), so a 1 KB load block covers 8 rows x 128 bytes, i.e. 8
+// whole 128-byte lines, where DmaKMajor's block touches 16 half lines.  The
+// pair region is ROWS x 128 bytes; chunk c (0..7) of row r sits at physical
+// chunk c ^ ((r >> 1) & 7), so the 16 rows a 16-lane group reads at one
+// logical chunk fall on 16 distinct 16-byte bank groups.  Lane L of block q
+// fills row 8 q + L / 8, physical chunk L % 8, and fetches the logical chunk
+// the swizzle places there, (L % 8) ^ ((4 (q & 1) + L / 16) & 7).
+template <typename T, int ROWS, int NT>
+struct DmaKMajor128 {
+  static constexpr bool kPairRows = true;
+  static constexpr int E = Elem<T>::kPerChunk;
+  static constexpr int NBLK = ROWS / 8, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
+  static_assert(NBLK % WAVES == 0, "blocks per wave");
+  static constexpr int kLoads = PER_WAVE;   // load instructions per wave and pair
+  static constexpr int kReads = 1;
+  static constexpr int kRegionBytes = ROWS * 128;
+  const T *base; long ld; int rows; int K;
+  // Fragment of the 32-row block at tile row r0, K sub-step s (0..3) of the
+  // pair: lane l holds row r0 + l % 32, logical chunk 2 s + l / 32.
+  __device__ static __forceinline__ uint4 frag(const char *region, int r0, int s, int lane) {
+    const int row = r0 + (lane & 31);
+    const int c = 2 * s + (lane >> 5);
+    return *reinterpret_cast<const uint4 *>(region + row * 128 + (((c ^ (row >> 1)) & 7) << 4));
+  }
+  __device__ __forceinline__ void issue(int row0, int k0, char *region) const {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const long nrow = rows - row0 < ROWS ? rows - row0 : ROWS;
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (long)row0 * ld, nrow * ld * (long)sizeof(T));
+    const int ldb = (int)(ld * sizeof(T));
+    unsigned voff[2];
+#pragma unroll
+    for (int par = 0; par < 2; ++par) {
+      const int c = (lane & 7) ^ ((4 * par + (lane >> 4)) & 7);
+      voff[par] = k0 + c * E < K ? (unsigned)((lane >> 3) * ldb + c * 16) : kOOB;
+    }
+#pragma unroll
+    for (int i = 0; i < PER_WAVE; ++i) {
+      const int q = wave * PER_WAVE + i;
+      dma16(rs, region + q * 1024, voff[q & 1], 8 * q * ldb + k0 * (int)sizeof(T));
     }
   }
 };
@@ -387,6 +434,130 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
     if (it + j < nk) slice(it + j, st[j], st[j + 1], st[(j + NS - 1) % NS]);
   wait_vm_lds_barrier<0>();                    // no load in flight into the stages
   epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, st[0], st[1]);
+}
+
+// ---------------------------------------------------------------------------
+// Kernel body for an A operand in 128-byte rows (DmaKMajor128) and a B
+// operand in 64-byte slices.  A pair p (slices 2p, 2p+1 of the block's K
+// range) lives in A region p % 3, slice kt of B in B stage kt % 4 (3 x BM x
+// 128 + 4 x BN x 64 bytes: 160 KB for 256 x 256).  The barrier in the middle
+// of slice kt (same conditions as in gemm_body) retires B stage (kt - 1) % 4,
+// which receives B slice kt + 3, and, for even kt, A region (kt / 2 - 1) % 3,
+// which receives pair kt / 2 + 2.  Loads are issued in the same order at
+// every barrier, so the wait for slice kt + 1 always leaves one B slice and
+// one A pair in flight.  The loop is unrolled by 12 slices (both rings come
+// back to their first stage).
+// ---------------------------------------------------------------------------
+template <typename T, class Cfg, class LA, class LB, class Epi>
+__device__ __forceinline__ void gemm_body_pairs(const LA &la, const LB &lb, const Epi &epi, int K,
+                                                const TileSched &ts, char *const *sa, char *const *sb) {
+  static_assert(sizeof(T) == 2, "pair rows are for bf16 operands");
+  constexpr int E = Elem<T>::kPerChunk;
+  constexpr int BK = 4 * E;                    // K elements per 64-byte slice
+  constexpr int MB = Cfg::MB, NB = Cfg::NB;
+  constexpr int LA2 = LA::kLoads, LB1 = LB::kLoads;
+  const int ntiles = ts.mt * ts.nt * ts.k_splits;
+  const int logical = xcd_remap(blockIdx.x, ntiles);
+  const int split = logical % ts.k_splits;
+  int tm, tn;
+  tile_coords(logical / ts.k_splits, ts.mt, ts.nt, ts.group_m, tm, tn);
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+
+  const int nk_total = (K + BK - 1) / BK;
+  int per = (nk_total + ts.k_splits - 1) / ts.k_splits;
+  per += per & 1;                              // K splits start on a pair
+  const int kt0 = split * per;
+  const int kt1 = min(nk_total, kt0 + per);
+  const int nk = kt1 > kt0 ? kt1 - kt0 : 0;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
+
+  f32x16 acc[MB][NB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  uint4 fa[2][MB], fb[2][NB];
+  const int ar0 = wm * Cfg::WM, br0 = wn * Cfg::WN;
+  // sub-step sa (0..3) of an A pair region, sub-step sb (0..1) of a B stage
+  auto read_frags = [&](const char *ra, int sa_, const char *rb, int sb_, uint4 *a, uint4 *b) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i) a[i] = LA::frag(ra, ar0 + 32 * i, sa_, lane);
+#pragma unroll
+    for (int j = 0; j < NB; ++j) b[j] = LB::frag(rb, br0 + 32 * j, sb_, lane);
+  };
+  auto issue_b = [&](int it, char *stage) {
+    lb.issue(n0, it < nk ? (kt0 + it) * BK : K, stage);
+  };
+  auto issue_a = [&](int p, char *region) {
+    la.issue(m0, 2 * p < nk ? (kt0 + 2 * p) * BK : K, region);
+  };
+  constexpr int NM = MB * NB;
+  constexpr int NR = MB * LA::kReads + NB * LB::kReads;
+  auto mfmas = [&](int s) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NB; ++j) mma32(fa[s][i], fb[s][j], acc[i][j], T{});
+  };
+  // slice it = 12 q + J (J fixes the stages at compile time)
+  auto slice = [&](int it, auto Jc) {
+    constexpr int J = decltype(Jc)::value;
+    constexpr int P = J / 2, H = J & 1;        // pair index mod 6, half of the pair
+    char *ra = sa[P % 3];
+    char *rb = sb[J % 4];
+    read_frags(ra, 2 * H + 1, rb, 1, fa[1], fb[1]);
+    mfmas(0);
+    sched_interleave<NM, NR>();
+    wait_vm_lds_barrier<LB1 + LA2, NR>();      // slice it+1 landed; B stage J-1, A region P-1 retired
+    issue_b(it + 3, sb[(J + 3) % 4]);
+    if constexpr (H == 0) issue_a(it / 2 + 2, sa[(P + 2) % 3]);
+    read_frags(sa[((J + 1) / 2) % 3], 2 * ((J + 1) & 1), sb[(J + 1) % 4], 0, fa[0], fb[0]);
+    mfmas(1);
+    sched_interleave<NM, NR, LB1 + (H == 0 ? LA2 : 0)>();
+  };
+
+  // the same issue order as the barriers of slices -4 .. -1 would produce
+  issue_a(0, sa[0]);
+  issue_b(0, sb[0]);
+  issue_b(1, sb[1]);
+  issue_a(1, sa[1]);
+  issue_b(2, sb[2]);
+  wait_vm_lds_barrier<2 * LB1 + LA2>();        // slice 0 (A pair 0, B slice 0) landed
+  read_frags(sa[0], 0, sb[0], 0, fa[0], fb[0]);
+  int it = 0;
+  for (; it + 11 < nk; it += 12) {
+    slice(it + 0, std::integral_constant<int, 0>{});
+    slice(it + 1, std::integral_constant<int, 1>{});
+    slice(it + 2, std::integral_constant<int, 2>{});
+    slice(it + 3, std::integral_constant<int, 3>{});
+    slice(it + 4, std::integral_constant<int, 4>{});
+    slice(it + 5, std::integral_constant<int, 5>{});
+    slice(it + 6, std::integral_constant<int, 6>{});
+    slice(it + 7, std::integral_constant<int, 7>{});
+    slice(it + 8, std::integral_constant<int, 8>{});
+    slice(it + 9, std::integral_constant<int, 9>{});
+    slice(it + 10, std::integral_constant<int, 10>{});
+    slice(it + 11, std::integral_constant<int, 11>{});
+  }
+  if (it + 0 < nk) slice(it + 0, std::integral_constant<int, 0>{});
+  if (it + 1 < nk) slice(it + 1, std::integral_constant<int, 1>{});
+  if (it + 2 < nk) slice(it + 2, std::integral_constant<int, 2>{});
+  if (it + 3 < nk) slice(it + 3, std::integral_constant<int, 3>{});
+  if (it + 4 < nk) slice(it + 4, std::integral_constant<int, 4>{});
+  if (it + 5 < nk) slice(it + 5, std::integral_constant<int, 5>{});
+  if (it + 6 < nk) slice(it + 6, std::integral_constant<int, 6>{});
+  if (it + 7 < nk) slice(it + 7, std::integral_constant<int, 7>{});
+  if (it + 8 < nk) slice(it + 8, std::integral_constant<int, 8>{});
+  if (it + 9 < nk) slice(it + 9, std::integral_constant<int, 9>{});
+  if (it + 10 < nk) slice(it + 10, std::integral_constant<int, 10>{});
+  wait_vm_lds_barrier<0>();                    // no load in flight into the stages
+  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, sa[0], sa[1]);
 }
 
 // Result-layout helpers: row / column of accumulator register r of block

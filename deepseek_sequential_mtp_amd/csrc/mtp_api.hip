@@ -77,6 +77,11 @@ template <typename T, class Cfg> using KA = DmaKMajor<T, Cfg::BM, Cfg::NT>;
 template <typename T, class Cfg> using KB = DmaKMajor<T, Cfg::BN, Cfg::NT>;
 template <typename T, class Cfg> using MA = DmaMNMajor<T, Cfg::BM, Cfg::NT>;
 template <typename T, class Cfg> using MB_ = DmaMNMajor<T, Cfg::BN, Cfg::NT>;
+// A operand of the GEMMs whose B is K-major too: the 256x256 bf16 tile stages
+// it in 128-byte pair rows (whole 128-byte lines per load).
+template <typename T, class Cfg>
+using PA = std::conditional_t<sizeof(T) == 2 && Cfg::BM == 256, DmaKMajor128<T, Cfg::BM, Cfg::NT>,
+                              DmaKMajor<T, Cfg::BM, Cfg::NT>>;
 
 inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N, 256) >= 256; }
 
@@ -86,14 +91,14 @@ int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc
   EpiStore<OutT, ResT> epi{C, ldc, M, N, alpha, alpha_dev, R, ldr, accumulate, 0};
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, N)) {
-      KA<T, Big> la{A, lda, M, K};
+      PA<T, Big> la{A, lda, M, K};
       KB<T, Big> lb{Bm, ldb, N, K};
       MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, N, K, 8, 1, s)));
       return MTP_OK;
     }
   }
   {
-    KA<T, Small> la{A, lda, M, K};
+    PA<T, Small> la{A, lda, M, K};
     KB<T, Small> lb{Bm, ldb, N, K};
     MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, N, K, 8, 1, s)));
   }
@@ -105,7 +110,7 @@ int gemm_qkv_rope_cfg(const T *xa, const T *W, T *qkv, const int *pos, const flo
                       int A, hipStream_t s) {
   const int N = 3 * A;
   EpiRope<T, HALF> epi{qkv, (long)N, M, N, A, pos, rope};
-  KA<T, Cfg> la{xa, (long)d, M, d};
+  PA<T, Cfg> la{xa, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, N, d};
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, N, d, 8, 1, s)));
   return MTP_OK;
@@ -135,7 +140,7 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, 2L * f)) {
       EpiSwiGLU<T> epi{out, (long)f, M, f};
-      KA<T, Big> la{y, (long)d, M, d};
+      PA<T, Big> la{y, (long)d, M, d};
       DmaKMajorSwiGLU<T, Big> lb{Wg, Wu, (long)d, f, d};
       MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, 1, s)));
       return MTP_OK;
@@ -143,7 +148,7 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
   }
   {
     EpiSwiGLU<T> epi{out, (long)f, M, f};
-    KA<T, Small> la{y, (long)d, M, d};
+    PA<T, Small> la{y, (long)d, M, d};
     DmaKMajorSwiGLU<T, Small> lb{Wg, Wu, (long)d, f, d};
     MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, 2 * ceil_div(f, Small::BN / 2) * (Small::BN / 2), d, 8,
                                    1, s)));
@@ -156,7 +161,7 @@ int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, flo
                     int V, int d, hipStream_t s) {
   const int nt = ceil_div(V, Cfg::BN);
   EpiCEFwd epi{lab, part, target, z, M, V, nt};
-  KA<T, Cfg> la{xhat, (long)d, M, d};
+  PA<T, Cfg> la{xhat, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, V, d};
   // all row tiles of one vocabulary tile run next to each other: W is read once
   MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
