@@ -177,21 +177,33 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
         for (int nb = 0; nb < NBQ; ++nb) mma32(a, qreg[nb][st], s[mb][nb], T{});
       }
     }
-    // ---- mask, online softmax (base 2) with a lazily raised running max
+    // ---- mask, online softmax (base 2) with a lazily raised running max.
+    // The max is taken on the raw scores (scale_log2 > 0 keeps the order) and
+    // each probability is one FMA and one hardware exp2 (results below 2^-126
+    // flush to zero).  `full` is the same for the whole wave: a tile visible
+    // to every query of the wave skips the mask arithmetic.
 #pragma unroll
     for (int nb = 0; nb < NBQ; ++nb) {
-      float mx = -INFINITY;
+      float mraw = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int mb = 0; mb < 2; ++mb)
+        for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const bool ok = full | ((qi[nb] < T_len) & (key <= qi[nb]) & (key >= rsq[nb]));
-          const float x = ok ? s[mb][nb][r] * scale_log2 : -INFINITY;
-          s[mb][nb][r] = x;
-          mx = fmaxf(mx, x);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+          for (int r = 0; r < 16; ++r) mraw = fmaxf(mraw, s[mb][nb][r]);
+      } else {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const bool ok = (qi[nb] < T_len) & (key <= qi[nb]) & (key >= rsq[nb]);
+            const float x = ok ? s[mb][nb][r] : -INFINITY;
+            s[mb][nb][r] = x;
+            mraw = fmaxf(mraw, x);
+          }
+      }
+      mraw = fmaxf(mraw, __shfl_xor(mraw, 32));
+      const float mx = mraw * scale_log2;                 // -inf stays -inf
       const bool raise = mx > m[nb] + kRescale;          // same in both lanes of a query
       const float mnew = raise ? mx : m[nb];
       if (__builtin_amdgcn_read_exec() & __ballot(raise)) {
@@ -203,12 +215,14 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
           for (int r = 0; r < 16; ++r) o[md][nb][r] *= alpha;
       }
       m[nb] = mnew;
+      // no visible key yet: every score is -inf and every p must be 0
+      const float neg = mnew == -INFINITY ? 0.f : -mnew;
       float ls = 0.f;
 #pragma unroll
       for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = (mnew == -INFINITY) ? 0.f : exp2f(s[mb][nb][r] - mnew);
+          const float p = __builtin_amdgcn_exp2f(fmaf(s[mb][nb][r], scale_log2, neg));
           s[mb][nb][r] = p;
           ls += p;
         }
@@ -233,8 +247,8 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
             float rr[8];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-              rr[2 * i] = v[2 * i] - bf16_to_f32(static_cast<uint16_t>(w[i] & 0xffff));
-              rr[2 * i + 1] = v[2 * i + 1] - bf16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+              rr[2 * i] = v[2 * i] - bf16_lo_f32(w[i]);
+              rr[2 * i + 1] = v[2 * i + 1] - bf16_hi_f32(w[i]);
             }
             pl[nb] = f32_to_chunk(rr, T{});
           }

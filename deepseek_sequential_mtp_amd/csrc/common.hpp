@@ -34,16 +34,25 @@ __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
   return __builtin_bit_cast(uint16_t, h);
 }
 
+// Two values rounded to nearest even and packed (a in the low half): one
+// v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  typedef float f2 __attribute__((ext_vector_type(2)));
+  typedef __bf16 h2 __attribute__((ext_vector_type(2)));
+  const f2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, h2));
+}
+// The two halves of a packed pair as floats.
+__device__ __forceinline__ float bf16_lo_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi_f32(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
 __device__ __forceinline__ float load_elem(const bf16_t *p, long i) { return bf16_to_f32(p[i].bits); }
 __device__ __forceinline__ float load_elem(const float *p, long i) { return p[i]; }
 __device__ __forceinline__ void store_elem(bf16_t *p, long i, float v) { p[i].bits = f32_to_bf16(v); }
 __device__ __forceinline__ void store_elem(float *p, long i, float v) { p[i] = v; }
 // 4 consecutive values in one store (p 8-byte aligned for bf16, 16 for f32).
 __device__ __forceinline__ void store4(bf16_t *p, const float (&v)[4]) {
-  uint2 w;
-  w.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-  w.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-  *reinterpret_cast<uint2 *>(p) = w;
+  *reinterpret_cast<uint2 *>(p) = make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
 }
 __device__ __forceinline__ void store4(float *p, const float (&v)[4]) {
   *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
@@ -63,12 +72,8 @@ __device__ __forceinline__ void chunk_to_f32(const uint4 &c, float *o, float) {
   o[2] = __uint_as_float(c.z); o[3] = __uint_as_float(c.w);
 }
 __device__ __forceinline__ uint4 f32_to_chunk(const float *v, bf16_t) {
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = static_cast<uint32_t>(f32_to_bf16(v[2 * i])) |
-           (static_cast<uint32_t>(f32_to_bf16(v[2 * i + 1])) << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
+  return make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                    pack_bf16x2(v[6], v[7]));
 }
 __device__ __forceinline__ uint4 f32_to_chunk(const float *v, float) {
   return make_uint4(__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]),
