@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const float *__restrict__ z,
                                                     int V) {
   const long row = blockIdx.y;
   const int lab = labels[row];
-  const float l = lse[row];
+  const float nl = -lse[row] * kLog2e;
   const float4 *zr = reinterpret_cast<const float4 *>(z + row * V);
   T *dr = dz + row * V;
   for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
@@ -54,8 +54,11 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const float *__restrict__ z,
     if (lab >= 0) {
       const float4 v = zr[c4];
       const float zz[4] = {v.x, v.y, v.z, v.w};
+      // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
+      // (probabilities below 2^-126 flush to zero)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) g[e] = exp2f((zz[e] - l) * kLog2e) - (4 * c4 + e == lab ? 1.f : 0.f);
+      for (int e = 0; e < 4; ++e)
+        g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, nl)) - (4 * c4 + e == lab ? 1.f : 0.f);
     }
     store4(dr + 4 * c4, g);
   }

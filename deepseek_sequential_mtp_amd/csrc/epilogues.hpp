@@ -154,7 +154,7 @@ struct EpiSwiGLU {
         for (int r = 0; r < 16; ++r) {
           const int rl = acc_row<Cfg>(wm, i, r, lane);
           const float g = acc[i][j][r], u = acc[i][j + NBh][r];
-          const float sw = g / (1.f + __expf(-g));
+          const float sw = __fdividef(g, 1.f + __expf(-g));
           buf_store_elem(rc, fok ? (unsigned)(((long)rl * ldc + feat) * sizeof(OutT)) : kOOB, sw * u, OutT{});
         }
       }
@@ -215,7 +215,7 @@ struct EpiCEFwd {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = acc_row<Cfg>(wm, i, r, lane);
-        const float m = fmaxf(redm[rr], redm[Cfg::BM + rr]);
+        const float nm = -fmaxf(redm[rr], redm[Cfg::BM + rr]) * kLog2e;
         const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(rr * 4), 0, 0);
         const int lab = rr < rows ? lab0 : -1;
         float s = 0.f, tv = 0.f;
@@ -223,7 +223,7 @@ struct EpiCEFwd {
 #pragma unroll
         for (int j = 0; j < Cfg::NB; ++j) {
           const float z = acc[i][j][r];
-          s += cok[j] ? exp2f((z - m) * kLog2e) : 0.f;
+          s += cok[j] ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
           buf_store_elem(rz, cok[j] ? (unsigned)(((long)rr * V + col[j]) * 4) : kOOB, z, float{});
           const bool hit = col[j] == lab;
           tv = hit ? z : tv;
