@@ -249,36 +249,131 @@ struct PairRows : std::false_type {};
 template <class L>
 struct PairRows<L, std::void_t<decltype(L::kPairRows)>> : std::bool_constant<L::kPairRows> {};
 
-template <typename T, class Cfg, class LA, class LB, class Epi>
-__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
-  if constexpr (PairRows<LA>::value) {
-    __shared__ __attribute__((aligned(1024))) char a0[Cfg::BM * 128];
-    __shared__ __attribute__((aligned(1024))) char a1[Cfg::BM * 128];
-    __shared__ __attribute__((aligned(1024))) char a2[Cfg::BM * 128];
-    __shared__ __attribute__((aligned(1024))) char b0[Cfg::BN * 64];
-    __shared__ __attribute__((aligned(1024))) char b1[Cfg::BN * 64];
-    __shared__ __attribute__((aligned(1024))) char b2[Cfg::BN * 64];
-    __shared__ __attribute__((aligned(1024))) char b3[Cfg::BN * 64];
-    char *const sa[3] = {a0, a1, a2};
-    char *const sb[4] = {b0, b1, b2, b3};
-    gemm_body_pairs<T, Cfg>(la, lb, epi, K, ts, sa, sb);
-  } else {
-    __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE];
-    __shared__ __attribute__((aligned(1024))) char st1[Cfg::LDS_STAGE];
-    __shared__ __attribute__((aligned(1024))) char st2[Cfg::LDS_STAGE];
-    __shared__ __attribute__((aligned(1024))) char st3[Cfg::LDS_STAGE];
-    if constexpr (Cfg::NS == 5) {
-      __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];
-      char *const st[5] = {st0, st1, st2, st3, st4};
-      gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
-    } else {
-      char *const st[4] = {st0, st1, st2, st3};
-      gemm_body<T, Cfg>(la, lb, epi, K, ts, st);
-    }
-  }
+// One BM x BN tile, K slices [kt0, kt0 + nk), into acc.
+template <typename T, class Cfg, class LA, class LB>
+__device__ __forceinline__ void gemm_segment(const LA &la, const LB &lb, int m0, int n0, int kt0, int nk, int K,
+                                             char *const *r0, char *const *r1, f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+  if constexpr (PairRows<LA>::value) gemm_mainloop_pairs<T, Cfg>(la, lb, m0, n0, kt0, nk, K, r0, r1, acc);
+  else gemm_mainloop<T, Cfg>(la, lb, m0, n0, kt0, nk, K, r0, acc);
 }
 
-// Host-side launch helper (grid = tiles * K splits, one block per tile).
+// LDS of one GEMM block: the pair-row layout (3 A regions of BM x 128 bytes,
+// 4 B stages of BN x 64 bytes) or NS stages of (BM + BN) x 64 bytes.  An
+// epilogue may use the first two regions as scratch once the main loop has
+// returned.
+#define MTP_GEMM_LDS(Cfg, LA)                                                                   \
+  char *r0[PairRows<LA>::value ? 3 : Cfg::NS];                                                  \
+  char *r1[4];                                                                                  \
+  if constexpr (PairRows<LA>::value) {                                                          \
+    __shared__ __attribute__((aligned(1024))) char a0[Cfg::BM * 128], a1[Cfg::BM * 128],        \
+        a2[Cfg::BM * 128];                                                                      \
+    __shared__ __attribute__((aligned(1024))) char b0[Cfg::BN * 64], b1[Cfg::BN * 64],          \
+        b2[Cfg::BN * 64], b3[Cfg::BN * 64];                                                     \
+    r0[0] = a0; r0[1] = a1; r0[2] = a2;                                                         \
+    r1[0] = b0; r1[1] = b1; r1[2] = b2; r1[3] = b3;                                             \
+  } else {                                                                                      \
+    __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE], st1[Cfg::LDS_STAGE],    \
+        st2[Cfg::LDS_STAGE], st3[Cfg::LDS_STAGE];                                               \
+    r0[0] = st0; r0[1] = st1; r0[2] = st2; r0[3] = st3;                                         \
+    if constexpr (Cfg::NS == 5) {                                                               \
+      __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];                       \
+      r0[Cfg::NS - 1] = st4;                                                                    \
+    }                                                                                           \
+  }
+
+// Floats of one partial tile (the block's accumulators).
+template <class Cfg>
+constexpr long partial_floats() { return (long)Cfg::MB * Cfg::NB * 16 * Cfg::NT; }
+
+// Partial tiles are kept in the accumulator layout: float4 q of thread t at
+// slot[(q * NT + t) * 4], so each wave moves 1 KB per instruction.
+template <class Cfg>
+__device__ __forceinline__ void store_partial(float *slot, const f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+  float4 *p = reinterpret_cast<float4 *>(slot) + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int q = (i * Cfg::NB + j) * 4 + c;
+        p[q * Cfg::NT] = make_float4(acc[i][j][4 * c], acc[i][j][4 * c + 1], acc[i][j][4 * c + 2],
+                                     acc[i][j][4 * c + 3]);
+      }
+}
+template <class Cfg>
+__device__ __forceinline__ void add_partial(const float *slot, f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
+  const float4 *p = reinterpret_cast<const float4 *>(slot) + threadIdx.x;
+#pragma unroll
+  for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const float4 v = p[((i * Cfg::NB + j) * 4 + c) * Cfg::NT];
+        acc[i][j][4 * c] += v.x;
+        acc[i][j][4 * c + 1] += v.y;
+        acc[i][j][4 * c + 2] += v.z;
+        acc[i][j][4 * c + 3] += v.w;
+      }
+}
+
+// One block per tile and K split.  The launch covers tiles [tile0, tile0 +
+// ntiles) of the grouped raster order, split-major (blocks that run together
+// share a K range and neighbouring tiles).  Without ws each block hands its
+// accumulators to the epilogue (K splits then write separate output slabs);
+// with ws it stores them as an fp32 partial tile, slot split * ntiles + tile,
+// for gemm_fixup_kernel.
+template <typename T, class Cfg, class LA, class LB, class Epi>
+__global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, int K, TileSched ts) {
+  constexpr int BK = 4 * Elem<T>::kPerChunk;
+  MTP_GEMM_LDS(Cfg, LA)
+  const int logical = xcd_remap(blockIdx.x, ts.ntiles * ts.k_splits);
+  const int split = logical / ts.ntiles;
+  const int tl = logical - split * ts.ntiles;
+  int tm, tn;
+  tile_coords(ts.tile0 + tl, ts.mt, ts.nt, ts.group_m, tm, tn);
+  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
+  const int nk_total = (K + BK - 1) / BK;
+  int per = (nk_total + ts.k_splits - 1) / ts.k_splits;
+  if constexpr (PairRows<LA>::value) per += per & 1;   // K splits start on a pair
+  const int kt0 = split * per;
+  const int kt1 = min(nk_total, kt0 + per);
+  const int nk = kt1 > kt0 ? kt1 - kt0 : 0;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  f32x16 acc[Cfg::MB][Cfg::NB];
+  gemm_segment<T, Cfg>(la, lb, m0, n0, kt0, nk, K, r0, r1, acc);
+  if (ts.ws != nullptr) {
+    store_partial<Cfg>(ts.ws + ((long)split * ts.ntiles + tl) * partial_floats<Cfg>(), acc);
+    return;
+  }
+  epi.template apply<Cfg>(acc, m0, n0, wave / Cfg::WGN, wave % Cfg::WGN, lane, split, r0[0], r0[1]);
+}
+
+// Block b sums the k_splits partial tiles of tile tile0 + b and runs the
+// epilogue on the sum.
+template <class Cfg, class Epi>
+__global__ __launch_bounds__(Cfg::NT) void gemm_fixup_kernel(Epi epi, TileSched ts) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * Cfg::BM * sizeof(float)];
+  const int tl = blockIdx.x;
+  int tm, tn;
+  tile_coords(ts.tile0 + tl, ts.mt, ts.nt, ts.group_m, tm, tn);
+  f32x16 acc[Cfg::MB][Cfg::NB];
+#pragma unroll
+  for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  for (int sp = 0; sp < ts.k_splits; ++sp)
+    add_partial<Cfg>(ts.ws + ((long)sp * ts.ntiles + tl) * partial_floats<Cfg>(), acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  epi.template apply<Cfg>(acc, tm * Cfg::BM, tn * Cfg::BN, wave / Cfg::WGN, wave % Cfg::WGN, lane, 0, lds,
+                          lds);
+}
+
+// Host-side launch helpers.  launch_gemm: every tile, K split k_splits ways,
+// each split through the epilogue.
 template <typename T, class Cfg, class LA, class LB, class Epi>
 inline hipError_t launch_gemm(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K,
                               int group_m, int k_splits, hipStream_t stream) {
@@ -287,10 +382,77 @@ inline hipError_t launch_gemm(const LA &la, const LB &lb, const Epi &epi, int M,
   ts.nt = (N + Cfg::BN - 1) / Cfg::BN;
   ts.group_m = group_m < 1 ? 1 : (group_m > ts.mt ? ts.mt : group_m);
   ts.k_splits = k_splits < 1 ? 1 : k_splits;
-  const long tiles = (long)ts.mt * ts.nt * ts.k_splits;
-  if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)tiles), dim3(Cfg::NT), 0,
-                     stream, la, lb, epi, K, ts);
+  ts.tile0 = 0;
+  ts.ntiles = ts.mt * ts.nt;
+  ts.ws = nullptr;
+  const long blocks = (long)ts.ntiles * ts.k_splits;
+  if (blocks <= 0) return hipSuccess;
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)blocks), dim3(Cfg::NT), 0, stream, la,
+                     lb, epi, K, ts);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Balanced launch for tiles that take a whole compute unit each (kGemmSlots
+// blocks resident at a time).  The tiles fill floor(T / G) whole rounds; the
+// R = T mod G left over would leave the last round partly idle, so they are
+// split s ways over K (s chosen so that R * s fills whole rounds best),
+// stored as partial tiles and summed by gemm_fixup_kernel, which runs the
+// epilogue once per tile.
+// ---------------------------------------------------------------------------
+constexpr int kGemmSlots = 256;
+constexpr int kTailSlots = 3 * kGemmSlots;      // partial tiles of the tail at most
+
+template <class Cfg>
+constexpr size_t tail_ws_bytes() { return (size_t)kTailSlots * partial_floats<Cfg>() * sizeof(float); }
+
+// K splits for R tail tiles of nk slices: the fewest rounds per unit of
+// work, if that beats one unsplit round.
+inline int tail_splits(long R, int nk) {
+  if (R <= 0) return 1;
+  int best = 1;
+  double best_t = 1.0;
+  for (int s = 2; s <= 8; ++s) {
+    if (R * s > kTailSlots || 2 * s > nk) break;
+    const double t = (double)((R * s + kGemmSlots - 1) / kGemmSlots) / s;
+    if (t < best_t - 1e-9) { best_t = t; best = s; }
+  }
+  return best;
+}
+
+template <typename T, class Cfg, class LA, class LB, class Epi>
+inline hipError_t launch_gemm_balanced(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K,
+                                       int group_m, float *ws, hipStream_t stream) {
+  constexpr int BK = 4 * Elem<T>::kPerChunk;
+  TileSched ts;
+  ts.mt = (M + Cfg::BM - 1) / Cfg::BM;
+  ts.nt = (N + Cfg::BN - 1) / Cfg::BN;
+  ts.group_m = group_m < 1 ? 1 : (group_m > ts.mt ? ts.mt : group_m);
+  const long ntiles = (long)ts.mt * ts.nt;
+  if (ntiles <= 0) return hipSuccess;
+  const long R = ntiles % kGemmSlots;
+  const int s = ws == nullptr ? 1 : tail_splits(R, (K + BK - 1) / BK);
+  // whole rounds (every tile if the tail is not split)
+  ts.k_splits = 1;
+  ts.tile0 = 0;
+  ts.ntiles = (int)(s > 1 ? ntiles - R : ntiles);
+  ts.ws = nullptr;
+  if (ts.ntiles > 0) {
+    hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)ts.ntiles), dim3(Cfg::NT), 0, stream,
+                       la, lb, epi, K, ts);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (s == 1) return hipSuccess;
+  ts.k_splits = s;
+  ts.tile0 = (int)(ntiles - R);
+  ts.ntiles = (int)R;
+  ts.ws = ws;
+  hipLaunchKernelGGL((gemm_kernel<T, Cfg, LA, LB, Epi>), dim3((unsigned)(R * s)), dim3(Cfg::NT), 0, stream, la,
+                     lb, epi, K, ts);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gemm_fixup_kernel<Cfg, Epi>), dim3((unsigned)R), dim3(Cfg::NT), 0, stream, epi, ts);
   return hipGetLastError();
 }
 

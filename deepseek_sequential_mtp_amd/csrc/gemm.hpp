@@ -306,7 +306,11 @@ __device__ __forceinline__ void tile_coords(int logical, int mt, int nt, int gro
   tn = in / gsz;
 }
 
-struct TileSched { int mt, nt, group_m, k_splits; };
+struct TileSched {
+  int mt, nt, group_m, k_splits;
+  int tile0, ntiles;   // the launch covers tiles [tile0, tile0 + ntiles)
+  float *ws;           // partial-tile slots (the split tail of the balanced schedule)
+};
 
 // Waits until at most VM of this wave's vector-memory operations and at most
 // LGKM of its LDS operations are outstanding, then barriers.  s_waitcnt
@@ -339,8 +343,9 @@ __device__ __forceinline__ void sched_interleave() {
 }
 
 // ---------------------------------------------------------------------------
-// The kernel body.  Each block computes one BM x BN tile (optionally one K
-// split of it) and hands the accumulators to the epilogue.
+// Main loop over slices [kt0, kt0 + nk) of one BM x BN tile at (m0, n0):
+// leaves the tile's partial sums in acc.  On return no load is in flight and
+// every wave has finished reading the stages (an epilogue may reuse them).
 //
 // Slice kt lives in stage kt % NS and is consumed in two sub-steps of 32
 // bytes of K each.  In the middle of slice kt (after the first
@@ -350,35 +355,20 @@ __device__ __forceinline__ void sched_interleave() {
 // read it issued before this slice's second sub-step has completed; the
 // block barrier then makes both true for all waves.  Stage (kt - 1) % NS is
 // thereby retired and receives the loads of slice kt + NS - 1.  Slices past
-// the block's K range are issued as all-out-of-range loads (no memory
-// traffic), so the number of loads in flight, and with it the wait count, is
-// the same for every slice.
+// the range are issued as all-out-of-range loads (no memory traffic), so the
+// number of loads in flight, and with it the wait count, is the same for
+// every slice.
 // ---------------------------------------------------------------------------
-template <typename T, class Cfg, class LA, class LB, class Epi>
-__device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi &epi, int K,
-                                          const TileSched &ts, char *const *st) {
+template <typename T, class Cfg, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop(const LA &la, const LB &lb, int m0, int n0, int kt0, int nk, int K,
+                                              char *const *st, f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
   constexpr int E = Elem<T>::kPerChunk;
   constexpr int BK = 4 * E;                    // K elements per 64-byte slice
   constexpr int MB = Cfg::MB, NB = Cfg::NB, NS = Cfg::NS;
   constexpr int LOADS = LA::kLoads + LB::kLoads;   // load instructions per wave and slice
-  const int ntiles = ts.mt * ts.nt * ts.k_splits;
-  const int logical = xcd_remap(blockIdx.x, ntiles);
-  const int split = logical % ts.k_splits;
-  int tm, tn;
-  tile_coords(logical / ts.k_splits, ts.mt, ts.nt, ts.group_m, tm, tn);
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-
-  const int nk_total = (K + BK - 1) / BK;
-  const int per = (nk_total + ts.k_splits - 1) / ts.k_splits;
-  const int kt0 = split * per;
-  const int kt1 = min(nk_total, kt0 + per);
-  const int nk = kt1 > kt0 ? kt1 - kt0 : 0;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
-
-  f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -433,48 +423,32 @@ __device__ __forceinline__ void gemm_body(const LA &la, const LB &lb, const Epi 
   for (int j = 0; j < NS - 1; ++j)
     if (it + j < nk) slice(it + j, st[j], st[j + 1], st[(j + NS - 1) % NS]);
   wait_vm_lds_barrier<0>();                    // no load in flight into the stages
-  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, st[0], st[1]);
 }
 
 // ---------------------------------------------------------------------------
-// Kernel body for an A operand in 128-byte rows (DmaKMajor128) and a B
-// operand in 64-byte slices.  A pair p (slices 2p, 2p+1 of the block's K
+// Main loop (as gemm_mainloop) for an A operand in 128-byte rows
+// (DmaKMajor128) and a B operand in 64-byte slices; kt0 must be even.  A pair p (slices 2p, 2p+1 of the block's K
 // range) lives in A region p % 3, slice kt of B in B stage kt % 4 (3 x BM x
 // 128 + 4 x BN x 64 bytes: 160 KB for 256 x 256).  The barrier in the middle
-// of slice kt (same conditions as in gemm_body) retires B stage (kt - 1) % 4,
+// of slice kt (same conditions as in gemm_mainloop) retires B stage (kt - 1) % 4,
 // which receives B slice kt + 3, and, for even kt, A region (kt / 2 - 1) % 3,
 // which receives pair kt / 2 + 2.  Loads are issued in the same order at
 // every barrier, so the wait for slice kt + 1 always leaves one B slice and
 // one A pair in flight.  The loop is unrolled by 12 slices (both rings come
 // back to their first stage).
 // ---------------------------------------------------------------------------
-template <typename T, class Cfg, class LA, class LB, class Epi>
-__device__ __forceinline__ void gemm_body_pairs(const LA &la, const LB &lb, const Epi &epi, int K,
-                                                const TileSched &ts, char *const *sa, char *const *sb) {
+template <typename T, class Cfg, class LA, class LB>
+__device__ __forceinline__ void gemm_mainloop_pairs(const LA &la, const LB &lb, int m0, int n0, int kt0, int nk,
+                                                    int K, char *const *sa, char *const *sb,
+                                                    f32x16 (&acc)[Cfg::MB][Cfg::NB]) {
   static_assert(sizeof(T) == 2, "pair rows are for bf16 operands");
   constexpr int E = Elem<T>::kPerChunk;
   constexpr int BK = 4 * E;                    // K elements per 64-byte slice
   constexpr int MB = Cfg::MB, NB = Cfg::NB;
   constexpr int LA2 = LA::kLoads, LB1 = LB::kLoads;
-  const int ntiles = ts.mt * ts.nt * ts.k_splits;
-  const int logical = xcd_remap(blockIdx.x, ntiles);
-  const int split = logical % ts.k_splits;
-  int tm, tn;
-  tile_coords(logical / ts.k_splits, ts.mt, ts.nt, ts.group_m, tm, tn);
-  const int m0 = tm * Cfg::BM, n0 = tn * Cfg::BN;
-
-  const int nk_total = (K + BK - 1) / BK;
-  int per = (nk_total + ts.k_splits - 1) / ts.k_splits;
-  per += per & 1;                              // K splits start on a pair
-  const int kt0 = split * per;
-  const int kt1 = min(nk_total, kt0 + per);
-  const int nk = kt1 > kt0 ? kt1 - kt0 : 0;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave / Cfg::WGN, wn = wave % Cfg::WGN;
-
-  f32x16 acc[MB][NB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -557,7 +531,6 @@ __device__ __forceinline__ void gemm_body_pairs(const LA &la, const LB &lb, cons
   if (it + 9 < nk) slice(it + 9, std::integral_constant<int, 9>{});
   if (it + 10 < nk) slice(it + 10, std::integral_constant<int, 10>{});
   wait_vm_lds_barrier<0>();                    // no load in flight into the stages
-  epi.template apply<Cfg>(acc, m0, n0, wm, wn, lane, split, sa[0], sa[1]);
 }
 
 // Result-layout helpers: row / column of accumulator register r of block

@@ -85,15 +85,26 @@ using PA = std::conditional_t<sizeof(T) == 2 && Cfg::BM == 256, DmaKMajor128<T, 
 
 inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N, 256) >= 256; }
 
+// One GEMM without K splits: the 256x256 tile (one block per compute unit)
+// on the balanced schedule (skws: tail_ws_bytes<Big>() of scratch), the
+// 128x128 tile one block per tile.
+template <typename T, class Cfg, class LA, class LB, class Epi>
+hipError_t run_gemm(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K, int group_m, float *skws,
+                    hipStream_t s) {
+  if constexpr (std::is_same_v<Cfg, Big>) return launch_gemm_balanced<T, Cfg>(la, lb, epi, M, N, K, group_m, skws, s);
+  else return launch_gemm<T, Cfg>(la, lb, epi, M, N, K, group_m, 1, s);
+}
+
 template <typename T, typename OutT, typename ResT>
 int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc, const ResT *R, long ldr,
-                  int M, int N, int K, float alpha, const float *alpha_dev, int accumulate, hipStream_t s) {
+                  int M, int N, int K, float alpha, const float *alpha_dev, int accumulate, float *skws,
+                  hipStream_t s) {
   EpiStore<OutT, ResT> epi{C, ldc, M, N, alpha, alpha_dev, R, ldr, accumulate, 0};
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, N)) {
       PA<T, Big> la{A, lda, M, K};
       KB<T, Big> lb{Bm, ldb, N, K};
-      MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, N, K, 8, 1, s)));
+      MTP_TRY((run_gemm<T, Big>(la, lb, epi, M, N, K, 8, skws, s)));
       return MTP_OK;
     }
   }
@@ -107,42 +118,42 @@ int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc
 
 template <typename T, int HALF, class Cfg>
 int gemm_qkv_rope_cfg(const T *xa, const T *W, T *qkv, const int *pos, const float2 *rope, int M, int d,
-                      int A, hipStream_t s) {
+                      int A, float *skws, hipStream_t s) {
   const int N = 3 * A;
   EpiRope<T, HALF> epi{qkv, (long)N, M, N, A, pos, rope};
   PA<T, Cfg> la{xa, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, N, d};
-  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, N, d, 8, 1, s)));
+  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, N, d, 8, skws, s)));
   return MTP_OK;
 }
 
 template <typename T>
 int gemm_qkv_rope(const T *xa, const T *W, T *qkv, const int *pos, const float2 *rope, int M, int d, int A,
-                  int hd, hipStream_t s) {
+                  int hd, float *skws, hipStream_t s) {
   // The wave's column range (WN) must cover whole heads for HALF >= 32.
   if constexpr (sizeof(T) == 2) {
     switch (hd) {
-      case 32: return gemm_qkv_rope_cfg<T, 16, Big>(xa, W, qkv, pos, rope, M, d, A, s);
-      case 64: return gemm_qkv_rope_cfg<T, 32, Big>(xa, W, qkv, pos, rope, M, d, A, s);
-      case 128: return gemm_qkv_rope_cfg<T, 64, Big>(xa, W, qkv, pos, rope, M, d, A, s);
+      case 32: return gemm_qkv_rope_cfg<T, 16, Big>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+      case 64: return gemm_qkv_rope_cfg<T, 32, Big>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+      case 128: return gemm_qkv_rope_cfg<T, 64, Big>(xa, W, qkv, pos, rope, M, d, A, skws, s);
       default: return MTP_ERR_UNSUPPORTED;
     }
   } else switch (hd) {
-    case 16: return gemm_qkv_rope_cfg<T, 8, Small>(xa, W, qkv, pos, rope, M, d, A, s);
-    case 32: return gemm_qkv_rope_cfg<T, 16, Small>(xa, W, qkv, pos, rope, M, d, A, s);
-    case 64: return gemm_qkv_rope_cfg<T, 32, Small>(xa, W, qkv, pos, rope, M, d, A, s);
+    case 16: return gemm_qkv_rope_cfg<T, 8, Small>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+    case 32: return gemm_qkv_rope_cfg<T, 16, Small>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+    case 64: return gemm_qkv_rope_cfg<T, 32, Small>(xa, W, qkv, pos, rope, M, d, A, skws, s);
     default: return MTP_ERR_UNSUPPORTED;
   }
 }
 
 template <typename T>
-int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, hipStream_t s) {
+int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, float *skws, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
     if (use_big(M, 2L * f)) {
       EpiSwiGLU<T> epi{out, (long)f, M, f};
       PA<T, Big> la{y, (long)d, M, d};
       DmaKMajorSwiGLU<T, Big> lb{Wg, Wu, (long)d, f, d};
-      MTP_TRY((launch_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, 1, s)));
+      MTP_TRY((run_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, skws, s)));
       return MTP_OK;
     }
   }
@@ -158,35 +169,36 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
 
 template <typename T, class Cfg>
 int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, float *z, int M,
-                    int V, int d, hipStream_t s) {
+                    int V, int d, float *skws, hipStream_t s) {
   const int nt = ceil_div(V, Cfg::BN);
   EpiCEFwd epi{lab, part, target, z, M, V, nt};
   PA<T, Cfg> la{xhat, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, V, d};
   // all row tiles of one vocabulary tile run next to each other: W is read once
-  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, 1, s)));
+  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, V, d, 1 << 30, skws, s)));
   return MTP_OK;
 }
 
 // dx[split] = scale * dz[:, split range] W_out[split range, :]  (B operand MN-major)
 template <typename T, class Cfg>
 int gemm_dx_cfg(const T *dz, const T *W, float *dxs, long slab, int M, int V, int d, const float *scale,
-                int splits, hipStream_t s) {
+                int splits, float *skws, hipStream_t s) {
   EpiStore<float, float> epi{dxs, (long)d, M, d, 1.f, scale, nullptr, 0, 0, slab};
   KA<T, Cfg> la{dz, (long)V, M, V};
   MB_<T, Cfg> lb{W, (long)d, d, V};
-  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, d, V, 8, splits, s)));
+  if (splits == 1) MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, d, V, 8, skws, s)));
+  else MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, M, d, V, 8, splits, s)));
   return MTP_OK;
 }
 
 // dW (+)= scale * dz^T xhat  (both operands MN-major)
 template <typename T, class Cfg>
 int gemm_dw_cfg(const T *dz, const T *xhat, float *dW, int M, int V, int d, const float *scale, int accumulate,
-                hipStream_t s) {
+                float *skws, hipStream_t s) {
   EpiStore<float, float> epi{dW, (long)d, V, d, 1.f, scale, nullptr, 0, accumulate, 0};
   MA<T, Cfg> la{dz, (long)V, V, M};
   MB_<T, Cfg> lb{xhat, (long)d, d, M};
-  MTP_TRY((launch_gemm<T, Cfg>(la, lb, epi, V, d, M, 8, 1, s)));
+  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, V, d, M, 8, skws, s)));
   return MTP_OK;
 }
 
@@ -252,7 +264,7 @@ int check_chain_ptrs(const mtp_chain_args *a) {
   return MTP_OK;
 }
 
-constexpr int kChainParts = 13;  // workspace regions of the chain call
+constexpr int kChainParts = 14;  // workspace regions of the chain call
 
 template <typename T>
 size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
@@ -271,6 +283,7 @@ size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
   parts[10] = c.take<float>(N * d);                            // a (residual stream, f32)
   parts[11] = c.take<T>(N * d);                                // y
   parts[12] = c.take<T>(N * (long)f);                          // silu(gate) * up
+  parts[13] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
   return c.off;
 }
 
@@ -288,6 +301,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
   float *u = (float *)p[6];
   float *abuf = (float *)p[10];
   T *ybuf = (T *)p[11], *gsw = (T *)p[12];
+  float *skws = sizeof(T) == 2 ? (float *)p[13] : nullptr;
 
   {
   MTP_STAGE(MTP_STAGE_ROWS);
@@ -310,7 +324,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     {
       MTP_STAGE(MTP_STAGE_EH_PROJ);
       st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d, 1.f,
-                                          nullptr, 0, s);
+                                          nullptr, 0, skws, s);
     }
     if (st) return st;
     {
@@ -319,7 +333,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_QKV);
-      st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, s);
+      st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, skws, s);
     }
     if (st) return st;
     {
@@ -328,7 +342,8 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_O_PROJ);
-      st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0, s);
+      st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0, skws,
+                                          s);
     }
     if (st) return st;
     {
@@ -337,13 +352,13 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_GATE_UP);
-      st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, s);
+      st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, skws, s);
     }
     if (st) return st;
     {
       MTP_STAGE(MTP_STAGE_DOWN);
       st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
-                                      s);
+                                      skws, s);
     }
     if (st) return st;
     h_prev = h_out;
@@ -402,11 +417,14 @@ CeDims ce_dims(const mtp_ce_args *a) {
   c.nt = ceil_div(c.V, c.big ? 256 : 128);
   // the dx_hat GEMM (group rows x d, K = V) may also fill the chip with K splits
   c.big_dx = sizeof(T) == 2 && (long)ceil_div(c.group, 256) * ceil_div(c.d, 256) * 8 >= 256;
-  c.splits = dx_splits((int)c.group, c.d, c.V, c.big_dx);
+  // with a round of 256x256 tiles or more the dx GEMM needs no K splits of
+  // its own: the balanced schedule splits only the last partial round
+  const bool dx_balanced = c.big_dx && (long)ceil_div(c.group, 256) * ceil_div(c.d, 256) >= kGemmSlots;
+  c.splits = dx_balanced ? 1 : dx_splits((int)c.group, c.d, c.V, c.big_dx);
   return c;
 }
 
-constexpr int kCeParts = 14;     // workspace regions of the CE call
+constexpr int kCeParts = 15;     // workspace regions of the CE call
 
 template <typename T>
 size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
@@ -425,6 +443,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
   p[13] = c.take<float>(m.slab * m.V);           // fp32 logits of the slab
+  p[14] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
   return c.off;
 }
 
@@ -447,6 +466,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   float *dxs = (float *)p[11];
   float *dg_part = (float *)p[12];
   float *zbuf = (float *)p[13];
+  float *skws = sizeof(T) == 2 ? (float *)p[14] : nullptr;
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
   const long sstride = m.N * m.d;                // stride of the dx_hat split partials
@@ -476,7 +496,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
           MTP_STAGE(MTP_STAGE_CE_FWD);
           st = pick<T>(m.big, [&](auto cfg) {
             return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat + r0 * d, (const T *)a->W_out, ls, part, target + r0,
-                                                      zbuf, nr, V, d, s);
+                                                      zbuf, nr, V, d, skws, s);
           });
         }
         if (st) return st;
@@ -494,7 +514,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         MTP_STAGE(MTP_STAGE_CE_DX);
         st = pick<T>(m.big_dx, [&](auto cfg) {
           return gemm_dx_cfg<T, decltype(cfg)>(dz, (const T *)a->W_out, dxs + g0 * d, sstride, gn, V, d, scale + k,
-                                               m.splits, s);
+                                               m.splits, skws, s);
         });
       }
       if (st) return st;
@@ -502,7 +522,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         MTP_STAGE(MTP_STAGE_CE_DW);
         st = pick<T>(big_dw, [&](auto cfg) {
           return gemm_dw_cfg<T, decltype(cfg)>(dz, xhat + g0 * d, a->dW_out, gn, V, d, scale + k,
-                                               dw_acc0 || g0 > 0, s);
+                                               dw_acc0 || g0 > 0, skws, s);
         });
       }
       if (st) return st;

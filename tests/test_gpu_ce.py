@@ -107,13 +107,15 @@ def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
     _assert(cfg, res, ref, labels, accumulate=True)
 
 
-@pytest.mark.parametrize("slab_rows,d", [(0, 1024), (256, 1024), (0, 1056)])
-def test_ce_bf16_big_tiles(slab_rows, d):
-    # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each); slab_rows=256
-    # runs the 1024 rows as four slabs in two dz groups; d=1056 gives the
-    # forward GEMM an odd number of 32-element K slices (a half-filled last
-    # pair of 128-byte A rows)
-    cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=d, V=16384, D=1, seg_lo=100,
+@pytest.mark.parametrize("slab_rows,d,V", [(0, 1024, 16384), (256, 1024, 16384), (0, 1056, 16384),
+                                            (0, 1024, 20480)])
+def test_ce_bf16_big_tiles(slab_rows, d, V):
+    # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each, stream-K
+    # schedule); slab_rows=256 runs the 1024 rows as four slabs in two dz
+    # groups; d=1056 gives the forward GEMM an odd number of 32-element K
+    # slices (a half-filled last pair of 128-byte A rows); V=20480 makes 320
+    # tiles, so 256 stream-K blocks share tiles and the fixup pass runs
+    cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=d, V=V, D=1, seg_lo=100,
                        seg_hi=700, sigma_w=0.02)
     res, ref, labels = _case(cfg, slab_rows=slab_rows)
     _assert(cfg, res, ref, labels)
