@@ -172,9 +172,15 @@ struct EpiSwiGLU {
 // label accesses go through buffer resources ending at row M (branch-free);
 // the target store is skipped by the whole wave when no lane holds a label
 // column.  Requires BM * V * 4 < 2^31 (checked by the caller).
+//
+// ZT = float keeps the logits as they are.  ZT = _Float16 keeps z - m_t, the
+// logit relative to its tile's row max (<= 0; part[] holds m_t), in half
+// precision: half the bytes, with a rounding error of at most 2^-11 |z - m_t|
+// (exact near the max, where the softmax weight is).
 // ---------------------------------------------------------------------------
+template <typename ZT>
 struct EpiCEFwd {
-  const int *labels; float2 *part; float *target; float *zout; int M, V, nt;
+  const int *labels; float2 *part; float *target; ZT *zout; int M, V, nt;
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
                                         int wn, int lane, int, char *lds, char *) const {
@@ -186,7 +192,7 @@ struct EpiCEFwd {
     float *reds = redm + 2 * Cfg::BM;                        // [2][BM] row sum-exp per column wave
     const bool writer = (lane & 31) == 0;
     const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
-    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + (long)m0 * V, rows * V * 4L);
+    const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + (long)m0 * V, rows * V * (long)sizeof(ZT));
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(labels + m0, rows * 4L);
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(target + m0, rows * 4L);
     int col[Cfg::NB];
@@ -215,7 +221,8 @@ struct EpiCEFwd {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int rr = acc_row<Cfg>(wm, i, r, lane);
-        const float nm = -fmaxf(redm[rr], redm[Cfg::BM + rr]) * kLog2e;
+        const float mt = fmaxf(redm[rr], redm[Cfg::BM + rr]);
+        const float nm = -mt * kLog2e;
         const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(rr * 4), 0, 0);
         const int lab = rr < rows ? lab0 : -1;
         float s = 0.f, tv = 0.f;
@@ -224,7 +231,13 @@ struct EpiCEFwd {
         for (int j = 0; j < Cfg::NB; ++j) {
           const float z = acc[i][j][r];
           s += cok[j] ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
-          buf_store_elem(rz, cok[j] ? (unsigned)(((long)rr * V + col[j]) * 4) : kOOB, z, float{});
+          const unsigned zoff = cok[j] ? (unsigned)(((long)rr * V + col[j]) * sizeof(ZT)) : kOOB;
+          if constexpr (sizeof(ZT) == 4) {
+            buf_store_elem(rz, zoff, z, float{});
+          } else {
+            const _Float16 h = (_Float16)(z - mt);
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), rz, zoff, 0, 0);
+          }
           const bool hit = col[j] == lab;
           tv = hit ? z : tv;
           has = has || hit;

@@ -40,9 +40,9 @@ hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, int 
 hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s);
 
 // CE reductions
-template <typename T>
-hipError_t launch_ce_dz(const float *z, const float *lse, const int32_t *labels, T *dz, int N, int V,
-                        hipStream_t s);
+template <typename T, typename ZT>
+hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
+                        const int32_t *labels, T *dz, int N, int V, hipStream_t s);
 hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
                              float *lse, float *lse_out, float *row_loss, int N, hipStream_t s);
 hipError_t launch_ce_reduce(const float *row_loss, const int32_t *labels, int N, int k, int D,

@@ -167,11 +167,16 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
   return MTP_OK;
 }
 
+// Storage of the kept logits: bf16 runs keep fp16 offsets from the tile max,
+// f32 runs keep fp32 logits.
+template <typename T>
+using LogitT = std::conditional_t<sizeof(T) == 2, _Float16, float>;
+
 template <typename T, class Cfg>
-int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, float *z, int M,
+int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, float *target, LogitT<T> *z, int M,
                     int V, int d, float *skws, hipStream_t s) {
   const int nt = ceil_div(V, Cfg::BN);
-  EpiCEFwd epi{lab, part, target, z, M, V, nt};
+  EpiCEFwd<LogitT<T>> epi{lab, part, target, z, M, V, nt};
   PA<T, Cfg> la{xhat, (long)d, M, d};
   KB<T, Cfg> lb{W, (long)d, V, d};
   // all row tiles of one vocabulary tile run next to each other: W is read once
@@ -442,7 +447,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[10] = c.take<T>(m.group * m.V);              // dz = softmax - onehot of the row group
   p[11] = c.take<float>((size_t)m.splits * m.N * m.d);   // dx_hat split partials
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
-  p[13] = c.take<float>(m.slab * m.V);           // fp32 logits of the slab
+  p[13] = c.take<LogitT<T>>(m.slab * m.V);       // logits of the slab (LogitT)
   p[14] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
   return c.off;
 }
@@ -465,7 +470,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   T *dz = (T *)p[10];
   float *dxs = (float *)p[11];
   float *dg_part = (float *)p[12];
-  float *zbuf = (float *)p[13];
+  LogitT<T> *zbuf = (LogitT<T> *)p[13];
   float *skws = sizeof(T) == 2 ? (float *)p[14] : nullptr;
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
@@ -507,7 +512,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         }
         {
           MTP_STAGE(MTP_STAGE_CE_GRAD);
-          MTP_TRY(launch_ce_dz<T>(zbuf, lse + r0, ls, dz + (r0 - g0) * V, nr, V, s));
+          MTP_TRY((launch_ce_dz<T, LogitT<T>>(zbuf, part, m.nt, m.big ? Big::BN : Small::BN, lse + r0, ls,
+                                              dz + (r0 - g0) * V, nr, V, s)));
         }
       }
       {
