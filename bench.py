@@ -152,6 +152,78 @@ def algorithmic_flops(cfg, state_mask, counts, run_start_fn):
     return per
 
 
+# Algorithmic HBM bytes per depth of the memory-bound stages (N rows): what
+# each kernel must read and write once (bf16 activations, fp32 residual
+# stream and head gradients, fp16 logits).
+def stage_bytes(cfg):
+    N, d, V = cfg.N, cfg.d, cfg.V
+    return {"DUAL_NORM": 8.0 * N * d,      # h, gathered E rows -> [h_norm, e_norm]
+            "NORM_A": 6.0 * N * d,         # u (f32) -> x_a
+            "NORM_F": 6.0 * N * d,         # a (f32) -> y
+            "OUT_NORM": 4.0 * N * d,       # h -> x_hat
+            "CE_GRAD": 4.0 * N * V,        # fp16 logits -> bf16 softmax - onehot
+            "CE_NORM_BWD": 10.0 * N * d}   # dx_hat (f32), h -> dh (f32)
+
+
+def stage_table(cfg, stage_ms, per):
+    """Per-stage time of one step and its roofline: algorithmic TFLOP/s
+    against the bf16 MFMA peak, or algorithmic GB/s against HBM."""
+    flops_keys = ("EH_PROJ", "QKV", "ATTN", "O_PROJ", "GATE_UP", "DOWN", "CE_FWD", "CE_DX", "CE_DW")
+    nbytes = stage_bytes(cfg)
+    out = {}
+    for name, ms in stage_ms.items():
+        row = {"ms": round(ms, 4)}
+        if name in flops_keys:
+            a = sum(p[name] for p in per) / (ms * 1e-3) / 1e12
+            row.update(bound="mfma", achieved=round(a, 1), unit="TFLOP/s", frac=round(a / PEAK_BF16_TFLOPS, 4))
+        elif name in nbytes:
+            a = nbytes[name] * cfg.D / (ms * 1e-3) / 1e9
+            row.update(bound="hbm", achieved=round(a, 1), unit="GB/s", frac=round(a / PEAK_HBM_GBS, 4))
+        else:
+            row.update(bound="latency")
+        out[name] = row
+    return out
+
+
+def bench_verify(torch, _lib, synth, reps=20):
+    """mtp_verify on the retained-module verify workload (256 requests,
+    V = 129280, gamma = 1..4): kernel time from HIP events around its
+    launches, and the bandwidth of one read of every logit row."""
+    dev = torch.device("cuda:0")
+    res = []
+    for gamma in (1, 2, 3, 4):
+        vc = synth.verify_config(gamma)
+        R, V = vc.R, vc.V
+        g = torch.Generator(device=dev).manual_seed(1234 + gamma)
+        zt32 = torch.randn((R, gamma + 1, V), generator=g, device=dev) * vc.target_sigma
+        zd = (zt32[:, :gamma] + vc.draft_noise * torch.randn((R, gamma, V), generator=g, device=dev))
+        zd = zd.to(torch.bfloat16)
+        zt = zt32.to(torch.bfloat16)
+        del zt32
+        q = torch.softmax(zd.float(), dim=-1).view(-1, V)
+        y = torch.multinomial(q, 1, generator=g).view(R, gamma).to(torch.int32)
+        del q
+        ua = torch.rand((R, gamma), generator=g, device=dev)
+        us = torch.rand((R, gamma + 1), generator=g, device=dev)
+        cache = {}
+        out = _lib.verify(zt, zd, y, ua, us, cache=cache)
+        torch.cuda.synchronize()
+        with _lib.StageTimer("VERIFY", 4 * reps) as tm:
+            for _ in range(reps):
+                _lib.verify(zt, zd, y, ua, us, out=out, cache=cache)
+            torch.cuda.synchronize()
+        ts = tm.times_ms()
+        ms = float(np.sum(ts)) / reps
+        nbytes = R * (2 * gamma + 1) * V * 2.0
+        gbs = nbytes / (ms * 1e-3) / 1e9
+        acc = float(out["accepted_len"].float().mean())
+        res.append({"gamma": gamma, "R": R, "V": V, "ms": round(ms, 4), "achieved": round(gbs, 1),
+                    "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "bytes": nbytes,
+                    "mean_accepted": round(acc, 3)})
+        del zt, zd, y, ua, us, out, cache
+    return res
+
+
 def main():
     args = parse()
     if args.ingest_pmc:
@@ -273,6 +345,13 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
+    stages = stage_table(cfg, stage_ms, per)
+    verify = bench_verify(torch, _lib, synth)
+    if args.stages:
+        for v in verify:
+            print(f"  verify gamma={v['gamma']}: {v['ms']:.3f} ms, {v['achieved']:.0f} GB/s "
+                  f"({100 * v['frac']:.1f}% of HBM), mean accepted {v['mean_accepted']}", file=sys.stderr)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_rows)
@@ -300,6 +379,8 @@ def main():
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": traffic, "launch_ms": round(dom_avg_ms, 4),
                      "launches_per_step": len(dom_times) // args.steps, "flops_basis": dom_note},
+        "stages": stages,
+        "verify": verify,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

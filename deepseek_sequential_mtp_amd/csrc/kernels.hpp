@@ -53,6 +53,7 @@ hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int
                               int32_t *counts, float *loss, float *loss_mtp, hipStream_t s);
 
 // verify
+size_t verify_workspace_bytes(int R, int G, int V, int bf16);
 hipError_t launch_verify(const void *zt, const void *zd, int bf16, const int32_t *y, const float *ua,
                          const float *us, int R, int G, int V, float tau, int32_t *A, int32_t *tok,
                          int32_t *status, float *margin, double *ws, hipStream_t s);

@@ -558,7 +558,7 @@ int check_verify(const mtp_verify_args *a) {
 }
 
 size_t verify_bytes(const mtp_verify_args *a) {
-  return (size_t)a->R * (2 * a->gamma + 1) * 2 * sizeof(double);
+  return verify_workspace_bytes(a->R, a->gamma, a->V, a->logits_dtype == MTP_BF16 ? 1 : 0);
 }
 
 }  // namespace

@@ -101,4 +101,8 @@ def test_verify_host_errors(lib):
     assert run(args(temperature=0.0)) == -6
     assert run(args(logits_dtype=3)) == -4
     assert run(args()) == -1
-    assert lib.mtp_verify_workspace_size(C.byref(args())) == 4 * 5 * 2 * 8
+    # row log-sum-exps (2 doubles per row), 16-byte test outcomes, one
+    # double per chunk of emission weights (chunks of 8 bf16 logits when V
+    # is a multiple of 8, single logits otherwise) and per tile of 256 chunks
+    assert lib.mtp_verify_workspace_size(C.byref(args())) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (100 + 1) * 8
+    assert lib.mtp_verify_workspace_size(C.byref(args(V=128))) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (16 + 1) * 8
