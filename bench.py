@@ -49,13 +49,15 @@ def parse():
     return ap.parse_args()
 
 
-# Kernel-name patterns of each stage (demangled names as rocprofv3 prints them).
+# Kernel-name patterns of each stage; rocprofv3 prints some names demangled
+# and some mangled (templates with a _Float16 argument), so each pattern
+# matches both spellings.
 STAGE_KERNELS = {
-    "CE_DW": r"gemm_kernel<.*DmaMNMajor<[^>]*>, mtp::DmaMNMajor",
-    "CE_DX": r"gemm_kernel<.*DmaKMajor<[^>]*>, mtp::DmaMNMajor",
-    "CE_FWD": r"gemm_kernel<.*EpiCEFwd",
-    "QKV": r"gemm_kernel<.*EpiRope",
-    "GATE_UP": r"gemm_kernel<.*EpiSwiGLU",
+    "CE_DW": r"gemm_kernel.*DmaMNMajor(<[^>]*>, mtp::|IS1_Li256ELi512EEENS_10)DmaMNMajor",
+    "CE_DX": r"gemm_kernel.*DmaKMajor(<[^>]*>, mtp::|IS1_Li256ELi512EEENS_10)DmaMNMajor",
+    "CE_FWD": r"gemm_kernel.*EpiCEFwd",
+    "QKV": r"gemm_kernel.*EpiRope",
+    "GATE_UP": r"gemm_kernel.*EpiSwiGLU",
     "ATTN": r"attention_kernel",
 }
 COPY_BYTES = 256 << 20          # one direction of the calibration copy
