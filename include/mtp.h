@@ -152,8 +152,10 @@ typedef struct {
  * R * V * 4 <= logit_slab_bytes (R rounded down to a multiple of 256 when it
  * is at least 256, and at least 1).  Per slab the forward GEMM reduces each
  * vocabulary tile to an online (max, sum-exp) partial per row and keeps the
- * slab's fp32 logits; the partials give the row's log-sum-exp and softmax -
- * onehot is formed from the kept logits, stored in dtype.  That gradient is
+ * slab's logits (f32: as fp32; bf16: as fp16 offsets from the row's maximum
+ * over its 256-wide vocabulary tile, which are <= 0); the partials give the
+ * row's log-sum-exp and softmax - onehot is formed from the kept logits,
+ * stored in dtype.  That gradient is
  * kept for a group of G rows, G * V * sizeof(dtype) <= logit_slab_bytes (a
  * whole number of slabs, at least one; two for bf16), and the dx_hat and
  * dW_out GEMMs run once per group.  Workspace grows with the slab, not with
@@ -225,8 +227,9 @@ typedef struct {
  *          decision from its threshold (|u - p/q| over the tests made, and the
  *          sample's distance to the nearer CDF step relative to the mass).
  * Checks in order: uniforms, token ids, then per used row: non-finite row,
- * q_j(y_j) = 0, zero residual mass.  Rows after the first rejection are not
- * read.
+ * q_j(y_j) = 0, zero residual mass.  Every logit row is read once (its
+ * log-sum-exp); rows after the first rejection do not affect any output
+ * (a non-finite value there is not reported).
  * Requirements: R >= 1, gamma >= 1, V >= 1, temperature > 0.
  * ---------------------------------------------------------------------- */
 typedef struct {
