@@ -90,7 +90,7 @@ def ingest_pmc(stage, fetch_csv, write_csv, workload):
     out = {"stage": stage, "workload": workload, "kernel_regex": STAGE_KERNELS[stage],
            "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
            "bytes_per_launch": fetch + write, "copy_factor_fetch": ff, "copy_factor_write": fw,
-           "launches_counted": [nf, nw], "source_hash": _kernel_hash()}
+           "launches_counted": [nf, nw], "source_hash": _kernel_hash(stage)}
     path = os.path.join(ROOT, "profiles", f"traffic_{stage.lower()}_{workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
@@ -328,7 +328,7 @@ def main():
         try:
             with open(tfile) as fh:
                 tr = json.load(fh)
-            if tr.get("source_hash") == _kernel_hash():
+            if tr.get("source_hash") == _kernel_hash(dominant):
                 traffic = tr.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
@@ -388,11 +388,15 @@ def main():
     print(json.dumps(line), flush=True)
 
 
-def _kernel_hash() -> str:
+def _kernel_hash(stage: str) -> str:
+    """Hash of the sources the stage's kernel is compiled from (the GEMM
+    templates, or the attention kernel), so that a stored traffic figure is
+    dropped once that kernel changes."""
     import hashlib
+    files = ["common.hpp", "attention.hip"] if stage == "ATTN" else ["common.hpp", "gemm.hpp", "epilogues.hpp"]
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "deepseek_sequential_mtp_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in files:
         with open(os.path.join(csrc, name), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]

@@ -256,6 +256,12 @@ int check_chain(const mtp_chain_args *a) {
   return MTP_OK;
 }
 
+// Kernels access tensors in 16-byte vectors: every device pointer (NULL
+// aside) must be 16-byte aligned.
+inline bool al16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+template <typename... P>
+bool all_al16(const P *...p) { return (al16(p) && ...); }
+
 int check_chain_ptrs(const mtp_chain_args *a) {
   if (!a->tokens || !a->segment_ids || !a->h0 || !a->embed || !a->w || !a->h_out || !a->state_mask ||
       !a->loss_mask || !a->labels || !a->counts || !a->device_error)
@@ -265,6 +271,14 @@ int check_chain_ptrs(const mtp_chain_args *a) {
     if (!w.g_h || !w.g_e || !w.g_attn || !w.g_ffn || !w.M || !w.Wqkv || !w.Wo || !w.Wgate || !w.Wup ||
         !w.Wdown || !a->h_out[k])
       return MTP_ERR_NULL;
+  }
+  if (!all_al16(a->tokens, a->segment_ids, a->h0, a->embed, a->state_mask, a->loss_mask, a->labels, a->counts,
+                a->device_error, a->workspace))
+    return MTP_ERR_ARG;
+  for (int k = 0; k < a->D; ++k) {
+    const mtp_depth_weights &w = a->w[k];
+    if (!all_al16(w.g_h, w.g_e, w.g_attn, w.g_ffn, w.M, w.Wqkv, w.Wo, w.Wgate, w.Wup, w.Wdown, a->h_out[k]))
+      return MTP_ERR_ARG;
   }
   return MTP_OK;
 }
@@ -392,6 +406,11 @@ int check_ce_ptrs(const mtp_ce_args *a) {
     return MTP_ERR_NULL;
   for (int k = 0; k < a->D; ++k)
     if (!a->h[k] || !a->dh[k]) return MTP_ERR_NULL;
+  if (!all_al16(a->labels, a->W_out, a->g_out, a->loss_sum, a->counts, a->loss, a->loss_mtp, a->lse, a->dW_out,
+                a->dg_out, a->device_error, a->workspace))
+    return MTP_ERR_ARG;
+  for (int k = 0; k < a->D; ++k)
+    if (!all_al16(a->h[k], a->dh[k])) return MTP_ERR_ARG;
   return MTP_OK;
 }
 
@@ -642,6 +661,9 @@ int mtp_verify(const mtp_verify_args *a, void *stream) {
   if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->u_accept || !a->u_sample ||
       !a->accepted_len || !a->next_token || !a->status)
     return MTP_ERR_NULL;
+  if (!all_al16(a->target_logits, a->draft_logits, a->draft_tokens, a->u_accept, a->u_sample, a->accepted_len,
+                a->next_token, a->status, a->margin, a->workspace))
+    return MTP_ERR_ARG;
   if (!a->workspace || a->workspace_bytes < verify_bytes(a)) return MTP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   MTP_STAGE(MTP_STAGE_VERIFY);

@@ -134,6 +134,77 @@ __global__ __launch_bounds__(kNormThreads) void out_norm_bwd_kernel(
   }
 }
 
+// Four consecutive elements of a row as floats (d is a multiple of 4).
+__device__ __forceinline__ float4 load4(const float *p, int c) { return reinterpret_cast<const float4 *>(p)[c]; }
+__device__ __forceinline__ float4 load4(const bf16_t *p, int c) {
+  const uint2 w = reinterpret_cast<const uint2 *>(p)[c];
+  return make_float4(bf16_lo_f32(w.x), bf16_hi_f32(w.x), bf16_lo_f32(w.y), bf16_hi_f32(w.y));
+}
+
+// Output-norm backward over a block of rows, with its dg partial: for each
+// row n, x = r_n h_n, dh_n = r_n (g * v - x * mean(g * v * x)) with v the
+// sum of the dx_hat split slabs; part[block][j] = sum over the block's rows
+// of v[j] x[j].  Thread t owns the 4-column chunks t, t + 256, ... (CPT of
+// them), so the row is read once into registers and the dg partial stays in
+// registers across the rows.
+template <typename T, int CPT>
+__global__ __launch_bounds__(kNormThreads) void out_norm_bwd_rows_kernel(
+    const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h, const float *__restrict__ r,
+    const float *__restrict__ g, float *__restrict__ dh, float *__restrict__ part, int N, int d,
+    int rows_per_block) {
+  __shared__ float sh[kNormThreads / 64];
+  const int t = threadIdx.x;
+  const int nch = d >> 2;
+  const int n0 = blockIdx.x * rows_per_block;
+  const int n1 = min(N, n0 + rows_per_block);
+  float4 gg[CPT], dg[CPT];
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = t + i * kNormThreads;
+    gg[i] = c < nch ? load4(g, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+    dg[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  for (int n = n0; n < n1; ++n) {
+    const float rn = r[n];
+    float4 v[CPT], x[CPT];
+    float acc = 0.f;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = t + i * kNormThreads;
+      if (c < nch) {
+        float4 a = load4(dx + (long)n * d, c);
+        for (int sp = 1; sp < splits; ++sp) {
+          const float4 b = load4(dx + sp * slab + (long)n * d, c);
+          a.x += b.x; a.y += b.y; a.z += b.z; a.w += b.w;
+        }
+        const float4 hv = load4(h + (long)n * d, c);
+        v[i] = a;
+        x[i] = make_float4(rn * hv.x, rn * hv.y, rn * hv.z, rn * hv.w);
+        acc += gg[i].x * a.x * x[i].x + gg[i].y * a.y * x[i].y + gg[i].z * a.z * x[i].z + gg[i].w * a.w * x[i].w;
+      }
+    }
+    const float mean = block_sum(acc, sh) / d;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = t + i * kNormThreads;
+      if (c < nch) {
+        reinterpret_cast<float4 *>(dh + (long)n * d)[c] =
+            make_float4(rn * (gg[i].x * v[i].x - x[i].x * mean), rn * (gg[i].y * v[i].y - x[i].y * mean),
+                        rn * (gg[i].z * v[i].z - x[i].z * mean), rn * (gg[i].w * v[i].w - x[i].w * mean));
+        dg[i].x += v[i].x * x[i].x;
+        dg[i].y += v[i].y * x[i].y;
+        dg[i].z += v[i].z * x[i].z;
+        dg[i].w += v[i].w * x[i].w;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < CPT; ++i) {
+    const int c = t + i * kNormThreads;
+    if (c < nch) reinterpret_cast<float4 *>(part + (long)blockIdx.x * d)[c] = dg[i];
+  }
+}
+
 // dg partials: part[rb][j] = sum over rows in row block rb of dx[n][j] * x_n[n][j].
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void dg_partial_kernel(
@@ -159,14 +230,28 @@ __global__ __launch_bounds__(kNormThreads) void dg_partial_kernel(
                                      sh[3][threadIdx.x];
 }
 
-// dg[j] (+)= sum_rb part[rb][j], in row-block order.
-__global__ void dg_reduce_kernel(const float *__restrict__ part, int nrb, int d, float *__restrict__ dg,
-                                 int accumulate) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
-  if (j >= d) return;
+// dg[j] (+)= sum_rb part[rb][j].  A block covers 64 columns with 16 row
+// groups; group q sums the row blocks q, q + 16, ... in ascending order and
+// the groups are added in order, so the result does not depend on timing.
+constexpr int kDgGroups = 16;
+__global__ __launch_bounds__(64 * kDgGroups) void dg_reduce_kernel(const float *__restrict__ part, int nrb, int d,
+                                                                   float *__restrict__ dg, int accumulate) {
+  __shared__ float sh[kDgGroups][64];
+  const int lane = threadIdx.x & 63, q = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
   float s = 0.f;
-  for (int b = 0; b < nrb; ++b) s += part[(long)b * d + j];
-  dg[j] = accumulate ? dg[j] + s : s;
+  if (j < d) {
+#pragma unroll 4
+    for (int b = q; b < nrb; b += kDgGroups) s += part[(long)b * d + j];
+  }
+  sh[q][lane] = s;
+  __syncthreads();
+  if (q == 0 && j < d) {
+    float t = 0.f;
+#pragma unroll
+    for (int i = 0; i < kDgGroups; ++i) t += sh[i][lane];
+    dg[j] = accumulate ? dg[j] + t : t;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -196,13 +281,25 @@ template <typename T>
 hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *h, const float *r,
                                const float *g, float *dh, float *dg_part, float *dg, int accumulate,
                                int N, int d, hipStream_t s) {
-  hipLaunchKernelGGL(out_norm_bwd_kernel<T>, dim3(N), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g,
-                     dh, d);
   const int nrb = dg_row_blocks(N);
   const int rpb = (N + nrb - 1) / nrb;
-  hipLaunchKernelGGL(dg_partial_kernel<T>, dim3((d + 63) / 64, nrb), dim3(kNormThreads), 0, s, dx, splits,
-                     slab, h, r, dg_part, N, d, rpb);
-  hipLaunchKernelGGL(dg_reduce_kernel, dim3((d + 255) / 256), dim3(256), 0, s, dg_part, nrb, d, dg,
+  const int cpt = (d / 4 + kNormThreads - 1) / kNormThreads;
+  if (cpt <= 8) {
+    auto go = [&](auto kern) {
+      hipLaunchKernelGGL(kern, dim3(nrb), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g, dh, dg_part, N, d,
+                         rpb);
+    };
+    if (cpt <= 1) go(out_norm_bwd_rows_kernel<T, 1>);
+    else if (cpt <= 2) go(out_norm_bwd_rows_kernel<T, 2>);
+    else if (cpt <= 4) go(out_norm_bwd_rows_kernel<T, 4>);
+    else go(out_norm_bwd_rows_kernel<T, 8>);
+  } else {
+    hipLaunchKernelGGL(out_norm_bwd_kernel<T>, dim3(N), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g,
+                       dh, d);
+    hipLaunchKernelGGL(dg_partial_kernel<T>, dim3((d + 63) / 64, nrb), dim3(kNormThreads), 0, s, dx, splits,
+                       slab, h, r, dg_part, N, d, rpb);
+  }
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3((d + 63) / 64), dim3(64 * kDgGroups), 0, s, dg_part, nrb, d, dg,
                      accumulate);
   return hipGetLastError();
 }

@@ -16,6 +16,9 @@
  *     [B, T] layout, row index b*T + i.
  *   - Matrices follow the y = x W^T convention: a weight W of shape [out, in]
  *     is stored row-major with `in` contiguous.
+ *   - Every device pointer (NULL aside) must be 16-byte aligned: the kernels
+ *     access tensors in 16-byte vectors.  A misaligned pointer is rejected
+ *     with MTP_ERR_ARG.
  *   - The caller allocates and frees every buffer, including the workspace
  *     (size from the matching *_workspace_size call).  The library keeps no
  *     device memory of its own.

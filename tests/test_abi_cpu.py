@@ -106,3 +106,47 @@ def test_verify_host_errors(lib):
     # is a multiple of 8, single logits otherwise) and per tile of 256 chunks
     assert lib.mtp_verify_workspace_size(C.byref(args())) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (100 + 1) * 8
     assert lib.mtp_verify_workspace_size(C.byref(args(V=128))) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (16 + 1) * 8
+
+
+def test_misaligned_pointers_are_rejected_before_any_launch(lib):
+    """Device pointers must be 16-byte aligned; the checks run on the host and
+    return before anything is launched (the fake addresses are never used:
+    with no workspace the call stops at MTP_ERR_WORKSPACE)."""
+    fake = 0x7f0000001000
+    names = ("target_logits", "draft_logits", "draft_tokens", "u_accept", "u_sample", "accepted_len",
+             "next_token", "status")
+
+    def vargs(bad=None, off=8):
+        a = _lib.VerifyArgs()
+        a.R, a.gamma, a.V, a.temperature, a.logits_dtype = 4, 2, 128, 1.0, _lib.MTP_BF16
+        for i, n in enumerate(names):
+            setattr(a, n, fake + 0x10000 * i + (off if n == bad else 0))
+        return a
+    run = lambda a: lib.mtp_verify(C.byref(a), None)
+    assert run(vargs()) == -5                    # aligned: stops at the missing workspace
+    for n in names:
+        assert run(vargs(n)) == -6, n
+    a = vargs()
+    a.margin = fake + 4                          # optional output, still checked
+    assert run(a) == -6
+
+    D = 2
+    hs = (C.c_void_p * D)(fake, fake + 0x100000)
+    dhs = (C.c_void_p * D)(fake + 0x200000, fake + 0x300000)
+    ce_names = ("labels", "W_out", "g_out", "loss_sum", "counts", "loss", "loss_mtp", "dW_out", "dg_out")
+
+    def cargs(bad=None):
+        a = _lib.CeArgs()
+        a.B, a.T, a.d, a.V, a.D = 2, 16, 64, 512, D
+        a.dtype, a.eps, a.lambda_, a.reduce, a.denom = _lib.MTP_BF16, 1e-6, 0.1, 0, 0.0
+        a.h = C.cast(hs, C.POINTER(C.c_void_p))
+        a.dh = C.cast(dhs, C.POINTER(C.c_void_p))
+        for i, n in enumerate(ce_names):
+            setattr(a, n, fake + 0x400000 + 0x10000 * i + (2 if n == bad else 0))
+        return a
+    runc = lambda a: lib.mtp_head_ce_fwd_bwd(C.byref(a), None)
+    assert runc(cargs()) == -5
+    for n in ce_names:
+        assert runc(cargs(n)) == -6, n
+    hs[1] = fake + 0x100000 + 4
+    assert runc(cargs()) == -6
