@@ -10,6 +10,60 @@
 namespace mtp {
 
 // ---------------------------------------------------------------------------
+// Cross-lane helpers for the result layout.
+//
+// Lane-pair stores for 2-byte outputs: lanes l and l ^ 1 hold columns c and
+// c ^ 1 of the same rows, and registers r, r + 1 (r even) hold rows R, R + 1
+// of one column.  Trading one value over the lane pair (a DPP move) leaves
+// the even lane with row R and the odd lane with row R + 1, each with the two
+// adjacent columns (c & ~1, c | 1): one 4-byte store instead of two 2-byte
+// stores, and a half-wave writes whole 128-byte lines.  (4-byte outputs keep
+// one store per value: a half-wave already covers a whole line per row.)
+// Every output stored this way has an even row length.
+//
+// Half-wave reductions: max or sum over the 32 lanes of a half-wave (one
+// accumulator row) with DPP moves folded into the arithmetic: the two quad
+// permutations, the half-row and row mirrors reduce each 16-lane row, and a
+// broadcast of lane 15 of rows 0 and 2 into rows 1 and 3 completes the
+// half-wave, whose result is valid in lanes 16..31 and 48..63.
+// ---------------------------------------------------------------------------
+template <int CTRL, int ROW_MASK = 0xF>
+__device__ __forceinline__ float dpp_f(float old, float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(x), CTRL, ROW_MASK, 0xF,
+                                                    false));
+}
+__device__ __forceinline__ void pair_rows(float a, float b, bool odd, float &lo, float &hi) {
+  const float got = dpp_f<0xB1>(0.f, odd ? a : b);   // quad_perm [1,0,3,2]: lane l ^ 1
+  lo = odd ? got : a;
+  hi = odd ? b : got;
+}
+template <typename OutT>
+__device__ __forceinline__ void store_pair(__amdgpu_buffer_rsrc_t r, unsigned off, float lo, float hi) {
+  if constexpr (sizeof(OutT) == 4) {
+    typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 v = {__float_as_uint(lo), __float_as_uint(hi)};
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+  } else if constexpr (std::is_same_v<OutT, bf16_t>) {
+    __builtin_amdgcn_raw_buffer_store_b32(pack_bf16x2(lo, hi), r, off, 0, 0);
+  } else {
+    typedef _Float16 h2 __attribute__((ext_vector_type(2)));
+    const h2 v = {(_Float16)lo, (_Float16)hi};
+    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned, v), r, off, 0, 0);
+  }
+}
+template <bool MAX>
+__device__ __forceinline__ float halfwave_reduce(float x) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+  const float id = MAX ? -INFINITY : 0.f;
+  x = op(x, dpp_f<0xB1>(id, x));          // quad_perm [1,0,3,2]
+  x = op(x, dpp_f<0x4E>(id, x));          // quad_perm [2,3,0,1]
+  x = op(x, dpp_f<0x141>(id, x));         // row_half_mirror
+  x = op(x, dpp_f<0x140>(id, x));         // row_mirror
+  x = op(x, dpp_f<0x142, 0xA>(id, x));    // row_bcast:15 into rows 1 and 3
+  return x;
+}
+
+// ---------------------------------------------------------------------------
 // C = alpha * acc (+ residual) (+ C if accumulate).  One K-split writes its
 // own slab C + split * split_stride.  Branch-free: C and R are addressed
 // through buffer resources that start at the tile's first row and end at
@@ -55,8 +109,23 @@ struct EpiStore {
 #pragma unroll
           for (int r = 0; r < 16; ++r) v[r] += buf_load_elem(rc, oc[r], OutT{});
         }
+        if constexpr (sizeof(OutT) == 2) {
+          // lane-pair stores (whole 128-byte lines per half-wave): row R (even
+          // lane) or R + 1 (odd lane), columns c & ~1, c | 1
+          const bool odd = lane & 1;
+          const unsigned pc = (unsigned)((col & ~1) * sizeof(OutT));
 #pragma unroll
-        for (int r = 0; r < 16; ++r) buf_store_elem(rc, oc[r], v[r], OutT{});
+          for (int r = 0; r < 16; r += 2) {
+            float lo, hi;
+            pair_rows(v[r], v[r + 1], odd, lo, hi);
+            const int row = acc_row<Cfg>(wm, i, r, lane) + (odd ? 1 : 0);
+            store_pair<OutT>(rc, cok ? pc + (unsigned)((long)row * ldc * sizeof(OutT)) : kOOB, lo, hi);
+          }
+        } else {
+          // 4-byte values: a half-wave already writes one whole 128-byte line per row
+#pragma unroll
+          for (int r = 0; r < 16; ++r) buf_store_elem(rc, oc[r], v[r], OutT{});
+        }
       }
   }
 };
@@ -85,43 +154,70 @@ struct EpiRope {
     const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (long)m0 * ldc, rows * ldc * (long)sizeof(OutT));
     const __amdgpu_buffer_rsrc_t rp = make_rsrc(pos + m0, rows * (long)sizeof(int));
+    const bool odd = lane & 1;
+    // rotated values of block j into out[j]; then lane-pair stores
+    float out[Cfg::NB][16];
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i) {
       int p[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r)
         p[r] = (int)__builtin_amdgcn_raw_buffer_load_b32(rp, (unsigned)(acc_row<Cfg>(wm, i, r, lane) * 4), 0, 0);
+      if constexpr (HALF >= 32) {
+        // block j (j & PB == 0) holds the first half of a head, block j | PB
+        // the second half of the same columns: one (cos, sin) serves both
+        constexpr int PB = HALF / 32;
+#pragma unroll
+        for (int j = 0; j < Cfg::NB; ++j) {
+          if ((j & PB) != 0) continue;
+          const int col = n0 + acc_col<Cfg>(wn, j, lane);
+          const int jj = col % HD;                         // < HALF
+          const int col0 = n0 + acc_col<Cfg>(wn, j, 0);
+          const bool rot = rope != nullptr && __builtin_amdgcn_readfirstlane(col0) < 2 * A;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float xl = acc[i][j][r], xh = acc[i][j | PB][r];
+            out[j][r] = xl;
+            out[j | PB][r] = xh;
+            if (rot) {
+              const float2 cs = rope[(long)p[r] * HALF + jj];
+              out[j][r] = xl * cs.x - xh * cs.y;
+              out[j | PB][r] = xh * cs.x + xl * cs.y;
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < Cfg::NB; ++j) {
+          const int col = n0 + acc_col<Cfg>(wn, j, lane);
+          const int jh = col % HD;
+          const bool lo = jh < HALF;
+          const int jj = lo ? jh : jh - HALF;
+          const int col0 = n0 + acc_col<Cfg>(wn, j, 0);
+          const bool rot = rope != nullptr && __builtin_amdgcn_readfirstlane(col0) < 2 * A;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float x = acc[i][j][r];
+            const float partner = __shfl_xor(x, HALF);
+            out[j][r] = x;
+            if (rot) {
+              const float2 cs = rope[(long)p[r] * HALF + jj];
+              out[j][r] = lo ? (x * cs.x - partner * cs.y) : (x * cs.x + partner * cs.y);
+            }
+          }
+        }
+      }
 #pragma unroll
       for (int j = 0; j < Cfg::NB; ++j) {
         const int col = n0 + acc_col<Cfg>(wn, j, lane);
-        const int jh = col % HD;
-        const bool lo = jh < HALF;
-        const int jj = lo ? jh : jh - HALF;
-        // 2A is a multiple of 32: the whole block column is q/k or v
-        const int col0 = n0 + acc_col<Cfg>(wn, j, 0);
-        const bool rot = rope != nullptr && __builtin_amdgcn_readfirstlane(col0) < 2 * A;
-        float v[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float x = acc[i][j][r];
-          float partner;
-          if constexpr (HALF >= 32) {
-            constexpr int PB = HALF / 32;
-            partner = acc[i][j ^ PB][r];
-          } else {
-            partner = __shfl_xor(x, HALF);
-          }
-          v[r] = x;
-          if (rot) {
-            const float2 cs = rope[(long)p[r] * HALF + jj];
-            v[r] = lo ? (x * cs.x - partner * cs.y) : (x * cs.x + partner * cs.y);
-          }
-        }
+        const unsigned pc = (unsigned)((col & ~1) * sizeof(OutT));
         const bool cok = col < N;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rl = acc_row<Cfg>(wm, i, r, lane);
-          buf_store_elem(rc, cok ? (unsigned)(((long)rl * ldc + col) * sizeof(OutT)) : kOOB, v[r], OutT{});
+        for (int r = 0; r < 16; r += 2) {
+          float lo, hi;
+          pair_rows(out[j][r], out[j][r + 1], odd, lo, hi);
+          const int row = acc_row<Cfg>(wm, i, r, lane) + (odd ? 1 : 0);
+          store_pair<OutT>(rc, cok ? pc + (unsigned)((long)row * ldc * sizeof(OutT)) : kOOB, lo, hi);
         }
       }
     }
@@ -150,12 +246,20 @@ struct EpiSwiGLU {
       for (int j = 0; j < NBh; ++j) {
         const int feat = tile_n * (Cfg::BN / 2) + wn * (Cfg::WN / 2) + j * 32 + (lane & 31);
         const bool fok = feat < f;
+        const bool odd = lane & 1;
+        const unsigned pc = (unsigned)((feat & ~1) * sizeof(OutT));
+        float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int rl = acc_row<Cfg>(wm, i, r, lane);
           const float g = acc[i][j][r], u = acc[i][j + NBh][r];
-          const float sw = __fdividef(g, 1.f + __expf(-g));
-          buf_store_elem(rc, fok ? (unsigned)(((long)rl * ldc + feat) * sizeof(OutT)) : kOOB, sw * u, OutT{});
+          v[r] = __fdividef(g, 1.f + __expf(-g)) * u;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          float lo, hi;
+          pair_rows(v[r], v[r + 1], odd, lo, hi);
+          const int row = acc_row<Cfg>(wm, i, r, lane) + (odd ? 1 : 0);
+          store_pair<OutT>(rc, fok ? pc + (unsigned)((long)row * ldc * sizeof(OutT)) : kOOB, lo, hi);
         }
       }
   }
@@ -190,7 +294,8 @@ struct EpiCEFwd {
     static_assert(Cfg::WGN == 2, "two column waves per row");
     float *redm = reinterpret_cast<float *>(lds);          // [2][BM] row max per column wave
     float *reds = redm + 2 * Cfg::BM;                        // [2][BM] row sum-exp per column wave
-    const bool writer = (lane & 31) == 0;
+    const bool writer = (lane & 31) == 31;                   // holds the half-wave reductions
+    const bool odd = lane & 1;
     const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
     const __amdgpu_buffer_rsrc_t rz = make_rsrc(zout + (long)m0 * V, rows * V * (long)sizeof(ZT));
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(labels + m0, rows * 4L);
@@ -210,43 +315,58 @@ struct EpiCEFwd {
         float mx = -INFINITY;
 #pragma unroll
         for (int j = 0; j < Cfg::NB; ++j) mx = cok[j] ? fmaxf(mx, acc[i][j][r]) : mx;
-#pragma unroll
-        for (int o = 16; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        mx = halfwave_reduce<true>(mx);
         if (writer) redm[wn * Cfg::BM + acc_row<Cfg>(wm, i, r, lane)] = mx;
       }
     __syncthreads();
     // 2) sum of exp(z - m_row) over this wave's columns; target logit; logits
+    //    (two rows at a time for the lane-pair stores)
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = acc_row<Cfg>(wm, i, r, lane);
-        const float mt = fmaxf(redm[rr], redm[Cfg::BM + rr]);
-        const float nm = -mt * kLog2e;
-        const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(rr * 4), 0, 0);
-        const int lab = rr < rows ? lab0 : -1;
-        float s = 0.f, tv = 0.f;
-        bool has = false;
+      for (int r = 0; r < 16; r += 2) {
+        float zs[2][Cfg::NB];
 #pragma unroll
-        for (int j = 0; j < Cfg::NB; ++j) {
-          const float z = acc[i][j][r];
-          s += cok[j] ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
-          const unsigned zoff = cok[j] ? (unsigned)(((long)rr * V + col[j]) * sizeof(ZT)) : kOOB;
-          if constexpr (sizeof(ZT) == 4) {
-            buf_store_elem(rz, zoff, z, float{});
-          } else {
-            const _Float16 h = (_Float16)(z - mt);
-            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(unsigned short, h), rz, zoff, 0, 0);
+        for (int h = 0; h < 2; ++h) {
+          const int rr = acc_row<Cfg>(wm, i, r + h, lane);
+          const float mt = fmaxf(redm[rr], redm[Cfg::BM + rr]);
+          const float nm = -mt * kLog2e;
+          const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(rr * 4), 0, 0);
+          const int lab = rr < rows ? lab0 : -1;
+          float sum = 0.f, tv = 0.f;
+          bool has = false;
+#pragma unroll
+          for (int j = 0; j < Cfg::NB; ++j) {
+            const float z = acc[i][j][r + h];
+            sum += cok[j] ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
+            zs[h][j] = sizeof(ZT) == 4 ? z : z - mt;
+            const bool hit = col[j] == lab;
+            tv = hit ? z : tv;
+            has = has || hit;
           }
-          const bool hit = col[j] == lab;
-          tv = hit ? z : tv;
-          has = has || hit;
+          if (__builtin_amdgcn_ballot_w64(has) != 0)
+            buf_store_elem(rt, has ? (unsigned)(rr * 4) : kOOB, tv, float{});
+          sum = halfwave_reduce<false>(sum);
+          if (writer) reds[wn * Cfg::BM + rr] = sum;
         }
-        if (__builtin_amdgcn_ballot_w64(has) != 0)
-          buf_store_elem(rt, has ? (unsigned)(rr * 4) : kOOB, tv, float{});
+        if constexpr (sizeof(ZT) == 2) {
+          const int row = acc_row<Cfg>(wm, i, r, lane) + (odd ? 1 : 0);
 #pragma unroll
-        for (int o = 16; o > 0; o >>= 1) s += __shfl_xor(s, o);
-        if (writer) reds[wn * Cfg::BM + rr] = s;
+          for (int j = 0; j < Cfg::NB; ++j) {
+            float lo, hi;
+            pair_rows(zs[0][j], zs[1][j], odd, lo, hi);
+            const unsigned zoff = cok[j] ? (unsigned)(((long)row * V + (col[j] & ~1)) * sizeof(ZT)) : kOOB;
+            store_pair<ZT>(rz, zoff, lo, hi);
+          }
+        } else {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            const int row = acc_row<Cfg>(wm, i, r + h, lane);
+#pragma unroll
+            for (int j = 0; j < Cfg::NB; ++j)
+              buf_store_elem(rz, cok[j] ? (unsigned)(((long)row * V + col[j]) * 4) : kOOB, zs[h][j], float{});
+          }
+        }
       }
     __syncthreads();
     const int t = threadIdx.x;
