@@ -110,11 +110,12 @@ def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
 @pytest.mark.parametrize("slab_rows,d,V", [(0, 1024, 16384), (256, 1024, 16384), (0, 1056, 16384),
                                             (0, 1024, 20480)])
 def test_ce_bf16_big_tiles(slab_rows, d, V):
-    # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each, stream-K
+    # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each, balanced
     # schedule); slab_rows=256 runs the 1024 rows as four slabs in two dz
     # groups; d=1056 gives the forward GEMM an odd number of 32-element K
     # slices (a half-filled last pair of 128-byte A rows); V=20480 makes 320
-    # tiles, so 256 stream-K blocks share tiles and the fixup pass runs
+    # tiles: one whole round of 256, the other 64 split over K into partial
+    # tiles that the fixup pass sums
     cfg = synth.scaled(synth.D1, name="ce_big", B=1, T=1024, d=d, V=V, D=1, seg_lo=100,
                        seg_hi=700, sigma_w=0.02)
     res, ref, labels = _case(cfg, slab_rows=slab_rows)
@@ -128,6 +129,17 @@ def test_ce_bf16_big_dx_tiles_sparse_labels():
                        seg_lo=4096, seg_hi=4096, sigma_w=0.01)
     rows = np.random.default_rng(3).choice(4095, 64, replace=False)
     res, ref, labels = _case(cfg, label_rows=rows)
+    _assert(cfg, res, ref, labels)
+
+
+@pytest.mark.parametrize("d", [3072, 8200])
+def test_ce_bf16_output_norm_backward_widths(d):
+    # the output-norm backward keeps a row block in registers for d <= 8192
+    # (d = 3072: three 4-column chunks per thread) and takes the two-pass
+    # kernels beyond (d = 8200)
+    cfg = synth.scaled(synth.D1, name="ce_wide", B=2, T=40, d=d, V=256, D=1, seg_lo=10, seg_hi=40,
+                       sigma_w=0.02)
+    res, ref, labels = _case(cfg)
     _assert(cfg, res, ref, labels)
 
 
