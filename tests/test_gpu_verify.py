@@ -68,6 +68,17 @@ def test_verify_full_vocab_sampled_requests(gamma):
     assert ((g["accepted_len"] >= 0) & (g["accepted_len"] <= gamma)).all()
 
 
+@pytest.mark.parametrize("dtype,V", [(torch.bfloat16, 1003), (torch.float32, 997)])
+def test_verify_vocab_not_a_chunk_multiple(dtype, V):
+    # V not a multiple of a 16-byte chunk (8 bf16 or 4 float32 logits): the
+    # rows are read logit by logit
+    vc, d, y = _inputs(3, R=64, V=V, seed=5)
+    print(f"[verify] gamma=3 R=64 V={V} {dtype}", flush=True)
+    g = _gpu(d, y, dtype)
+    assert _compare(d, y, g) == 0
+    assert (g["status"] == 0).all()
+
+
 def test_verify_float32_logits_and_statuses():
     R, G, V = 8, 2, 64
     rng = np.random.default_rng(5)
