@@ -66,10 +66,11 @@ def test_chain_tiny_f32_depth3_and_degenerate_rows():
     _check(cfg, _inp, out, EXACT, 1e-4)
 
 
-@pytest.mark.parametrize("hd", [128, 64])
+@pytest.mark.parametrize("hd", [128, 64, 32])
 def test_chain_bf16_ragged(hd):
     # several tiles in every GEMM, ragged row / feature / vocabulary tails,
-    # packed segments of mixed lengths, two depths
+    # packed segments of mixed lengths, two depths; head_dim 32 puts the
+    # rotary partner 16 lanes away (the others: in the same lane)
     cfg = synth.scaled(synth.D1, name=f"ragged_hd{hd}", B=2, T=300, d=256, n_heads=256 // hd,
                        head_dim=hd, ffn=688, V=1000, D=2, seg_lo=20, seg_hi=200, sigma_w=0.05)
     inp, out = _run(cfg)
