@@ -161,8 +161,9 @@ typedef struct {
  * stored in dtype.  That gradient is
  * kept for a group of G rows, G * V * sizeof(dtype) <= logit_slab_bytes (a
  * whole number of slabs, at least one; two for bf16), and the dx_hat and
- * dW_out GEMMs run once per group.  Workspace grows with the slab, not with
- * B*T.
+ * dW_out GEMMs run once per group.  The logit and gradient buffers are
+ * bounded by the slab and the group, not by B*T (the per-row buffers, such
+ * as x_hat [B*T, d], do grow with B*T).
  *
  * Inputs : h [host] D pointers [B*T, d] (dtype); labels int32 [D,B,T]
  *          (-1 = no loss, as written by mtp_chain_forward); W_out [V, d]
