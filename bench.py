@@ -251,8 +251,8 @@ def main():
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.ingest_pmc[2], args.workload)
         return
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the multi-GPU "
-              "sharding is a design only, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py runs on one GPU; --gpus {args.gpus} is not supported (the path has no "
+              "multi-GPU implementation: data-parallel sharding is a design only)", file=sys.stderr)
         sys.exit(2)
     import torch
 
