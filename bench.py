@@ -309,16 +309,16 @@ def main():
     timer = _lib.StageTimer(dominant, 64 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     with timer:
-        e0.record()
-        for _ in range(args.steps):
+        ev[0].record()
+        for i in range(args.steps):
             step()
-        e1.record()
+            ev[i + 1].record()
         torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ms_step = e0.elapsed_time(e1) / args.steps
+    ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
+    per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     dom_times = timer.times_ms()
     assert len(dom_times) == timer.count and len(dom_times) % args.steps == 0
     dom_avg_ms = float(np.mean(dom_times))
@@ -385,6 +385,8 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
+        "ms_per_step_median": round(float(np.median(per_step)), 4),
+        "ms_per_step_min": round(float(np.min(per_step)), 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
