@@ -164,6 +164,31 @@ def algorithmic_flops(cfg, state_mask, counts, run_start_fn):
     return per
 
 
+def executed_tflop(cfg, run_start):
+    """MFMA work the kernels execute per step (multiply-add = 2): every row of
+    the dense layout, GEMM tiles padded to 256, attention over the key tiles
+    each 32-query wave visits (masked pairs included) with the probabilities'
+    hi and lo products, and no recomputation."""
+    def pad(x):
+        return -(-x // 256) * 256
+    d, A, f, V, N, hd = cfg.d, cfg.A_w, cfg.ffn, cfg.V, cfg.N, cfg.head_dim
+    gemm = 2.0 * pad(N) * (pad(d) * 2 * d + pad(3 * A) * d + pad(d) * A + pad(2 * f) * d + pad(d) * f)
+    head = 3 * 2.0 * pad(N) * pad(V) * d
+    T = cfg.T
+    wave_tiles = 0
+    for b in range(cfg.B):
+        rs = run_start[b]
+        for q0 in range(0, T, 256):
+            kbeg = rs[q0] // 64 * 64
+            for w in range(q0, min(q0 + 256, T), 32):
+                hi = min(w + 31, T - 1)
+                lo = rs[w]
+                first = kbeg + max(0, -(-(lo - 63 - kbeg) // 64)) * 64
+                wave_tiles += max(0, (hi - first) // 64 + 1)
+    attn = wave_tiles * cfg.n_heads * (2.0 + 4.0) * 32 * 64 * hd
+    return cfg.D * (gemm + head + attn) / 1e12
+
+
 # Algorithmic HBM bytes per depth of the memory-bound stages (N rows): what
 # each kernel must read and write once (bf16 activations, fp32 residual
 # stream and head gradients, fp16 logits).
@@ -397,6 +422,7 @@ def main():
                    "reduce": "fixed (B*T)", "parallelism": "none (1 GPU)"},
         "mfma_frac_step": round(step_frac, 4),
         "algorithmic_tflop_per_step": round(alg_step / 1e12, 3),
+        "executed_tflop_per_step": round(executed_tflop(cfg, run_starts(seg)), 3),
         "wall_s_timed": round(wall, 3),
         "roofline": {"bound": "mfma", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
