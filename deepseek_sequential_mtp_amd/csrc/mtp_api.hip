@@ -86,13 +86,24 @@ using PA = std::conditional_t<sizeof(T) == 2 && Cfg::BM == 256, DmaKMajor128<T, 
 inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N, 256) >= 256; }
 
 // One GEMM without K splits: the 256x256 tile (one block per compute unit)
-// on the balanced schedule (skws: tail_ws_bytes<Big>() of scratch), the
-// 128x128 tile one block per tile.
+// on the balanced schedule (skws: tail_ws_bytes<Big>() of scratch) when it
+// has at least kBalancedRounds rounds of tiles or a long K
+// (kBalancedK elements), else one block per tile (the 128x128 tile always).
+// With few rounds and a short K, the split tail's short partial tiles cost
+// more than the idle compute units of a plain last round: the chip is
+// power-limited and runs a partly filled round at a higher clock (measured
+// at M 4096, N 7168: K 14336 8% faster plain, K 18432 even, K 129280 5%
+// faster balanced).
+constexpr long kBalancedRounds = 4;
+constexpr int kBalancedK = 65536;
 template <typename T, class Cfg, class LA, class LB, class Epi>
 hipError_t run_gemm(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K, int group_m, float *skws,
                     hipStream_t s) {
-  if constexpr (std::is_same_v<Cfg, Big>) return launch_gemm_balanced<T, Cfg>(la, lb, epi, M, N, K, group_m, skws, s);
-  else return launch_gemm<T, Cfg>(la, lb, epi, M, N, K, group_m, 1, s);
+  if constexpr (std::is_same_v<Cfg, Big>) {
+    if ((long)ceil_div(M, Cfg::BM) * ceil_div(N, Cfg::BN) >= kBalancedRounds * kGemmSlots || K >= kBalancedK)
+      return launch_gemm_balanced<T, Cfg>(la, lb, epi, M, N, K, group_m, skws, s);
+  }
+  return launch_gemm<T, Cfg>(la, lb, epi, M, N, K, group_m, 1, s);
 }
 
 template <typename T, typename OutT, typename ResT>
