@@ -259,6 +259,9 @@ int check_chain(const mtp_chain_args *a) {
   const int A = a->n_heads * a->head_dim;
   if (a->d % E || a->ffn % E || A % E) return MTP_ERR_SHAPE;
   if ((long)a->B * a->T > (1L << 30) || (long)a->V * a->d > (1L << 40)) return MTP_ERR_SHAPE;
+  // attention addresses one batch row's keys and values through a 32-bit
+  // buffer range: T rows of the [q | k | v] activation must span < 2 GiB
+  if ((long)a->T * 3 * A * (a->dtype == MTP_BF16 ? 2 : 4) >= (1L << 31) - 4096) return MTP_ERR_UNSUPPORTED;
   if (a->dtype == MTP_BF16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
     return MTP_ERR_UNSUPPORTED;
   if (a->dtype == MTP_F32 && a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64)

@@ -127,7 +127,9 @@ typedef struct {
  * Requirements: B,T,d,n_heads,ffn,V >= 1, D >= 1;
  *   bf16: d, ffn, n_heads*head_dim multiples of 8; head_dim in {32, 64, 128};
  *   f32 : d, ffn, n_heads*head_dim multiples of 4; head_dim in {16, 32, 64}
- *   (other widths return MTP_ERR_UNSUPPORTED).
+ *   (other widths return MTP_ERR_UNSUPPORTED); B*T <= 2^30; one batch row's
+ *   [q | k | v] activation, T * 3 * n_heads * head_dim elements, must span
+ *   less than 2 GiB (else MTP_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, d, n_heads, head_dim, ffn, V, D;

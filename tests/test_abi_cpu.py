@@ -62,6 +62,11 @@ def test_chain_host_errors(lib):
     assert run(_chain_args(dtype=_lib.MTP_BF16, ffn=176, head_dim=16)) == -8
     assert run(_chain_args(dtype=_lib.MTP_BF16)) == -2                # ffn 172 not a multiple of 8
     assert run(_chain_args(eps=-1.0)) == -6
+    # one batch row's [q | k | v] must span < 2 GiB: 65536 x 3 x 16384 bf16 does not,
+    # 32768 x 3 x 8192 x 2 bytes (1.5 GiB) does
+    big = dict(dtype=_lib.MTP_BF16, d=1024, ffn=2816, n_heads=128, head_dim=128, B=1)
+    assert run(_chain_args(T=65536, **big)) == -8
+    assert run(_chain_args(T=32768, **dict(big, n_heads=64))) == -1
     assert run(_chain_args()) == -1                                  # pointers missing
     assert lib.mtp_chain_workspace_size(C.byref(_chain_args(D=0))) == 0
     ws = lib.mtp_chain_workspace_size(C.byref(_chain_args()))
