@@ -586,6 +586,7 @@ int check_verify(const mtp_verify_args *a) {
   if (a->logits_dtype != MTP_F32 && a->logits_dtype != MTP_BF16) return MTP_ERR_DTYPE;
   if (a->R < 1 || a->gamma < 1 || a->V < 1) return MTP_ERR_SHAPE;
   if ((long)a->R * (2 * a->gamma + 1) > (1L << 31) - 1) return MTP_ERR_SHAPE;
+  if (a->R > 65535) return MTP_ERR_UNSUPPORTED;   // requests are a grid dimension of the mass pass
   if (!(a->temperature > 0.f) || !isfinite(a->temperature)) return MTP_ERR_ARG;
   return MTP_OK;
 }

@@ -236,7 +236,8 @@ typedef struct {
  * q_j(y_j) = 0, zero residual mass.  Every logit row is read once (its
  * log-sum-exp); rows after the first rejection do not affect any output
  * (a non-finite value there is not reported).
- * Requirements: R >= 1, gamma >= 1, V >= 1, temperature > 0.
+ * Requirements: R >= 1, gamma >= 1, V >= 1, temperature > 0 and finite;
+ * R <= 65535 (else MTP_ERR_UNSUPPORTED).
  * ---------------------------------------------------------------------- */
 typedef struct {
   int R, gamma, V;

@@ -103,6 +103,8 @@ def test_verify_host_errors(lib):
         return a
     run = lambda a: lib.mtp_verify(C.byref(a), None)
     assert run(args(gamma=0)) == -2
+    assert run(args(R=65536)) == -8        # more requests than one grid dimension holds
+    assert run(args(R=65535)) == -1        # accepted; fails on the null pointers
     assert run(args(temperature=0.0)) == -6
     assert run(args(logits_dtype=3)) == -4
     assert run(args()) == -1
