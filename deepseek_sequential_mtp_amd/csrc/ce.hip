@@ -48,33 +48,35 @@ template <typename T, typename ZT>
 __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, const float2 *__restrict__ part,
                                                     int nt, int tile_cols, const float *__restrict__ lse,
                                                     const int32_t *__restrict__ labels, T *__restrict__ dz,
-                                                    int V) {
-  const long row = blockIdx.y;
-  const int lab = labels[row];
-  const float nl = -lse[row] * kLog2e;
-  const ZT *zr = z + row * V;
-  T *dr = dz + row * V;
-  for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
-    float g[4] = {0.f, 0.f, 0.f, 0.f};
-    if (lab >= 0) {
-      float zz[4];
-      float off = nl;
-      if constexpr (sizeof(ZT) == 4) {
-        const float4 v = reinterpret_cast<const float4 *>(zr)[c4];
-        zz[0] = v.x; zz[1] = v.y; zz[2] = v.z; zz[3] = v.w;
-      } else {
-        typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-        const h4 v = reinterpret_cast<const h4 *>(zr)[c4];
-        zz[0] = (float)v[0]; zz[1] = (float)v[1]; zz[2] = (float)v[2]; zz[3] = (float)v[3];
-        off = fmaf(part[row * nt + (4 * c4) / tile_cols].x, kLog2e, nl);
-      }
-      // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
-      // (probabilities below 2^-126 flush to zero)
+                                                    int V, int N) {
+  // column blocks on x, rows on y (a row stride covers N > 65535)
+  for (long row = blockIdx.y; row < N; row += gridDim.y) {
+    const int lab = labels[row];
+    const float nl = -lse[row] * kLog2e;
+    const ZT *zr = z + row * V;
+    T *dr = dz + row * V;
+    for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
+      float g[4] = {0.f, 0.f, 0.f, 0.f};
+      if (lab >= 0) {
+        float zz[4];
+        float off = nl;
+        if constexpr (sizeof(ZT) == 4) {
+          const float4 v = reinterpret_cast<const float4 *>(zr)[c4];
+          zz[0] = v.x; zz[1] = v.y; zz[2] = v.z; zz[3] = v.w;
+        } else {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          const h4 v = reinterpret_cast<const h4 *>(zr)[c4];
+          zz[0] = (float)v[0]; zz[1] = (float)v[1]; zz[2] = (float)v[2]; zz[3] = (float)v[3];
+          off = fmaf(part[row * nt + (4 * c4) / tile_cols].x, kLog2e, nl);
+        }
+        // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
+        // (probabilities below 2^-126 flush to zero)
 #pragma unroll
-      for (int e = 0; e < 4; ++e)
-        g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, off)) - (4 * c4 + e == lab ? 1.f : 0.f);
+        for (int e = 0; e < 4; ++e)
+          g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, off)) - (4 * c4 + e == lab ? 1.f : 0.f);
+      }
+      store4(dr + 4 * c4, g);
     }
-    store4(dr + 4 * c4, g);
   }
 }
 
@@ -83,8 +85,8 @@ hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, 
                         const int32_t *labels, T *dz, int N, int V, hipStream_t s) {
   if (N == 0) return hipSuccess;
   const int bx = min((V / 4 + 1023) / 1024, 65535);
-  hipLaunchKernelGGL((ce_dz_kernel<T, ZT>), dim3(bx, N), dim3(256), 0, s, z, part, nt, tile_cols, lse, labels,
-                     dz, V);
+  hipLaunchKernelGGL((ce_dz_kernel<T, ZT>), dim3(bx, min(N, 65535)), dim3(256), 0, s, z, part, nt, tile_cols,
+                     lse, labels, dz, V, N);
   return hipGetLastError();
 }
 template hipError_t launch_ce_dz<bf16_t, _Float16>(const _Float16 *, const float2 *, int, int, const float *,

@@ -210,9 +210,9 @@ template <typename T>
 __global__ __launch_bounds__(kNormThreads) void dg_partial_kernel(
     const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h,
     const float *__restrict__ r, float *__restrict__ part, int N, int d, int rows_per_block) {
-  const int j = blockIdx.x * 64 + (threadIdx.x & 63);
+  const int j = blockIdx.y * 64 + (threadIdx.x & 63);   // row blocks on x, column blocks on y
   const int rg = threadIdx.x >> 6;
-  const int n0 = blockIdx.y * rows_per_block;
+  const int n0 = blockIdx.x * rows_per_block;
   const int n1 = min(N, n0 + rows_per_block);
   __shared__ float sh[4][64];
   float acc = 0.f;
@@ -226,7 +226,7 @@ __global__ __launch_bounds__(kNormThreads) void dg_partial_kernel(
   sh[rg][threadIdx.x & 63] = acc;
   __syncthreads();
   if (rg == 0 && j < d)
-    part[(long)blockIdx.y * d + j] = sh[0][threadIdx.x] + sh[1][threadIdx.x] + sh[2][threadIdx.x] +
+    part[(long)blockIdx.x * d + j] = sh[0][threadIdx.x] + sh[1][threadIdx.x] + sh[2][threadIdx.x] +
                                      sh[3][threadIdx.x];
 }
 
@@ -296,7 +296,7 @@ hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *
   } else {
     hipLaunchKernelGGL(out_norm_bwd_kernel<T>, dim3(N), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g,
                        dh, d);
-    hipLaunchKernelGGL(dg_partial_kernel<T>, dim3((d + 63) / 64, nrb), dim3(kNormThreads), 0, s, dx, splits,
+    hipLaunchKernelGGL(dg_partial_kernel<T>, dim3(nrb, (d + 63) / 64), dim3(kNormThreads), 0, s, dx, splits,
                        slab, h, r, dg_part, N, d, rpb);
   }
   hipLaunchKernelGGL(dg_reduce_kernel, dim3((d + 63) / 64), dim3(64 * kDgGroups), 0, s, dg_part, nrb, d, dg,

@@ -132,6 +132,20 @@ def test_ce_bf16_big_dx_tiles_sparse_labels():
     _assert(cfg, res, ref, labels)
 
 
+def test_ce_bf16_more_rows_than_one_grid_dimension():
+    # 70000 rows in one logit slab: the softmax-gradient pass strides its rows
+    # over a grid dimension of at most 65535 blocks; labels on 256 sampled rows
+    # (160 of them beyond row 65535) keep the oracle cheap
+    cfg = synth.scaled(synth.D1, name="ce_tall", B=1, T=70000, d=64, V=256, D=1, seg_lo=2000,
+                       seg_hi=9000, sigma_w=0.05)
+    rng = np.random.default_rng(4)
+    rows = np.concatenate([rng.choice(65536, 96, replace=False),
+                           65536 + rng.choice(70000 - 65536, 160, replace=False)])
+    res, ref, labels = _case(cfg, label_rows=rows)
+    assert int((labels[0, 65536:] >= 0).sum()) > 100
+    _assert(cfg, res, ref, labels)
+
+
 @pytest.mark.parametrize("d", [3072, 8200])
 def test_ce_bf16_output_norm_backward_widths(d):
     # the output-norm backward keeps a row block in registers for d <= 8192
