@@ -24,10 +24,18 @@ With x_n = r * h, r = 1 / sqrt(mean(h^2) + eps) and x_hat = g_out * x_n:
 (the RMSNorm derivative written out; x_hat's storage rounding is treated as
 the identity, as any straight-through store is).
 
+Top-1 accuracy by depth (M7.6 0x0E and M7.4 0x0C list it among the
+training metrics without defining it further; read here as the plain
+definition): pred_i = argmax_v z_iv on each loss row, the lowest id among
+equal maxima; correct_k = #{loss rows with pred_i = label_i};
+accuracy_k = correct_k / |V_k|, 0 for an empty depth.
+
 Pins: W_out = 0 gives loss log V per row and dz = c (1/V - onehot); central
 finite differences of L_MTP in float64 for h, W_out and g_out (M7.4 0x04C);
 each dz row sums to 0 so sum_v dW_out[v, :] = 0; L_paper = (|V_k| / T) L_valid
-(M7.6 0x05).
+(M7.6 0x05); accuracy: rows of W_out parallel to one vector put the
+argmax at the largest or smallest scale by the sign of the projection,
+W_out = 0 ties every logit (pred 0), brute-force loops on a tiny case.
 """
 from __future__ import annotations
 
@@ -82,6 +90,9 @@ def head_ce(hs: Sequence[np.ndarray], labels: np.ndarray, W_out: np.ndarray,
     counts = np.zeros(D, dtype=np.int64)
     loss_k = np.zeros(D)
     lse_all = np.full((D, N), np.nan)
+    pred = np.full((D, N), -1, dtype=np.int64)
+    correct = np.zeros(D, dtype=np.int64)
+    accuracy = np.zeros(D)
     dW = np.zeros((V, d))
     dg = np.zeros(d)
     dhs: List[np.ndarray] = []
@@ -97,6 +108,11 @@ def head_ce(hs: Sequence[np.ndarray], labels: np.ndarray, W_out: np.ndarray,
         z = x_hat @ W.T
         lse = logsumexp_rows(z)
         lse_all[k, rows] = lse
+        # np.argmax returns the first index among equal maxima
+        pk = np.argmax(z, axis=1)
+        pred[k, rows] = pk
+        correct[k] = int((pk == y).sum())
+        accuracy[k] = correct[k] / rows.size
         ell = lse - z[np.arange(rows.size), y]
         loss_sum[k] = ell.sum()
         den = denom if reduce == "fixed" else float(rows.size)
@@ -113,7 +129,8 @@ def head_ce(hs: Sequence[np.ndarray], labels: np.ndarray, W_out: np.ndarray,
             dh[rows] = r[:, None] * (g * dx_hat - x_n * t.mean(axis=1, keepdims=True))
         dhs.append(dh)
     loss_mtp = lam / D * loss_k.sum()
-    out = dict(loss_sum=loss_sum, counts=counts, loss=loss_k, loss_mtp=loss_mtp, lse=lse_all)
+    out = dict(loss_sum=loss_sum, counts=counts, loss=loss_k, loss_mtp=loss_mtp, lse=lse_all,
+               pred=pred, correct=correct, accuracy=accuracy)
     if grads:
         out.update(dh=dhs, dW_out=dW, dg_out=dg)
     return out

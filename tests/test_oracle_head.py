@@ -145,3 +145,83 @@ def test_gradients_vs_autograd():
         np.testing.assert_allclose(out["dh"][k], ht[k].grad.numpy(), rtol=1e-11, atol=1e-15)
     np.testing.assert_allclose(out["dW_out"], Wt.grad.numpy(), rtol=1e-11, atol=1e-15)
     np.testing.assert_allclose(out["dg_out"], gt.grad.numpy(), rtol=1e-11, atol=1e-15)
+
+
+def test_accuracy_parallel_head_rows():
+    """W_out[v] = s_v u: z_iv = s_v (x_hat_i . u), so the argmax is the largest
+    scale where the projection is positive and the smallest where negative."""
+    hs, labels, counts, W, g = _setup(5, D=2, V=13)
+    rng = np.random.default_rng(7)
+    V, d = W.shape
+    u = rng.standard_normal(d)
+    s = rng.permutation(V).astype(np.float64) - 4.0
+    Wp = s[:, None] * u[None, :]
+    out = head.head_ce(hs, labels, Wp, g, 1e-6, 0.1, grads=False)
+    for k in range(len(hs)):
+        rws = np.nonzero(labels[k] >= 0)[0]
+        xh, _, _ = head.output_norm(hs[k][rws], g, 1e-6)
+        proj = xh @ u
+        exp = np.where(proj > 0, np.argmax(s), np.argmin(s))
+        np.testing.assert_array_equal(out["pred"][k, rws], exp)
+        assert np.all(out["pred"][k, labels[k] < 0] == -1)
+        assert out["correct"][k] == int((exp == labels[k, rws]).sum())
+    # labels set to the known argmax: every loss row is correct
+    lab2 = labels.copy()
+    for k in range(len(hs)):
+        rws = np.nonzero(labels[k] >= 0)[0]
+        xh, _, _ = head.output_norm(hs[k][rws], g, 1e-6)
+        lab2[k, rws] = np.where(xh @ u > 0, np.argmax(s), np.argmin(s))
+    out2 = head.head_ce(hs, lab2, Wp, g, 1e-6, 0.1, grads=False)
+    np.testing.assert_array_equal(out2["correct"], counts)
+    np.testing.assert_array_equal(out2["accuracy"], np.where(counts > 0, 1.0, 0.0))
+
+
+def test_accuracy_ties_take_the_lowest_id():
+    hs, labels, counts, W, g = _setup(6, D=2)
+    out = head.head_ce(hs, labels, np.zeros_like(W), g, 1e-6, 0.1, grads=False)
+    for k in range(len(hs)):
+        rws = labels[k] >= 0
+        assert np.all(out["pred"][k, rws] == 0)
+        assert out["correct"][k] == int((labels[k, rws] == 0).sum())
+    # two equal maxima at ids 3 and 7 on every row: 3 wins
+    V, d = W.shape
+    W2 = np.full((V, d), 0.0)
+    W2[3] = W2[7] = 1.0
+    pos = [np.abs(h) + 0.1 for h in hs]        # x_hat . 1 > 0
+    out = head.head_ce(pos, labels, W2, np.abs(g), 1e-6, 0.1, grads=False)
+    for k in range(len(hs)):
+        assert np.all(out["pred"][k, labels[k] >= 0] == 3)
+
+
+def test_accuracy_brute_force_loops():
+    hs, labels, counts, W, g = _setup(8, D=2, T=7, d=4, V=9)
+    out = head.head_ce(hs, labels, W, g, 1e-6, 0.1, grads=False)
+    D, N = labels.shape
+    for k in range(D):
+        correct = 0
+        for i in range(N):
+            if labels[k, i] < 0:
+                assert out["pred"][k, i] == -1
+                continue
+            h = hs[k][i]
+            ms = sum(float(x) * float(x) for x in h) / len(h)
+            xh = [g[j] * h[j] / np.sqrt(ms + 1e-6) for j in range(len(h))]
+            best, arg = None, -1
+            for v in range(W.shape[0]):
+                zv = sum(xh[j] * W[v, j] for j in range(len(h)))
+                if best is None or zv > best:
+                    best, arg = zv, v
+            assert out["pred"][k, i] == arg
+            correct += int(arg == labels[k, i])
+        assert out["correct"][k] == correct
+        assert out["accuracy"][k] == (correct / counts[k] if counts[k] else 0.0)
+
+
+def test_accuracy_of_an_empty_depth_is_zero():
+    hs, labels, counts, W, g = _setup(9, D=2)
+    labels = labels.copy()
+    labels[1] = -1
+    out = head.head_ce(hs, labels, W, g, 1e-6, 0.1, grads=False)
+    assert out["correct"][1] == 0 and out["accuracy"][1] == 0.0
+    assert np.all(out["pred"][1] == -1)
+    assert 0 <= out["correct"][0] <= out["counts"][0]
