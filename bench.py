@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--stages", action="store_true", help="print the per-stage time table to stderr")
+    ap.add_argument("--accuracy", action="store_true",
+                    help="also compute the top-1 accuracy by depth in every step (printed to stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="after the timed region, run a plain 256 MiB fp32 copy kernel 3 times (the "
                          "reference dispatch that scales FETCH_SIZE / WRITE_SIZE counters)")
@@ -301,6 +303,10 @@ def main():
                   dh=[torch.empty((N, cfg.d), device=dev) for _ in range(D)],
                   dW_out=torch.empty((cfg.V, cfg.d), device=dev), dg_out=torch.empty((cfg.d,), device=dev),
                   device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    if args.accuracy:
+        ce_out.update(pred=torch.empty((D, N), dtype=torch.int32, device=dev),
+                      correct=torch.empty(D, dtype=torch.int32, device=dev),
+                      accuracy=torch.empty(D, device=dev))
     cache = {}
 
     def step():
@@ -314,6 +320,9 @@ def main():
         step()
     torch.cuda.synchronize()
     assert int(chain_out["device_error"][0]) == 0
+    if args.accuracy:
+        print(f"top-1 accuracy by depth {ce_out['accuracy'].tolist()} "
+              f"(correct {ce_out['correct'].tolist()} of {ce_out['counts'].tolist()})", file=sys.stderr)
 
     # per-stage times (one profiled step per stage, outside the timed region)
     stage_ms = {}

@@ -45,6 +45,9 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
+ABI_VERSION = 3     # the struct layouts below mirror include/mtp.h at this version
+
+
 class CeArgs(C.Structure):
     _fields_ = [("B", C.c_int), ("T", C.c_int), ("d", C.c_int), ("V", C.c_int), ("D", C.c_int),
                 ("dtype", C.c_int), ("eps", C.c_float), ("lambda_", C.c_float), ("reduce", C.c_int),
@@ -52,6 +55,7 @@ class CeArgs(C.Structure):
                 ("g_out", vp), ("loss_sum", vp), ("counts", vp), ("loss", vp), ("loss_mtp", vp),
                 ("lse", vp), ("dh", C.POINTER(vp)), ("dW_out", vp), ("dg_out", vp),
                 ("accumulate", C.c_int), ("device_error", vp), ("logit_slab_bytes", C.c_size_t),
+                ("pred", vp), ("correct", vp), ("accuracy", vp),
                 ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
@@ -88,6 +92,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_abi_version.restype = C.c_int
         lib.mtp_profile_stage.argtypes = [C.c_int, C.POINTER(vp), C.POINTER(vp), C.c_int]
         lib.mtp_profile_count.restype = C.c_int
+        if lib.mtp_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{path} has ABI version {lib.mtp_abi_version()}, this binding "
+                               f"expects {ABI_VERSION}: rebuild it")
         _lib = lib
     return _lib
 
@@ -173,11 +180,13 @@ def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Ten
 def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: torch.Tensor,
                     g_out: torch.Tensor, *, lam: float, eps: float = 1e-6, reduce: str = "fixed",
                     denom: float = 0.0, accumulate: bool = False, want_lse: bool = False,
-                    logit_slab_bytes: int = 0, out: Optional[Dict] = None, cache: Optional[Dict] = None,
-                    stream=None) -> Dict:
+                    want_accuracy: bool = False, logit_slab_bytes: int = 0, out: Optional[Dict] = None,
+                    cache: Optional[Dict] = None, stream=None) -> Dict:
     """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].  logit_slab_bytes
     bounds the fp32 logit slab and the dz row group (0: the library default).
-    Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error)."""
+    Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error,
+    pred, correct, accuracy); the last three (top-1 accuracy by depth) only with
+    want_accuracy (or when ``out`` holds them)."""
     D, B, T = labels.shape
     V, d = W_out.shape
     dev = W_out.device
@@ -191,13 +200,18 @@ def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: tor
                    dW_out=torch.zeros((V, d), dtype=torch.float32, device=dev),
                    dg_out=torch.zeros((d,), dtype=torch.float32, device=dev),
                    device_error=torch.empty(1, dtype=torch.int32, device=dev))
+        if want_accuracy:
+            out.update(pred=torch.empty((D, B * T), dtype=torch.int32, device=dev),
+                       correct=torch.empty(D, dtype=torch.int32, device=dev),
+                       accuracy=torch.empty(D, dtype=torch.float32, device=dev))
     hp = (vp * D)(*[h.data_ptr() for h in hs])
     dhp = (vp * D)(*[x.data_ptr() for x in out["dh"]])
     red = {"fixed": MTP_REDUCE_FIXED, "valid_mean": MTP_REDUCE_VALID_MEAN}[reduce]
     a = CeArgs(B, T, d, V, D, _dtype_code(W_out), eps, lam, red, float(denom), hp, _p(labels),
                _p(W_out), _p(g_out), _p(out["loss_sum"]), _p(out["counts"]), _p(out["loss"]),
                _p(out["loss_mtp"]), _p(out["lse"]), dhp, _p(out["dW_out"]), _p(out["dg_out"]),
-               1 if accumulate else 0, _p(out["device_error"]), int(logit_slab_bytes), None, 0)
+               1 if accumulate else 0, _p(out["device_error"]), int(logit_slab_bytes),
+               _p(out.get("pred")), _p(out.get("correct")), _p(out.get("accuracy")), None, 0)
     lib = load()
     nbytes = lib.mtp_ce_workspace_size(C.byref(a))
     if nbytes == 0:

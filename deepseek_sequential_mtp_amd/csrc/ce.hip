@@ -8,12 +8,16 @@
 namespace mtp {
 
 // One wave per row: lse = M + log(sum_t s_t exp(m_t - M)) over the nt tile
-// partials; row loss = lse - z[label] on labelled rows, else 0.
+// partials; row loss = lse - z[label] on labelled rows, else 0.  With pred
+// (top-1 accuracy requested) the row maximum M is kept and pred is seeded
+// with V on labelled rows (the softmax-gradient pass lowers it to the argmax)
+// and -1 on the others.
 __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restrict__ part, int nt,
                                                          const float *__restrict__ target,
                                                          const int32_t *__restrict__ labels,
                                                          float *__restrict__ lse, float *__restrict__ lse_out,
-                                                         float *__restrict__ row_loss, int N) {
+                                                         float *__restrict__ row_loss, float *__restrict__ rowmax,
+                                                         int32_t *__restrict__ pred, int V, int N) {
   const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (row >= N) return;
@@ -33,6 +37,10 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restric
     if (lse_out != nullptr) lse_out[row] = l;
     const int lab = labels[row];
     row_loss[row] = lab >= 0 ? l - target[row] : 0.f;
+    if (pred != nullptr) {
+      rowmax[row] = mx;
+      pred[row] = lab >= 0 ? V : -1;
+    }
   }
 }
 
@@ -44,15 +52,21 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restric
 // part[row * nt + col / tile_cols]).  V is a multiple of 4 and of the tile
 // width's divisors used here: each thread handles 4 consecutive columns of
 // one tile.
+// With pred, the same pass finds each labelled row's argmax: a column is a
+// maximum when its logit equals the row maximum rowmax (fp16 offsets: its
+// tile's maximum is the row's and its offset is 0); atomicMin keeps the
+// lowest such column.
 template <typename T, typename ZT>
 __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, const float2 *__restrict__ part,
                                                     int nt, int tile_cols, const float *__restrict__ lse,
                                                     const int32_t *__restrict__ labels, T *__restrict__ dz,
+                                                    const float *__restrict__ rowmax, int32_t *__restrict__ pred,
                                                     int V, int N) {
   // column blocks on x, rows on y (a row stride covers N > 65535)
   for (long row = blockIdx.y; row < N; row += gridDim.y) {
     const int lab = labels[row];
     const float nl = -lse[row] * kLog2e;
+    const float rmax = (pred != nullptr && lab >= 0) ? rowmax[row] : 0.f;
     const ZT *zr = z + row * V;
     T *dr = dz + row * V;
     for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
@@ -60,6 +74,7 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
       if (lab >= 0) {
         float zz[4];
         float off = nl;
+        float top = rmax;            // the value a maximal column holds
         if constexpr (sizeof(ZT) == 4) {
           const float4 v = reinterpret_cast<const float4 *>(zr)[c4];
           zz[0] = v.x; zz[1] = v.y; zz[2] = v.z; zz[3] = v.w;
@@ -67,7 +82,15 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
           typedef _Float16 h4 __attribute__((ext_vector_type(4)));
           const h4 v = reinterpret_cast<const h4 *>(zr)[c4];
           zz[0] = (float)v[0]; zz[1] = (float)v[1]; zz[2] = (float)v[2]; zz[3] = (float)v[3];
-          off = fmaf(part[row * nt + (4 * c4) / tile_cols].x, kLog2e, nl);
+          const float mt = part[row * nt + (4 * c4) / tile_cols].x;
+          off = fmaf(mt, kLog2e, nl);
+          top = mt == rmax ? 0.f : 1.f;  // offsets are <= 0: 1 matches none
+        }
+        if (pred != nullptr) {
+          int first = -1;
+#pragma unroll
+          for (int e = 3; e >= 0; --e) first = zz[e] == top ? 4 * c4 + e : first;
+          if (first >= 0) atomicMin(pred + row, first);
         }
         // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
         // (probabilities below 2^-126 flush to zero)
@@ -82,44 +105,61 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
 
 template <typename T, typename ZT>
 hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
-                        const int32_t *labels, T *dz, int N, int V, hipStream_t s) {
+                        const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,
+                        hipStream_t s) {
   if (N == 0) return hipSuccess;
   const int bx = min((V / 4 + 1023) / 1024, 65535);
   hipLaunchKernelGGL((ce_dz_kernel<T, ZT>), dim3(bx, min(N, 65535)), dim3(256), 0, s, z, part, nt, tile_cols,
-                     lse, labels, dz, V, N);
+                     lse, labels, dz, rowmax, pred, V, N);
   return hipGetLastError();
 }
 template hipError_t launch_ce_dz<bf16_t, _Float16>(const _Float16 *, const float2 *, int, int, const float *,
-                                                    const int32_t *, bf16_t *, int, int, hipStream_t);
+                                                    const int32_t *, bf16_t *, const float *, int32_t *, int, int,
+                                                    hipStream_t);
 template hipError_t launch_ce_dz<float, float>(const float *, const float2 *, int, int, const float *,
-                                               const int32_t *, float *, int, int, hipStream_t);
+                                               const int32_t *, float *, const float *, int32_t *, int, int,
+                                               hipStream_t);
 
 // One block: sum of the row losses of depth k (double, fixed order) and the
 // count of labelled rows; scale[k] = lambda / (D * denom_k) for the backward
 // (0 for an empty depth under the valid-row mean).  With row_loss = nullptr
 // only the count and the scale are produced (they depend on the labels alone).
+// With pred: the count of labelled rows whose argmax is the label goes to
+// acc_correct[k], and pred is copied to pred_out when that is given.
 __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict__ row_loss,
                                                          const int32_t *__restrict__ labels, int N, int k,
                                                          int D, int valid_mean, double denom, float lambda,
-                                                         double *acc_sum, int32_t *acc_cnt, float *scale) {
+                                                         double *acc_sum, int32_t *acc_cnt, float *scale,
+                                                         const int32_t *__restrict__ pred,
+                                                         int32_t *__restrict__ pred_out, int32_t *acc_correct) {
   __shared__ double shs[16];
-  __shared__ int shc[16];
+  __shared__ int shc[16], shh[16];
   const int t = threadIdx.x;
   double s = 0.0;
-  int c = 0;
+  int c = 0, hits = 0;
   for (int i = t; i < N; i += 1024) {
     if (row_loss != nullptr) s += (double)row_loss[i];
-    c += labels[i] >= 0 ? 1 : 0;
+    const int lab = labels[i];
+    c += lab >= 0 ? 1 : 0;
+    if (pred != nullptr) {
+      const int p = pred[i];
+      hits += (lab >= 0 && p == lab) ? 1 : 0;
+      if (pred_out != nullptr) pred_out[i] = p;
+    }
   }
   s = warp_sum(s);
-  for (int o = 32; o > 0; o >>= 1) c += __shfl_xor(c, o);
-  if ((t & 63) == 0) { shs[t >> 6] = s; shc[t >> 6] = c; }
+  for (int o = 32; o > 0; o >>= 1) {
+    c += __shfl_xor(c, o);
+    hits += __shfl_xor(hits, o);
+  }
+  if ((t & 63) == 0) { shs[t >> 6] = s; shc[t >> 6] = c; shh[t >> 6] = hits; }
   __syncthreads();
   if (t == 0) {
     double ts = 0.0;
-    int tc = 0;
-    for (int w = 0; w < 16; ++w) { ts += shs[w]; tc += shc[w]; }
+    int tc = 0, th = 0;
+    for (int w = 0; w < 16; ++w) { ts += shs[w]; tc += shc[w]; th += shh[w]; }
     if (row_loss != nullptr) acc_sum[k] = ts;
+    if (pred != nullptr) acc_correct[k] = th;
     acc_cnt[k] = tc;
     const double den = valid_mean ? (double)tc : denom;
     scale[k] = den > 0.0 ? (float)((double)lambda / ((double)D * den)) : 0.f;
@@ -128,7 +168,8 @@ __global__ __launch_bounds__(1024) void ce_reduce_kernel(const float *__restrict
 
 __global__ void ce_finalize_kernel(const double *acc_sum, const int32_t *acc_cnt, int D, int valid_mean,
                                    double denom, float lambda, float *loss_sum, int32_t *counts,
-                                   float *loss, float *loss_mtp) {
+                                   float *loss, float *loss_mtp, const int32_t *acc_correct, int32_t *correct,
+                                   float *accuracy) {
   if (threadIdx.x != 0) return;
   double total = 0.0;
   for (int k = 0; k < D; ++k) {
@@ -138,28 +179,34 @@ __global__ void ce_finalize_kernel(const double *acc_sum, const int32_t *acc_cnt
     counts[k] = acc_cnt[k];
     loss[k] = (float)lk;
     total += lk;
+    if (correct != nullptr) correct[k] = acc_correct[k];
+    if (accuracy != nullptr)
+      accuracy[k] = acc_cnt[k] > 0 ? (float)((double)acc_correct[k] / (double)acc_cnt[k]) : 0.f;
   }
   loss_mtp[0] = (float)((double)lambda / D * total);
 }
 
 hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
-                             float *lse, float *lse_out, float *row_loss, int N, hipStream_t s) {
+                             float *lse, float *lse_out, float *row_loss, float *rowmax, int32_t *pred, int V,
+                             int N, hipStream_t s) {
   hipLaunchKernelGGL(ce_combine_kernel, dim3((N + 3) / 4), dim3(256), 0, s, part, nt, target, labels, lse,
-                     lse_out, row_loss, N);
+                     lse_out, row_loss, rowmax, pred, V, N);
   return hipGetLastError();
 }
 hipError_t launch_ce_reduce(const float *row_loss, const int32_t *labels, int N, int k, int D,
                             int valid_mean, double denom, float lambda, double *acc_sum, int32_t *acc_cnt,
-                            float *scale, hipStream_t s) {
+                            float *scale, const int32_t *pred, int32_t *pred_out, int32_t *acc_correct,
+                            hipStream_t s) {
   hipLaunchKernelGGL(ce_reduce_kernel, dim3(1), dim3(1024), 0, s, row_loss, labels, N, k, D, valid_mean,
-                     denom, lambda, acc_sum, acc_cnt, scale);
+                     denom, lambda, acc_sum, acc_cnt, scale, pred, pred_out, acc_correct);
   return hipGetLastError();
 }
 hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int D, int valid_mean,
                               double denom, float lambda, float *loss_sum, int32_t *counts, float *loss,
-                              float *loss_mtp, hipStream_t s) {
+                              float *loss_mtp, const int32_t *acc_correct, int32_t *correct, float *accuracy,
+                              hipStream_t s) {
   hipLaunchKernelGGL(ce_finalize_kernel, dim3(1), dim3(64), 0, s, acc_sum, acc_cnt, D, valid_mean, denom,
-                     lambda, loss_sum, counts, loss, loss_mtp);
+                     lambda, loss_sum, counts, loss, loss_mtp, acc_correct, correct, accuracy);
   return hipGetLastError();
 }
 

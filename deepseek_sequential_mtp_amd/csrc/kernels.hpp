@@ -43,15 +43,19 @@ hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStre
 // CE reductions
 template <typename T, typename ZT>
 hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
-                        const int32_t *labels, T *dz, int N, int V, hipStream_t s);
+                        const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,
+                        hipStream_t s);
 hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
-                             float *lse, float *lse_out, float *row_loss, int N, hipStream_t s);
+                             float *lse, float *lse_out, float *row_loss, float *rowmax, int32_t *pred, int V,
+                             int N, hipStream_t s);
 hipError_t launch_ce_reduce(const float *row_loss, const int32_t *labels, int N, int k, int D,
                             int reduce_valid_mean, double denom, float lambda, double *acc_sum,
-                            int32_t *acc_cnt, float *scale, hipStream_t s);
+                            int32_t *acc_cnt, float *scale, const int32_t *pred, int32_t *pred_out,
+                            int32_t *acc_correct, hipStream_t s);
 hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int D,
                               int reduce_valid_mean, double denom, float lambda, float *loss_sum,
-                              int32_t *counts, float *loss, float *loss_mtp, hipStream_t s);
+                              int32_t *counts, float *loss, float *loss_mtp, const int32_t *acc_correct,
+                              int32_t *correct, float *accuracy, hipStream_t s);
 
 // verify
 size_t verify_workspace_bytes(int R, int G, int V, int bf16);

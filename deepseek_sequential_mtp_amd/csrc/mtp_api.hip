@@ -421,7 +421,8 @@ int check_ce_ptrs(const mtp_ce_args *a) {
   for (int k = 0; k < a->D; ++k)
     if (!a->h[k] || !a->dh[k]) return MTP_ERR_NULL;
   if (!all_al16(a->labels, a->W_out, a->g_out, a->loss_sum, a->counts, a->loss, a->loss_mtp, a->lse, a->dW_out,
-                a->dg_out, a->device_error, a->workspace))
+                a->dg_out, a->device_error, a->workspace) ||
+      !all_al16(a->pred, a->correct, a->accuracy))
     return MTP_ERR_ARG;
   for (int k = 0; k < a->D; ++k)
     if (!all_al16(a->h[k], a->dh[k])) return MTP_ERR_ARG;
@@ -462,7 +463,7 @@ CeDims ce_dims(const mtp_ce_args *a) {
   return c;
 }
 
-constexpr int kCeParts = 15;     // workspace regions of the CE call
+constexpr int kCeParts = 18;     // workspace regions of the CE call
 
 template <typename T>
 size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
@@ -482,6 +483,11 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[12] = c.take<float>((size_t)dg_row_blocks((int)m.N) * m.d);  // dg partials
   p[13] = c.take<LogitT<T>>(m.slab * m.V);       // logits of the slab (LogitT)
   p[14] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
+  // top-1 accuracy: row maxima of the slab, argmax per row, hits per depth
+  const bool acc = a->pred || a->correct || a->accuracy;
+  p[15] = c.take<float>(acc ? m.slab : 0);
+  p[16] = c.take<int32_t>(acc ? m.N : 0);
+  p[17] = c.take<int32_t>(acc ? a->D : 0);
   return c.off;
 }
 
@@ -505,6 +511,10 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   float *dg_part = (float *)p[12];
   LogitT<T> *zbuf = (LogitT<T> *)p[13];
   float *skws = sizeof(T) == 2 ? (float *)p[14] : nullptr;
+  const bool want_acc = a->pred || a->correct || a->accuracy;
+  float *rowmax = want_acc ? (float *)p[15] : nullptr;
+  int32_t *pred = want_acc ? (int32_t *)p[16] : nullptr;
+  int32_t *acc_correct = want_acc ? (int32_t *)p[17] : nullptr;
   const bool valid_mean = a->reduce == MTP_REDUCE_VALID_MEAN;
   const double denom = valid_mean ? 0.0 : (a->denom > 0.0 ? a->denom : (double)N);
   const long sstride = m.N * m.d;                // stride of the dx_hat split partials
@@ -523,7 +533,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     {
       // the backward scale depends on the labels only: known before any slab
       MTP_STAGE(MTP_STAGE_CE_REDUCE);
-      MTP_TRY(launch_ce_reduce(nullptr, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
+      MTP_TRY(launch_ce_reduce(nullptr, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale,
+                               nullptr, nullptr, nullptr, s));
     }
     for (long g0 = 0; g0 < m.N; g0 += m.group) {
       const int gn = (int)(m.N - g0 < m.group ? m.N - g0 : m.group);
@@ -541,12 +552,14 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         {
           MTP_STAGE(MTP_STAGE_CE_REDUCE);
           MTP_TRY(launch_ce_combine(part, m.nt, target + r0, ls, lse + r0,
-                                    a->lse ? a->lse + (long)k * N + r0 : nullptr, row_loss + r0, nr, s));
+                                    a->lse ? a->lse + (long)k * N + r0 : nullptr, row_loss + r0, rowmax,
+                                    want_acc ? pred + r0 : nullptr, V, nr, s));
         }
         {
           MTP_STAGE(MTP_STAGE_CE_GRAD);
           MTP_TRY((launch_ce_dz<T, LogitT<T>>(zbuf, part, m.nt, m.big ? Big::BN : Small::BN, lse + r0, ls,
-                                              dz + (r0 - g0) * V, nr, V, s)));
+                                              dz + (r0 - g0) * V, rowmax, want_acc ? pred + r0 : nullptr, nr,
+                                              V, s)));
         }
       }
       {
@@ -568,7 +581,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_CE_REDUCE);
-      MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale, s));
+      MTP_TRY(launch_ce_reduce(row_loss, lab, N, k, D, valid_mean, denom, a->lambda, acc_sum, acc_cnt, scale,
+                               pred, a->pred ? a->pred + (long)k * N : nullptr, acc_correct, s));
     }
     {
       MTP_STAGE(MTP_STAGE_CE_NORM_BWD);
@@ -577,7 +591,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     }
   }
   MTP_TRY(launch_ce_finalize(acc_sum, acc_cnt, D, valid_mean, denom, a->lambda, a->loss_sum, a->counts, a->loss,
-                             a->loss_mtp, s));
+                             a->loss_mtp, acc_correct, a->correct, a->accuracy, s));
   return MTP_OK;
 }
 
@@ -599,7 +613,7 @@ size_t verify_bytes(const mtp_verify_args *a) {
 
 extern "C" {
 
-int mtp_abi_version(void) { return 2; }
+int mtp_abi_version(void) { return 3; }
 
 int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n) {
   if (stage < 0) {

@@ -178,7 +178,15 @@ typedef struct {
  *          head (written, not accumulated; 0 on unlabelled rows);
  *          dW_out f32 [V, d] and dg_out f32 [d]: the depths' contributions
  *          summed; accumulate = 1 adds them to the existing values (e.g. the
- *          main loss's), 0 overwrites.
+ *          main loss's), 0 overwrites;
+ *          pred int32 [D, B*T], correct int32 [D], accuracy f32 [D]
+ *          (each optional, may be NULL): top-1 accuracy by depth ([M7.6]
+ *          0x0E; [M7.4] 0x0C).  pred is the argmax of each labelled row's
+ *          logits (the lowest id among equal maxima; -1 on unlabelled rows),
+ *          correct[k] counts the labelled rows with pred = label and
+ *          accuracy[k] = correct[k] / counts[k] (0 for an empty depth).  The
+ *          decision is taken on the fp32 logits (bf16 runs: on the kept fp16
+ *          offsets, so values within 2^-25 of the row maximum tie with it).
  * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
  *          MTP_REDUCE_VALID_MEAN (denom ignored).
  * logit_slab_bytes: bound on the fp32 logit slab and on the gradient group
@@ -206,6 +214,9 @@ typedef struct {
   int accumulate;
   int32_t *device_error;             /* optional                               */
   size_t logit_slab_bytes;           /* 0 = 1 GiB                              */
+  int32_t *pred;                     /* optional                               */
+  int32_t *correct;                  /* optional                               */
+  float *accuracy;                   /* optional                               */
   void *workspace;
   size_t workspace_bytes;
 } mtp_ce_args;

@@ -36,7 +36,7 @@ def test_header_declares_the_three_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mtp_abi_version() == 2
+    assert lib.mtp_abi_version() == _lib.ABI_VERSION == 3
     assert lib.mtp_strerror(0) == b"ok"
     assert lib.mtp_strerror(-3) == b"depth must be positive"
 
@@ -92,6 +92,14 @@ def test_ce_host_errors(lib):
     assert run(args(V=(1 << 21) - 4)) == -1  # shape accepted; fails on the null pointers
     assert run(args()) == -1
     assert lib.mtp_ce_workspace_size(C.byref(args())) > 0
+    # top-1 accuracy adds the slab's row maxima, one argmax per row and a hit
+    # count per depth (32 + 32 + 1 four-byte values here, plus alignment)
+    base = lib.mtp_ce_workspace_size(C.byref(args()))
+    for name in ("pred", "correct", "accuracy"):
+        a = args()
+        setattr(a, name, 0x7f0000000000)
+        extra = lib.mtp_ce_workspace_size(C.byref(a)) - base
+        assert 65 * 4 <= extra <= 65 * 4 + 3 * 256, (name, extra)
 
 
 def test_verify_host_errors(lib):
@@ -140,7 +148,8 @@ def test_misaligned_pointers_are_rejected_before_any_launch(lib):
     D = 2
     hs = (C.c_void_p * D)(fake, fake + 0x100000)
     dhs = (C.c_void_p * D)(fake + 0x200000, fake + 0x300000)
-    ce_names = ("labels", "W_out", "g_out", "loss_sum", "counts", "loss", "loss_mtp", "dW_out", "dg_out")
+    ce_names = ("labels", "W_out", "g_out", "loss_sum", "counts", "loss", "loss_mtp", "dW_out", "dg_out",
+                "pred", "correct", "accuracy")
 
     def cargs(bad=None):
         a = _lib.CeArgs()

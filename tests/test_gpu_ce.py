@@ -13,14 +13,28 @@ from tests.gpu_util import compare, rel_fro, tdev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, seed=0, slab_rows=0):
+def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, seed=0, slab_rows=0,
+          want_accuracy=False, mirror_head=False, plant_hits=False):
     inp = synth.make_head_inputs(cfg, seed)
+    if mirror_head:                       # W_out[V-1-v] = W_out[v]: every logit appears twice
+        W = inp["W_out"]
+        W[cfg.V // 2:] = W[:cfg.V // 2][::-1]
     _, _, labels, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], cfg.D)
     labels = labels.reshape(cfg.D, -1)
     if label_rows is not None:            # keep labels only on these rows
         keep = np.zeros(labels.shape[1], bool)
         keep[label_rows] = True
         labels = np.where(keep[None, :], labels, -1)
+    model = BF16 if cfg.dtype == "bf16" else EXACT
+    if plant_hits:                        # half the loss rows labelled with the oracle's argmax
+        pre = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], cfg.eps, cfg.lam, "fixed",
+                            None, model, grads=False)
+        rng = np.random.default_rng(seed + 11)
+        labels = labels.copy()
+        for k in range(cfg.D):
+            rws = np.nonzero(labels[k] >= 0)[0]
+            pick = rws[rng.random(rws.size) < 0.5]
+            labels[k, pick] = pre["pred"][k, pick]
     dtype = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     hs = [tdev(h, dtype) for h in inp["h"]]
     W = tdev(inp["W_out"], dtype)
@@ -37,14 +51,48 @@ def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, see
                    dW_out=torch.full((cfg.V, cfg.d), 0.25, device="cuda"),
                    dg_out=torch.full((cfg.d,), -0.5, device="cuda"),
                    device_error=torch.empty(1, dtype=torch.int32, device="cuda"))
+    if out is not None and want_accuracy:
+        out.update(pred=torch.empty((cfg.D, cfg.N), dtype=torch.int32, device="cuda"),
+                   correct=torch.empty(cfg.D, dtype=torch.int32, device="cuda"),
+                   accuracy=torch.empty(cfg.D, device="cuda"))
     res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, reduce=reduce, denom=denom,
-                               accumulate=accumulate, want_lse=True, out=out,
+                               accumulate=accumulate, want_lse=True, want_accuracy=want_accuracy, out=out,
                                logit_slab_bytes=slab_rows * cfg.V * 4)
     torch.cuda.synchronize()
-    model = BF16 if cfg.dtype == "bf16" else EXACT
     ref = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], cfg.eps, cfg.lam, reduce,
                         denom if denom > 0 else None, model)
+    if want_accuracy:
+        _assert_accuracy(cfg, res, ref, labels, inp, model)
     return res, ref, labels
+
+
+def _assert_accuracy(cfg, res, ref, labels, inp, model):
+    """Top-1 accuracy by depth.  The argmax is unique where the best logit
+    leads the runner-up by more than the logits' rounding difference (fp32
+    vs float64 accumulation: 1e-3 in bf16 runs, 1e-5 in f32 runs); elsewhere
+    the GPU's choice must be a valid maximum of the oracle's logits within
+    that window.  correct is exact given the GPU's argmax."""
+    pred = to_np(res["pred"]).reshape(cfg.D, -1).astype(np.int64)
+    correct = to_np(res["correct"]).astype(np.int64)
+    acc = to_np(res["accuracy"])
+    tol = 1e-5 if cfg.dtype == "f32" else 1e-3
+    W = np.asarray(inp["W_out"], np.float64)
+    for k in range(cfg.D):
+        m = labels[k] >= 0
+        np.testing.assert_array_equal(pred[k, ~m], -1)
+        assert np.all((pred[k, m] >= 0) & (pred[k, m] < cfg.V))
+        assert correct[k] == int((pred[k, m] == labels[k, m]).sum())
+        exp_acc = correct[k] / m.sum() if m.sum() else 0.0
+        np.testing.assert_allclose(acc[k], exp_acc, rtol=1e-6)
+        diff = np.nonzero(m & (pred[k] != ref["pred"][k]))[0]
+        if diff.size:
+            xh, _, _ = ohead.output_norm(np.asarray(inp["h"][k])[diff], inp["g_out"], cfg.eps, model)
+            zo = xh @ W.T
+            gap = zo[np.arange(diff.size), ref["pred"][k, diff]] - zo[np.arange(diff.size), pred[k, diff]]
+            assert np.all(gap <= tol), (k, diff[:8], gap.max())
+        assert abs(int(correct[k]) - int(ref["correct"][k])) <= diff.size
+        print(f"  accuracy[{k}] {acc[k]:.4f} (oracle {ref['accuracy'][k]:.4f}); "
+              f"{diff.size} near-tie rows of {int(m.sum())}", flush=True)
 
 
 def _assert(cfg, res, ref, labels, accumulate=False):
@@ -132,6 +180,44 @@ def test_ce_bf16_big_dx_tiles_sparse_labels():
     _assert(cfg, res, ref, labels)
 
 
+@pytest.mark.parametrize("slab_rows", [0, 5])
+def test_ce_tiny_f32_accuracy(slab_rows):
+    cfg = synth.TINY
+    res, ref, labels = _case(cfg, slab_rows=slab_rows, want_accuracy=True, plant_hits=True)
+    _assert(cfg, res, ref, labels)
+
+
+@pytest.mark.parametrize("slab_rows,accumulate", [(0, False), (80, True)])
+def test_ce_bf16_accuracy_two_depths(slab_rows, accumulate):
+    cfg = synth.scaled(synth.D1, name="ce_acc_d2", B=2, T=300, d=256, V=1000, D=2, seg_lo=20,
+                       seg_hi=200, sigma_w=0.05)
+    res, ref, labels = _case(cfg, slab_rows=slab_rows, accumulate=accumulate, want_accuracy=True,
+                             plant_hits=True)
+    _assert(cfg, res, ref, labels, accumulate=accumulate)
+    assert np.all(to_np(res["accuracy"]) > 0.4)
+
+
+@pytest.mark.parametrize("dtype,V", [("f32", 512), ("bf16", 16384)])
+def test_ce_accuracy_exact_ties_take_the_lowest_id(dtype, V):
+    # the head's second half mirrors its first: each logit appears at v and
+    # V-1-v, in another vocabulary tile, and the lower id must win
+    cfg = synth.scaled(synth.D1, name="ce_ties", B=1, T=512, d=256, V=V, D=1, seg_lo=512,
+                       seg_hi=512, sigma_w=0.05, dtype=dtype)
+    res, ref, labels = _case(cfg, want_accuracy=True, mirror_head=True)
+    pred = to_np(res["pred"]).reshape(-1)
+    m = labels[0] >= 0
+    assert np.all(pred[m] < V // 2)
+
+
+@pytest.mark.parametrize("slab_rows", [0, 256])
+def test_ce_bf16_big_tiles_accuracy(slab_rows):
+    cfg = synth.scaled(synth.D1, name="ce_big_acc", B=1, T=1024, d=1024, V=16384, D=1, seg_lo=100,
+                       seg_hi=700, sigma_w=0.02)
+    res, ref, labels = _case(cfg, slab_rows=slab_rows, want_accuracy=True, plant_hits=True)
+    _assert(cfg, res, ref, labels)
+    assert to_np(res["accuracy"])[0] > 0.4
+
+
 def test_ce_bf16_more_rows_than_one_grid_dimension():
     # 70000 rows in one logit slab: the softmax-gradient pass strides its rows
     # over a grid dimension of at most 65535 blocks; labels on 256 sampled rows
@@ -141,7 +227,7 @@ def test_ce_bf16_more_rows_than_one_grid_dimension():
     rng = np.random.default_rng(4)
     rows = np.concatenate([rng.choice(65536, 96, replace=False),
                            65536 + rng.choice(70000 - 65536, 160, replace=False)])
-    res, ref, labels = _case(cfg, label_rows=rows)
+    res, ref, labels = _case(cfg, label_rows=rows, want_accuracy=True)
     assert int((labels[0, 65536:] >= 0).sum()) > 100
     _assert(cfg, res, ref, labels)
 
