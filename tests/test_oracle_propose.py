@@ -1,0 +1,101 @@
+"""Pins of the retained-module proposer oracle (one recurrent draft step)."""
+import numpy as np
+import pytest
+
+from deepseek_sequential_mtp_amd import synth
+from oracle import chain, propose
+from oracle.numerics import BF16, EXACT
+
+
+def _tiny(seed=0, T=12):
+    cfg = synth.scaled(synth.TINY, name="prop_tiny", B=1, T=T, D=1, seg_lo=T, seg_hi=T)
+    inp = synth.make_chain_inputs(cfg, seed)
+    inp["segment_ids"] = np.zeros((1, T), np.int32)       # one segment from position 0
+    return cfg, inp
+
+
+@pytest.mark.parametrize("theta", [10000.0, 0.0])
+def test_slot_by_slot_steps_equal_teacher_forced_chain_rows(theta):
+    """Slot j's input is (h0_j, x_(j+1)): the step at slot p over slots 0..p is
+    row p of the dense chain oracle's depth-1 module on that segment."""
+    cfg, inp = _tiny()
+    w = inp["depths"][0]
+    T = cfg.T
+    ref = chain.module_forward(inp["h0"], inp["tokens"], inp["segment_ids"], 1, w, inp["E"], cfg.n_heads,
+                               cfg.head_dim, cfg.eps, theta, EXACT)
+    toks = inp["tokens"][0]
+    for p in (0, 1, 5, T - 2):
+        h, _, _ = propose.module_rows(inp["h0"][:p + 1], toks[1:p + 2], w, inp["E"], cfg.n_heads, cfg.head_dim,
+                                      cfg.eps, theta, EXACT)
+        np.testing.assert_allclose(h, ref[:p + 1], rtol=1e-11, atol=1e-12)
+
+
+def test_bf16_rounding_points_match_the_chain():
+    cfg, inp = _tiny(1)
+    w = inp["depths"][0]
+    ref = chain.module_forward(inp["h0"], inp["tokens"], inp["segment_ids"], 1, w, inp["E"], cfg.n_heads,
+                               cfg.head_dim, cfg.eps, 1e4, BF16)
+    p = cfg.T - 2
+    h, _, _ = propose.module_rows(inp["h0"][:p + 1], inp["tokens"][0][1:p + 2], w, inp["E"], cfg.n_heads,
+                                  cfg.head_dim, cfg.eps, 1e4, BF16)
+    # same rounding points; only the summation order differs, which can move
+    # a value across a bf16 rounding boundary (one ulp) now and then
+    err = np.abs(h - ref[:p + 1])
+    assert np.mean(err == 0.0) > 0.9 and err.max() < 0.05
+
+
+def test_one_slot_attends_only_to_itself():
+    """With one slot the softmax weight is 1 whatever the query: the query
+    block of Wqkv has no effect."""
+    cfg, inp = _tiny(2)
+    w = dict(inp["depths"][0])
+    A = cfg.n_heads * cfg.head_dim
+    h1, _, _ = propose.module_rows(inp["h0"][:1], [3], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4)
+    W2 = np.array(w["Wqkv"], copy=True)
+    W2[:A] = np.random.default_rng(9).standard_normal((A, W2.shape[1]))
+    w["Wqkv"] = W2
+    h2, _, _ = propose.module_rows(inp["h0"][:1], [3], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4)
+    np.testing.assert_array_equal(h1, h2)
+    # ... while with two slots it does
+    h3, _, _ = propose.module_rows(inp["h0"][:2], [3, 4], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4)
+    w["Wqkv"] = inp["depths"][0]["Wqkv"]
+    h4, _, _ = propose.module_rows(inp["h0"][:2], [3, 4], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4)
+    assert not np.allclose(h3[1], h4[1])
+
+
+def test_draw_closed_forms():
+    V = 50
+    z = np.zeros(V)
+    for u in (0.0, 0.019, 0.02, 0.5, 0.999):
+        tok, st, _ = propose.draw(z, u, 1.0)
+        assert st == propose.OK and tok == int(np.floor(u * V))
+    z[17] = 80.0                                   # every other weight about e^-80 of the mass
+    for u in (1e-20, 0.3, 0.999999):
+        assert propose.draw(z, u, 1.0)[0] == 17
+    # u = 0: the smallest id whose cumulative weight exceeds 0 -- id 0, whose
+    # weight e^-80 is still positive
+    assert propose.draw(z, 0.0, 1.0)[0] == 0
+    assert propose.draw(z, 1.0, 1.0)[1] == propose.BAD_UNIFORM
+    z[3] = np.inf
+    assert propose.draw(z, 0.5, 1.0)[1] == propose.NONFINITE
+
+
+def test_rollout_feeds_back_state_and_token():
+    cfg, inp = _tiny(3)
+    w = inp["depths"][0]
+    P = 4
+    toks = inp["tokens"][0]
+    us = [0.1, 0.7, 0.4]
+    res = propose.rollout(inp["h0"][:P], toks[1:P + 1], inp["h0"][P], int(toks[P + 1]), 3, w, inp["E"],
+                          inp["W_out"], inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4, 1.0, us)
+    assert len(res) == 3 and all(r["status"] == propose.OK for r in res)
+    # step 2 by hand: slots 0..P+2 with the fed-back states and tokens
+    rows_h = list(inp["h0"][:P + 1]) + [res[0]["h"], res[1]["h"]]
+    rows_t = list(toks[1:P + 2]) + [res[0]["token"], res[1]["token"]]
+    r2 = propose.propose_step(np.array(rows_h), rows_t, w, inp["E"], inp["W_out"], inp["g_out"], cfg.n_heads,
+                              cfg.head_dim, cfg.eps, 1e4, 1.0, us[2])
+    np.testing.assert_array_equal(r2["h"], res[2]["h"])
+    assert r2["token"] == res[2]["token"]
+    bad = propose.propose_step(np.array(rows_h), rows_t[:-1] + [cfg.V], w, inp["E"], inp["W_out"],
+                               inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4, 1.0, 0.5)
+    assert bad["status"] == propose.BAD_TOKEN
