@@ -19,9 +19,10 @@ MTP_REDUCE_FIXED, MTP_REDUCE_VALID_MEAN = 0, 1
 STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEPTH",
           -4: "MTP_ERR_DTYPE", -5: "MTP_ERR_WORKSPACE", -6: "MTP_ERR_ARG", -7: "MTP_ERR_HIP",
           -8: "MTP_ERR_UNSUPPORTED"}
-EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_chain_workspace_size",
-           "mtp_ce_workspace_size", "mtp_verify_workspace_size", "mtp_strerror", "mtp_abi_version",
-           "mtp_profile_stage", "mtp_profile_count")
+EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step",
+           "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
+           "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
+           "mtp_profile_count")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
           "VERIFY")
@@ -67,6 +68,16 @@ class VerifyArgs(C.Structure):
                 ("workspace_bytes", C.c_size_t)]
 
 
+class ProposeArgs(C.Structure):
+    _fields_ = [("R", C.c_int), ("L_max", C.c_int), ("d", C.c_int), ("n_heads", C.c_int),
+                ("head_dim", C.c_int), ("ffn", C.c_int), ("V", C.c_int), ("dtype", C.c_int),
+                ("eps", C.c_float), ("rope_theta", C.c_float), ("temperature", C.c_float),
+                ("w", C.POINTER(DepthWeights)), ("embed", vp), ("W_out", vp), ("g_out", vp),
+                ("h_prev", vp), ("tokens", vp), ("positions", vp), ("u_sample", vp), ("kv_cache", vp),
+                ("h_out", vp), ("logits", vp), ("draft_token", vp), ("status", vp), ("margin", vp),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
 _lib = None
 
 
@@ -81,6 +92,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_chain_forward.argtypes = [C.POINTER(ChainArgs), vp]
         lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
         lib.mtp_verify.argtypes = [C.POINTER(VerifyArgs), vp]
+        lib.mtp_propose_step.argtypes = [C.POINTER(ProposeArgs), vp]
+        lib.mtp_propose_workspace_size.argtypes = [C.POINTER(ProposeArgs)]
+        lib.mtp_propose_workspace_size.restype = C.c_size_t
         lib.mtp_chain_workspace_size.argtypes = [C.POINTER(ChainArgs)]
         lib.mtp_chain_workspace_size.restype = C.c_size_t
         lib.mtp_ce_workspace_size.argtypes = [C.POINTER(CeArgs)]
@@ -249,6 +263,46 @@ def verify(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens
     a.workspace, a.workspace_bytes = _p(ws), ws.numel()
     _check(lib.mtp_verify(C.byref(a), _stream(stream)))
     out["_keep"] = (ws,)
+    return out
+
+
+def propose_step(h_prev: torch.Tensor, tokens: torch.Tensor, positions: torch.Tensor,
+                 u_sample: torch.Tensor, kv_cache: torch.Tensor, weights: Dict[str, torch.Tensor],
+                 embed: torch.Tensor, W_out: torch.Tensor, g_out: torch.Tensor, *, n_heads: int,
+                 head_dim: int, eps: float = 1e-6, rope_theta: float = 10000.0, temperature: float = 1.0,
+                 want_margin: bool = True, out: Optional[Dict] = None, cache: Optional[Dict] = None,
+                 stream=None) -> Dict:
+    """mtp_propose_step.  h_prev [R,d]; tokens, positions int32 [R]; u_sample f32 [R];
+    kv_cache [R, 2, L_max, n_heads*head_dim] (updated in place at each request's slot);
+    weights: one module's dict (g_h, g_e, M, g_a, Wqkv, Wo, g_f, Wgate, Wup, Wdown).
+    Returns dict(h_out, logits, draft_token, status, margin)."""
+    R, d = h_prev.shape
+    V = embed.shape[0]
+    L_max = kv_cache.shape[2]
+    dev = h_prev.device
+    if out is None:
+        out = dict(h_out=torch.empty_like(h_prev),
+                   logits=torch.empty((R, V), dtype=h_prev.dtype, device=dev),
+                   draft_token=torch.empty(R, dtype=torch.int32, device=dev),
+                   status=torch.empty(R, dtype=torch.int32, device=dev),
+                   margin=torch.empty(R, dtype=torch.float32, device=dev) if want_margin else None)
+    w = weights
+    warr = (DepthWeights * 1)()
+    warr[0] = DepthWeights(_p(w["g_h"]), _p(w["g_e"]), _p(w["g_a"]), _p(w["g_f"]), _p(w["M"]),
+                           _p(w["Wqkv"]), _p(w["Wo"]), _p(w["Wgate"]), _p(w["Wup"]), _p(w["Wdown"]))
+    a = ProposeArgs(R, L_max, d, n_heads, head_dim, w["Wgate"].shape[0], V, _dtype_code(h_prev), eps,
+                    rope_theta, temperature, warr, _p(embed), _p(W_out), _p(g_out), _p(h_prev),
+                    _p(tokens), _p(positions), _p(u_sample), _p(kv_cache), _p(out["h_out"]),
+                    _p(out["logits"]), _p(out["draft_token"]), _p(out["status"]), _p(out.get("margin")),
+                    None, 0)
+    lib = load()
+    nbytes = lib.mtp_propose_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_propose_step(C.byref(a), _stream(stream)))
+    ws = _workspace(nbytes, dev, cache, "propose_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_propose_step(C.byref(a), _stream(stream)))
+    out["_keep"] = (warr, ws)
     return out
 
 

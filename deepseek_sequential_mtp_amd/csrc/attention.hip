@@ -371,6 +371,130 @@ hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *
   }
 }
 
+// Attention of one decode step of the retained-module proposer (M7.6 0x09A:
+// the module serves from its own K/V cache; 0x09D: one module rolled out over
+// several draft steps).  One block of four waves per (request, head).  The
+// step's key (after RoPE) and value are read from the QKV activation and
+// written to cache slot pos; the query attends to slots 0..pos.  Each wave
+// keeps an online (max, sum, output) over its share of the slots, four
+// consecutive slots per iteration (chunk c = wave, wave + 4, ...), and the
+// four waves' states are merged through LDS.  Lanes own head-dim elements
+// lane and lane + 64 (head_dim <= 128).  Cache layout per request r:
+// K of slot j at cache[((r * 2 + 0) * L_max + j) * A + h * hd ...], V at
+// cache[((r * 2 + 1) * L_max + j) * A + ...].
+template <typename T>
+__global__ __launch_bounds__(256) void decode_attention_kernel(const T *__restrict__ qkv, T *__restrict__ cache,
+                                                              T *__restrict__ out,
+                                                              const int32_t *__restrict__ pos, int H, int hd,
+                                                              long L_max, float scale_log2) {
+  __shared__ float sm[4], sl[4], so[4][128];
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const long A = (long)H * hd;
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  const int p = pos[r];                      // 0 <= p < L_max (checked before the launch)
+  const T *qrow = qkv + (long)r * 3 * A + (long)h * hd;
+  const T *knew = qrow + A, *vnew = qrow + 2 * A;
+  T *kc = cache + (long)r * 2 * L_max * A + (long)h * hd;
+  T *vc = kc + L_max * A;
+  float q[2], o[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int dd = lane + 64 * i;
+    q[i] = dd < hd ? load_elem(qrow, dd) : 0.f;
+    o[i] = 0.f;
+    if (w == 0 && dd < hd) {
+      store_elem(kc, (long)p * A + dd, load_elem(knew, dd));
+      store_elem(vc, (long)p * A + dd, load_elem(vnew, dd));
+    }
+  }
+  // slot p is read from the activation, slots < p from the cache
+  auto krow = [&](int j) { return j == p ? knew : kc + (long)j * A; };
+  auto vrow = [&](int j) { return j == p ? vnew : vc + (long)j * A; };
+  float m = -INFINITY, l = 0.f;
+  for (int c = w; 4 * c <= p; c += 4) {
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * c + u;
+      float acc = 0.f;
+      if (j <= p) {
+        const T *kr = krow(j);
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+          const int dd = lane + 64 * i;
+          if (dd < hd) acc = fmaf(q[i], load_elem(kr, dd), acc);
+        }
+      }
+      sc[u] = acc;
+    }
+    float cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      sc[u] = 4 * c + u <= p ? warp_sum(sc[u]) * scale_log2 : -INFINITY;
+      cm = fmaxf(cm, sc[u]);
+    }
+    const float mn = fmaxf(m, cm);                       // finite: slot 4c <= p
+    const float corr = exp2f(m - mn);                    // m = -inf: 0
+    l *= corr;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) o[i] *= corr;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = 4 * c + u;
+      if (j > p) break;
+      const float pu = exp2f(sc[u] - mn);
+      l += pu;
+      const T *vr = vrow(j);
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int dd = lane + 64 * i;
+        if (dd < hd) o[i] = fmaf(pu, load_elem(vr, dd), o[i]);
+      }
+    }
+    m = mn;
+  }
+  if (lane == 0) { sm[w] = m; sl[w] = l; }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int dd = lane + 64 * i;
+    if (dd < hd) so[w][dd] = o[i];
+  }
+  __syncthreads();
+  if (w == 0) {
+    float M = sm[0];
+    for (int k = 1; k < 4; ++k) M = fmaxf(M, sm[k]);
+    float L = 0.f, f[4];
+    for (int k = 0; k < 4; ++k) {
+      f[k] = sm[k] == -INFINITY ? 0.f : exp2f(sm[k] - M);   // a wave with no slot contributes 0
+      L += sl[k] * f[k];
+    }
+    const float inv = 1.f / L;                                // slot p is always seen: L >= 1
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int dd = lane + 64 * i;
+      if (dd < hd) {
+        float acc = 0.f;
+        for (int k = 0; k < 4; ++k) acc = fmaf(so[k][dd], f[k], acc);
+        store_elem(out, (long)r * A + (long)h * hd + dd, acc * inv);
+      }
+    }
+  }
+}
+
+template <typename T>
+hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, int hd,
+                                   long L_max, hipStream_t s) {
+  if (hd > 128 || R < 1) return hipErrorInvalidValue;
+  const float scale_log2 = kLog2e / sqrtf((float)hd);
+  hipLaunchKernelGGL((decode_attention_kernel<T>), dim3((unsigned)((long)R * H)), dim3(256), 0, s, qkv, cache, out,
+                     pos, H, hd, L_max, scale_log2);
+  return hipGetLastError();
+}
+template hipError_t launch_decode_attention<bf16_t>(const bf16_t *, bf16_t *, bf16_t *, const int32_t *, int, int,
+                                                    int, long, hipStream_t);
+template hipError_t launch_decode_attention<float>(const float *, float *, float *, const int32_t *, int, int, int,
+                                                   long, hipStream_t);
+
 // RoPE table: table[p][j] = (cos(p w_j), sin(p w_j)), w_j = theta^(-2j/hd),
 // evaluated in double precision, p < max_pos, j < half.
 __global__ void rope_table_kernel(float2 *table, int max_pos, int half, double theta) {
@@ -381,6 +505,25 @@ __global__ void rope_table_kernel(float2 *table, int max_pos, int half, double t
   double sn, cs;
   sincos((double)p * w, &sn, &cs);
   table[i] = make_float2((float)cs, (float)sn);
+}
+
+// Rotary rows of the proposer's requests: table[r][j] = (cos, sin) of
+// pos[r] w_j, as rope_table_kernel computes them.
+__global__ void rope_rows_kernel(float2 *table, const int32_t *__restrict__ pos, int R, int half, double theta) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= (long)R * half) return;
+  const int r = (int)(i / half), j = (int)(i % half);
+  const double w = pow(theta, -2.0 * j / (2.0 * half));
+  double sn, cs;
+  sincos((double)pos[r] * w, &sn, &cs);
+  table[i] = make_float2((float)cs, (float)sn);
+}
+
+hipError_t rope_rows(float2 *table, const int32_t *pos, int R, int half, float theta, hipStream_t s) {
+  const long n = (long)R * half;
+  hipLaunchKernelGGL(rope_rows_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, table, pos, R, half,
+                     (double)theta);
+  return hipGetLastError();
 }
 
 hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s) {

@@ -39,6 +39,9 @@ template <typename T>
 hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, int B, int T_len, int H,
                             int hd, hipStream_t s);
 hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s);
+template <typename T>
+hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, int hd,
+                                   long L_max, hipStream_t s);
 
 // CE reductions
 template <typename T, typename ZT>
@@ -59,6 +62,11 @@ hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int
 
 // verify
 size_t verify_workspace_bytes(int R, int G, int V, int bf16);
+hipError_t launch_propose_prepare(const int32_t *tokens, const int32_t *positions, int R, int V, int L_max,
+                                  int32_t *tok_s, int32_t *pos_s, int32_t *st, int32_t *iota, hipStream_t s);
+hipError_t rope_rows(float2 *table, const int32_t *pos, int R, int half, float theta, hipStream_t s);
+hipError_t launch_propose_finish(const int32_t *st_prep, const int32_t *st_draw, int R, int32_t *tok,
+                                 int32_t *st_out, hipStream_t s);
 hipError_t launch_verify(const void *zt, const void *zd, int bf16, const int32_t *y, const float *ua,
                          const float *us, int R, int G, int V, float tau, int32_t *A, int32_t *tok,
                          int32_t *status, float *margin, double *ws, hipStream_t s);

@@ -609,6 +609,114 @@ size_t verify_bytes(const mtp_verify_args *a) {
   return verify_workspace_bytes(a->R, a->gamma, a->V, a->logits_dtype == MTP_BF16 ? 1 : 0);
 }
 
+int check_propose(const mtp_propose_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->dtype != MTP_F32 && a->dtype != MTP_BF16) return MTP_ERR_DTYPE;
+  if (a->R < 1 || a->L_max < 1 || a->d < 1 || a->n_heads < 1 || a->head_dim < 2 || a->ffn < 1 || a->V < 1)
+    return MTP_ERR_SHAPE;
+  const int E = a->dtype == MTP_BF16 ? 8 : 4;
+  const long A = (long)a->n_heads * a->head_dim;
+  if (a->head_dim % 2 || a->d % E || a->ffn % E || A % E || a->V % E) return MTP_ERR_SHAPE;
+  if (a->L_max > (1 << 20) || a->V >= (1 << 21) || (long)a->V * a->d > (1L << 40)) return MTP_ERR_SHAPE;
+  if (a->R > 65535) return MTP_ERR_UNSUPPORTED;   // requests are a grid dimension of the draw's mass pass
+  if (a->dtype == MTP_BF16 && a->head_dim != 32 && a->head_dim != 64 && a->head_dim != 128)
+    return MTP_ERR_UNSUPPORTED;
+  if (a->dtype == MTP_F32 && a->head_dim != 16 && a->head_dim != 32 && a->head_dim != 64)
+    return MTP_ERR_UNSUPPORTED;
+  if (!(a->eps >= 0.f) || !(a->rope_theta >= 0.f) || !(a->temperature > 0.f) || !isfinite(a->temperature))
+    return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+int check_propose_ptrs(const mtp_propose_args *a) {
+  if (!a->w || !a->embed || !a->W_out || !a->g_out || !a->h_prev || !a->tokens || !a->positions ||
+      !a->u_sample || !a->kv_cache || !a->h_out || !a->logits || !a->draft_token || !a->status)
+    return MTP_ERR_NULL;
+  const mtp_depth_weights &w = a->w[0];
+  if (!w.g_h || !w.g_e || !w.g_attn || !w.g_ffn || !w.M || !w.Wqkv || !w.Wo || !w.Wgate || !w.Wup || !w.Wdown)
+    return MTP_ERR_NULL;
+  if (!all_al16(a->embed, a->W_out, a->g_out, a->h_prev, a->tokens, a->positions, a->u_sample, a->kv_cache,
+                a->h_out, a->logits, a->draft_token, a->status, a->margin, a->workspace) ||
+      !all_al16(w.g_h, w.g_e, w.g_attn, w.g_ffn, w.M, w.Wqkv, w.Wo, w.Wgate, w.Wup, w.Wdown))
+    return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+constexpr int kProposeParts = 18;  // workspace regions of the proposer step
+
+template <typename T>
+size_t propose_layout(const mtp_propose_args *a, Carve &c, void **p) {
+  const long R = a->R;
+  const int d = a->d, f = a->ffn, half = a->head_dim / 2;
+  const long A = (long)a->n_heads * a->head_dim;
+  for (int i = 0; i < 6; ++i) p[i] = c.take<int32_t>(R);  // tokens, positions, status (checked), iota, A, status (draw)
+  p[6] = c.take<float2>(R * half);                          // rotary rows
+  p[7] = c.take<T>(R * 2 * d);                              // c
+  p[8] = c.take<float>(R * d);                              // u (f32)
+  p[9] = c.take<T>(R * d);                                  // x_a
+  p[10] = c.take<T>(R * 3 * A);                             // qkv
+  p[11] = c.take<T>(R * A);                                 // o
+  p[12] = c.take<float>(R * d);                             // a (f32)
+  p[13] = c.take<T>(R * d);                                 // y
+  p[14] = c.take<T>(R * f);                                 // silu(gate) * up
+  p[15] = c.take<T>(R * d);                                 // x_hat
+  p[16] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
+  p[17] = c.take<double>(verify_workspace_bytes(a->R, 0, a->V, sizeof(T) == 2 ? 1 : 0) / sizeof(double) + 1);
+  return c.off;
+}
+
+template <typename T>
+int propose_run(const mtp_propose_args *a, hipStream_t s) {
+  void *p[kProposeParts];
+  Carve c(a->workspace);
+  propose_layout<T>(a, c, p);
+  const int R = a->R, d = a->d, H = a->n_heads, hd = a->head_dim, f = a->ffn, V = a->V;
+  const int A = H * hd;
+  int32_t *tok_s = (int32_t *)p[0], *pos_s = (int32_t *)p[1], *st_prep = (int32_t *)p[2];
+  int32_t *iota = (int32_t *)p[3], *vA = (int32_t *)p[4], *st_draw = (int32_t *)p[5];
+  float2 *rope = (float2 *)p[6];
+  T *cbuf = (T *)p[7], *xa = (T *)p[9], *qkv = (T *)p[10], *o = (T *)p[11], *ybuf = (T *)p[13];
+  T *gsw = (T *)p[14], *xhat = (T *)p[15];
+  float *u = (float *)p[8], *abuf = (float *)p[12];
+  float *skws = sizeof(T) == 2 ? (float *)p[16] : nullptr;
+  double *vws = (double *)p[17];
+  const mtp_depth_weights &w = a->w[0];
+  const T *E = static_cast<const T *>(a->embed);
+  T *h_out = static_cast<T *>(a->h_out);
+  T *logits = static_cast<T *>(a->logits);
+  const bool use_rope = a->rope_theta > 0.f;
+
+  MTP_TRY(launch_propose_prepare(a->tokens, a->positions, R, V, a->L_max, tok_s, pos_s, st_prep, iota, s));
+  if (use_rope) MTP_TRY(rope_rows(rope, pos_s, R, hd / 2, a->rope_theta, s));
+  // one row per request: B = R rows of length 1, the token of the row itself
+  MTP_TRY(launch_dual_norm_concat<T>(static_cast<const T *>(a->h_prev), E, tok_s, w.g_h, w.g_e, cbuf, R, 1, d, V,
+                                     0, a->eps, s));
+  int st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, R, d, 2 * d, 1.f,
+                                          nullptr, 0, skws, s);
+  if (st) return st;
+  MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, R, d, a->eps, s)));
+  st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, iota, use_rope ? rope : nullptr, R, d, A, hd, skws, s);
+  if (st) return st;
+  MTP_TRY(launch_decode_attention<T>(qkv, static_cast<T *>(a->kv_cache), o, pos_s, R, H, hd, a->L_max, s));
+  st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, R, d, A, 1.f, nullptr, 0, skws, s);
+  if (st) return st;
+  MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, R, d, a->eps, s)));
+  st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, R, d, f, skws, s);
+  if (st) return st;
+  st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, R, d, f, 1.f, nullptr, 0, skws,
+                                  s);
+  if (st) return st;
+  MTP_TRY((launch_rmsnorm<T, T>(h_out, a->g_out, xhat, nullptr, R, d, a->eps, s)));
+  st = gemm_nt_store<T, T, float>(xhat, d, (const T *)a->W_out, d, logits, V, nullptr, 0, R, V, d, 1.f, nullptr, 0,
+                                  skws, s);
+  if (st) return st;
+  // the draw: verify's emission pass with no drafts (A = 0: p_0 from the stored logits)
+  MTP_TRY(launch_verify(logits, nullptr, sizeof(T) == 2 ? 1 : 0, nullptr, nullptr, a->u_sample, R, 0, V,
+                        a->temperature, vA, a->draft_token, st_draw, a->margin, vws, s));
+  MTP_TRY(launch_propose_finish(st_prep, st_draw, R, a->draft_token, a->status, s));
+  return MTP_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -700,6 +808,22 @@ int mtp_verify(const mtp_verify_args *a, void *stream) {
                         a->u_accept, a->u_sample, a->R, a->gamma, a->V, a->temperature, a->accepted_len,
                         a->next_token, a->status, a->margin, static_cast<double *>(a->workspace), s));
   return MTP_OK;
+}
+
+size_t mtp_propose_workspace_size(const mtp_propose_args *a) {
+  if (check_propose(a) != MTP_OK) return 0;
+  Carve c(nullptr);
+  void *p[kProposeParts];
+  return a->dtype == MTP_BF16 ? propose_layout<bf16_t>(a, c, p) : propose_layout<float>(a, c, p);
+}
+
+int mtp_propose_step(const mtp_propose_args *a, void *stream) {
+  int st = check_propose(a);
+  if (st) return st;
+  if ((st = check_propose_ptrs(a))) return st;
+  if (!a->workspace || a->workspace_bytes < mtp_propose_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return a->dtype == MTP_BF16 ? propose_run<bf16_t>(a, s) : propose_run<float>(a, s);
 }
 
 }  // extern "C"

@@ -513,4 +513,47 @@ hipError_t launch_verify(const void *zt, const void *zd, int bf16, const int32_t
   return hipGetLastError();
 }
 
+// Proposer step, before any other launch: tokens and positions clamped into
+// range for the kernels (a bad request still runs, on in-range values), the
+// request's status for them, and iota[r] = r (the row index through which
+// the QKV epilogue reads each request's rotary row).
+__global__ void propose_prepare_kernel(const int32_t *__restrict__ tokens, const int32_t *__restrict__ positions,
+                                       int R, int V, int L_max, int32_t *__restrict__ tok_s,
+                                       int32_t *__restrict__ pos_s, int32_t *__restrict__ st,
+                                       int32_t *__restrict__ iota) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  iota[r] = r;
+  const int tk = tokens[r], ps = positions[r];
+  const bool badp = ps < 0 || ps >= L_max;
+  const bool badt = tk < 0 || tk >= V;
+  tok_s[r] = badt ? 0 : tk;
+  pos_s[r] = badp ? 0 : ps;
+  st[r] = badp ? 6 : (badt ? 2 : 0);
+}
+
+// After the draw: a status from the preparation wins over the draw's.
+__global__ void propose_finish_kernel(const int32_t *__restrict__ st_prep, const int32_t *__restrict__ st_draw,
+                                      int R, int32_t *__restrict__ tok, int32_t *__restrict__ st_out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int sp = st_prep[r];
+  const int st = sp != 0 ? sp : st_draw[r];
+  st_out[r] = st;
+  if (st != 0) tok[r] = -1;
+}
+
+hipError_t launch_propose_prepare(const int32_t *tokens, const int32_t *positions, int R, int V, int L_max,
+                                  int32_t *tok_s, int32_t *pos_s, int32_t *st, int32_t *iota, hipStream_t s) {
+  hipLaunchKernelGGL(propose_prepare_kernel, dim3((R + 255) / 256), dim3(256), 0, s, tokens, positions, R, V,
+                     L_max, tok_s, pos_s, st, iota);
+  return hipGetLastError();
+}
+hipError_t launch_propose_finish(const int32_t *st_prep, const int32_t *st_draw, int R, int32_t *tok,
+                                 int32_t *st_out, hipStream_t s) {
+  hipLaunchKernelGGL(propose_finish_kernel, dim3((R + 255) / 256), dim3(256), 0, s, st_prep, st_draw, R, tok,
+                     st_out);
+  return hipGetLastError();
+}
+
 }  // namespace mtp

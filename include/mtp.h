@@ -74,7 +74,8 @@ enum {
   MTP_VERIFY_BAD_TOKEN = 2,        /* a draft token outside [0, V)               */
   MTP_VERIFY_ZERO_DRAFT_PROB = 3,  /* a tested draft token has q = 0             */
   MTP_VERIFY_ZERO_RESIDUAL = 4,    /* rejection with zero residual mass          */
-  MTP_VERIFY_NONFINITE = 5         /* a used logit row has NaN/+inf or is all -inf */
+  MTP_VERIFY_NONFINITE = 5,        /* a used logit row has NaN/+inf or is all -inf */
+  MTP_VERIFY_BAD_POSITION = 6      /* mtp_propose_step: a position outside [0, L_max) */
 };
 
 /* ------------------------------------------------------------------------
@@ -267,15 +268,70 @@ typedef struct {
   size_t workspace_bytes;
 } mtp_verify_args;
 
+/* ------------------------------------------------------------------------
+ * mtp_propose_step: one recurrent draft step of a retained MTP module for R
+ * requests ([M7.6] 0x09: the proposal after the incoming token f is seeded by
+ * the saved parent hidden state and E(f), and y is drawn from the module's
+ * normalised distribution q that verification then uses; 0x09A: a module
+ * served autoregressively keeps its own K/V cache; 0x09D: one module rolled
+ * out for several draft steps feeds back its own output state and the
+ * drafted token).  Per request r, with p = positions[r]:
+ *   the module of mtp_chain_forward on the one row (h_prev[r], E[tokens[r]])
+ *   at RoPE position p, its attention reading the cached keys and values of
+ *   slots 0..p-1 and the row's own, which it writes to slot p;
+ *   h_out[r]  = the module output (stored in dtype);
+ *   logits[r] = W_out RMSNorm_{g_out}(h_out[r]), stored in dtype;
+ *   draft_token[r] = the draw from q = softmax(logits[r] / temperature)
+ *   over the stored logits (the values mtp_verify reads) by inverse CDF with
+ *   u_sample[r]: the smallest t with cdf(t) > u * mass, float64 sums.
+ * A gamma-token rollout calls again with h_prev = h_out, tokens =
+ * draft_token and positions + 1, and hands the stored logits to mtp_verify as
+ * draft_logits.  Slots of drafts that verification rejects are the caller's
+ * to discard (a later step at the same position overwrites them).
+ *
+ * Inputs : h_prev [R, d] and the module's weights (one mtp_depth_weights),
+ *          embed [V, d], W_out [V, d] (dtype), g_out [d] f32;
+ *          tokens int32 [R]; positions int32 [R]; u_sample f32 [R].
+ * In/out : kv_cache [R, 2, L_max, n_heads * head_dim] (dtype): K (after RoPE)
+ *          and V of every slot; slots < p are read, slot p is written.
+ * Outputs: h_out [R, d], logits [R, V] (dtype), draft_token int32 [R],
+ *          status int32 [R] (MTP_VERIFY_BAD_POSITION, _BAD_TOKEN for tokens
+ *          outside [0, V), _BAD_UNIFORM, _NONFINITE for a non-finite logit
+ *          row; on a nonzero status draft_token = -1 and that request's other
+ *          outputs and cache slot are unspecified), margin f32 [R] optional:
+ *          the draw's distance to the nearer CDF step relative to the mass.
+ * Requirements: as mtp_chain_forward for d, n_heads, head_dim, ffn, V and
+ * dtype; 1 <= R <= 65535; 1 <= L_max <= 2^20; temperature > 0 and finite.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int R, L_max, d, n_heads, head_dim, ffn, V;
+  mtp_dtype dtype;
+  float eps, rope_theta, temperature;
+  const mtp_depth_weights *w;        /* [host] one entry                       */
+  const void *embed, *W_out;
+  const float *g_out;
+  const void *h_prev;
+  const int32_t *tokens, *positions;
+  const float *u_sample;
+  void *kv_cache;
+  void *h_out, *logits;
+  int32_t *draft_token, *status;
+  float *margin;                     /* optional                               */
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_propose_args;
+
 int mtp_chain_forward(const mtp_chain_args *a, void *stream);
 int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
 int mtp_verify(const mtp_verify_args *a, void *stream);
+int mtp_propose_step(const mtp_propose_args *a, void *stream);
 
 /* Workspace bytes the call needs for these arguments (pointers are not
  * inspected); 0 if the arguments are invalid. */
 size_t mtp_chain_workspace_size(const mtp_chain_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);
 size_t mtp_verify_workspace_size(const mtp_verify_args *a);
+size_t mtp_propose_workspace_size(const mtp_propose_args *a);
 
 /* ------------------------------------------------------------------------
  * Optional instrumentation.  mtp_profile_stage arms the library to record

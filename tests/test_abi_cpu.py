@@ -26,9 +26,9 @@ def lib():
     return _lib.load()
 
 
-def test_header_declares_the_three_entry_points():
+def test_header_declares_the_entry_points():
     decl = _declared_functions()
-    for name in ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify"):
+    for name in ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step"):
         assert name in decl
     assert set(decl) == set(_lib.EXPORTS)
 
@@ -121,6 +121,31 @@ def test_verify_host_errors(lib):
     # is a multiple of 8, single logits otherwise) and per tile of 256 chunks
     assert lib.mtp_verify_workspace_size(C.byref(args())) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (100 + 1) * 8
     assert lib.mtp_verify_workspace_size(C.byref(args(V=128))) == 4 * 5 * 2 * 8 + 4 * 16 + 4 * (16 + 1) * 8
+
+
+def test_propose_host_errors(lib):
+    def args(**kw):
+        a = _lib.ProposeArgs()
+        a.R, a.L_max, a.d, a.n_heads, a.head_dim, a.ffn, a.V = 4, 32, 64, 4, 16, 172, 512
+        a.dtype, a.eps, a.rope_theta, a.temperature = _lib.MTP_F32, 1e-6, 1e4, 1.0
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    run = lambda a: lib.mtp_propose_step(C.byref(a), None)
+    assert lib.mtp_propose_step(None, None) == -1
+    assert run(args(dtype=5)) == -4
+    assert run(args(R=0)) == -2
+    assert run(args(L_max=0)) == -2
+    assert run(args(L_max=(1 << 20) + 1)) == -2
+    assert run(args(V=510)) == -2
+    assert run(args(head_dim=48)) == -8
+    assert run(args(R=65536)) == -8
+    assert run(args(temperature=0.0)) == -6
+    assert run(args(temperature=float("inf"))) == -6
+    assert run(args()) == -1                      # pointers missing
+    ws = lib.mtp_propose_workspace_size(C.byref(args()))
+    assert ws > 0 and lib.mtp_propose_workspace_size(C.byref(args(R=8))) > ws
+    assert lib.mtp_propose_workspace_size(C.byref(args(R=0))) == 0
 
 
 def test_misaligned_pointers_are_rejected_before_any_launch(lib):
