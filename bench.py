@@ -224,6 +224,54 @@ def stage_table(cfg, stage_ms, per):
     return out
 
 
+def bench_propose(torch, _lib, cfg, inp, R=64, prefix=2048, reps=10):
+    """mtp_propose_step at the workload's module width: R requests, each with
+    ``prefix`` cached slots of the module's own K/V (random bf16; the step
+    reads them all and writes slot ``prefix``), the retained module's weights
+    and the shared head of the chain inputs.  Time from HIP events around the
+    call on its stream; GB/s on the algorithmic HBM bytes of one step: the
+    module and head weights once, the cached keys and values once, the
+    gathered embedding rows, the state in and out, the stored logits written
+    and read once by the draw."""
+    dev = inp["h0"].device
+    A = cfg.n_heads * cfg.head_dim
+    L_max = prefix + 64
+    g = torch.Generator(device=dev).manual_seed(4321)
+    kv = (torch.randn((R, 2, L_max, A), generator=g, device=dev, dtype=torch.float32) * 0.5).to(torch.bfloat16)
+    h = inp["h0"][:R].contiguous()
+    tok = inp["tokens"].reshape(-1)[1:R + 1].clone()          # a fresh (16-byte aligned) buffer
+    pos = torch.full((R,), prefix, dtype=torch.int32, device=dev)
+    us = torch.rand((R,), generator=g, device=dev)
+    w = inp["depths"][0]
+    cache = {}
+    run = lambda out=None: _lib.propose_step(h, tok, pos, us, kv, w, inp["E"], inp["W_out"], inp["g_out"],
+                                             n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps,
+                                             rope_theta=cfg.rope_theta, out=out, cache=cache)
+    out = run()
+    torch.cuda.synchronize()
+    assert int((out["status"] != 0).sum()) == 0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    times = []
+    for _ in range(reps):
+        e0.record()
+        run(out)
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1))
+    ms = float(np.median(times))
+    d, f, V = cfg.d, cfg.ffn, cfg.V
+    weights = (2 * d * d + 4 * A * d + 3 * f * d + V * d) * 2.0
+    kv_bytes = R * prefix * A * 2 * 2.0 + R * A * 2 * 2.0
+    rows = R * d * 2 * 3.0 + R * V * 2 * 2.0
+    total = weights + kv_bytes + rows
+    gbs = total / (ms * 1e-3) / 1e9
+    del kv
+    return {"R": R, "cached_slots": prefix, "d": d, "n_heads": cfg.n_heads, "head_dim": cfg.head_dim,
+            "ffn": f, "V": V, "ms": round(ms, 4), "bytes": total, "bytes_weights": weights,
+            "bytes_kv": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
+            "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
 def bench_verify(torch, _lib, synth, reps=20):
     """mtp_verify on the retained-module verify workload (256 requests,
     V = 129280, gamma = 1..4): kernel time from HIP events around its
@@ -407,6 +455,11 @@ def main():
                   f"({100 * v['frac']:.1f}% of HBM), {v['achieved_full_read']:.0f} GB/s on all rows, "
                   f"mean accepted {v['mean_accepted']}", file=sys.stderr)
 
+    propose = bench_propose(torch, _lib, cfg, inp)
+    if args.stages:
+        print(f"  propose R={propose['R']} cached={propose['cached_slots']}: {propose['ms']:.3f} ms, "
+              f"{propose['achieved']:.0f} GB/s ({100 * propose['frac']:.1f}% of HBM)", file=sys.stderr)
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(cfg, args.cpu_rows)
@@ -439,6 +492,7 @@ def main():
                      "launches_per_step": len(dom_times) // args.steps, "flops_basis": dom_note},
         "stages": stages,
         "verify": verify,
+        "propose": propose,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

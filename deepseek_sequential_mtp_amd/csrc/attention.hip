@@ -373,127 +373,162 @@ hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *
 
 // Attention of one decode step of the retained-module proposer (M7.6 0x09A:
 // the module serves from its own K/V cache; 0x09D: one module rolled out over
-// several draft steps).  One block of four waves per (request, head).  The
-// step's key (after RoPE) and value are read from the QKV activation and
-// written to cache slot pos; the query attends to slots 0..pos.  Each wave
-// keeps an online (max, sum, output) over its share of the slots, four
-// consecutive slots per iteration (chunk c = wave, wave + 4, ...), and the
-// four waves' states are merged through LDS.  Lanes own head-dim elements
-// lane and lane + 64 (head_dim <= 128).  Cache layout per request r:
-// K of slot j at cache[((r * 2 + 0) * L_max + j) * A + h * hd ...], V at
+// several draft steps).  One block of four waves per (request, head); wave w
+// takes a contiguous quarter of the slots 0..pos.  A key row of HD elements
+// is CPK 16-byte chunks: CPK lanes hold one key (lane c holds chunk c of the
+// query), so one load instruction brings G = 64 / CPK keys (1 KB), and U of
+// them are in flight per iteration.  Each lane group keeps its own online
+// (max, sum, output chunk) over the keys it sees; the groups of a wave are
+// merged with lane shuffles and the four waves through LDS.  The step's key
+// (after RoPE) and value are read from the QKV activation for slot pos and
+// copied to that slot of the cache.  Cache layout per request r: K of slot j
+// at cache[((r * 2 + 0) * L_max + j) * A + h * HD ...], V at
 // cache[((r * 2 + 1) * L_max + j) * A + ...].
-template <typename T>
+template <typename T, int HD>
 __global__ __launch_bounds__(256) void decode_attention_kernel(const T *__restrict__ qkv, T *__restrict__ cache,
                                                               T *__restrict__ out,
-                                                              const int32_t *__restrict__ pos, int H, int hd,
-                                                              long L_max, float scale_log2) {
-  __shared__ float sm[4], sl[4], so[4][128];
+                                                              const int32_t *__restrict__ pos, int H, long L_max,
+                                                              float scale_log2) {
+  constexpr int E = 16 / (int)sizeof(T);       // elements per chunk
+  constexpr int CPK = HD / E;                  // lanes (chunks) per key
+  constexpr int G = 64 / CPK;                  // keys per load instruction
+  constexpr int U = 4;                         // load instructions per iteration
+  static_assert(CPK >= 1 && 64 % CPK == 0, "head row of 16-byte chunks");
+  __shared__ float sm[4], sl[4];
+  __shared__ float so[4][HD];
   const int r = blockIdx.x / H, h = blockIdx.x % H;
-  const long A = (long)H * hd;
+  const long A = (long)H * HD;
   const int t = threadIdx.x, lane = t & 63, w = t >> 6;
-  const int p = pos[r];                      // 0 <= p < L_max (checked before the launch)
-  const T *qrow = qkv + (long)r * 3 * A + (long)h * hd;
+  const int c = lane % CPK, g = lane / CPK;
+  const int p = pos[r];                        // 0 <= p < L_max (checked before the launch)
+  const T *qrow = qkv + (long)r * 3 * A + (long)h * HD;
   const T *knew = qrow + A, *vnew = qrow + 2 * A;
-  T *kc = cache + (long)r * 2 * L_max * A + (long)h * hd;
+  T *kc = cache + (long)r * 2 * L_max * A + (long)h * HD;
   T *vc = kc + L_max * A;
-  float q[2], o[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int dd = lane + 64 * i;
-    q[i] = dd < hd ? load_elem(qrow, dd) : 0.f;
-    o[i] = 0.f;
-    if (w == 0 && dd < hd) {
-      store_elem(kc, (long)p * A + dd, load_elem(knew, dd));
-      store_elem(vc, (long)p * A + dd, load_elem(vnew, dd));
-    }
+  if (w == 0 && lane < CPK) {
+    *reinterpret_cast<uint4 *>(kc + (long)p * A + c * E) = *reinterpret_cast<const uint4 *>(knew + c * E);
+    *reinterpret_cast<uint4 *>(vc + (long)p * A + c * E) = *reinterpret_cast<const uint4 *>(vnew + c * E);
   }
-  // slot p is read from the activation, slots < p from the cache
-  auto krow = [&](int j) { return j == p ? knew : kc + (long)j * A; };
-  auto vrow = [&](int j) { return j == p ? vnew : vc + (long)j * A; };
+  float q[E], o[E];
+  chunk_to_f32(*reinterpret_cast<const uint4 *>(qrow + c * E), q, T{});
+#pragma unroll
+  for (int e = 0; e < E; ++e) o[e] = 0.f;
   float m = -INFINITY, l = 0.f;
-  for (int c = w; 4 * c <= p; c += 4) {
-    float sc[4];
+  const int n = p + 1, per = (n + 3) / 4;
+  const int k0 = w * per, k1 = min(n, k0 + per);
+  for (int base = k0; base < k1; base += G * U) {
+    uint4 kr[U], vr[U];
+    bool ok[U];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 4 * c + u;
-      float acc = 0.f;
-      if (j <= p) {
-        const T *kr = krow(j);
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int dd = lane + 64 * i;
-          if (dd < hd) acc = fmaf(q[i], load_elem(kr, dd), acc);
-        }
-      }
-      sc[u] = acc;
+    for (int u = 0; u < U; ++u) {
+      const int key = base + u * G + g;
+      ok[u] = key < k1;
+      const int kk = ok[u] ? key : k0;         // a valid slot of this wave
+      const T *kp = kk == p ? knew : kc + (long)kk * A;
+      const T *vp = kk == p ? vnew : vc + (long)kk * A;
+      kr[u] = *reinterpret_cast<const uint4 *>(kp + c * E);
+      vr[u] = *reinterpret_cast<const uint4 *>(vp + c * E);
     }
+    float sc[U];
     float cm = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      sc[u] = 4 * c + u <= p ? warp_sum(sc[u]) * scale_log2 : -INFINITY;
+    for (int u = 0; u < U; ++u) {
+      float kv[E];
+      chunk_to_f32(kr[u], kv, T{});
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc = fmaf(q[e], kv[e], acc);
+#pragma unroll
+      for (int off = 1; off < CPK; off <<= 1) acc += __shfl_xor(acc, off);
+      sc[u] = ok[u] ? acc * scale_log2 : -INFINITY;
       cm = fmaxf(cm, sc[u]);
     }
-    const float mn = fmaxf(m, cm);                       // finite: slot 4c <= p
-    const float corr = exp2f(m - mn);                    // m = -inf: 0
+    const float mn = fmaxf(m, cm);
+    const float corr = mn == -INFINITY ? 1.f : exp2f(m - mn);   // m = -inf, mn finite: 0
     l *= corr;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) o[i] *= corr;
+    for (int e = 0; e < E; ++e) o[e] *= corr;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 4 * c + u;
-      if (j > p) break;
-      const float pu = exp2f(sc[u] - mn);
+    for (int u = 0; u < U; ++u) {
+      const float pu = ok[u] ? exp2f(sc[u] - mn) : 0.f;
+      float vv[E];
+      chunk_to_f32(vr[u], vv, T{});
       l += pu;
-      const T *vr = vrow(j);
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int dd = lane + 64 * i;
-        if (dd < hd) o[i] = fmaf(pu, load_elem(vr, dd), o[i]);
-      }
+      for (int e = 0; e < E; ++e) o[e] = fmaf(pu, vv[e], o[e]);
     }
     m = mn;
   }
-  if (lane == 0) { sm[w] = m; sl[w] = l; }
+  // merge the lane groups of the wave (same chunk c, different keys)
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int dd = lane + 64 * i;
-    if (dd < hd) so[w][dd] = o[i];
+  for (int off = CPK; off < 64; off <<= 1) {
+    const float m2 = __shfl_xor(m, off), l2 = __shfl_xor(l, off);
+    const float M = fmaxf(m, m2);
+    const float fa = m == -INFINITY ? 0.f : exp2f(m - M);
+    const float fb = m2 == -INFINITY ? 0.f : exp2f(m2 - M);
+    l = l * fa + l2 * fb;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float o2 = __shfl_xor(o[e], off);
+      o[e] = o[e] * fa + o2 * fb;
+    }
+    m = M;
+  }
+  if (lane == 0) { sm[w] = m; sl[w] = l; }
+  if (lane < CPK) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) so[w][c * E + e] = o[e];
   }
   __syncthreads();
-  if (w == 0) {
+  if (w == 0 && lane < CPK) {
     float M = sm[0];
     for (int k = 1; k < 4; ++k) M = fmaxf(M, sm[k]);
-    float L = 0.f, f[4];
+    float f[4], L = 0.f;
     for (int k = 0; k < 4; ++k) {
-      f[k] = sm[k] == -INFINITY ? 0.f : exp2f(sm[k] - M);   // a wave with no slot contributes 0
+      f[k] = sm[k] == -INFINITY ? 0.f : exp2f(sm[k] - M);      // a wave with no slot contributes 0
       L += sl[k] * f[k];
     }
-    const float inv = 1.f / L;                                // slot p is always seen: L >= 1
+    const float inv = 1.f / L;                                  // the maximal slot gives L >= 1
+    float v[E];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int dd = lane + 64 * i;
-      if (dd < hd) {
-        float acc = 0.f;
-        for (int k = 0; k < 4; ++k) acc = fmaf(so[k][dd], f[k], acc);
-        store_elem(out, (long)r * A + (long)h * hd + dd, acc * inv);
-      }
+    for (int e = 0; e < E; ++e) {
+      float acc = 0.f;
+      for (int k = 0; k < 4; ++k) acc = fmaf(so[k][c * E + e], f[k], acc);
+      v[e] = acc * inv;
     }
+    *reinterpret_cast<uint4 *>(out + (long)r * A + (long)h * HD + c * E) = f32_to_chunk(v, T{});
   }
 }
 
-template <typename T>
-hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, int hd,
-                                   long L_max, hipStream_t s) {
-  if (hd > 128 || R < 1) return hipErrorInvalidValue;
-  const float scale_log2 = kLog2e / sqrtf((float)hd);
-  hipLaunchKernelGGL((decode_attention_kernel<T>), dim3((unsigned)((long)R * H)), dim3(256), 0, s, qkv, cache, out,
-                     pos, H, hd, L_max, scale_log2);
+template <typename T, int HD>
+hipError_t decode_launch(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, long L_max,
+                         hipStream_t s) {
+  const float scale_log2 = kLog2e / sqrtf((float)HD);
+  hipLaunchKernelGGL((decode_attention_kernel<T, HD>), dim3((unsigned)((long)R * H)), dim3(256), 0, s, qkv, cache,
+                     out, pos, H, L_max, scale_log2);
   return hipGetLastError();
 }
-template hipError_t launch_decode_attention<bf16_t>(const bf16_t *, bf16_t *, bf16_t *, const int32_t *, int, int,
-                                                    int, long, hipStream_t);
-template hipError_t launch_decode_attention<float>(const float *, float *, float *, const int32_t *, int, int, int,
-                                                   long, hipStream_t);
+
+template <>
+hipError_t launch_decode_attention<bf16_t>(const bf16_t *qkv, bf16_t *cache, bf16_t *out, const int32_t *pos, int R,
+                                           int H, int hd, long L_max, hipStream_t s) {
+  switch (hd) {
+    case 32: return decode_launch<bf16_t, 32>(qkv, cache, out, pos, R, H, L_max, s);
+    case 64: return decode_launch<bf16_t, 64>(qkv, cache, out, pos, R, H, L_max, s);
+    case 128: return decode_launch<bf16_t, 128>(qkv, cache, out, pos, R, H, L_max, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+template <>
+hipError_t launch_decode_attention<float>(const float *qkv, float *cache, float *out, const int32_t *pos, int R,
+                                          int H, int hd, long L_max, hipStream_t s) {
+  switch (hd) {
+    case 16: return decode_launch<float, 16>(qkv, cache, out, pos, R, H, L_max, s);
+    case 32: return decode_launch<float, 32>(qkv, cache, out, pos, R, H, L_max, s);
+    case 64: return decode_launch<float, 64>(qkv, cache, out, pos, R, H, L_max, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 // RoPE table: table[p][j] = (cos(p w_j), sin(p w_j)), w_j = theta^(-2j/hd),
 // evaluated in double precision, p < max_pos, j < half.
