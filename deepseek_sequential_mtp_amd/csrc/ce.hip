@@ -210,6 +210,29 @@ hipError_t launch_ce_finalize(const double *acc_sum, const int32_t *acc_cnt, int
   return hipGetLastError();
 }
 
+// out[i] = sum over s of part[s * n + i] (+ res[i]): the partial products of
+// a GEMM split over K, summed in split order, with the residual of the
+// product's epilogue.
+template <typename TO>
+__global__ __launch_bounds__(256) void splitk_sum_kernel(const float *__restrict__ part, int splits, long n,
+                                                         const float *__restrict__ res, TO *__restrict__ out) {
+  for (long i = (long)blockIdx.x * 256 + threadIdx.x; i < n; i += (long)gridDim.x * 256) {
+    float v = res != nullptr ? res[i] : 0.f;
+    float acc = 0.f;
+    for (int sp = 0; sp < splits; ++sp) acc += part[(long)sp * n + i];
+    store_elem(out, i, acc + v);
+  }
+}
+template <typename TO>
+hipError_t launch_splitk_sum(const float *part, int splits, long n, const float *res, TO *out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const long blocks = (n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096;
+  hipLaunchKernelGGL((splitk_sum_kernel<TO>), dim3((unsigned)blocks), dim3(256), 0, s, part, splits, n, res, out);
+  return hipGetLastError();
+}
+template hipError_t launch_splitk_sum<float>(const float *, int, long, const float *, float *, hipStream_t);
+template hipError_t launch_splitk_sum<bf16_t>(const float *, int, long, const float *, bf16_t *, hipStream_t);
+
 __global__ void fill_i32_kernel(int32_t *p, long n, int32_t v) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;

@@ -48,6 +48,8 @@ template <typename T, typename ZT>
 hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
                         const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,
                         hipStream_t s);
+template <typename TO>
+hipError_t launch_splitk_sum(const float *part, int splits, long n, const float *res, TO *out, hipStream_t s);
 hipError_t launch_ce_combine(const float2 *part, int nt, const float *target, const int32_t *labels,
                              float *lse, float *lse_out, float *row_loss, float *rowmax, int32_t *pred, int V,
                              int N, hipStream_t s);

@@ -642,7 +642,34 @@ int check_propose_ptrs(const mtp_propose_args *a) {
   return MTP_OK;
 }
 
-constexpr int kProposeParts = 18;  // workspace regions of the proposer step
+// K splits of a GEMM with few rows (the proposer's R requests) and N = d:
+// enough blocks to stream the weights with most compute units, at least 8 K
+// slices of 32 per split.
+constexpr int kMaxSplits = 16;
+inline int few_row_splits(int M, int N, int K) {
+  const long tiles = (long)ceil_div(M, Small::BM) * ceil_div(N, Small::BN);
+  long sp = 512 / (tiles > 0 ? tiles : 1);
+  const long by_k = K / (32 * 8);
+  sp = sp < by_k ? sp : by_k;
+  sp = sp < kMaxSplits ? sp : kMaxSplits;
+  return sp < 1 ? 1 : (int)sp;
+}
+
+// C = A B^T (+ res) for few rows: K-split partial products into part, then
+// summed with the residual into out.
+template <typename T, typename TO>
+int gemm_few_rows(const T *A, long lda, const T *Bm, long ldb, float *part, TO *out, const float *res, int M, int N,
+                  int K, hipStream_t s) {
+  const int sp = few_row_splits(M, N, K);
+  EpiStore<float, float> epi{part, (long)N, M, N, 1.f, nullptr, nullptr, 0, 0, (long)M * N};
+  PA<T, Small> la{A, lda, M, K};
+  KB<T, Small> lb{Bm, ldb, N, K};
+  MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, N, K, 8, sp, s)));
+  MTP_TRY(launch_splitk_sum<TO>(part, sp, (long)M * N, res, out, s));
+  return MTP_OK;
+}
+
+constexpr int kProposeParts = 19;  // workspace regions of the proposer step
 
 template <typename T>
 size_t propose_layout(const mtp_propose_args *a, Carve &c, void **p) {
@@ -662,6 +689,7 @@ size_t propose_layout(const mtp_propose_args *a, Carve &c, void **p) {
   p[15] = c.take<T>(R * d);                                 // x_hat
   p[16] = c.take<float>(sizeof(T) == 2 ? tail_ws_bytes<Big>() / 4 : 0);  // partial tiles of split tail GEMM tiles
   p[17] = c.take<double>(verify_workspace_bytes(a->R, 0, a->V, sizeof(T) == 2 ? 1 : 0) / sizeof(double) + 1);
+  p[18] = c.take<float>((size_t)kMaxSplits * R * d);      // K-split partial products (N = d GEMMs)
   return c.off;
 }
 
@@ -691,20 +719,19 @@ int propose_run(const mtp_propose_args *a, hipStream_t s) {
   // one row per request: B = R rows of length 1, the token of the row itself
   MTP_TRY(launch_dual_norm_concat<T>(static_cast<const T *>(a->h_prev), E, tok_s, w.g_h, w.g_e, cbuf, R, 1, d, V,
                                      0, a->eps, s));
-  int st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, R, d, 2 * d, 1.f,
-                                          nullptr, 0, skws, s);
+  float *part = (float *)p[18];
+  int st = gemm_few_rows<T, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, part, u, nullptr, R, d, 2 * d, s);
   if (st) return st;
   MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, R, d, a->eps, s)));
   st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, iota, use_rope ? rope : nullptr, R, d, A, hd, skws, s);
   if (st) return st;
   MTP_TRY(launch_decode_attention<T>(qkv, static_cast<T *>(a->kv_cache), o, pos_s, R, H, hd, a->L_max, s));
-  st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, R, d, A, 1.f, nullptr, 0, skws, s);
+  st = gemm_few_rows<T, float>(o, A, (const T *)w.Wo, A, part, abuf, u, R, d, A, s);
   if (st) return st;
   MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, R, d, a->eps, s)));
   st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, R, d, f, skws, s);
   if (st) return st;
-  st = gemm_nt_store<T, T, float>(gsw, f, (const T *)w.Wdown, f, h_out, d, abuf, d, R, d, f, 1.f, nullptr, 0, skws,
-                                  s);
+  st = gemm_few_rows<T, T>(gsw, f, (const T *)w.Wdown, f, part, h_out, abuf, R, d, f, s);
   if (st) return st;
   MTP_TRY((launch_rmsnorm<T, T>(h_out, a->g_out, xhat, nullptr, R, d, a->eps, s)));
   st = gemm_nt_store<T, T, float>(xhat, d, (const T *)a->W_out, d, logits, V, nullptr, 0, R, V, d, 1.f, nullptr, 0,
