@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=2048)
     ap.add_argument("--stages", action="store_true", help="print the per-stage time table to stderr")
+    ap.add_argument("--propose-only", action="store_true",
+                    help="time only the retained-module proposer step and print its JSON object")
     ap.add_argument("--accuracy", action="store_true",
                     help="also compute the top-1 accuracy by depth in every step (printed to stderr)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -338,6 +340,9 @@ def main():
     print(f"[bench] workload {cfg.name}: B={cfg.B} T={cfg.T} d={cfg.d} H={cfg.n_heads}x{cfg.head_dim} "
           f"ffn={cfg.ffn} V={cfg.V} D={cfg.D}", file=sys.stderr, flush=True)
     inp = device_inputs(cfg, torch)
+    if args.propose_only:
+        print(json.dumps(bench_propose(torch, _lib, cfg, inp)), flush=True)
+        return
     dev = inp["h0"].device
     D, N = cfg.D, cfg.N
     chain_out = dict(h=[torch.empty_like(inp["h0"]) for _ in range(D)],
