@@ -26,10 +26,10 @@ from tests.gpu_util import bf16_ulp, chain_tensors, compare, tdev, to_np
 pytestmark = pytest.mark.gpu
 
 
-def _setup(dtype, seed=0, R=3, P=24, L_max=64):
+def _setup(dtype, seed=0, R=3, P=24, L_max=64, hd=128):
     if dtype == "bf16":
-        cfg = synth.scaled(synth.D1, name="prop_bf16", B=R, T=P + 8, d=256, n_heads=2, head_dim=128, ffn=704,
-                           V=1024, D=1, seg_lo=P + 8, seg_hi=P + 8, sigma_w=0.05)
+        cfg = synth.scaled(synth.D1, name=f"prop_bf16_hd{hd}", B=R, T=P + 8, d=256, n_heads=256 // hd,
+                           head_dim=hd, ffn=704, V=1024, D=1, seg_lo=P + 8, seg_hi=P + 8, sigma_w=0.05)
     else:
         cfg = synth.scaled(synth.TINY, name="prop_f32", B=R, T=P + 8, D=1, seg_lo=P + 8, seg_hi=P + 8)
     inp = synth.make_chain_inputs(cfg, seed)
@@ -75,9 +75,9 @@ def _check_step(cfg, out, ref_h, ref_z, us, tau, model, tag):
     return err_h, err_z, exact
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_prefill_by_decode_then_rollout(dtype):
-    cfg, inp, t, cache, model = _setup(dtype)
+@pytest.mark.parametrize("dtype,hd", [("f32", 16), ("bf16", 128), ("bf16", 64), ("bf16", 32)])
+def test_prefill_by_decode_then_rollout(dtype, hd):
+    cfg, inp, t, cache, model = _setup(dtype, hd=hd)
     R, P, G = cfg.B, 24, 3
     w = inp["depths"][0]
     wt = t["depths"][0]
@@ -106,6 +106,20 @@ def test_prefill_by_decode_then_rollout(dtype):
         eh, ez, _ = _check_step(cfg, out, ref_h, ref_z, us, tau, model, f"prefill slot {s}")
         worst = [max(worst[0], eh), max(worst[1], ez)]
     print(f"  prefill: max |h err| {worst[0]:.3e}, max |logit err| {worst[1]:.3e}", flush=True)
+
+    # one launch with the requests at different slots (each rewrites its slot
+    # with the same teacher-forced row, so the cache is unchanged)
+    sl = np.array([P - 1, 5, 0][:R] + [3] * max(0, R - 3), np.int32)
+    us = rng.random(R).astype(np.float32)
+    hsel = torch.stack([h0_dev[r, sl[r]] for r in range(R)]).contiguous()
+    out = _lib.propose_step(hsel, tdev(np.array([toks[r, sl[r] + 1] for r in range(R)], np.int32), torch.int32),
+                            tdev(sl, torch.int32), tdev(us, torch.float32), cache, wt, t["E"], t["W_out"],
+                            t["g_out"], n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps,
+                            rope_theta=cfg.rope_theta, temperature=tau, cache=wcache)
+    torch.cuda.synchronize()
+    ref_h = np.stack([ref[r][sl[r]] for r in range(R)])
+    ref_z = np.stack([propose.head_logits(ref_h[r], inp["W_out"], inp["g_out"], cfg.eps, model) for r in range(R)])
+    _check_step(cfg, out, ref_h, ref_z, us, tau, model, f"slots {sl.tolist()}")
 
     # rollout from slot P: seed = (h0_P, x_(P+1)); the oracle's draws set the token path
     us_roll = rng.random((G, R)).astype(np.float32)
