@@ -1,7 +1,8 @@
 /*
  * mtp.h -- C ABI of the MI355X (gfx950) library for the teacher-forced
  * sequential multi-token-prediction (MTP) depth chain, its shared-head masked
- * cross-entropy (forward and backward) and draft verification.
+ * cross-entropy (forward and backward, with top-1 accuracy by depth), draft
+ * verification, and one recurrent draft step of a retained module.
  *
  * Sources (web pages; cited by title and section):
  *   [M7.6] "M7.6 - DeepSeek MTP: Sequential Modules, Teacher Forcing, and
