@@ -118,7 +118,7 @@ def _ce_case(cfg, n_rows, seed=0):
     W = tdev(inp["W_out"], torch.bfloat16)
     g = tdev(inp["g_out"], torch.float32)
     lab_t = tdev(labels.reshape(cfg.D, cfg.B, cfg.T).astype(np.int32), torch.int32)
-    res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, want_lse=True)
+    res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, want_lse=True, want_accuracy=True)
     torch.cuda.synchronize()
     del hs, W
     print(f"[full-ce] {cfg.name}: oracle on {n_rows} labelled rows per depth", flush=True)
@@ -147,6 +147,22 @@ def _ce_case(cfg, n_rows, seed=0):
     rf = rel_fro(dg, ref["dg_out"])
     print(f"  dg relF {rf:.2e}", flush=True)
     assert compare(dg, ref["dg_out"], 2e-2)[2] and rf < 1e-2
+    # top-1 accuracy by depth: the argmax of every sampled row equals the
+    # oracle's, or is a near-tie of the oracle's logits (within 1e-3)
+    pred = to_np(res["pred"]).reshape(cfg.D, -1).astype(np.int64)
+    correct = to_np(res["correct"]).astype(np.int64)
+    for k in range(cfg.D):
+        m = labels[k] >= 0
+        assert np.all(pred[k, ~m] == -1)
+        assert correct[k] == int((pred[k, m] == labels[k, m]).sum())
+        diff = np.nonzero(m & (pred[k] != ref["pred"][k]))[0]
+        if diff.size:
+            xh, _, _ = ohead.output_norm(np.asarray(inp["h"][k])[diff], inp["g_out"], cfg.eps, BF16)
+            W64 = np.asarray(inp["W_out"], np.float64)
+            gap = (np.einsum("nd,nd->n", xh, W64[ref["pred"][k, diff]]) -
+                   np.einsum("nd,nd->n", xh, W64[pred[k, diff]]))
+            assert np.all(gap <= 1e-3), gap
+        print(f"  accuracy[{k}] {float(to_np(res['accuracy'])[k]):.4f}, {diff.size} near-tie rows", flush=True)
 
 
 @pytest.mark.timeout(600)
