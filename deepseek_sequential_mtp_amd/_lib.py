@@ -19,7 +19,7 @@ MTP_REDUCE_FIXED, MTP_REDUCE_VALID_MEAN = 0, 1
 STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEPTH",
           -4: "MTP_ERR_DTYPE", -5: "MTP_ERR_WORKSPACE", -6: "MTP_ERR_ARG", -7: "MTP_ERR_HIP",
           -8: "MTP_ERR_UNSUPPORTED"}
-EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step",
+EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step", "mtp_round_commit",
            "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
            "mtp_profile_count")
@@ -78,6 +78,13 @@ class ProposeArgs(C.Structure):
                 ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
+class RoundArgs(C.Structure):
+    _fields_ = [("R", C.c_int), ("gamma", C.c_int), ("eos", C.c_int), ("draft_tokens", vp),
+                ("accepted_len", vp), ("next_token", vp), ("status", vp), ("remaining", vp),
+                ("new_tokens", vp), ("n_new", vp), ("rows_to_keep", vp), ("pending_frontier", vp),
+                ("stopped", vp)]
+
+
 _lib = None
 
 
@@ -93,6 +100,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
         lib.mtp_verify.argtypes = [C.POINTER(VerifyArgs), vp]
         lib.mtp_propose_step.argtypes = [C.POINTER(ProposeArgs), vp]
+        lib.mtp_round_commit.argtypes = [C.POINTER(RoundArgs), vp]
         lib.mtp_propose_workspace_size.argtypes = [C.POINTER(ProposeArgs)]
         lib.mtp_propose_workspace_size.restype = C.c_size_t
         lib.mtp_chain_workspace_size.argtypes = [C.POINTER(ChainArgs)]
@@ -303,6 +311,25 @@ def propose_step(h_prev: torch.Tensor, tokens: torch.Tensor, positions: torch.Te
     a.workspace, a.workspace_bytes = _p(ws), ws.numel()
     _check(lib.mtp_propose_step(C.byref(a), _stream(stream)))
     out["_keep"] = (warr, ws)
+    return out
+
+
+def round_commit(draft_tokens: torch.Tensor, accepted_len: torch.Tensor, next_token: torch.Tensor,
+                 status: torch.Tensor, remaining: torch.Tensor, *, eos: int = -1, out: Optional[Dict] = None,
+                 stream=None) -> Dict:
+    """mtp_round_commit.  draft_tokens int32 [R, gamma]; accepted_len, next_token, status,
+    remaining int32 [R].  Returns dict(new_tokens [R, gamma+1], n_new, rows_to_keep,
+    pending_frontier, stopped)."""
+    R, G = draft_tokens.shape
+    dev = draft_tokens.device
+    if out is None:
+        out = dict(new_tokens=torch.empty((R, G + 1), dtype=torch.int32, device=dev),
+                   **{k: torch.empty(R, dtype=torch.int32, device=dev)
+                      for k in ("n_new", "rows_to_keep", "pending_frontier", "stopped")})
+    a = RoundArgs(R, G, eos, _p(draft_tokens), _p(accepted_len), _p(next_token), _p(status), _p(remaining),
+                  _p(out["new_tokens"]), _p(out["n_new"]), _p(out["rows_to_keep"]), _p(out["pending_frontier"]),
+                  _p(out["stopped"]))
+    _check(load().mtp_round_commit(C.byref(a), _stream(stream)))
     return out
 
 

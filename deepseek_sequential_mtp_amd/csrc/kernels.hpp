@@ -67,6 +67,9 @@ size_t verify_workspace_bytes(int R, int G, int V, int bf16);
 hipError_t launch_propose_prepare(const int32_t *tokens, const int32_t *positions, int R, int V, int L_max,
                                   int32_t *tok_s, int32_t *pos_s, int32_t *st, int32_t *iota, hipStream_t s);
 hipError_t rope_rows(float2 *table, const int32_t *pos, int R, int half, float theta, hipStream_t s);
+hipError_t launch_round_commit(int R, int G, int eos, const int32_t *drafts, const int32_t *A, const int32_t *tok,
+                               const int32_t *st, const int32_t *rem, int32_t *out_tok, int32_t *n_new,
+                               int32_t *keep, int32_t *pending, int32_t *stopped, hipStream_t s);
 hipError_t launch_propose_finish(const int32_t *st_prep, const int32_t *st_draw, int R, int32_t *tok,
                                  int32_t *st_out, hipStream_t s);
 hipError_t launch_verify(const void *zt, const void *zd, int bf16, const int32_t *y, const float *ua,

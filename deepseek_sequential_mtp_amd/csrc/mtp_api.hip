@@ -837,6 +837,21 @@ int mtp_verify(const mtp_verify_args *a, void *stream) {
   return MTP_OK;
 }
 
+int mtp_round_commit(const mtp_round_args *a, void *stream) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->R < 1 || a->gamma < 1 || (long)a->R * (a->gamma + 1) > (1L << 31) - 1) return MTP_ERR_SHAPE;
+  if (!a->draft_tokens || !a->accepted_len || !a->next_token || !a->status || !a->remaining || !a->new_tokens ||
+      !a->n_new || !a->rows_to_keep || !a->pending_frontier || !a->stopped)
+    return MTP_ERR_NULL;
+  if (!all_al16(a->draft_tokens, a->accepted_len, a->next_token, a->status, a->remaining, a->new_tokens, a->n_new,
+                a->rows_to_keep, a->pending_frontier, a->stopped))
+    return MTP_ERR_ARG;
+  MTP_TRY(launch_round_commit(a->R, a->gamma, a->eos, a->draft_tokens, a->accepted_len, a->next_token, a->status,
+                              a->remaining, a->new_tokens, a->n_new, a->rows_to_keep, a->pending_frontier,
+                              a->stopped, static_cast<hipStream_t>(stream)));
+  return MTP_OK;
+}
+
 size_t mtp_propose_workspace_size(const mtp_propose_args *a) {
   if (check_propose(a) != MTP_OK) return 0;
   Carve c(nullptr);

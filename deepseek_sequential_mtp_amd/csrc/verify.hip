@@ -543,6 +543,47 @@ __global__ void propose_finish_kernel(const int32_t *__restrict__ st_prep, const
   if (st != 0) tok[r] = -1;
 }
 
+// Round bookkeeping, one thread per request (the rules are in mtp.h).
+__global__ void round_commit_kernel(int R, int G, int eos, const int32_t *__restrict__ drafts,
+                                    const int32_t *__restrict__ A_in, const int32_t *__restrict__ tok_in,
+                                    const int32_t *__restrict__ st_in, const int32_t *__restrict__ rem_in,
+                                    int32_t *__restrict__ out_tok, int32_t *__restrict__ n_new,
+                                    int32_t *__restrict__ keep, int32_t *__restrict__ pending,
+                                    int32_t *__restrict__ stopped) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r >= R) return;
+  const int A = A_in[r], rem = rem_in[r], t = tok_in[r];
+  int32_t *o = out_tok + (long)r * (G + 1);
+  int n = 0, pend = -1, stop = 1, kp = 0;
+  if (st_in[r] == 0 && rem >= 1 && A >= 0 && A <= G) {
+    kp = A + 1;
+    stop = 0;
+    for (int j = 0; j < A && !stop; ++j) {
+      const int y = drafts[(long)r * G + j];
+      o[n++] = y;
+      stop = (n == rem || (eos >= 0 && y == eos)) ? 1 : 0;
+    }
+    if (!stop) {
+      o[n++] = t;
+      pend = t;
+      stop = (n == rem || (eos >= 0 && t == eos)) ? 1 : 0;
+    }
+  }
+  for (int j = n; j <= G; ++j) o[j] = -1;
+  n_new[r] = n;
+  keep[r] = kp;
+  pending[r] = pend;
+  stopped[r] = stop;
+}
+
+hipError_t launch_round_commit(int R, int G, int eos, const int32_t *drafts, const int32_t *A, const int32_t *tok,
+                               const int32_t *st, const int32_t *rem, int32_t *out_tok, int32_t *n_new,
+                               int32_t *keep, int32_t *pending, int32_t *stopped, hipStream_t s) {
+  hipLaunchKernelGGL(round_commit_kernel, dim3((R + 255) / 256), dim3(256), 0, s, R, G, eos, drafts, A, tok, st,
+                     rem, out_tok, n_new, keep, pending, stopped);
+  return hipGetLastError();
+}
+
 hipError_t launch_propose_prepare(const int32_t *tokens, const int32_t *positions, int R, int V, int L_max,
                                   int32_t *tok_s, int32_t *pos_s, int32_t *st, int32_t *iota, hipStream_t s) {
   hipLaunchKernelGGL(propose_prepare_kernel, dim3((R + 255) / 256), dim3(256), 0, s, tokens, positions, R, V,

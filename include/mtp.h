@@ -322,10 +322,40 @@ typedef struct {
   size_t workspace_bytes;
 } mtp_propose_args;
 
+/* ------------------------------------------------------------------------
+ * mtp_round_commit: the bookkeeping of one carried-frontier round per request
+ * ([M7.6] 0x09: the selector's new tokens, target rows to keep, pending
+ * frontier and stop flag, with its EOS and budget truncation; 0x09C: only
+ * verified rows are committed; generalised to gamma drafts by [SPEC]).
+ * Per request, from mtp_verify's outputs: the accepted drafts
+ * y_0 .. y_(A-1) are emitted in order, then next_token (the correction, or
+ * the bonus when A = gamma); emission stops once `remaining` tokens are out
+ * or right after an emitted EOS, so an accepted EOS or a last-budget draft
+ * gets no bonus.  rows_to_keep = A + 1 (the incoming frontier's target row
+ * and the accepted drafts' rows); pending_frontier = next_token when it was
+ * emitted (it has no target row yet), else -1; stopped = the budget is used
+ * up or the last emitted token is EOS.  A request with a nonzero status,
+ * remaining < 1 or A outside [0, gamma] emits nothing: n_new = 0,
+ * rows_to_keep = 0, pending_frontier = -1, stopped = 1.
+ * Inputs : draft_tokens int32 [R, gamma]; accepted_len, next_token, status
+ *          int32 [R] (as written by mtp_verify); remaining int32 [R]; eos
+ *          (a token id, or -1 for none).
+ * Outputs: new_tokens int32 [R, gamma + 1] (the emitted tokens, then -1),
+ *          n_new, rows_to_keep, pending_frontier, stopped int32 [R].
+ * No workspace.  Requirements: R >= 1, gamma >= 1,
+ * R * (gamma + 1) < 2^31.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  int R, gamma, eos;
+  const int32_t *draft_tokens, *accepted_len, *next_token, *status, *remaining;
+  int32_t *new_tokens, *n_new, *rows_to_keep, *pending_frontier, *stopped;
+} mtp_round_args;
+
 int mtp_chain_forward(const mtp_chain_args *a, void *stream);
 int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
 int mtp_verify(const mtp_verify_args *a, void *stream);
 int mtp_propose_step(const mtp_propose_args *a, void *stream);
+int mtp_round_commit(const mtp_round_args *a, void *stream);
 
 /* Workspace bytes the call needs for these arguments (pointers are not
  * inspected); 0 if the arguments are invalid. */

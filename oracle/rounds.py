@@ -12,8 +12,10 @@ Generalised to gamma drafts with the speculative-decoding explainer page's
 round: the accepted drafts y_0 .. y_(A-1) come first, then the correction or
 bonus token t.
 
-Reading for a verification error (status != 0, where the page raises): the
-request emits nothing, keeps no row, has no pending frontier and stops.
+Reading for a verification error (status != 0), for no output slot left
+(remaining < 1) and for an accepted count outside [0, gamma] (where the page
+raises): the request emits nothing, keeps no row, has no pending frontier and
+stops.
 
 Pins (tests/test_oracle_rounds.py): the selector's branches at gamma = 1
 written out from the page (accept with bonus, accept at the last budget slot,
@@ -30,7 +32,7 @@ def commit(drafts: Sequence[int], A: int, token: int, status: int, remaining: in
     """One request.  drafts: the gamma draft tokens; A: accepted count;
     token: the correction (A < gamma) or bonus (A == gamma); remaining: new
     output slots available (>= 1); eos: the EOS id, -1 for none."""
-    if status != 0:
+    if status != 0 or remaining < 1 or not (0 <= A <= len(drafts)):
         return dict(new_tokens=[], keep=0, pending=-1, stopped=1)
     out = []
     stopped = False

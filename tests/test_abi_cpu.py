@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     decl = _declared_functions()
-    for name in ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step"):
+    for name in ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step",
+                 "mtp_round_commit"):
         assert name in decl
     assert set(decl) == set(_lib.EXPORTS)
 
@@ -146,6 +147,25 @@ def test_propose_host_errors(lib):
     ws = lib.mtp_propose_workspace_size(C.byref(args()))
     assert ws > 0 and lib.mtp_propose_workspace_size(C.byref(args(R=8))) > ws
     assert lib.mtp_propose_workspace_size(C.byref(args(R=0))) == 0
+
+
+def test_round_commit_host_errors(lib):
+    run = lambda a: lib.mtp_round_commit(C.byref(a), None)
+    assert lib.mtp_round_commit(None, None) == -1
+    a = _lib.RoundArgs()
+    a.R, a.gamma, a.eos = 4, 0, -1
+    assert run(a) == -2
+    a.gamma, a.R = 4, 0
+    assert run(a) == -2
+    a.R = 4
+    assert run(a) == -1                          # pointers missing
+    fake = 0x7f0000001000
+    names = ("draft_tokens", "accepted_len", "next_token", "status", "remaining", "new_tokens", "n_new",
+             "rows_to_keep", "pending_frontier", "stopped")
+    for i, n in enumerate(names):
+        setattr(a, n, fake + 0x1000 * i)
+    a.stopped = fake + 0x1000 * 9 + 4            # misaligned: rejected before any launch
+    assert run(a) == -6
 
 
 def test_misaligned_pointers_are_rejected_before_any_launch(lib):

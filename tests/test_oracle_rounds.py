@@ -20,8 +20,9 @@ def test_one_proposal_branches():
     assert commit([7], 0, 2, 0, remaining=5, eos=2)["stopped"] == 1
     # bonus EOS: emitted and stops
     assert commit([7], 1, 2, 0, remaining=5, eos=2) == dict(new_tokens=[7, 2], keep=2, pending=2, stopped=1)
-    # verification error: nothing emitted
-    assert commit([7], 0, -1, 3, remaining=5) == dict(new_tokens=[], keep=0, pending=-1, stopped=1)
+    # verification error, no slot left, an impossible A: nothing emitted
+    for args in (([7], 0, -1, 3, 5), ([7], 1, 9, 0, 0), ([7], 2, 9, 0, 5), ([7], -1, 9, 0, 5)):
+        assert commit(*args) == dict(new_tokens=[], keep=0, pending=-1, stopped=1)
 
 
 def test_invariants_at_gamma_drafts():
