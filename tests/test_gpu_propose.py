@@ -75,9 +75,13 @@ def _check_step(cfg, out, ref_h, ref_z, us, tau, model, tag):
     return err_h, err_z, exact
 
 
-@pytest.mark.parametrize("dtype,hd", [("f32", 16), ("bf16", 128), ("bf16", 64), ("bf16", 32)])
-def test_prefill_by_decode_then_rollout(dtype, hd):
+@pytest.mark.parametrize("dtype,hd,tau,theta", [("f32", 16, 1.0, None), ("bf16", 128, 1.0, None),
+                                              ("bf16", 64, 1.0, None), ("bf16", 32, 1.0, None),
+                                              ("f32", 16, 0.7, 0.0), ("bf16", 128, 1.6, 0.0)])
+def test_prefill_by_decode_then_rollout(dtype, hd, tau, theta):
     cfg, inp, t, cache, model = _setup(dtype, hd=hd)
+    if theta is not None:                 # RoPE off
+        cfg = synth.scaled(cfg, rope_theta=theta)
     R, P, G = cfg.B, 24, 3
     w = inp["depths"][0]
     wt = t["depths"][0]
@@ -85,8 +89,7 @@ def test_prefill_by_decode_then_rollout(dtype, hd):
     h0 = inp["h0"].reshape(R, cfg.T, cfg.d)
     h0_dev = t["h0"].reshape(R, cfg.T, cfg.d)
     rng = np.random.default_rng(7)
-    tau = 1.0
-    print(f"[propose] {cfg.name} R={R} P={P} gamma={G} d={cfg.d} H={cfg.n_heads}x{cfg.head_dim} V={cfg.V}",
+    print(f"[propose] {cfg.name} tau={tau} theta={cfg.rope_theta} R={R} P={P} gamma={G} d={cfg.d} H={cfg.n_heads}x{cfg.head_dim} V={cfg.V}",
           flush=True)
     # oracle rows of every request over slots 0..P-1 (teacher-forced inputs)
     ref = [propose.module_rows(h0[r, :P], toks[r, 1:P + 1], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps,
