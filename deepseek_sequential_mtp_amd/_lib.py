@@ -56,7 +56,7 @@ class CeArgs(C.Structure):
                 ("g_out", vp), ("loss_sum", vp), ("counts", vp), ("loss", vp), ("loss_mtp", vp),
                 ("lse", vp), ("dh", C.POINTER(vp)), ("dW_out", vp), ("dg_out", vp),
                 ("accumulate", C.c_int), ("device_error", vp), ("logit_slab_bytes", C.c_size_t),
-                ("pred", vp), ("correct", vp), ("accuracy", vp),
+                ("dh_accumulate", C.c_int), ("pred", vp), ("correct", vp), ("accuracy", vp),
                 ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
@@ -202,7 +202,8 @@ def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Ten
 def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: torch.Tensor,
                     g_out: torch.Tensor, *, lam: float, eps: float = 1e-6, reduce: str = "fixed",
                     denom: float = 0.0, accumulate: bool = False, want_lse: bool = False,
-                    want_accuracy: bool = False, logit_slab_bytes: int = 0, out: Optional[Dict] = None,
+                    want_accuracy: bool = False, dh_accumulate: bool = False, logit_slab_bytes: int = 0,
+                    out: Optional[Dict] = None,
                     cache: Optional[Dict] = None, stream=None) -> Dict:
     """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].  logit_slab_bytes
     bounds the fp32 logit slab and the dz row group (0: the library default).
@@ -233,7 +234,7 @@ def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: tor
                _p(W_out), _p(g_out), _p(out["loss_sum"]), _p(out["counts"]), _p(out["loss"]),
                _p(out["loss_mtp"]), _p(out["lse"]), dhp, _p(out["dW_out"]), _p(out["dg_out"]),
                1 if accumulate else 0, _p(out["device_error"]), int(logit_slab_bytes),
-               _p(out.get("pred")), _p(out.get("correct")), _p(out.get("accuracy")), None, 0)
+               1 if dh_accumulate else 0, _p(out.get("pred")), _p(out.get("correct")), _p(out.get("accuracy")), None, 0)
     lib = load()
     nbytes = lib.mtp_ce_workspace_size(C.byref(a))
     if nbytes == 0:

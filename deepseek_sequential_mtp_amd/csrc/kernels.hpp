@@ -30,7 +30,7 @@ hipError_t launch_out_norm(const T *h, const float *g, T *xhat, float *r, const 
 template <typename T>
 hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *h, const float *r,
                                const float *g, float *dh, float *dg_part, float *dg, int accumulate,
-                               int N, int d, hipStream_t s);
+                               int N, int d, int dh_acc, hipStream_t s);
 // Row blocks of the output-norm backward (8 rows each); one dg partial row per block.
 inline int dg_row_blocks(int N) { int b = (N + 7) / 8; return b < 1 ? 1 : b; }
 

@@ -587,7 +587,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
     {
       MTP_STAGE(MTP_STAGE_CE_NORM_BWD);
       MTP_TRY(launch_out_norm_bwd<T>(dxs, m.splits, sstride, h, r, a->g_out, static_cast<float *>(a->dh[k]),
-                                     dg_part, a->dg_out, dw_acc0, N, d, s));
+                                     dg_part, a->dg_out, dw_acc0, N, d, a->dh_accumulate ? 1 : 0, s));
     }
   }
   MTP_TRY(launch_ce_finalize(acc_sum, acc_cnt, D, valid_mean, denom, a->lambda, a->loss_sum, a->counts, a->loss,

@@ -114,7 +114,7 @@ __global__ __launch_bounds__(kNormThreads) void out_norm_kernel(
 template <typename T>
 __global__ __launch_bounds__(kNormThreads) void out_norm_bwd_kernel(
     const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h,
-    const float *__restrict__ r, const float *__restrict__ g, float *__restrict__ dh, int d) {
+    const float *__restrict__ r, const float *__restrict__ g, float *__restrict__ dh, int d, int dh_acc) {
   __shared__ float sh[kNormThreads / 64];
   const long n = blockIdx.x;
   const float rn = r[n];
@@ -130,7 +130,8 @@ __global__ __launch_bounds__(kNormThreads) void out_norm_bwd_kernel(
     float v = 0.f;
     for (int s = 0; s < splits; ++s) v += dx[s * slab + n * d + j];
     const float xn = rn * load_elem(hr, j);
-    dh[n * d + j] = rn * (g[j] * v - xn * mean);
+    const float o = rn * (g[j] * v - xn * mean);
+    dh[n * d + j] = dh_acc ? dh[n * d + j] + o : o;
   }
 }
 
@@ -151,7 +152,7 @@ template <typename T, int CPT>
 __global__ __launch_bounds__(kNormThreads) void out_norm_bwd_rows_kernel(
     const float *__restrict__ dx, int splits, long slab, const T *__restrict__ h, const float *__restrict__ r,
     const float *__restrict__ g, float *__restrict__ dh, float *__restrict__ part, int N, int d,
-    int rows_per_block) {
+    int rows_per_block, int dh_acc) {
   __shared__ float sh[kNormThreads / 64];
   const int t = threadIdx.x;
   const int nch = d >> 2;
@@ -188,9 +189,14 @@ __global__ __launch_bounds__(kNormThreads) void out_norm_bwd_rows_kernel(
     for (int i = 0; i < CPT; ++i) {
       const int c = t + i * kNormThreads;
       if (c < nch) {
-        reinterpret_cast<float4 *>(dh + (long)n * d)[c] =
-            make_float4(rn * (gg[i].x * v[i].x - x[i].x * mean), rn * (gg[i].y * v[i].y - x[i].y * mean),
-                        rn * (gg[i].z * v[i].z - x[i].z * mean), rn * (gg[i].w * v[i].w - x[i].w * mean));
+        float4 o = make_float4(rn * (gg[i].x * v[i].x - x[i].x * mean), rn * (gg[i].y * v[i].y - x[i].y * mean),
+                               rn * (gg[i].z * v[i].z - x[i].z * mean), rn * (gg[i].w * v[i].w - x[i].w * mean));
+        float4 *dp = reinterpret_cast<float4 *>(dh + (long)n * d) + c;
+        if (dh_acc) {
+          const float4 prev = *dp;
+          o.x += prev.x; o.y += prev.y; o.z += prev.z; o.w += prev.w;
+        }
+        *dp = o;
         dg[i].x += v[i].x * x[i].x;
         dg[i].y += v[i].y * x[i].y;
         dg[i].z += v[i].z * x[i].z;
@@ -280,14 +286,14 @@ hipError_t launch_out_norm(const T *h, const float *g, T *xhat, float *r, const 
 template <typename T>
 hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *h, const float *r,
                                const float *g, float *dh, float *dg_part, float *dg, int accumulate,
-                               int N, int d, hipStream_t s) {
+                               int N, int d, int dh_acc, hipStream_t s) {
   const int nrb = dg_row_blocks(N);
   const int rpb = (N + nrb - 1) / nrb;
   const int cpt = (d / 4 + kNormThreads - 1) / kNormThreads;
   if (cpt <= 8) {
     auto go = [&](auto kern) {
       hipLaunchKernelGGL(kern, dim3(nrb), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g, dh, dg_part, N, d,
-                         rpb);
+                         rpb, dh_acc);
     };
     if (cpt <= 1) go(out_norm_bwd_rows_kernel<T, 1>);
     else if (cpt <= 2) go(out_norm_bwd_rows_kernel<T, 2>);
@@ -295,7 +301,7 @@ hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *
     else go(out_norm_bwd_rows_kernel<T, 8>);
   } else {
     hipLaunchKernelGGL(out_norm_bwd_kernel<T>, dim3(N), dim3(kNormThreads), 0, s, dx, splits, slab, h, r, g,
-                       dh, d);
+                       dh, d, dh_acc);
     hipLaunchKernelGGL(dg_partial_kernel<T>, dim3(nrb, (d + 63) / 64), dim3(kNormThreads), 0, s, dx, splits,
                        slab, h, r, dg_part, N, d, rpb);
   }
@@ -312,7 +318,7 @@ hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *
                                          int32_t *, int32_t *, long, int, int, float, hipStream_t);       \
   template hipError_t launch_out_norm_bwd<T>(const float *, int, long, const T *, const float *,          \
                                              const float *, float *, float *, float *, int, int, int,     \
-                                             hipStream_t);
+                                             int, hipStream_t);
 MTP_NORM_INST(bf16_t)
 MTP_NORM_INST(float)
 template hipError_t launch_rmsnorm<bf16_t, bf16_t>(const bf16_t *, const float *, bf16_t *, float *, long,

@@ -177,7 +177,10 @@ typedef struct {
  *          lse f32 [D, B*T] (optional, may be NULL: log-sum-exp of every
  *          row's logits; unlabelled rows included);
  *          dh [host] D pointers, each f32 [B*T, d] = dL_MTP/dh^(k) through the
- *          head (written, not accumulated; 0 on unlabelled rows);
+ *          head (0 on unlabelled rows); written, or added to the existing
+ *          values with dh_accumulate = 1 (D pointers to one buffer then sum
+ *          the depths' gradients: the trunk gradient of independent
+ *          horizons that all read one hidden state, [M7.4] 0x02, 0x06A);
  *          dW_out f32 [V, d] and dg_out f32 [d]: the depths' contributions
  *          summed; accumulate = 1 adds them to the existing values (e.g. the
  *          main loss's), 0 overwrites;
@@ -216,6 +219,7 @@ typedef struct {
   int accumulate;
   int32_t *device_error;             /* optional                               */
   size_t logit_slab_bytes;           /* 0 = 1 GiB                              */
+  int dh_accumulate;                 /* 1: add into dh[k]                      */
   int32_t *pred;                     /* optional                               */
   int32_t *correct;                  /* optional                               */
   float *accuracy;                   /* optional                               */

@@ -1,0 +1,56 @@
+"""GPU parity of independent prediction horizons on one trunk state
+(oracle/horizons.py): mtp_head_ce_fwd_bwd with the K horizons as its depths,
+every depth pointing at the same hidden state, the horizon labels, and
+dh_accumulate = 1 so that the K gradients sum into one trunk gradient.  The
+head runs horizon by horizon, forward and backward, never holding more than
+a slab of logits (M7.4 0x06A).  Tolerances as the head CE tests."""
+import numpy as np
+import pytest
+import torch
+
+from deepseek_sequential_mtp_amd import _lib, synth
+from oracle import horizons
+from oracle.numerics import BF16, EXACT
+from tests.gpu_util import compare, rel_fro, tdev, to_np
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("dtype,K,slab_rows", [("f32", 2, 0), ("bf16", 3, 0), ("bf16", 4, 128)])
+def test_independent_horizons_on_one_trunk_state(dtype, K, slab_rows):
+    if dtype == "f32":
+        cfg = synth.TINY
+    else:
+        cfg = synth.scaled(synth.D1, name="horizons", B=2, T=300, d=256, V=1000, D=1, seg_lo=20, seg_hi=200,
+                           sigma_w=0.05)
+    inp = synth.make_head_inputs(cfg, 2)
+    h = inp["h"][0]
+    labels = horizons.horizon_labels(inp["tokens"], inp["segment_ids"], K)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    model = BF16 if dtype == "bf16" else EXACT
+    h_dev = tdev(h, tdt)
+    dh = torch.zeros((cfg.N, cfg.d), device="cuda")
+    out = dict(loss_sum=torch.empty(K, device="cuda"), counts=torch.empty(K, dtype=torch.int32, device="cuda"),
+               loss=torch.empty(K, device="cuda"), loss_mtp=torch.empty(1, device="cuda"), lse=None,
+               dh=[dh] * K, dW_out=torch.empty((cfg.V, cfg.d), device="cuda"),
+               dg_out=torch.empty((cfg.d,), device="cuda"),
+               device_error=torch.empty(1, dtype=torch.int32, device="cuda"))
+    print(f"[horizons] {cfg.name} {dtype} K={K} N={cfg.N} d={cfg.d} V={cfg.V} labelled="
+          f"{(labels >= 0).sum(axis=1).tolist()}", flush=True)
+    res = _lib.head_ce_fwd_bwd([h_dev] * K, tdev(labels.reshape(K, cfg.B, cfg.T).astype(np.int32), torch.int32),
+                               tdev(inp["W_out"], tdt), tdev(inp["g_out"], torch.float32), lam=cfg.lam,
+                               eps=cfg.eps, dh_accumulate=True, out=out, logit_slab_bytes=slab_rows * cfg.V * 4)
+    torch.cuda.synchronize()
+    ref = horizons.independent_heads(h, inp["tokens"], inp["segment_ids"], K, inp["W_out"], inp["g_out"],
+                                     cfg.eps, cfg.lam, model)
+    f32 = dtype == "f32"
+    np.testing.assert_array_equal(to_np(res["counts"]), ref["counts"])
+    np.testing.assert_allclose(to_np(res["loss"]), ref["loss"], rtol=1e-5 if f32 else 2e-3)
+    np.testing.assert_allclose(to_np(res["loss_mtp"])[0], ref["loss_mtp"], rtol=1e-5 if f32 else 2e-3)
+    gate = 1e-4 if f32 else 1e-2
+    for name, got, want in (("dh_trunk", to_np(dh), ref["dh_trunk"]), ("dW", to_np(res["dW_out"]), ref["dW_out"]),
+                            ("dg", to_np(res["dg_out"]), ref["dg_out"])):
+        err, _, ok = compare(got, want, 2e-2)
+        rf = rel_fro(got, want)
+        print(f"  {name} max|err| {err:.3e} relF {rf:.2e}", flush=True)
+        assert ok and rf < gate, name
