@@ -8,8 +8,10 @@ label may be missing; a missing predecessor is an error).
 
 Two forms:
 
-* ``compile_mtp_rows`` -- the compact packed-stream compiler of M7.6 0x04C,
-  written from its stated semantics, with the same error conditions;
+* ``compile_mtp_rows`` -- compact rows of one packed stream (M7.6 0x04C),
+  written from the rules stated there (a state needs its whole teacher-forced
+  chain inside one document occurrence; a label is optional; a missing
+  predecessor is an error) over the end of each position's occurrence;
 * ``dense_rows`` -- the same sets on the dense [B, T] layout.  A *run* is a
   maximal stretch of one non-negative segment id inside a batch row; padding
   (id < 0) belongs to no run.  For position i in run [r0, r1]:
@@ -29,58 +31,61 @@ from typing import Dict, List, Sequence, Tuple
 import numpy as np
 
 
+def _occurrence_ends(segment_ids: Sequence[int], valid: Sequence[bool]) -> List[int]:
+    """For every position j, the last position of the stretch of available
+    inputs that continues j's document occurrence (j itself when the next
+    position is unavailable or belongs to another segment); -1 where j is not
+    available.  Built by one sweep from the end of the stream."""
+    n = len(segment_ids)
+    ends = [-1] * n
+    for j in range(n - 1, -1, -1):
+        if not valid[j]:
+            continue
+        continues = j + 1 < n and valid[j + 1] and segment_ids[j + 1] == segment_ids[j]
+        ends[j] = ends[j + 1] if continues else j
+    return ends
+
+
 def compile_mtp_rows(tokens: Sequence[int], segment_ids: Sequence[int],
                      valid: Sequence[bool], depth: int,
                      previous_bases: Sequence[int]) -> List[Dict[str, object]]:
-    """Compact row compiler for one packed stream (M7.6 0x04C).
+    """Compact rows of one packed stream at depth ``depth`` (M7.6 0x04C).
 
-    For each base position (ascending) whose teacher-forced chain
-    base..base+depth lies inside the stream, is all valid and all carries the
-    base's segment id, emit a state row.  Its label index is base+depth+1 when
-    that position exists, is valid and has the same segment id; otherwise the
-    row is a state-only row (loss_valid False).  ``previous_bases`` lists the
-    base of every row of the previous depth's tensor in physical row order.
+    The rules: base b is a state row iff every teacher-forced input b..b+depth
+    is available and in b's document occurrence, i.e. b + depth does not pass
+    the end of b's occurrence; it carries a loss iff its label position
+    b + depth + 1 is inside the occurrence too, else it is kept state-only.
+    The row reads the previous depth's output at the physical row whose base
+    is b (``previous_bases`` lists the base of every previous-depth row in
+    row order); a state row without such a row is an error, as are misaligned
+    inputs, a depth below one and invalid or repeated previous bases.
+    Rows come out in ascending base order.
     """
+    if type(depth) is not int or depth < 1:
+        raise ValueError("depth must be positive (an int >= 1)")
     n = len(tokens)
     if len(segment_ids) != n or len(valid) != n:
-        raise ValueError("unaligned packed inputs")
-    if type(depth) is not int or depth < 1:
-        raise ValueError("depth must be positive")
-    for b in previous_bases:
-        if type(b) is not int or b < 0 or b >= n:
-            raise ValueError("invalid previous base")
-    if len(set(previous_bases)) != len(previous_bases):
-        raise ValueError("duplicate previous base")
-    row_of_base = {}
+        raise ValueError("tokens, segment ids and validity flags are unaligned")
+    prev_row: Dict[int, int] = {}
     for r, b in enumerate(previous_bases):
-        row_of_base[b] = r
+        if type(b) is not int or not 0 <= b < n:
+            raise ValueError(f"invalid previous base {b!r}")
+        if b in prev_row:
+            raise ValueError(f"duplicate previous base {b}")
+        prev_row[b] = r
 
+    ends = _occurrence_ends(segment_ids, valid)
     out: List[Dict[str, object]] = []
-    for base in range(n):
-        teacher = base + depth
-        if teacher >= n:
-            continue
-        sid = segment_ids[base]
-        chain_ok = True
-        for j in range(base, teacher + 1):
-            if not valid[j] or segment_ids[j] != sid:
-                chain_ok = False
-                break
-        if not chain_ok:
-            continue
-        if base not in row_of_base:
-            raise ValueError("required predecessor state is missing")
-        lab = teacher + 1
-        has_label = lab < n and bool(valid[lab]) and segment_ids[lab] == sid
-        out.append({
-            "base": base,
-            "previous_depth_row": row_of_base[base],
-            "shifted_token_index": teacher,
-            "label_index": lab if has_label else None,
-            "loss_valid": bool(has_label),
-            "position": base,
-            "segment": sid,
-        })
+    for b, end in enumerate(ends):
+        if end < 0 or b + depth > end:
+            continue                      # no complete teacher-forced chain from b
+        if b not in prev_row:
+            raise ValueError(f"required predecessor state is missing for base {b}")
+        has_label = b + depth + 1 <= end
+        out.append(dict(base=b, previous_depth_row=prev_row[b],
+                        shifted_token_index=b + depth,
+                        label_index=b + depth + 1 if has_label else None,
+                        loss_valid=has_label, position=b, segment=segment_ids[b]))
     return out
 
 
