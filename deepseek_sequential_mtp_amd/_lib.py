@@ -46,7 +46,7 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 3     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 4     # the struct layouts below mirror include/mtp.h at this version
 
 
 class CeArgs(C.Structure):

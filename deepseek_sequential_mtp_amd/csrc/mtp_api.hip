@@ -725,7 +725,7 @@ int propose_run(const mtp_propose_args *a, hipStream_t s) {
   MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, R, d, a->eps, s)));
   st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, iota, use_rope ? rope : nullptr, R, d, A, hd, skws, s);
   if (st) return st;
-  MTP_TRY(launch_decode_attention<T>(qkv, static_cast<T *>(a->kv_cache), o, pos_s, R, H, hd, a->L_max, s));
+  MTP_TRY(launch_decode_attention<T>(qkv, static_cast<T *>(a->kv_cache), o, pos_s, st_prep, R, H, hd, a->L_max, s));
   st = gemm_few_rows<T, float>(o, A, (const T *)w.Wo, A, part, abuf, u, R, d, A, s);
   if (st) return st;
   MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, R, d, a->eps, s)));
@@ -748,7 +748,7 @@ int propose_run(const mtp_propose_args *a, hipStream_t s) {
 
 extern "C" {
 
-int mtp_abi_version(void) { return 3; }
+int mtp_abi_version(void) { return MTP_ABI_VERSION; }
 
 int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n) {
   if (stage < 0) {

@@ -303,7 +303,9 @@ typedef struct {
  *          status int32 [R] (MTP_VERIFY_BAD_POSITION, _BAD_TOKEN for tokens
  *          outside [0, V), _BAD_UNIFORM, _NONFINITE for a non-finite logit
  *          row; on a nonzero status draft_token = -1 and that request's other
- *          outputs and cache slot are unspecified), margin f32 [R] optional:
+ *          outputs are unspecified; a request rejected before the step
+ *          (bad position or token) leaves its kv_cache untouched), margin
+ *          f32 [R] optional:
  *          the draw's distance to the nearer CDF step relative to the mass.
  * Requirements: as mtp_chain_forward for d, n_heads, head_dim, ffn, V and
  * dtype; 1 <= R <= 65535; 1 <= L_max <= 2^20; temperature > 0 and finite.
@@ -391,7 +393,11 @@ int mtp_profile_count(void);
 /* Static string naming a status code. */
 const char *mtp_strerror(int status);
 
-/* ABI version of this header (incremented on incompatible changes). */
+/* ABI version of this header, incremented on every incompatible change (a
+ * struct field added, moved or retyped, a call's meaning changed).  A
+ * binding that mirrors the argument structs must refuse a library whose
+ * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
+#define MTP_ABI_VERSION 4
 int mtp_abi_version(void);
 
 #ifdef __cplusplus

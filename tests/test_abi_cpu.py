@@ -26,6 +26,12 @@ def lib():
     return _lib.load()
 
 
+def _header_abi_version():
+    m = re.search(r"#define\s+MTP_ABI_VERSION\s+(\d+)", open(HEADER).read())
+    assert m, "MTP_ABI_VERSION missing from the header"
+    return int(m.group(1))
+
+
 def test_header_declares_the_entry_points():
     decl = _declared_functions()
     for name in ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step",
@@ -37,7 +43,7 @@ def test_header_declares_the_entry_points():
 def test_every_declared_symbol_is_exported(lib):
     for name in _declared_functions():
         assert hasattr(lib, name), name
-    assert lib.mtp_abi_version() == _lib.ABI_VERSION == 3
+    assert lib.mtp_abi_version() == _lib.ABI_VERSION == _header_abi_version()
     assert lib.mtp_strerror(0) == b"ok"
     assert lib.mtp_strerror(-3) == b"depth must be positive"
 
@@ -211,3 +217,45 @@ def test_misaligned_pointers_are_rejected_before_any_launch(lib):
         assert runc(cargs(n)) == -6, n
     hs[1] = fake + 0x100000 + 4
     assert runc(cargs()) == -6
+
+
+def _c_name(field):
+    return "lambda" if field == "lambda_" else field
+
+
+@pytest.mark.skipif(__import__("shutil").which("gcc") is None, reason="gcc not available")
+def test_ctypes_struct_layouts_match_the_header(tmp_path):
+    """Every ctypes mirror of an argument struct has the header's field
+    offsets and size: a C program compiled against include/mtp.h prints
+    offsetof/sizeof for each field the binding declares."""
+    structs = {name: cls for name, cls in vars(_lib).items()
+               if isinstance(cls, type) and issubclass(cls, C.Structure) and cls is not C.Structure}
+    c_types = {"DepthWeights": "mtp_depth_weights", "ChainArgs": "mtp_chain_args", "CeArgs": "mtp_ce_args",
+               "VerifyArgs": "mtp_verify_args", "ProposeArgs": "mtp_propose_args",
+               "RoundArgs": "mtp_round_args"}
+    for name in structs:
+        assert name in c_types or name in getattr(_lib, "C_STRUCT_NAMES", {}), f"unmapped struct {name}"
+    c_types.update(getattr(_lib, "C_STRUCT_NAMES", {}))
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"', "int main(void) {"]
+    for name, cls in structs.items():
+        ct = c_types[name]
+        lines.append(f'  printf("{name} sizeof %zu\\n", sizeof({ct}));')
+        for f, _ in cls._fields_:
+            lines.append(f'  printf("{name} {f} %zu\\n", offsetof({ct}, {_c_name(f)}));')
+        # the header has no field the binding lacks: the last field ends the struct
+    lines.append("  return 0;\n}")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.run(["gcc", "-std=c11", "-Wall", "-Werror", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout.split("\n")
+    got = {}
+    for line in out:
+        if line:
+            s, f, v = line.split()
+            got[(s, f)] = int(v)
+    for name, cls in structs.items():
+        assert got[(name, "sizeof")] == C.sizeof(cls), name
+        for f, _ in cls._fields_:
+            assert got[(name, f)] == getattr(cls, f).offset, (name, f)
