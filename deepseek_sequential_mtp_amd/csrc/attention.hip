@@ -387,7 +387,8 @@ hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *
 template <typename T, int HD>
 __global__ __launch_bounds__(256) void decode_attention_kernel(const T *__restrict__ qkv, T *__restrict__ cache,
                                                               T *__restrict__ out,
-                                                              const int32_t *__restrict__ pos, int H, long L_max,
+                                                              const int32_t *__restrict__ pos,
+                                                              const int32_t *__restrict__ skip, int H, long L_max,
                                                               float scale_log2) {
   constexpr int E = 16 / (int)sizeof(T);       // elements per chunk
   constexpr int CPK = HD / E;                  // lanes (chunks) per key
@@ -405,7 +406,8 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const T *__restri
   const T *knew = qrow + A, *vnew = qrow + 2 * A;
   T *kc = cache + (long)r * 2 * L_max * A + (long)h * HD;
   T *vc = kc + L_max * A;
-  if (w == 0 && lane < CPK) {
+  // a request flagged in skip (a rejected position or token) leaves its cache untouched
+  if (w == 0 && lane < CPK && (skip == nullptr || skip[r] == 0)) {
     *reinterpret_cast<uint4 *>(kc + (long)p * A + c * E) = *reinterpret_cast<const uint4 *>(knew + c * E);
     *reinterpret_cast<uint4 *>(vc + (long)p * A + c * E) = *reinterpret_cast<const uint4 *>(vnew + c * E);
   }
@@ -501,31 +503,31 @@ __global__ __launch_bounds__(256) void decode_attention_kernel(const T *__restri
 }
 
 template <typename T, int HD>
-hipError_t decode_launch(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, long L_max,
-                         hipStream_t s) {
+hipError_t decode_launch(const T *qkv, T *cache, T *out, const int32_t *pos, const int32_t *skip, int R, int H,
+                         long L_max, hipStream_t s) {
   const float scale_log2 = kLog2e / sqrtf((float)HD);
   hipLaunchKernelGGL((decode_attention_kernel<T, HD>), dim3((unsigned)((long)R * H)), dim3(256), 0, s, qkv, cache,
-                     out, pos, H, L_max, scale_log2);
+                     out, pos, skip, H, L_max, scale_log2);
   return hipGetLastError();
 }
 
 template <>
-hipError_t launch_decode_attention<bf16_t>(const bf16_t *qkv, bf16_t *cache, bf16_t *out, const int32_t *pos, int R,
-                                           int H, int hd, long L_max, hipStream_t s) {
+hipError_t launch_decode_attention<bf16_t>(const bf16_t *qkv, bf16_t *cache, bf16_t *out, const int32_t *pos,
+                                           const int32_t *skip, int R, int H, int hd, long L_max, hipStream_t s) {
   switch (hd) {
-    case 32: return decode_launch<bf16_t, 32>(qkv, cache, out, pos, R, H, L_max, s);
-    case 64: return decode_launch<bf16_t, 64>(qkv, cache, out, pos, R, H, L_max, s);
-    case 128: return decode_launch<bf16_t, 128>(qkv, cache, out, pos, R, H, L_max, s);
+    case 32: return decode_launch<bf16_t, 32>(qkv, cache, out, pos, skip, R, H, L_max, s);
+    case 64: return decode_launch<bf16_t, 64>(qkv, cache, out, pos, skip, R, H, L_max, s);
+    case 128: return decode_launch<bf16_t, 128>(qkv, cache, out, pos, skip, R, H, L_max, s);
     default: return hipErrorInvalidValue;
   }
 }
 template <>
-hipError_t launch_decode_attention<float>(const float *qkv, float *cache, float *out, const int32_t *pos, int R,
-                                          int H, int hd, long L_max, hipStream_t s) {
+hipError_t launch_decode_attention<float>(const float *qkv, float *cache, float *out, const int32_t *pos,
+                                          const int32_t *skip, int R, int H, int hd, long L_max, hipStream_t s) {
   switch (hd) {
-    case 16: return decode_launch<float, 16>(qkv, cache, out, pos, R, H, L_max, s);
-    case 32: return decode_launch<float, 32>(qkv, cache, out, pos, R, H, L_max, s);
-    case 64: return decode_launch<float, 64>(qkv, cache, out, pos, R, H, L_max, s);
+    case 16: return decode_launch<float, 16>(qkv, cache, out, pos, skip, R, H, L_max, s);
+    case 32: return decode_launch<float, 32>(qkv, cache, out, pos, skip, R, H, L_max, s);
+    case 64: return decode_launch<float, 64>(qkv, cache, out, pos, skip, R, H, L_max, s);
     default: return hipErrorInvalidValue;
   }
 }

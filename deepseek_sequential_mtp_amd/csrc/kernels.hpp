@@ -40,8 +40,9 @@ hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, int 
                             int hd, hipStream_t s);
 hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s);
 template <typename T>
-hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t *pos, int R, int H, int hd,
-                                   long L_max, hipStream_t s);
+// skip (may be NULL): requests with skip[r] != 0 do not write their cache slot
+hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t *pos, const int32_t *skip, int R,
+                                   int H, int hd, long L_max, hipStream_t s);
 
 // CE reductions
 template <typename T, typename ZT>

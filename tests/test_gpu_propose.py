@@ -154,6 +154,10 @@ def test_statuses_per_request():
     R = cfg.B
     wt = t["depths"][0]
     h = t["h0"].reshape(R, cfg.T, cfg.d)[:, 0].contiguous()
+    # a recognisable cache: requests rejected before the step must leave it as it is
+    cache.copy_(torch.randn(cache.shape, generator=torch.Generator(device=cache.device).manual_seed(5),
+                            device=cache.device).to(cache.dtype))
+    before = cache.clone()
     toks = np.array([1, cfg.V, 3, 4, -1], np.int32)           # request 1 and 4: bad token
     pos = np.array([0, 0, 16, 0, 0], np.int32)               # request 2: position = L_max
     us = np.array([0.5, 0.5, 0.5, 1.0, 0.5], np.float32)     # request 3: u = 1
@@ -165,3 +169,9 @@ def test_statuses_per_request():
     tok = to_np(out["draft_token"])
     np.testing.assert_array_equal(st, [0, 2, 6, 1, 2])
     assert tok[0] >= 0 and np.all(tok[1:] == -1)
+    # rejected before the step (bad token, bad position): no slot written, slot 0 included
+    for r in (1, 2, 4):
+        assert torch.equal(cache[r], before[r]), r
+    # accepted requests wrote exactly their own slot
+    changed = (cache[0] != before[0]).reshape(2, 16, -1).any(dim=2)
+    assert changed[:, 0].all() and not changed[:, 1:].any()
