@@ -1,9 +1,9 @@
 """GPU parity of mtp_chain_forward against the oracle: masks, labels and
 counts bit-exact; h^(k) on state rows within tolerance (float32: 1e-4
-max-abs; bf16: 2e-2 max-abs with 4k bf16 ulps of the reference admitted at
-depth k -- rounding flips at the block's bf16 stores, amplified by attention
-and SwiGLU and inherited by the next depth; both: relative Frobenius error
-below 4e-3 k)."""
+max-abs and relative Frobenius error below 4e-3 k; bf16: max-abs 2e-2 or
+one bf16 ulp of the larger magnitude, no element beyond 4e-2, at most 0.2%
+of a depth's elements over 2e-2 and 0.05% beyond one ulp and 2e-2 (none at
+depth 1), relative Frobenius error below 2.5e-3 k -- ``tests.gpu_util.compare_h``)."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +11,7 @@ import torch
 from deepseek_sequential_mtp_amd import _lib, synth
 from oracle import chain as ochain, rows as orows
 from oracle.numerics import BF16, EXACT
-from tests.gpu_util import chain_tensors, compare, rel_fro, to_np
+from tests.gpu_util import chain_tensors, compare, compare_h, fmt_h, rel_fro, to_np
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,12 @@ def _check(cfg, inp, out, model, atol):
         rows_k = st[k].reshape(-1).astype(bool)
         g = to_np(out["h"][k])
         assert np.isfinite(g).all()
-        err, n_over, ok = compare(g[rows_k], hs[k][rows_k], atol, bf16_store=(model is BF16), ulps=4 * (k + 1))
+        if model is BF16:
+            stt = compare_h(g[rows_k], hs[k][rows_k], k + 1)
+            print(f"  depth {k + 1}: state rows {rows_k.sum()}, {fmt_h(stt)}", flush=True)
+            assert stt["ok"], (k, stt)
+            continue
+        err, n_over, ok = compare(g[rows_k], hs[k][rows_k], atol)
         rf = rel_fro(g[rows_k], hs[k][rows_k])
         print(f"  depth {k + 1}: state rows {rows_k.sum()}, max|err| {err:.3e}, "
               f"over atol {n_over}, relF {rf:.2e}", flush=True)

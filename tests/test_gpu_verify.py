@@ -57,13 +57,12 @@ def test_verify_small_vocab(gamma):
 
 
 @pytest.mark.parametrize("gamma", [1, 2, 3, 4])
-def test_verify_full_vocab_sampled_requests(gamma):
-    # the full launch (R = 256, V = 129280); the oracle checks 48 requests
+def test_verify_full_vocab_every_request(gamma):
+    # the full launch (R = 256, V = 129280); the oracle checks every request
     vc, d, y = _inputs(gamma, R=256, V=129280)
     print(f"[verify] gamma={gamma} R=256 V=129280", flush=True)
     g = _gpu(d, y)
-    req = np.random.default_rng(gamma).choice(256, 48, replace=False)
-    assert _compare(d, y, g, req) == 0
+    assert _compare(d, y, g) == 0
     assert (g["status"] == 0).all()
     assert ((g["accepted_len"] >= 0) & (g["accepted_len"] <= gamma)).all()
 
