@@ -18,11 +18,11 @@ MTP_F32, MTP_BF16 = 0, 1
 MTP_REDUCE_FIXED, MTP_REDUCE_VALID_MEAN = 0, 1
 STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEPTH",
           -4: "MTP_ERR_DTYPE", -5: "MTP_ERR_WORKSPACE", -6: "MTP_ERR_ARG", -7: "MTP_ERR_HIP",
-          -8: "MTP_ERR_UNSUPPORTED"}
+          -8: "MTP_ERR_UNSUPPORTED", -9: "MTP_ERR_TOO_LARGE"}
 EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step", "mtp_round_commit",
            "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
-           "mtp_profile_count")
+           "mtp_profile_count", "mtp_verify_noalloc")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
           "VERIFY")
@@ -46,7 +46,7 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 4     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 5     # the struct layouts below mirror include/mtp.h at this version
 
 
 class CeArgs(C.Structure):
@@ -99,6 +99,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_chain_forward.argtypes = [C.POINTER(ChainArgs), vp]
         lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
         lib.mtp_verify.argtypes = [C.POINTER(VerifyArgs), vp]
+        lib.mtp_verify_noalloc.argtypes = [C.POINTER(VerifyArgs), vp]
         lib.mtp_propose_step.argtypes = [C.POINTER(ProposeArgs), vp]
         lib.mtp_round_commit.argtypes = [C.POINTER(RoundArgs), vp]
         lib.mtp_propose_workspace_size.argtypes = [C.POINTER(ProposeArgs)]
@@ -272,6 +273,21 @@ def verify(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens
     a.workspace, a.workspace_bytes = _p(ws), ws.numel()
     _check(lib.mtp_verify(C.byref(a), _stream(stream)))
     out["_keep"] = (ws,)
+    return out
+
+
+def verify_noalloc(target_logits: torch.Tensor, draft_logits: torch.Tensor, draft_tokens: torch.Tensor,
+                   u_accept: torch.Tensor, u_sample: torch.Tensor, *, temperature: float = 1.0,
+                   out: Dict, stream=None) -> Dict:
+    """mtp_verify_noalloc: as ``verify`` with caller-allocated outputs ``out``
+    (accepted_len, next_token, status int32 [R]; margin f32 [R] or None) and
+    the library's static scratch instead of a workspace."""
+    R, G1, V = target_logits.shape
+    a = VerifyArgs(R, G1 - 1, V, temperature, _dtype_code(target_logits), _p(target_logits),
+                   _p(draft_logits), _p(draft_tokens), _p(u_accept), _p(u_sample),
+                   _p(out["accepted_len"]), _p(out["next_token"]), _p(out["status"]),
+                   _p(out.get("margin")), None, 0)
+    _check(load().mtp_verify_noalloc(C.byref(a), _stream(stream)))
     return out
 
 

@@ -4,13 +4,46 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/mtp.h"
 #include "epilogues.hpp"
 #include "kernels.hpp"
 
 using namespace mtp;
 
+// Scratch of mtp_verify_noalloc: one copy per device (the code object's
+// storage), held until the process ends.  Host code never passes `scratch`
+// itself to a kernel -- on the host it only names the symbol; its device
+// address comes from hipGetSymbolAddress (scratch_address below).
+static __device__ __align__(256) char scratch[MTP_NOALLOC_SCRATCH_BYTES];
+
 namespace {
+
+// Device address of `scratch` on the current device, resolved once per device
+// (with that device current) and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(hipStream_t s, void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MTP_ERR_HIP;
+  if (s != nullptr) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice(s, &sdev) != hipSuccess) return MTP_ERR_HIP;
+    if ((int)sdev != dev) return MTP_ERR_ARG;   // the stream must belong to the current device
+  }
+  if (dev < 0 || dev >= kMaxDevices) return MTP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MTP_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MTP_OK;
+}
 
 constexpr size_t kAlign = 256;
 
@@ -778,6 +811,7 @@ const char *mtp_strerror(int status) {
     case MTP_ERR_ARG: return "invalid argument";
     case MTP_ERR_HIP: return "HIP launch failed";
     case MTP_ERR_UNSUPPORTED: return "configuration not supported by the kernels";
+    case MTP_ERR_TOO_LARGE: return "request needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -819,22 +853,45 @@ size_t mtp_verify_workspace_size(const mtp_verify_args *a) {
   return verify_bytes(a);
 }
 
-int mtp_verify(const mtp_verify_args *a, void *stream) {
-  int st = check_verify(a);
-  if (st) return st;
+namespace {
+int check_verify_ptrs(const mtp_verify_args *a, const void *ws) {
   if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->u_accept || !a->u_sample ||
       !a->accepted_len || !a->next_token || !a->status)
     return MTP_ERR_NULL;
   if (!all_al16(a->target_logits, a->draft_logits, a->draft_tokens, a->u_accept, a->u_sample, a->accepted_len,
-                a->next_token, a->status, a->margin, a->workspace))
+                a->next_token, a->status, a->margin, ws))
     return MTP_ERR_ARG;
-  if (!a->workspace || a->workspace_bytes < verify_bytes(a)) return MTP_ERR_WORKSPACE;
-  hipStream_t s = static_cast<hipStream_t>(stream);
+  return MTP_OK;
+}
+
+int verify_run(const mtp_verify_args *a, double *ws, hipStream_t s) {
   MTP_STAGE(MTP_STAGE_VERIFY);
   MTP_TRY(launch_verify(a->target_logits, a->draft_logits, a->logits_dtype == MTP_BF16 ? 1 : 0, a->draft_tokens,
                         a->u_accept, a->u_sample, a->R, a->gamma, a->V, a->temperature, a->accepted_len,
-                        a->next_token, a->status, a->margin, static_cast<double *>(a->workspace), s));
+                        a->next_token, a->status, a->margin, ws, s));
   return MTP_OK;
+}
+}  // namespace
+
+int mtp_verify(const mtp_verify_args *a, void *stream) {
+  int st = check_verify(a);
+  if (st) return st;
+  if ((st = check_verify_ptrs(a, a->workspace))) return st;
+  if (!a->workspace || a->workspace_bytes < verify_bytes(a)) return MTP_ERR_WORKSPACE;
+  return verify_run(a, static_cast<double *>(a->workspace), static_cast<hipStream_t>(stream));
+}
+
+int mtp_verify_noalloc(const mtp_verify_args *a, void *stream) {
+  int st = check_verify(a);
+  if (st) return st;
+  if ((st = check_verify_ptrs(a, nullptr))) return st;
+  if (verify_bytes(a) > (size_t)MTP_NOALLOC_SCRATCH_BYTES) return MTP_ERR_TOO_LARGE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void *ws = nullptr;
+  if ((st = scratch_address(s, &ws))) return st;
+  // every workspace entry the verify kernels read is written earlier in the
+  // same call: nothing needs clearing between calls
+  return verify_run(a, static_cast<double *>(ws), s);
 }
 
 int mtp_round_commit(const mtp_round_args *a, void *stream) {

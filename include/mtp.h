@@ -22,7 +22,8 @@
  *     with MTP_ERR_ARG.
  *   - The caller allocates and frees every buffer, including the workspace
  *     (size from the matching *_workspace_size call).  The library keeps no
- *     device memory of its own.
+ *     device memory of its own, apart from the static scratch of
+ *     mtp_verify_noalloc (MTP_NOALLOC_SCRATCH_BYTES per device it runs on).
  *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = the default
  *     stream).  No call synchronises the host.  Calls on different streams
  *     with disjoint buffers may run concurrently.
@@ -57,7 +58,8 @@ typedef enum {
   MTP_ERR_WORKSPACE = -5,    /* workspace NULL or smaller than required          */
   MTP_ERR_ARG = -6,          /* other invalid argument (reduce mode, denom, ...)  */
   MTP_ERR_HIP = -7,          /* a HIP launch failed                              */
-  MTP_ERR_UNSUPPORTED = -8   /* valid request outside what the kernels handle    */
+  MTP_ERR_UNSUPPORTED = -8,  /* valid request outside what the kernels handle    */
+  MTP_ERR_TOO_LARGE = -9     /* *_noalloc: needs more than the static scratch    */
 } mtp_status;
 
 typedef enum { MTP_F32 = 0, MTP_BF16 = 1 } mtp_dtype;
@@ -360,6 +362,26 @@ typedef struct {
 int mtp_chain_forward(const mtp_chain_args *a, void *stream);
 int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
 int mtp_verify(const mtp_verify_args *a, void *stream);
+
+/* ------------------------------------------------------------------------
+ * mtp_verify_noalloc: mtp_verify for callers that cannot allocate device
+ * memory -- code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc.  Same arguments, checks, kernels and outputs as
+ * mtp_verify, except that `workspace` and `workspace_bytes` are ignored: the
+ * call uses a static scratch buffer of MTP_NOALLOC_SCRATCH_BYTES that the
+ * library holds on each device it runs on until the process ends.  It calls
+ * no allocating routine.  The caller still passes (and owns) the inputs and
+ * outputs.  Requests needing more scratch than that (the bytes
+ * mtp_verify_workspace_size reports; e.g. R <= 500 at V = 129280 and
+ * gamma = 4, bf16 logits) return MTP_ERR_TOO_LARGE and launch nothing.
+ * The stream must belong to the current device (else MTP_ERR_ARG).  All
+ * calls on one device share its scratch, which keeps the last call's
+ * contents: calls that overlap on one device (on different streams, or from
+ * different threads without ordering) race and must not be issued.
+ * ---------------------------------------------------------------------- */
+#define MTP_NOALLOC_SCRATCH_BYTES (64u << 20)
+int mtp_verify_noalloc(const mtp_verify_args *a, void *stream);
+
 int mtp_propose_step(const mtp_propose_args *a, void *stream);
 int mtp_round_commit(const mtp_round_args *a, void *stream);
 
@@ -397,7 +419,7 @@ const char *mtp_strerror(int status);
  * struct field added, moved or retyped, a call's meaning changed).  A
  * binding that mirrors the argument structs must refuse a library whose
  * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
-#define MTP_ABI_VERSION 4
+#define MTP_ABI_VERSION 5
 int mtp_abi_version(void);
 
 #ifdef __cplusplus

@@ -259,3 +259,16 @@ def test_ctypes_struct_layouts_match_the_header(tmp_path):
         assert got[(name, "sizeof")] == C.sizeof(cls), name
         for f, _ in cls._fields_:
             assert got[(name, f)] == getattr(cls, f).offset, (name, f)
+
+
+def test_verify_noalloc_refuses_beyond_its_scratch_on_the_host(lib):
+    # a request needing more than the static scratch returns MTP_ERR_TOO_LARGE
+    # before any launch (the pointers are never dereferenced)
+    fake = C.c_void_p(1 << 20)
+    a = _lib.VerifyArgs(600, 4, 129280, 1.0, _lib.MTP_BF16, fake, fake, fake, fake, fake, fake, fake, fake,
+                        None, None, 0)
+    assert lib.mtp_verify_workspace_size(C.byref(a)) > (64 << 20)
+    assert lib.mtp_verify_noalloc(C.byref(a), None) == -9
+    assert lib.mtp_verify_noalloc(None, None) == -1
+    a.R = 0
+    assert lib.mtp_verify_noalloc(C.byref(a), None) == -2
