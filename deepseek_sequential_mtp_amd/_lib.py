@@ -22,10 +22,12 @@ STATUS = {0: "MTP_OK", -1: "MTP_ERR_NULL", -2: "MTP_ERR_SHAPE", -3: "MTP_ERR_DEP
 EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propose_step", "mtp_round_commit",
            "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
-           "mtp_profile_count", "mtp_verify_noalloc")
+           "mtp_profile_count", "mtp_verify_noalloc", "mtp_chain_backward",
+           "mtp_chain_backward_workspace_size")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
-          "VERIFY")
+          "VERIFY", "BWD_RECOMPUTE", "BWD_MLP", "BWD_ATTN_PROJ", "BWD_ATTN", "BWD_QKV", "BWD_EH")
+GRAD_FIELDS = ("g_h", "g_e", "g_a", "g_f", "M", "Wqkv", "Wo", "Wgate", "Wup", "Wdown")
 
 vp = C.c_void_p
 fp = C.POINTER(C.c_float)
@@ -46,7 +48,25 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 5     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 6     # the struct layouts below mirror include/mtp.h at this version
+
+
+class DepthGrads(C.Structure):
+    _fields_ = [("g_h", vp), ("g_e", vp), ("g_attn", vp), ("g_ffn", vp), ("M", vp), ("Wqkv", vp),
+                ("Wo", vp), ("Wgate", vp), ("Wup", vp), ("Wdown", vp)]
+
+
+class ChainBwdArgs(C.Structure):
+    _fields_ = [("B", C.c_int), ("T", C.c_int), ("d", C.c_int), ("n_heads", C.c_int),
+                ("head_dim", C.c_int), ("ffn", C.c_int), ("V", C.c_int), ("D", C.c_int),
+                ("dtype", C.c_int), ("eps", C.c_float), ("rope_theta", C.c_float),
+                ("tokens", vp), ("segment_ids", vp), ("h0", vp), ("embed", vp),
+                ("w", C.POINTER(DepthWeights)), ("h", C.POINTER(vp)), ("dh", C.POINTER(vp)),
+                ("dh0", vp), ("dE", vp), ("dw", C.POINTER(DepthGrads)), ("accumulate", C.c_int),
+                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+C_STRUCT_NAMES = {"DepthGrads": "mtp_depth_grads", "ChainBwdArgs": "mtp_chain_bwd_args"}
 
 
 class CeArgs(C.Structure):
@@ -97,6 +117,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
                                "`python -m deepseek_sequential_mtp_amd.build`")
         lib = C.CDLL(path)
         lib.mtp_chain_forward.argtypes = [C.POINTER(ChainArgs), vp]
+        lib.mtp_chain_backward.argtypes = [C.POINTER(ChainBwdArgs), vp]
+        lib.mtp_chain_backward_workspace_size.argtypes = [C.POINTER(ChainBwdArgs)]
+        lib.mtp_chain_backward_workspace_size.restype = C.c_size_t
         lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
         lib.mtp_verify.argtypes = [C.POINTER(VerifyArgs), vp]
         lib.mtp_verify_noalloc.argtypes = [C.POINTER(VerifyArgs), vp]
@@ -197,6 +220,54 @@ def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Ten
     a.workspace, a.workspace_bytes = _p(ws), ws.numel()
     _check(lib.mtp_chain_forward(C.byref(a), _stream(stream)))
     out["_keep"] = (ws_arr, hout, ws)
+    return out
+
+
+def _depth_weights(depths) -> C.Array:
+    arr = (DepthWeights * len(depths))()
+    for k, w in enumerate(depths):
+        arr[k] = DepthWeights(_p(w["g_h"]), _p(w["g_e"]), _p(w["g_a"]), _p(w["g_f"]), _p(w["M"]),
+                              _p(w["Wqkv"]), _p(w["Wo"]), _p(w["Wgate"]), _p(w["Wup"]), _p(w["Wdown"]))
+    return arr
+
+
+def chain_backward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Tensor, embed: torch.Tensor,
+                   depths: Sequence[Dict[str, torch.Tensor]], hs: Sequence[torch.Tensor],
+                   dh: Sequence[torch.Tensor], *, n_heads: int, head_dim: int, eps: float = 1e-6,
+                   rope_theta: float = 10000.0, accumulate: bool = False, out: Optional[Dict] = None,
+                   cache: Optional[Dict] = None, stream=None) -> Dict:
+    """mtp_chain_backward.  hs: h^(1..D) from chain_forward; dh: D f32 tensors [B*T,d] (the
+    head's gradients).  Returns dict(dh0 f32 [B*T,d], dE f32 [V,d] (added to; zeros when
+    ``out`` is not given), dw = D dicts of f32 gradients keyed like the weights, device_error)."""
+    B, T = tokens.shape
+    V, d = embed.shape
+    D = len(depths)
+    ffn = depths[0]["Wgate"].shape[0]
+    dev = h0.device
+    if out is None:
+        out = dict(dh0=torch.empty((B * T, d), dtype=torch.float32, device=dev),
+                   dE=torch.zeros((V, d), dtype=torch.float32, device=dev),
+                   dw=[{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in GRAD_FIELDS}
+                       for w in depths],
+                   device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    warr = _depth_weights(depths)
+    garr = (DepthGrads * D)()
+    for k, g in enumerate(out["dw"]):
+        garr[k] = DepthGrads(_p(g["g_h"]), _p(g["g_e"]), _p(g["g_a"]), _p(g["g_f"]), _p(g["M"]), _p(g["Wqkv"]),
+                             _p(g["Wo"]), _p(g["Wgate"]), _p(g["Wup"]), _p(g["Wdown"]))
+    hp = (vp * D)(*[x.data_ptr() for x in hs])
+    dhp = (vp * D)(*[x.data_ptr() for x in dh])
+    a = ChainBwdArgs(B, T, d, n_heads, head_dim, ffn, V, D, _dtype_code(h0), eps, rope_theta, _p(tokens),
+                     _p(segment_ids), _p(h0), _p(embed), warr, hp, dhp, _p(out["dh0"]), _p(out["dE"]), garr,
+                     1 if accumulate else 0, _p(out["device_error"]), None, 0)
+    lib = load()
+    nbytes = lib.mtp_chain_backward_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_chain_backward(C.byref(a), _stream(stream)))
+    ws = _workspace(nbytes, dev, cache, "chain_bwd_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_chain_backward(C.byref(a), _stream(stream)))
+    out["_keep"] = (warr, garr, hp, dhp, ws)
     return out
 
 

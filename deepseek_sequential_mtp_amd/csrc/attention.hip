@@ -70,7 +70,8 @@ template <typename T, int HD>
 __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__restrict__ qkv,
                                                                 T *__restrict__ out,
                                                                 const int32_t *__restrict__ run_start,
-                                                                int B, int T_len, int H, float scale_log2) {
+                                                                float *__restrict__ lse2_out, int B,
+                                                                int T_len, int H, float scale_log2) {
   using C = AttnCfg<T, HD>;
   constexpr int E = C::E, CPR = C::CPR, ROWB = C::ROWB, SK = C::SK, MD = C::MD, KPS = C::KPS;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
@@ -316,6 +317,9 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
   for (int nb = 0; nb < NBQ; ++nb) {
     const float lt = l[nb] + __shfl_xor(l[nb], 32);
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
+    // base-2 log-sum-exp of the query's scaled scores (for the reverse pass)
+    if (lse2_out != nullptr && hl == 0 && qi[nb] < T_len)
+      lse2_out[(rowbase + qi[nb]) * H + h] = m[nb] + __log2f(lt);
     const int qb = wave * kQW + 32 * nb + c32;            // query inside the block
     char *ostage = qb < kQT / 2 ? st0 : st1;
     T *orow = reinterpret_cast<T *>(ostage) + (long)(qb % (kQT / 2)) * HD;
@@ -340,33 +344,33 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
 }
 
 template <typename T, int HD>
-static hipError_t attn_launch(const T *qkv, T *out, const int32_t *rs, int B, int T_len, int H,
+static hipError_t attn_launch(const T *qkv, T *out, const int32_t *rs, float *lse2, int B, int T_len, int H,
                               hipStream_t s) {
   const int nqt = (T_len + kQT - 1) / kQT;
   const long blocks = (long)nqt * H * B;
   const float scale_log2 = kLog2e / sqrtf((float)HD);
   hipLaunchKernelGGL((attention_kernel<T, HD>), dim3((unsigned)blocks), dim3(kAttnThreads), 0, s, qkv, out,
-                     rs, B, T_len, H, scale_log2);
+                     rs, lse2, B, T_len, H, scale_log2);
   return hipGetLastError();
 }
 
 template <>
-hipError_t launch_attention<bf16_t>(const bf16_t *qkv, bf16_t *out, const int32_t *rs, int B, int T_len,
-                                    int H, int hd, hipStream_t s) {
+hipError_t launch_attention<bf16_t>(const bf16_t *qkv, bf16_t *out, const int32_t *rs, float *lse2, int B,
+                                    int T_len, int H, int hd, hipStream_t s) {
   switch (hd) {
-    case 32: return attn_launch<bf16_t, 32>(qkv, out, rs, B, T_len, H, s);
-    case 64: return attn_launch<bf16_t, 64>(qkv, out, rs, B, T_len, H, s);
-    case 128: return attn_launch<bf16_t, 128>(qkv, out, rs, B, T_len, H, s);
+    case 32: return attn_launch<bf16_t, 32>(qkv, out, rs, lse2, B, T_len, H, s);
+    case 64: return attn_launch<bf16_t, 64>(qkv, out, rs, lse2, B, T_len, H, s);
+    case 128: return attn_launch<bf16_t, 128>(qkv, out, rs, lse2, B, T_len, H, s);
     default: return hipErrorInvalidValue;
   }
 }
 template <>
-hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *rs, int B, int T_len, int H,
-                                   int hd, hipStream_t s) {
+hipError_t launch_attention<float>(const float *qkv, float *out, const int32_t *rs, float *lse2, int B,
+                                   int T_len, int H, int hd, hipStream_t s) {
   switch (hd) {
-    case 16: return attn_launch<float, 16>(qkv, out, rs, B, T_len, H, s);
-    case 32: return attn_launch<float, 32>(qkv, out, rs, B, T_len, H, s);
-    case 64: return attn_launch<float, 64>(qkv, out, rs, B, T_len, H, s);
+    case 16: return attn_launch<float, 16>(qkv, out, rs, lse2, B, T_len, H, s);
+    case 32: return attn_launch<float, 32>(qkv, out, rs, lse2, B, T_len, H, s);
+    case 64: return attn_launch<float, 64>(qkv, out, rs, lse2, B, T_len, H, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -266,6 +266,64 @@ struct EpiSwiGLU {
 };
 
 // ---------------------------------------------------------------------------
+// Reverse of SwiGLU on the recomputed gate/up products (pairs with
+// DmaKMajorSwiGLU, as EpiSwiGLU): with gate g, up u and the incoming
+// gradient dgsw[row, feat] of silu(g) u,
+//   gsw[row, feat]       = silu(g) u                         (for dW_down)
+//   dgu[row, feat]       = dgsw u silu'(g),  silu'(g) = sig(g) (1 + g (1 - sig(g)))
+//   dgu[row, f + feat]   = dgsw silu(g)
+// All three in bf16 (dgu feeds the dy and dW_gate / dW_up products).
+// ---------------------------------------------------------------------------
+template <typename OutT>
+struct EpiSwiGLUBwd {
+  const OutT *dgsw; OutT *gsw; OutT *dgu; int M, f;
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *, char *) const {
+    constexpr int NBh = Cfg::NB / 2;
+    const int tile_n = n0 / Cfg::BN;
+    const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
+    const long ldg = f, ldd = 2L * f;
+    const __amdgpu_buffer_rsrc_t rin = make_rsrc(dgsw + (long)m0 * ldg, rows * ldg * (long)sizeof(OutT));
+    const __amdgpu_buffer_rsrc_t rg = make_rsrc(gsw + (long)m0 * ldg, rows * ldg * (long)sizeof(OutT));
+    const __amdgpu_buffer_rsrc_t rd = make_rsrc(dgu + (long)m0 * ldd, rows * ldd * (long)sizeof(OutT));
+    const bool odd = lane & 1;
+#pragma unroll
+    for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NBh; ++j) {
+        const int feat = tile_n * (Cfg::BN / 2) + wn * (Cfg::WN / 2) + j * 32 + (lane & 31);
+        const bool fok = feat < f;
+        float vs[16], vg[16], vu[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = acc_row<Cfg>(wm, i, r, lane);
+          const float dg_in =
+              buf_load_elem(rin, fok ? (unsigned)(((long)row * ldg + feat) * sizeof(OutT)) : kOOB, OutT{});
+          const float g = acc[i][j][r], u = acc[i][j + NBh][r];
+          const float sig = __fdividef(1.f, 1.f + __expf(-g));
+          const float sl = g * sig;
+          vs[r] = sl * u;
+          vg[r] = dg_in * u * sig * (1.f + g * (1.f - sig));
+          vu[r] = dg_in * sl;
+        }
+        const unsigned pc = (unsigned)((feat & ~1) * sizeof(OutT));
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) {
+          const int row = acc_row<Cfg>(wm, i, r, lane) + (odd ? 1 : 0);
+          float lo, hi;
+          pair_rows(vs[r], vs[r + 1], odd, lo, hi);
+          store_pair<OutT>(rg, fok ? pc + (unsigned)((long)row * ldg * sizeof(OutT)) : kOOB, lo, hi);
+          pair_rows(vg[r], vg[r + 1], odd, lo, hi);
+          store_pair<OutT>(rd, fok ? pc + (unsigned)((long)row * ldd * sizeof(OutT)) : kOOB, lo, hi);
+          pair_rows(vu[r], vu[r + 1], odd, lo, hi);
+          store_pair<OutT>(rd, fok ? pc + (unsigned)(((long)row * ldd + f) * sizeof(OutT)) : kOOB, lo, hi);
+        }
+      }
+  }
+};
+
+// ---------------------------------------------------------------------------
 // Linear-CE forward, one BM x BN tile of logits z = x_hat W^T: per row, the
 // tile's max m_t and s_t = sum exp(z - m_t) over its valid columns go to
 // part[row * nt + tile_n] (float2), and the target logit z[row, label[row]]

@@ -33,11 +33,38 @@ hipError_t launch_out_norm_bwd(const float *dx, int splits, long slab, const T *
                                int N, int d, int dh_acc, hipStream_t s);
 // Row blocks of the output-norm backward (8 rows each); one dg partial row per block.
 inline int dg_row_blocks(int N) { int b = (N + 7) / 8; return b < 1 ? 1 : b; }
+// dg[j] (+)= sum over the nrb partial rows, in a fixed order
+hipError_t launch_dg_reduce(const float *part, int nrb, int d, float *dg, int accumulate, hipStream_t s);
+
+// reverse pass of the chain (bf16 runs)
+// RMSNorm backward over rows (z row zrow[n] when zrow is set; d <= 8192):
+// dz = resid + (rowmask ? backward : 0), optional bf16 copy; gain gradient
+// into dg via part (dg_row_blocks(N) x d floats)
+template <typename TZ>
+hipError_t launch_rms_bwd(const float *dy, long ldy, const TZ *z, const int32_t *zrow, const float *g, float eps,
+                          const float *resid, const uint8_t *rowmask, float *dz, bf16_t *dzb, float *part,
+                          float *dg, int accumulate, int N, int d, hipStream_t s);
+// shifted tokens of depth k (tok), sort keys (token on state rows, V
+// elsewhere) and row indices
+hipError_t launch_shifted_rows(const int32_t *tokens, const uint8_t *state, int B, int T_len, int V, int depth,
+                               int32_t *tok, int32_t *key, int32_t *val, hipStream_t s);
+// dE[t] += sum of de rows whose key is t (stable sort by key, then one sum per run)
+size_t embed_grad_sort_bytes(int N, int V);
+hipError_t launch_embed_grad(const int32_t *key, const int32_t *val, int32_t *key_sorted, int32_t *val_sorted,
+                             void *sort_tmp, size_t sort_bytes, int N, int V, const float *de, int d, float *dE,
+                             hipStream_t s);
+// attention reverse: dqkv [B*T, 3A] (dq, dk after the inverse RoPE; dv) from
+// qkv, o, dO [B*T, A], the forward's lse2 [B*T, H]; Dd [B*T, H] scratch
+hipError_t launch_attention_bwd(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, const float *lse2,
+                                const int32_t *run_start, const int32_t *pos, const float2 *rope, float *Dd,
+                                bf16_t *dqkv, int B, int T_len, int H, int hd, hipStream_t s);
 
 // attention
+// lse2 (may be NULL): [B*T, H] base-2 log-sum-exp of each query's scores
+// scaled by log2(e)/sqrt(hd), for the reverse pass
 template <typename T>
-hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, int B, int T_len, int H,
-                            int hd, hipStream_t s);
+hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, float *lse2, int B, int T_len,
+                            int H, int hd, hipStream_t s);
 hipError_t rope_table(float2 *table, int max_pos, int half, float theta, hipStream_t s);
 template <typename T>
 // skip (may be NULL): requests with skip[r] != 0 do not write their cache slot

@@ -404,7 +404,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     if (st) return st;
     {
       MTP_STAGE(MTP_STAGE_ATTN);
-      MTP_TRY(launch_attention<T>(qkv, o, run_start, B, Tl, H, hd, s));
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, nullptr, B, Tl, H, hd, s));
     }
     {
       MTP_STAGE(MTP_STAGE_O_PROJ);
@@ -428,6 +428,258 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     }
     if (st) return st;
     h_prev = h_out;
+  }
+  return MTP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Reverse pass of the chain (bf16)
+// ---------------------------------------------------------------------------
+// C[M, N] (+)= A[M, K] B[K, N] with B stored [K, N] (N contiguous).
+template <typename T, typename OutT>
+int gemm_nn(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc, int M, int N, int K, int accumulate,
+            float *skws, hipStream_t s) {
+  EpiStore<OutT, float> epi{C, ldc, M, N, 1.f, nullptr, nullptr, 0, accumulate, 0};
+  return pick<T>(use_big(M, N), [&](auto cfg) -> int {
+    using Cfg = decltype(cfg);
+    KA<T, Cfg> la{A, lda, M, K};
+    MB_<T, Cfg> lb{Bm, ldb, N, K};
+    MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, N, K, 8, skws, s)));
+    return (int)MTP_OK;
+  });
+}
+
+// C[M, N] (+)= At^T Bt with At stored [K, M] and Bt stored [K, N] (the
+// weight gradient dW = dY^T X of y = x W^T: At = dY, Bt = X, K = rows).
+template <typename T>
+int gemm_tn(const T *At, long lda, const T *Bt, long ldb, float *C, long ldc, int M, int N, int K, int accumulate,
+            float *skws, hipStream_t s) {
+  EpiStore<float, float> epi{C, ldc, M, N, 1.f, nullptr, nullptr, 0, accumulate, 0};
+  return pick<T>(use_big(M, N), [&](auto cfg) -> int {
+    using Cfg = decltype(cfg);
+    MA<T, Cfg> la{At, lda, M, K};
+    MB_<T, Cfg> lb{Bt, ldb, N, K};
+    MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, N, K, 8, skws, s)));
+    return (int)MTP_OK;
+  });
+}
+
+// Recomputed gate/up products of y with the SwiGLU reverse in the epilogue.
+template <typename T>
+int gemm_swiglu_bwd(const T *y, const T *Wg, const T *Wu, const T *dgsw, T *gsw, T *dgu, int M, int d, int f,
+                    float *skws, hipStream_t s) {
+  EpiSwiGLUBwd<T> epi{dgsw, gsw, dgu, M, f};
+  return pick<T>(use_big(M, 2L * f), [&](auto cfg) -> int {
+    using Cfg = decltype(cfg);
+    PA<T, Cfg> la{y, (long)d, M, d};
+    DmaKMajorSwiGLU<T, Cfg> lb{Wg, Wu, (long)d, f, d};
+    MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, M, 2 * ceil_div(f, Cfg::BN / 2) * (Cfg::BN / 2), d, 8, skws, s)));
+    return (int)MTP_OK;
+  });
+}
+
+int check_chain_bwd(const mtp_chain_bwd_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  mtp_chain_args f{};
+  f.B = a->B; f.T = a->T; f.d = a->d; f.n_heads = a->n_heads; f.head_dim = a->head_dim; f.ffn = a->ffn;
+  f.V = a->V; f.D = a->D; f.dtype = a->dtype; f.eps = a->eps; f.rope_theta = a->rope_theta;
+  const int st = check_chain(&f);
+  if (st) return st;
+  if (a->dtype != MTP_BF16) return MTP_ERR_UNSUPPORTED;
+  if (a->head_dim != 64 && a->head_dim != 128) return MTP_ERR_UNSUPPORTED;
+  if (a->d > 8192) return MTP_ERR_UNSUPPORTED;
+  return MTP_OK;
+}
+
+int check_chain_bwd_ptrs(const mtp_chain_bwd_args *a) {
+  if (!a->tokens || !a->segment_ids || !a->h0 || !a->embed || !a->w || !a->h || !a->dh || !a->dh0 || !a->dE ||
+      !a->dw)
+    return MTP_ERR_NULL;
+  for (int k = 0; k < a->D; ++k) {
+    const mtp_depth_weights &w = a->w[k];
+    const mtp_depth_grads &g = a->dw[k];
+    if (!w.g_h || !w.g_e || !w.g_attn || !w.g_ffn || !w.M || !w.Wqkv || !w.Wo || !w.Wgate || !w.Wup || !w.Wdown ||
+        !g.g_h || !g.g_e || !g.g_attn || !g.g_ffn || !g.M || !g.Wqkv || !g.Wo || !g.Wgate || !g.Wup || !g.Wdown ||
+        !a->dh[k] || (k + 1 < a->D && !a->h[k]))
+      return MTP_ERR_NULL;
+    if (!all_al16(w.g_h, w.g_e, w.g_attn, w.g_ffn, w.M, w.Wqkv, w.Wo, w.Wgate, w.Wup, w.Wdown) ||
+        !all_al16(g.g_h, g.g_e, g.g_attn, g.g_ffn, g.M, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown) ||
+        !all_al16(a->dh[k], a->h[k]))
+      return MTP_ERR_ARG;
+  }
+  if (!all_al16(a->tokens, a->segment_ids, a->h0, a->embed, a->dh0, a->dE, a->device_error, a->workspace))
+    return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+constexpr int kBwdParts = 40;     // workspace regions of the reverse pass
+
+size_t chain_bwd_layout(const mtp_chain_bwd_args *a, Carve &c, void **p) {
+  using T = bf16_t;
+  const long N = (long)a->B * a->T;
+  const int d = a->d, A = a->n_heads * a->head_dim, f = a->ffn, H = a->n_heads, D = a->D;
+  p[0] = c.take<int32_t>(N);                      // run_start
+  p[1] = c.take<int32_t>(N);                      // pos
+  p[2] = c.take<int32_t>((size_t)D * a->B);       // count partials
+  p[3] = c.take<int32_t>(a->B);                   // error partials
+  p[4] = c.take<uint8_t>((size_t)D * N);          // state masks
+  p[5] = c.take<uint8_t>((size_t)D * N);          // loss masks
+  p[6] = c.take<int32_t>((size_t)D * N);          // labels
+  p[7] = c.take<int32_t>(D);                      // counts
+  p[8] = c.take<int32_t>(1);                      // error flag (when the caller passes none)
+  p[9] = c.take<float2>((size_t)a->T * (a->head_dim / 2));   // RoPE table
+  p[10] = c.take<T>(N * 2 * d);                   // c
+  p[11] = c.take<float>(N * d);                   // u
+  p[12] = c.take<T>(N * d);                       // x_a
+  p[13] = c.take<T>(N * 3 * (long)A);             // qkv
+  p[14] = c.take<T>(N * (long)A);                 // o
+  p[15] = c.take<float>(N * H);                   // lse2
+  p[16] = c.take<float>(N * d);                   // a
+  p[17] = c.take<T>(N * d);                       // y
+  p[18] = c.take<T>(N * (long)f);                 // silu(gate) * up
+  p[19] = c.take<float>(N * d);                   // gradient arriving at h^(k) (carry)
+  p[20] = c.take<T>(N * d);                       // its bf16 copy
+  p[21] = c.take<T>(N * (long)f);                 // d(silu(gate) * up)
+  p[22] = c.take<T>(N * 2 * (long)f);             // [d gate | d up]
+  p[23] = c.take<float>(N * d);                   // dy
+  p[24] = c.take<float>(N * d);                   // da
+  p[25] = c.take<T>(N * d);                       // da (bf16)
+  p[26] = c.take<T>(N * (long)A);                 // dO
+  p[27] = c.take<float>(N * H);                   // D = dO . o
+  p[28] = c.take<T>(N * 3 * (long)A);             // dqkv
+  p[29] = c.take<float>(N * d);                   // dx_a
+  p[30] = c.take<float>(N * d);                   // du
+  p[31] = c.take<T>(N * d);                       // du (bf16)
+  p[32] = c.take<float>(N * 2 * d);               // dc
+  p[33] = c.take<float>(N * d);                   // de
+  p[34] = c.take<int32_t>(5 * N);                 // shifted tokens, keys, rows, sorted keys, sorted rows
+  p[35] = c.take<char>(embed_grad_sort_bytes((int)N, a->V));   // radix sort scratch
+  p[36] = c.take<float>((size_t)dg_row_blocks((int)N) * d);    // gain-gradient partials
+  p[37] = c.take<float>(tail_ws_bytes<Big>() / 4);            // partial tiles of split tail GEMM tiles
+  p[38] = c.take<char>(0);
+  p[39] = c.take<char>(0);
+  return c.off;
+}
+
+__global__ void to_bf16_kernel(const float *__restrict__ x, bf16_t *__restrict__ y, long n4) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4 *>(x)[i];
+  reinterpret_cast<uint2 *>(y)[i] = make_uint2(pack_bf16x2(v.x, v.y), pack_bf16x2(v.z, v.w));
+}
+
+int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
+  using T = bf16_t;
+  void *p[kBwdParts];
+  Carve c(a->workspace);
+  chain_bwd_layout(a, c, p);
+  const int B = a->B, Tl = a->T, d = a->d, H = a->n_heads, hd = a->head_dim, f = a->ffn, V = a->V, D = a->D;
+  const int A = H * hd;
+  const int N = B * Tl;
+  int32_t *run_start = (int32_t *)p[0], *pos = (int32_t *)p[1];
+  uint8_t *state = (uint8_t *)p[4];
+  float2 *rope = (float2 *)p[9];
+  T *cbuf = (T *)p[10], *xa = (T *)p[12], *qkv = (T *)p[13], *o = (T *)p[14], *ybuf = (T *)p[17];
+  T *gsw = (T *)p[18];
+  float *u = (float *)p[11], *lse2 = (float *)p[15], *abuf = (float *)p[16];
+  float *gbuf = (float *)p[19];
+  T *gb = (T *)p[20], *dgsw = (T *)p[21], *dgu = (T *)p[22];
+  float *dy = (float *)p[23], *da = (float *)p[24];
+  T *dab = (T *)p[25], *dO = (T *)p[26];
+  float *Dd = (float *)p[27];
+  T *dqkv = (T *)p[28];
+  float *dxa = (float *)p[29], *du = (float *)p[30];
+  T *dub = (T *)p[31];
+  float *dc = (float *)p[32], *de = (float *)p[33];
+  int32_t *ids = (int32_t *)p[34];
+  int32_t *tok = ids, *key = ids + N, *val = ids + 2L * N, *key_s = ids + 3L * N, *val_s = ids + 4L * N;
+  void *sort_tmp = p[35];
+  const size_t sort_bytes = embed_grad_sort_bytes(N, V);
+  float *part = (float *)p[36];
+  float *skws = (float *)p[37];
+  const int acc = a->accumulate ? 1 : 0;
+  const T *E = static_cast<const T *>(a->embed);
+  const bool use_rope = a->rope_theta > 0.f;
+
+  MTP_TRY(launch_rows(a->tokens, a->segment_ids, B, Tl, V, D, run_start, pos, state, (uint8_t *)p[5],
+                      (int32_t *)p[6], (int32_t *)p[7], a->device_error ? a->device_error : (int32_t *)p[8],
+                      (int32_t *)p[2], (int32_t *)p[3], s));
+  if (use_rope) MTP_TRY(rope_table(rope, Tl, hd / 2, a->rope_theta, s));
+
+  for (int k = D; k >= 1; --k) {
+    const mtp_depth_weights &w = a->w[k - 1];
+    const mtp_depth_grads &g = a->dw[k - 1];
+    const T *hprev = static_cast<const T *>(k == 1 ? a->h0 : a->h[k - 2]);
+    const uint8_t *st_k = state + (long)(k - 1) * N;
+    const float *gcur = k == D ? a->dh[D - 1] : gbuf;
+    int st = 0;
+    // ---- the module's forward again (as chain_run), keeping lse2
+    {
+      MTP_STAGE(MTP_STAGE_BWD_RECOMPUTE);
+      MTP_TRY(launch_dual_norm_concat<T>(hprev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
+      if ((st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d,
+                                               1.f, nullptr, 0, skws, s)))
+        return st;
+      MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
+      if ((st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, skws, s)))
+        return st;
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, lse2, B, Tl, H, hd, s));
+      if ((st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0,
+                                               skws, s)))
+        return st;
+      MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
+    }
+    // ---- h = a + gsw W_down^T: the MLP's reverse and Norm_f's
+    {
+      MTP_STAGE(MTP_STAGE_BWD_MLP);
+      if (k == D) {
+        const long n4 = (long)N * d / 4;
+        hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, gcur, gb, n4);
+        MTP_TRY(hipGetLastError());
+      }
+      if ((st = gemm_nn<T, T>(gb, d, (const T *)w.Wdown, f, dgsw, f, N, f, d, 0, skws, s))) return st;
+      if ((st = gemm_swiglu_bwd<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, dgsw, gsw, dgu, N, d, f, skws, s)))
+        return st;
+      if ((st = gemm_tn<T>(gb, d, gsw, f, g.Wdown, f, d, f, N, acc, skws, s))) return st;
+      if ((st = gemm_nn<T, float>(dgu, 2L * f, (const T *)w.Wgate, d, dy, d, N, d, f, 0, skws, s))) return st;
+      if ((st = gemm_nn<T, float>(dgu + f, 2L * f, (const T *)w.Wup, d, dy, d, N, d, f, 1, skws, s))) return st;
+      if ((st = gemm_tn<T>(dgu, 2L * f, ybuf, d, g.Wgate, d, f, d, N, acc, skws, s))) return st;
+      if ((st = gemm_tn<T>(dgu + f, 2L * f, ybuf, d, g.Wup, d, f, d, N, acc, skws, s))) return st;
+      MTP_TRY(launch_rms_bwd<float>(dy, d, abuf, nullptr, w.g_ffn, a->eps, gcur, nullptr, da, dab, part, g.g_ffn,
+                                    acc, N, d, s));
+    }
+    // ---- a = u + o W_o^T
+    {
+      MTP_STAGE(MTP_STAGE_BWD_ATTN_PROJ);
+      if ((st = gemm_nn<T, T>(dab, d, (const T *)w.Wo, A, dO, A, N, A, d, 0, skws, s))) return st;
+      if ((st = gemm_tn<T>(dab, d, o, A, g.Wo, A, d, A, N, acc, skws, s))) return st;
+    }
+    {
+      MTP_STAGE(MTP_STAGE_BWD_ATTN);
+      MTP_TRY(launch_attention_bwd(qkv, o, dO, lse2, run_start, pos, use_rope ? rope : nullptr, Dd, dqkv, B, Tl, H,
+                                   hd, s));
+    }
+    // ---- qkv = x_a W_qkv^T, x_a = Norm_a(u)
+    {
+      MTP_STAGE(MTP_STAGE_BWD_QKV);
+      if ((st = gemm_nn<T, float>(dqkv, 3L * A, (const T *)w.Wqkv, d, dxa, d, N, d, 3 * A, 0, skws, s))) return st;
+      if ((st = gemm_tn<T>(dqkv, 3L * A, xa, d, g.Wqkv, d, 3 * A, d, N, acc, skws, s))) return st;
+      MTP_TRY(launch_rms_bwd<float>(dxa, d, u, nullptr, w.g_attn, a->eps, da, nullptr, du, dub, part, g.g_attn, acc,
+                                    N, d, s));
+    }
+    // ---- u = M [h_bar; e_bar]: eh_proj, enorm (into dE) and hnorm (the
+    // gradient carried to depth k-1, or dh0)
+    {
+      MTP_STAGE(MTP_STAGE_BWD_EH);
+      if ((st = gemm_nn<T, float>(dub, d, (const T *)w.M, 2L * d, dc, 2L * d, N, 2 * d, d, 0, skws, s))) return st;
+      if ((st = gemm_tn<T>(dub, d, cbuf, 2L * d, g.M, 2L * d, d, 2 * d, N, acc, skws, s))) return st;
+      MTP_TRY(launch_shifted_rows(a->tokens, st_k, B, Tl, V, k, tok, key, val, s));
+      MTP_TRY(launch_rms_bwd<T>(dc + d, 2L * d, E, tok, w.g_e, a->eps, nullptr, st_k, de, nullptr, part, g.g_e, acc,
+                                N, d, s));
+      MTP_TRY(launch_embed_grad(key, val, key_s, val_s, sort_tmp, sort_bytes, N, V, de, d, a->dE, s));
+      MTP_TRY(launch_rms_bwd<T>(dc, 2L * d, hprev, nullptr, w.g_h, a->eps, k > 1 ? a->dh[k - 2] : nullptr, st_k,
+                                k > 1 ? gbuf : a->dh0, k > 1 ? gb : nullptr, part, g.g_h, acc, N, d, s));
+    }
   }
   return MTP_OK;
 }
@@ -830,6 +1082,21 @@ int mtp_chain_forward(const mtp_chain_args *a, void *stream) {
   if (!a->workspace || a->workspace_bytes < mtp_chain_workspace_size(a)) return MTP_ERR_WORKSPACE;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return a->dtype == MTP_BF16 ? chain_run<bf16_t>(a, s) : chain_run<float>(a, s);
+}
+
+size_t mtp_chain_backward_workspace_size(const mtp_chain_bwd_args *a) {
+  if (check_chain_bwd(a) != MTP_OK) return 0;
+  Carve c(nullptr);
+  void *p[kBwdParts];
+  return chain_bwd_layout(a, c, p);
+}
+
+int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream) {
+  int st = check_chain_bwd(a);
+  if (st) return st;
+  if ((st = check_chain_bwd_ptrs(a))) return st;
+  if (!a->workspace || a->workspace_bytes < mtp_chain_backward_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  return chain_bwd_run(a, static_cast<hipStream_t>(stream));
 }
 
 size_t mtp_ce_workspace_size(const mtp_ce_args *a) {

@@ -260,6 +260,11 @@ __global__ __launch_bounds__(64 * kDgGroups) void dg_reduce_kernel(const float *
   }
 }
 
+hipError_t launch_dg_reduce(const float *part, int nrb, int d, float *dg, int accumulate, hipStream_t s) {
+  hipLaunchKernelGGL(dg_reduce_kernel, dim3((d + 63) / 64), dim3(64 * kDgGroups), 0, s, part, nrb, d, dg, accumulate);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 template <typename T>
 hipError_t launch_dual_norm_concat(const T *h, const T *E, const int32_t *tokens, const float *g_h,

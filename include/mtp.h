@@ -153,6 +153,74 @@ typedef struct {
 } mtp_chain_args;
 
 /* ------------------------------------------------------------------------
+ * mtp_chain_backward: the gradient of L_MTP through the whole depth chain
+ * ([M7.6] 0x05A: the MTP loss reaches each module's enorm, hnorm, eh_proj
+ * and Transformer block, the shared token embedding, and the main model
+ * through h^(0), a deeper loss passing through every module before it;
+ * 0x05B: a depth-j module's parameters receive its own loss and every deeper
+ * one, sum_{k=j..D} (lambda/D) dL^(k)/dtheta_j, and the shared embedding sums
+ * every depth's share).
+ *
+ * The call runs the modules in reverse, depth D down to 1.  Module k first
+ * recomputes its forward from h^(k-1) (h0 for k = 1, else h[k-2]) exactly as
+ * mtp_chain_forward does, then takes the gradient arriving at h^(k) -- dh[k-1]
+ * (the gradient from outside the chain, normally mtp_head_ce_fwd_bwd's dh
+ * for depth k) plus, for k < D, what module k+1 sent back through its hnorm
+ * input -- back through the block (SwiGLU MLP and its norm, segment-causal
+ * attention with RoPE and its norm, the residual adds), eh_proj and the two
+ * input norms.  The gradient at h^(0) is dh0; the embedding rows that module
+ * k read (x[b, i+k] on its state rows) receive their share in dE.
+ *
+ * Precision (bf16 only): the recomputed activations are stored in bf16 where
+ * the forward stores them; every gradient handed to a matrix product is
+ * rounded to bf16 once (the gradient entering a module, the SwiGLU product's
+ * and gate/up gradients, da, dO, dq/dk/dv, du); residual sums, norm
+ * statistics and all outputs are float32.
+ *
+ * Inputs : the arguments of mtp_chain_forward (tokens, segment_ids, h0,
+ *          embed, w, shapes, eps, rope_theta); h [host] D device pointers,
+ *          h^(1..D) [B*T, d] as mtp_chain_forward wrote them (h[D-1] is not
+ *          read); dh [host] D device pointers, f32 [B*T, d] each.
+ * Outputs: dh0 f32 [B*T, d] (written; 0 on rows no loss reaches, such as
+ *          padding and run-final rows);
+ *          dE f32 [V, d]: ADDED to (the main model's embedding gradient and
+ *          the MTP path's share one buffer, [M7.6] 0x05B; zero it first for
+ *          the MTP share alone);
+ *          dw [host] D entries of per-depth gradients (f32, the shapes of
+ *          mtp_depth_weights): written, or added to with accumulate = 1;
+ *          device_error int32 [1] (may be NULL): 1 if an active position
+ *          holds a token outside [0, V), else 0.
+ * Requirements: as mtp_chain_forward, and: dtype MTP_BF16 (MTP_F32 returns
+ * MTP_ERR_UNSUPPORTED), head_dim 64 or 128, d <= 8192.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  float *g_h, *g_e, *g_attn, *g_ffn;  /* [d]                                  */
+  float *M;                            /* [d, 2d]                              */
+  float *Wqkv;                         /* [3*H*hd, d]                          */
+  float *Wo;                           /* [d, H*hd]                            */
+  float *Wgate, *Wup;                  /* [ffn, d]                             */
+  float *Wdown;                        /* [d, ffn]                             */
+} mtp_depth_grads;
+
+typedef struct {
+  int B, T, d, n_heads, head_dim, ffn, V, D;
+  mtp_dtype dtype;
+  float eps, rope_theta;
+  const int32_t *tokens, *segment_ids;
+  const void *h0, *embed;
+  const mtp_depth_weights *w;        /* [host] D entries                       */
+  const void *const *h;              /* [host] D pointers (h^(1..D))           */
+  const float *const *dh;            /* [host] D pointers (f32)                */
+  float *dh0;
+  float *dE;
+  const mtp_depth_grads *dw;         /* [host] D entries                       */
+  int accumulate;                    /* 1: add into dw                         */
+  int32_t *device_error;             /* optional                               */
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_chain_bwd_args;
+
+/* ------------------------------------------------------------------------
  * mtp_head_ce_fwd_bwd: shared output head Norm_out + W_U, masked CE against
  * the labels of every depth, and the gradients of
  *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
@@ -360,6 +428,7 @@ typedef struct {
 } mtp_round_args;
 
 int mtp_chain_forward(const mtp_chain_args *a, void *stream);
+int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream);
 int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
 int mtp_verify(const mtp_verify_args *a, void *stream);
 
@@ -388,6 +457,7 @@ int mtp_round_commit(const mtp_round_args *a, void *stream);
 /* Workspace bytes the call needs for these arguments (pointers are not
  * inspected); 0 if the arguments are invalid. */
 size_t mtp_chain_workspace_size(const mtp_chain_args *a);
+size_t mtp_chain_backward_workspace_size(const mtp_chain_bwd_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);
 size_t mtp_verify_workspace_size(const mtp_verify_args *a);
 size_t mtp_propose_workspace_size(const mtp_propose_args *a);
@@ -407,7 +477,14 @@ typedef enum {
   MTP_STAGE_QKV = 4, MTP_STAGE_ATTN = 5, MTP_STAGE_O_PROJ = 6, MTP_STAGE_NORM_F = 7,
   MTP_STAGE_GATE_UP = 8, MTP_STAGE_DOWN = 9, MTP_STAGE_OUT_NORM = 10, MTP_STAGE_CE_FWD = 11,
   MTP_STAGE_CE_REDUCE = 12, MTP_STAGE_CE_GRAD = 13, MTP_STAGE_CE_DX = 14,
-  MTP_STAGE_CE_NORM_BWD = 15, MTP_STAGE_CE_DW = 16, MTP_STAGE_VERIFY = 17, MTP_STAGE_COUNT = 18
+  MTP_STAGE_CE_NORM_BWD = 15, MTP_STAGE_CE_DW = 16, MTP_STAGE_VERIFY = 17,
+  MTP_STAGE_BWD_RECOMPUTE = 18,     /* mtp_chain_backward: the module's forward again          */
+  MTP_STAGE_BWD_MLP = 19,           /* SwiGLU reverse, its products and Norm_f's reverse       */
+  MTP_STAGE_BWD_ATTN_PROJ = 20,     /* dO and dW_o products                                    */
+  MTP_STAGE_BWD_ATTN = 21,          /* the attention reverse                                   */
+  MTP_STAGE_BWD_QKV = 22,           /* dx_a, dW_qkv products and Norm_a's reverse              */
+  MTP_STAGE_BWD_EH = 23,            /* eh_proj products, hnorm / enorm reverse, dE             */
+  MTP_STAGE_COUNT = 24
 } mtp_stage;
 int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n);
 int mtp_profile_count(void);
@@ -419,7 +496,7 @@ const char *mtp_strerror(int status);
  * struct field added, moved or retyped, a call's meaning changed).  A
  * binding that mirrors the argument structs must refuse a library whose
  * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
-#define MTP_ABI_VERSION 5
+#define MTP_ABI_VERSION 6
 int mtp_abi_version(void);
 
 #ifdef __cplusplus

@@ -1,0 +1,119 @@
+"""GPU parity of mtp_chain_backward against the oracle's gradient of L_MTP
+through the whole chain (oracle/backward.py, bf16 model).
+
+Each side runs its own pipeline on the same seeded inputs: the GPU runs
+mtp_chain_forward, mtp_head_ce_fwd_bwd and mtp_chain_backward on its own
+outputs; the oracle runs oracle.backward.mtp_gradients.  Compared: dh^(0)
+(exactly 0 on rows no loss reaches), dE (exactly 0 on embedding rows no
+state row reads), and every per-depth weight and gain gradient.  Gradient
+entries are far below the 2e-2 max-abs bar, so the gate is the relative
+Frobenius error, below 1e-2 per tensor (bf16 storage of the recomputed
+activations and of every gradient handed to a matrix product, P and dS in
+bf16 inside the attention reverse, fp32 against fp64 accumulation)."""
+import numpy as np
+import pytest
+import torch
+
+from deepseek_sequential_mtp_amd import _lib, synth
+from oracle import backward as ob, rows as orows
+from oracle.numerics import BF16
+from tests.gpu_util import chain_tensors, rel_fro, to_np
+
+pytestmark = pytest.mark.gpu
+
+NAMES = {"g_h": "g_h", "g_e": "g_e", "g_a": "g_a", "g_f": "g_f", "M": "M", "Wqkv": "Wqkv", "Wo": "Wo",
+         "Wgate": "Wgate", "Wup": "Wup", "Wdown": "Wdown"}
+RELF = 1e-2
+
+
+def _gpu_pipeline(cfg, inp, seg=None):
+    t = chain_tensors(inp, torch.bfloat16)
+    fw = _lib.chain_forward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], n_heads=cfg.n_heads,
+                            head_dim=cfg.head_dim, eps=cfg.eps, rope_theta=cfg.rope_theta)
+    ce = _lib.head_ce_fwd_bwd(fw["h"], fw["labels"], t["W_out"], t["g_out"], lam=cfg.lam, eps=cfg.eps)
+    bw = _lib.chain_backward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], fw["h"], ce["dh"],
+                             n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps, rope_theta=cfg.rope_theta)
+    torch.cuda.synchronize()
+    return fw, ce, bw
+
+
+def _check(cfg, inp, bw):
+    print(f"[chain-bwd] oracle for {cfg.name}", flush=True)
+    ref = ob.mtp_gradients(inp["h0"], inp["tokens"], inp["segment_ids"], inp["depths"], inp["E"], inp["W_out"],
+                           inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, cfg.rope_theta, cfg.lam, model=BF16)
+    assert int(to_np(bw["device_error"])[0]) == 0
+    st, _, _, _ = orows.dense_rows(inp["tokens"], inp["segment_ids"], cfg.D)
+    s1 = st[0].reshape(-1).astype(bool)
+    dh0 = to_np(bw["dh0"])
+    assert np.isfinite(dh0).all()
+    assert np.all(dh0[~s1] == 0.0)                      # rows no loss reaches
+    rf = rel_fro(dh0, ref["dh0"])
+    print(f"  dh0 relF {rf:.2e}", flush=True)
+    assert rf < RELF
+    dE = to_np(bw["dE"])
+    read = np.abs(ref["dE"]).max(axis=1) > 0
+    assert np.all(dE[~read] == 0.0)
+    rf = rel_fro(dE, ref["dE"])
+    print(f"  dE relF {rf:.2e} ({int(read.sum())} rows read)", flush=True)
+    assert rf < RELF
+    for k in range(cfg.D):
+        for n, on in NAMES.items():
+            g = to_np(bw["dw"][k][n])
+            r = ref["depths"][k][on]
+            assert np.isfinite(g).all(), (k, n)
+            rf = rel_fro(g, r)
+            print(f"  depth {k + 1} d{n}: relF {rf:.2e}", flush=True)
+            assert rf < RELF, (k, n, rf)
+
+
+@pytest.mark.parametrize("hd", [128, 64])
+def test_chain_backward_bf16_ragged(hd):
+    # several GEMM tiles, ragged tails, packed segments of mixed lengths,
+    # two depths (the carry of depth 2's gradient into depth 1)
+    cfg = synth.scaled(synth.D1, name=f"bwd_hd{hd}", B=2, T=300, d=256, n_heads=256 // hd, head_dim=hd, ffn=688,
+                       V=1000, D=2, seg_lo=20, seg_hi=200, sigma_w=0.05)
+    inp = synth.make_chain_inputs(cfg)
+    print(f"[chain-bwd] {cfg.name} B={cfg.B} T={cfg.T} d={cfg.d} H={cfg.n_heads}x{hd} D={cfg.D}", flush=True)
+    _, _, bw = _gpu_pipeline(cfg, inp)
+    _check(cfg, inp, bw)
+
+
+def test_chain_backward_bf16_depth3_padding_no_rope():
+    cfg = synth.scaled(synth.D1, name="bwd_d3_pad", B=2, T=200, d=128, n_heads=1, head_dim=128, ffn=256, V=512,
+                       D=3, seg_lo=10, seg_hi=90, sigma_w=0.05, rope_theta=0.0)
+    inp = synth.make_chain_inputs(cfg)
+    seg = inp["segment_ids"].copy()
+    seg[1, 130:] = -1                                   # padded tail
+    seg[0, 50] = 77                                     # a one-token segment
+    inp["segment_ids"] = seg
+    print(f"[chain-bwd] {cfg.name}", flush=True)
+    _, _, bw = _gpu_pipeline(cfg, inp)
+    _check(cfg, inp, bw)
+
+
+def test_chain_backward_accumulate_and_dE_adds():
+    cfg = synth.scaled(synth.D1, name="bwd_acc", B=1, T=160, d=128, n_heads=1, head_dim=128, ffn=256, V=304,
+                       D=1, seg_lo=40, seg_hi=160, sigma_w=0.05)
+    inp = synth.make_chain_inputs(cfg)
+    t = chain_tensors(inp, torch.bfloat16)
+    fw = _lib.chain_forward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], n_heads=1, head_dim=128,
+                            eps=cfg.eps, rope_theta=cfg.rope_theta)
+    ce = _lib.head_ce_fwd_bwd(fw["h"], fw["labels"], t["W_out"], t["g_out"], lam=cfg.lam, eps=cfg.eps)
+    kw = dict(n_heads=1, head_dim=128, eps=cfg.eps, rope_theta=cfg.rope_theta)
+    one = _lib.chain_backward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], fw["h"], ce["dh"], **kw)
+    torch.cuda.synchronize()
+    first = {n: one["dw"][0][n].clone() for n in NAMES}
+    dE1 = one["dE"].clone()
+    two = _lib.chain_backward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], fw["h"], ce["dh"],
+                              accumulate=True, out=one, **kw)
+    torch.cuda.synchronize()
+    for n in NAMES:
+        torch.testing.assert_close(two["dw"][0][n], 2 * first[n], rtol=1e-6, atol=0)
+    torch.testing.assert_close(two["dE"], 2 * dE1, rtol=1e-6, atol=0)
+    # the same call twice gives the same bits (no atomics in the reverse pass)
+    three = _lib.chain_backward(t["tokens"], t["segment_ids"], t["h0"], t["E"], t["depths"], fw["h"], ce["dh"],
+                                **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(three["dh0"], one["dh0"]) and torch.equal(three["dE"], dE1)
+    for n in NAMES:
+        assert torch.equal(three["dw"][0][n], first[n]), n
