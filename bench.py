@@ -171,8 +171,7 @@ def algorithmic_flops(cfg, state_mask, counts, run_start_fn):
 def executed_tflop(cfg, run_start):
     """MFMA work the kernels execute per step (multiply-add = 2): every row of
     the dense layout, GEMM tiles padded to 256, attention over the key tiles
-    each 32-query wave visits (masked pairs included) with the probabilities'
-    hi and lo products, and no recomputation."""
+    each 32-query wave visits (masked pairs included), and no recomputation.""" 
     def pad(x):
         return -(-x // 256) * 256
     d, A, f, V, N, hd = cfg.d, cfg.A_w, cfg.ffn, cfg.V, cfg.N, cfg.head_dim
@@ -189,7 +188,7 @@ def executed_tflop(cfg, run_start):
                 lo = rs[w]
                 first = kbeg + max(0, -(-(lo - 63 - kbeg) // 64)) * 64
                 wave_tiles += max(0, (hi - first) // 64 + 1)
-    attn = wave_tiles * cfg.n_heads * (2.0 + 4.0) * 32 * 64 * hd
+    attn = wave_tiles * cfg.n_heads * (2.0 + 2.0) * 32 * 64 * hd
     return cfg.D * (gemm + head + attn) / 1e12
 
 
@@ -272,6 +271,51 @@ def bench_propose(torch, _lib, cfg, inp, R=64, prefix=2048, reps=10):
             "ffn": f, "V": V, "ms": round(ms, 4), "bytes": total, "bytes_weights": weights,
             "bytes_kv": kv_bytes, "achieved": round(gbs, 1), "unit": "GB/s",
             "frac": round(gbs / PEAK_HBM_GBS, 4)}
+
+
+def bench_backward(torch, _lib, cfg, inp, chain_out, ce_out, per, cache, reps=5):
+    """mtp_chain_backward after the timed step (its chain outputs and the head
+    CE's dh): the gradient of L_MTP through every module to h^(0), E and the
+    per-depth weights.  Algorithmic work credits the products of the reverse
+    pass once: the data and weight gradients of every chain GEMM (twice the
+    forward's FLOPs) and 8 A per attention pair (dV, dP, dQ, dK); the
+    module's forward recompute is executed but not credited."""
+    dev = inp["h0"].device
+    out = dict(dh0=torch.empty((cfg.N, cfg.d), dtype=torch.float32, device=dev),
+               dE=torch.zeros((cfg.V, cfg.d), dtype=torch.float32, device=dev),
+               dw=[{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in _lib.GRAD_FIELDS}
+                   for w in inp["depths"]],
+               device_error=torch.empty(1, dtype=torch.int32, device=dev))
+
+    def run():
+        _lib.chain_backward(inp["tokens"], inp["segment_ids"], inp["h0"], inp["E"], inp["depths"], chain_out["h"],
+                            ce_out["dh"], n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps,
+                            rope_theta=cfg.rope_theta, out=out, cache=cache)
+
+    run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    timer = _lib.AllStageTimer(64 * reps)
+    with timer:
+        e0.record()
+        for _ in range(reps):
+            run()
+        e1.record()
+        torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    stages = {k: {"ms": round(float(np.sum(v)) / reps, 4)} for k, v in timer.by_stage().items()}
+    fwd_gemm = sum(p[k] for p in per for k in ("EH_PROJ", "QKV", "O_PROJ", "GATE_UP", "DOWN"))
+    attn_pairs_flops = sum(p["ATTN"] for p in per)          # 4 A P
+    alg = 2.0 * fwd_gemm + 2.0 * attn_pairs_flops
+    # executed: the recompute (the forward, 4 A per pair), then dK/dV (S, dP,
+    # dV, dK) and dQ (S, dP, dQ): 4 + 14 = 18 A per pair
+    executed = 3.0 * fwd_gemm + 4.5 * attn_pairs_flops
+    tf = alg / (ms * 1e-3) / 1e12
+    del out
+    return {"ms": round(ms, 4), "algorithmic_tflop": round(alg / 1e12, 3),
+            "executed_tflop": round(executed / 1e12, 3), "achieved": round(tf, 1), "unit": "TFLOP/s",
+            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(cfg.N / (ms * 1e-3), 1),
+            "stages": stages, "flops_basis": "algorithmic reverse-pass FLOPs (recompute not credited) / call time"}
 
 
 def bench_verify(torch, _lib, synth, reps=20):
@@ -377,23 +421,11 @@ def main():
         print(f"top-1 accuracy by depth {ce_out['accuracy'].tolist()} "
               f"(correct {ce_out['correct'].tolist()} of {ce_out['counts'].tolist()})", file=sys.stderr)
 
-    # per-stage times (one profiled step per stage, outside the timed region)
-    stage_ms = {}
-    for name in _lib.STAGES:
-        if name == "VERIFY":
-            continue
-        with _lib.StageTimer(name, 64) as tm:
-            step()
-        ts = tm.times_ms()
-        if ts:
-            stage_ms[name] = sum(ts)
-    dominant = max((s for s in stage_ms if s in ("EH_PROJ", "QKV", "ATTN", "O_PROJ", "GATE_UP", "DOWN",
-                                                   "CE_FWD", "CE_GRAD", "CE_DX", "CE_DW")),
-                   key=lambda s: stage_ms[s])
-
-    # timed region; the dominant stage's launches carry HIP events (a stage
-    # launches once per depth and logit slab)
-    timer = _lib.StageTimer(dominant, 64 * args.steps)
+    # timed region: every launch of every stage carries a HIP event pair on
+    # the launch stream (a stage launches once per depth, logit slab or row
+    # group); the dominant stage is the MFMA stage with the most time in this
+    # region, and its roofline comes from the same launches
+    timer = _lib.AllStageTimer(256 * args.steps)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
@@ -406,8 +438,12 @@ def main():
     wall = time.perf_counter() - t0
     ms_step = ev[0].elapsed_time(ev[-1]) / args.steps
     per_step = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
-    dom_times = timer.times_ms()
-    assert len(dom_times) == timer.count and len(dom_times) % args.steps == 0
+    launches = timer.by_stage()
+    stage_ms = {name: float(np.sum(ts)) / args.steps for name, ts in launches.items()}
+    mfma_stages = ("EH_PROJ", "QKV", "ATTN", "O_PROJ", "GATE_UP", "DOWN", "CE_FWD", "CE_DX", "CE_DW")
+    dominant = max((s_ for s_ in stage_ms if s_ in mfma_stages), key=lambda s_: stage_ms[s_])
+    dom_times = launches[dominant]
+    assert len(dom_times) % args.steps == 0
     dom_avg_ms = float(np.mean(dom_times))
     dom_step_ms = float(np.sum(dom_times)) / args.steps
 
@@ -460,6 +496,13 @@ def main():
                   f"({100 * v['frac']:.1f}% of HBM), {v['achieved_full_read']:.0f} GB/s on all rows, "
                   f"mean accepted {v['mean_accepted']}", file=sys.stderr)
 
+    backward = bench_backward(torch, _lib, cfg, inp, chain_out, ce_out, per, cache)
+    if args.stages:
+        print(f"  chain backward: {backward['ms']:.3f} ms, {backward['achieved']:.0f} TFLOP/s algorithmic "
+              f"({100 * backward['frac']:.1f}% of peak)", file=sys.stderr)
+        for k, v in sorted(backward["stages"].items(), key=lambda kv: -kv[1]["ms"]):
+            print(f"    {k:14s} {v['ms']:9.3f} ms", file=sys.stderr)
+
     propose = bench_propose(torch, _lib, cfg, inp)
     if args.stages:
         print(f"  propose R={propose['R']} cached={propose['cached_slots']}: {propose['ms']:.3f} ms, "
@@ -497,6 +540,7 @@ def main():
                      "launches_per_step": len(dom_times) // args.steps, "flops_basis": dom_note},
         "stages": stages,
         "verify": verify,
+        "chain_backward": backward,
         "propose": propose,
         "cpu_baseline": cpu,
     }

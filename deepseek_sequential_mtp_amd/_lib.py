@@ -23,7 +23,7 @@ EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propos
            "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
            "mtp_profile_count", "mtp_verify_noalloc", "mtp_chain_backward",
-           "mtp_chain_backward_workspace_size")
+           "mtp_chain_backward_workspace_size", "mtp_profile_all")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
           "VERIFY", "BWD_RECOMPUTE", "BWD_MLP", "BWD_ATTN_PROJ", "BWD_ATTN", "BWD_QKV", "BWD_EH")
@@ -48,7 +48,7 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 6     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 7     # the struct layouts below mirror include/mtp.h at this version
 
 
 class DepthGrads(C.Structure):
@@ -138,6 +138,7 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_abi_version.restype = C.c_int
         lib.mtp_profile_stage.argtypes = [C.c_int, C.POINTER(vp), C.POINTER(vp), C.c_int]
         lib.mtp_profile_count.restype = C.c_int
+        lib.mtp_profile_all.argtypes = [C.POINTER(vp), C.POINTER(vp), C.POINTER(C.c_int), C.c_int]
         if lib.mtp_abi_version() != ABI_VERSION:
             raise RuntimeError(f"{path} has ABI version {lib.mtp_abi_version()}, this binding "
                                f"expects {ABI_VERSION}: rebuild it")
@@ -448,3 +449,37 @@ class StageTimer:
         torch.cuda.synchronize()
         k = min(self.count, self.n)
         return [self.start[i].elapsed_time(self.stop[i]) for i in range(k)]
+
+
+class AllStageTimer:
+    """Arms mtp_profile_all with ``n`` hipEvent pairs: every launch of every
+    stage records a pair and its stage id.  ``by_stage()`` returns the launch
+    times (ms) grouped by stage name (the first ``n`` launches)."""
+
+    def __init__(self, n: int):
+        self.start = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        self.stop = [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+        for e in self.start + self.stop:
+            e.record()
+        torch.cuda.synchronize()
+        self._s = (vp * n)(*[e.cuda_event for e in self.start])
+        self._e = (vp * n)(*[e.cuda_event for e in self.stop])
+        self._ids = (C.c_int * n)()
+        self.n = n
+
+    def __enter__(self):
+        _check(load().mtp_profile_all(self._s, self._e, self._ids, self.n))
+        return self
+
+    def __exit__(self, *exc):
+        self.count = load().mtp_profile_count()
+        load().mtp_profile_stage(-1, None, None, 0)
+
+    def by_stage(self):
+        torch.cuda.synchronize()
+        if self.count > self.n:
+            raise RuntimeError(f"{self.count} launches recorded into {self.n} slots")
+        out: Dict[str, List[float]] = {}
+        for i in range(self.count):
+            out.setdefault(STAGES[self._ids[i]], []).append(self.start[i].elapsed_time(self.stop[i]))
+        return out

@@ -18,8 +18,9 @@
 //                    MFMA's K-slots are mapped to the keys those registers
 //                    hold, and V^T is read with the transposing LDS read at
 //                    the same key order).
-// P enters the bf16 product as hi + lo (two MFMAs), carrying ~16 mantissa
-// bits of the probabilities (they are no stored tensor of the method).
+// P enters the bf16 product rounded to bf16 once (an unmirrored rounding:
+// the probabilities are no stored tensor of the method; relative error at
+// most 2^-9 per weight).
 #include "gemm.hpp"
 #include "kernels.hpp"
 
@@ -236,23 +237,13 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     for (int mb = 0; mb < 2; ++mb)
 #pragma unroll
       for (int j = 0; j < 32 / KPS; ++j) {
-        uint4 pb[NBQ], pl[NBQ];
+        uint4 pb[NBQ];
 #pragma unroll
         for (int nb = 0; nb < NBQ; ++nb) {
           float v[E];
 #pragma unroll
           for (int e = 0; e < E; ++e) v[e] = s[mb][nb][E * j + e];
           pb[nb] = f32_to_chunk(v, T{});
-          if constexpr (sizeof(T) == 2) {
-            const uint32_t w[4] = {pb[nb].x, pb[nb].y, pb[nb].z, pb[nb].w};
-            float rr[8];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              rr[2 * i] = v[2 * i] - bf16_lo_f32(w[i]);
-              rr[2 * i + 1] = v[2 * i + 1] - bf16_hi_f32(w[i]);
-            }
-            pl[nb] = f32_to_chunk(rr, T{});
-          }
         }
 #pragma unroll
         for (int md = 0; md < MD; ++md) {
@@ -286,10 +277,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
             a = make_uint4(w[0], w[1], w[2], w[3]);
           }
 #pragma unroll
-          for (int nb = 0; nb < NBQ; ++nb) {
-            mma32(a, pb[nb], o[md][nb], T{});
-            if constexpr (sizeof(T) == 2) mma32(a, pl[nb], o[md][nb], T{});
-          }
+          for (int nb = 0; nb < NBQ; ++nb) mma32(a, pb[nb], o[md][nb], T{});
         }
       }
   };

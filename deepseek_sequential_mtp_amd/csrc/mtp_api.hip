@@ -74,6 +74,8 @@ inline int ceil_div(long a, long b) { return (int)((a + b - 1) / b); }
 // ---------------------------------------------------------------------------
 struct Profile {
   int stage = -1;
+  bool all = false;            // every stage (mtp_profile_all)
+  int *ids = nullptr;          // [host] stage of each slot (mtp_profile_all)
   hipEvent_t *start = nullptr, *stop = nullptr;
   int n = 0, count = 0;
 };
@@ -83,9 +85,11 @@ struct StageScope {
   hipStream_t s;
   bool on;
   int slot;
-  StageScope(int stage, hipStream_t st) : s(st), on(g_prof.stage == stage && g_prof.n > 0), slot(0) {
+  StageScope(int stage, hipStream_t st)
+      : s(st), on((g_prof.all || g_prof.stage == stage) && g_prof.n > 0), slot(0) {
     if (on) {
       slot = g_prof.count % g_prof.n;
+      if (g_prof.ids != nullptr) g_prof.ids[slot] = stage;
       (void)hipEventRecord(g_prof.start[slot], s);
     }
   }
@@ -1047,6 +1051,18 @@ int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_ev
   g_prof.stop = reinterpret_cast<hipEvent_t *>(const_cast<void **>(stop_events));
   g_prof.n = n;
   g_prof.count = 0;
+  return MTP_OK;
+}
+
+int mtp_profile_all(void *const *start_events, void *const *stop_events, int *stage_ids, int n) {
+  if (n < 1) return MTP_ERR_ARG;
+  if (!start_events || !stop_events || !stage_ids) return MTP_ERR_NULL;
+  g_prof = Profile();
+  g_prof.all = true;
+  g_prof.ids = stage_ids;
+  g_prof.start = reinterpret_cast<hipEvent_t *>(const_cast<void **>(start_events));
+  g_prof.stop = reinterpret_cast<hipEvent_t *>(const_cast<void **>(stop_events));
+  g_prof.n = n;
   return MTP_OK;
 }
 

@@ -487,6 +487,11 @@ typedef enum {
   MTP_STAGE_COUNT = 24
 } mtp_stage;
 int mtp_profile_stage(int stage, void *const *start_events, void *const *stop_events, int n);
+/* As mtp_profile_stage for every stage at once: launch j of any stage
+ * records start_events[j % n] / stop_events[j % n] and writes the stage's
+ * id to stage_ids[j % n] ([host] array owned by the caller).
+ * mtp_profile_stage(-1, ...) disarms. */
+int mtp_profile_all(void *const *start_events, void *const *stop_events, int *stage_ids, int n);
 int mtp_profile_count(void);
 
 /* Static string naming a status code. */
@@ -496,7 +501,7 @@ const char *mtp_strerror(int status);
  * struct field added, moved or retyped, a call's meaning changed).  A
  * binding that mirrors the argument structs must refuse a library whose
  * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
-#define MTP_ABI_VERSION 6
+#define MTP_ABI_VERSION 7
 int mtp_abi_version(void);
 
 #ifdef __cplusplus
