@@ -103,6 +103,47 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
   }
 }
 
+// xT[c, r] = x[r, c] for an [R, C] bf16 matrix (C % 8 == 0); xT has leading
+// dimension ldT >= R rounded up to 8 (the pad columns are written as 0).
+// 64 x 64 tiles through LDS: 16-byte reads along C, 16-byte writes along R.
+__global__ __launch_bounds__(256) void transpose_bf16_kernel(const bf16_t *__restrict__ x, int R, int C,
+                                                             bf16_t *__restrict__ xT, long ldT) {
+  __shared__ uint16_t tile[64][64 + 2];
+  const int r0 = blockIdx.x * 64, c0 = blockIdx.y * 64;   // row tiles on x (no 65535 limit)
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int rr = q >> 3, cc = (q & 7) * 8;
+    const int r = r0 + rr, c = c0 + cc;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (r < R && c < C) v = *reinterpret_cast<const uint4 *>(x + (long)r * C + c);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[rr][cc + 2 * e] = (uint16_t)(w[e] & 0xffffu);
+      tile[rr][cc + 2 * e + 1] = (uint16_t)(w[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int q = threadIdx.x; q < 512; q += 256) {
+    const int cc = q >> 3, rr = (q & 7) * 8;
+    const int c = c0 + cc, r = r0 + rr;
+    if (c >= C || r >= ldT) continue;
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = r + 2 * e < R ? tile[rr + 2 * e][cc] : 0u;
+      const uint32_t hi = r + 2 * e + 1 < R ? tile[rr + 2 * e + 1][cc] : 0u;
+      w[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<uint4 *>(xT + (long)c * ldT + r) = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
+hipError_t launch_transpose_bf16(const bf16_t *x, int R, int C, bf16_t *xT, long ldT, hipStream_t s) {
+  if (R == 0 || C == 0) return hipSuccess;
+  hipLaunchKernelGGL(transpose_bf16_kernel, dim3((R + 63) / 64, (C + 63) / 64), dim3(256), 0, s, x, R, C, xT, ldT);
+  return hipGetLastError();
+}
+
 template <typename T, typename ZT>
 hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
                         const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,

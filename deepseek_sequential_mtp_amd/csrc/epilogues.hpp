@@ -434,6 +434,117 @@ struct EpiCEFwd {
   }
 };
 
+// ---------------------------------------------------------------------------
+// Linear-CE forward on the transposed tile: one BM x BN tile of z^T = W x_hat^T
+// (vocabulary ids on rows, the slab's rows -- "tokens" -- on columns), so that
+// the shared head W is the pair-row A operand and x_hat^T the MN-major B
+// operand (both move in whole 128-byte lines).  Per token column: the tile's
+// max m_t and s_t = sum exp(z - m_t) over its valid vocabulary rows go to
+// part[token * nt + tile_m] (float2), the target logit to target[token] when
+// the label falls in this tile, and the fp16 offsets z - m_t to zout[token, v]
+// (4 consecutive ids per 8-byte store).  A lane holds one token column and 16
+// vocabulary rows per block; the 32 rows of a block pair live in lanes l and
+// l ^ 32, and the WGM row waves meet through LDS (2 x WGM x BN floats).
+// Requires BN * V * 2 < 2^31 and V % 4 == 0 (checked by the caller).
+// ---------------------------------------------------------------------------
+struct EpiCEFwdT {
+  const int *labels; float2 *part; float *target; _Float16 *zout; int M, V, ntok, nt;
+  // stage: 64 token rows x 256 ids of fp16 (32 KB) for the coalesced logit stores
+  template <class Cfg>
+  __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
+                                        int wn, int lane, int, char *lds, char *stage) const {
+    static_assert(Cfg::BM == 256 && Cfg::WGN == 2, "staged stores assume 256 ids and two column waves");
+    float *redm = reinterpret_cast<float *>(lds);          // [WGM][BN] column max per row wave
+    float *reds = redm + Cfg::WGM * Cfg::BN;               // [WGM][BN] column sum-exp per row wave
+    const int hl = lane >> 5, c32 = lane & 31;
+    const long cols = ntok - n0 < Cfg::BN ? ntok - n0 : Cfg::BN;
+    const __amdgpu_buffer_rsrc_t rl = make_rsrc(labels + n0, cols * 4L);
+    const __amdgpu_buffer_rsrc_t rt = make_rsrc(target + n0, cols * 4L);
+    // 1) column max over this wave's rows
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          mx = m0 + acc_row<Cfg>(wm, i, r, lane) < M ? fmaxf(mx, acc[i][j][r]) : mx;
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      if (hl == 0) redm[wm * Cfg::BN + acc_col<Cfg>(wn, j, lane)] = mx;
+    }
+    __syncthreads();
+    // 2) per column: the tile max, sum of exp(z - m_t), the target logit
+    float mtj[Cfg::NB];
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j) {
+      const int col = acc_col<Cfg>(wn, j, lane);
+      float mt = redm[col];
+#pragma unroll
+      for (int w = 1; w < Cfg::WGM; ++w) mt = fmaxf(mt, redm[w * Cfg::BN + col]);
+      mtj[j] = mt;
+      const float nm = -mt * kLog2e;
+      const int lab0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rl, (unsigned)(col * 4), 0, 0);
+      // the label's row relative to this wave's first row, if it is one of this lane's
+      const int rel = (col < cols ? lab0 : -1) - (m0 + wm * Cfg::WM);
+      float sum = 0.f, tv = 0.f;
+#pragma unroll
+      for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int vr = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const float z = acc[i][j][r];
+          sum += m0 + wm * Cfg::WM + vr < M ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
+          tv = vr == rel ? z : tv;
+        }
+      const bool has = rel >= 0 && rel < Cfg::WM && ((rel >> 2) & 1) == hl;
+      if (__builtin_amdgcn_ballot_w64(has) != 0) buf_store_elem(rt, has ? (unsigned)(col * 4) : kOOB, tv, float{});
+      sum += __shfl_xor(sum, 32);
+      if (hl == 0) reds[wm * Cfg::BN + col] = sum;
+    }
+    // 3) logits as fp16 offsets z - m_t: per column block j, the 64 token rows
+    //    of both column waves staged in LDS (8-byte unit u of token row t at
+    //    u ^ (t & 63): a half-wave's 32 rows hit distinct banks), then copied
+    //    out in 16-byte chunks along each token's row
+    const int nthr = Cfg::NT;
+#pragma unroll
+    for (int j = 0; j < Cfg::NB; ++j) {
+      __syncthreads();
+      const int tl = wn * 32 + c32;                          // token row in the stage
+#pragma unroll
+      for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+          const h4 hv = {(_Float16)(acc[i][j][4 * q] - mtj[j]), (_Float16)(acc[i][j][4 * q + 1] - mtj[j]),
+                         (_Float16)(acc[i][j][4 * q + 2] - mtj[j]), (_Float16)(acc[i][j][4 * q + 3] - mtj[j])};
+          const int u = (wm * Cfg::WM + i * 32 + 8 * q + 4 * hl) >> 2;   // 8-byte unit of the id row
+          *reinterpret_cast<h4 *>(stage + tl * 512 + ((u ^ (tl & 63)) << 3)) = hv;
+        }
+      __syncthreads();
+      for (int c = threadIdx.x; c < 64 * 32; c += nthr) {
+        const int row = c >> 5, cu = (c & 31) * 2;             // token row, first 8-byte unit
+        const int tok = n0 + (row >> 5) * Cfg::WN + j * 32 + (row & 31);
+        const int v = m0 + cu * 4;
+        if (tok >= ntok || v >= M) continue;
+        const uint2 lo = *reinterpret_cast<const uint2 *>(stage + row * 512 + ((cu ^ (row & 63)) << 3));
+        const uint2 hi = *reinterpret_cast<const uint2 *>(stage + row * 512 + (((cu + 1) ^ (row & 63)) << 3));
+        *reinterpret_cast<uint4 *>(zout + (long)tok * V + v) = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      }
+    }
+    __syncthreads();
+    const int t = threadIdx.x;
+    if (t < Cfg::BN && n0 + t < ntok) {
+      float mt = redm[t], st = reds[t];
+#pragma unroll
+      for (int w = 1; w < Cfg::WGM; ++w) {
+        mt = fmaxf(mt, redm[w * Cfg::BN + t]);
+        st += reds[w * Cfg::BN + t];
+      }
+      part[(long)(n0 + t) * nt + m0 / Cfg::BM] = make_float2(mt, st);
+    }
+  }
+};
+
 // Whether a loader stages its operand in 128-byte pair rows.
 template <class L, class = void>
 struct PairRows : std::false_type {};
@@ -545,7 +656,9 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_kernel(LA la, LB lb, Epi epi, in
 // epilogue on the sum.
 template <class Cfg, class Epi>
 __global__ __launch_bounds__(Cfg::NT) void gemm_fixup_kernel(Epi epi, TileSched ts) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * Cfg::BM * sizeof(float)];
+  __shared__ __attribute__((aligned(16))) char lds[2 * Cfg::WGM * (Cfg::BM > Cfg::BN ? Cfg::BM : Cfg::BN) * sizeof(float)];
+  // a second region for epilogues that stage their stores (32 KB)
+  __shared__ __attribute__((aligned(16))) char lds2[std::is_same_v<Epi, EpiCEFwdT> ? 32768 : 16];
   const int tl = blockIdx.x;
   int tm, tn;
   tile_coords(ts.tile0 + tl, ts.mt, ts.nt, ts.group_m, tm, tn);
@@ -560,7 +673,7 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fixup_kernel(Epi epi, TileSched 
     add_partial<Cfg>(ts.ws + ((long)sp * ts.ntiles + tl) * partial_floats<Cfg>(), acc);
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   epi.template apply<Cfg>(acc, tm * Cfg::BM, tn * Cfg::BN, wave / Cfg::WGN, wave % Cfg::WGN, lane, 0, lds,
-                          lds);
+                          lds2);
 }
 
 // Host-side launch helpers.  launch_gemm: every tile, K split k_splits ways,

@@ -72,6 +72,8 @@ hipError_t launch_decode_attention(const T *qkv, T *cache, T *out, const int32_t
                                    int H, int hd, long L_max, hipStream_t s);
 
 // CE reductions
+// xT[c, r] = x[r, c] (bf16 [R, C], C % 8 == 0; ldT >= R rounded up to 8, pad written 0)
+hipError_t launch_transpose_bf16(const bf16_t *x, int R, int C, bf16_t *xT, long ldT, hipStream_t s);
 template <typename T, typename ZT>
 hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, const float *lse,
                         const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,

@@ -232,6 +232,21 @@ int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, flo
   return MTP_OK;
 }
 
+// Transposed tile (bf16): z^T = W_out x_hat^T with W_out the pair-row A
+// operand and x_hat^T [d, ldT] the MN-major B operand (whole 128-byte lines
+// for both); the token tiles of one vocabulary tile run next to each other,
+// so W_out is read once.
+template <typename T, class Cfg>
+int gemm_ce_fwd_t_cfg(const T *xhatT, long ldT, const T *W, const int *lab, float2 *part, float *target,
+                      _Float16 *z, int rows, int V, int d, float *skws, hipStream_t s) {
+  const int nt = ceil_div(V, Cfg::BM);
+  EpiCEFwdT epi{lab, part, target, z, V, V, rows, nt};
+  PA<T, Cfg> la{W, (long)d, V, d};
+  MB_<T, Cfg> lb{xhatT, ldT, rows, d};
+  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, V, rows, d, 1, skws, s)));
+  return MTP_OK;
+}
+
 // dx[split] = scale * dz[:, split range] W_out[split range, :]  (B operand MN-major)
 template <typename T, class Cfg>
 int gemm_dx_cfg(const T *dz, const T *W, float *dxs, long slab, int M, int V, int d, const float *scale,
@@ -719,7 +734,7 @@ int check_ce_ptrs(const mtp_ce_args *a) {
 }
 
 struct CeDims {
-  long N; int d, V, nt, splits; bool big, big_dx;
+  long N, ldT; int d, V, nt, splits; bool big, big_dx;
   long slab;          // rows per fp32 logit slab
   long group;         // rows per dz buffer: a whole number of slabs (or all N rows)
 };
@@ -743,6 +758,7 @@ CeDims ce_dims(const mtp_ce_args *a) {
   c.group = g < c.slab ? c.slab : (g > c.N ? c.N : g);
   c.big = sizeof(T) == 2 && use_big(c.slab, c.V);
   c.nt = ceil_div(c.V, c.big ? 256 : 128);
+  c.ldT = (c.N + 7) / 8 * 8;                    // x_hat^T leading dimension (bf16 runs)
   // the dx_hat GEMM (group rows x d, K = V) may also fill the chip with K splits
   c.big_dx = sizeof(T) == 2 && (long)ceil_div(c.group, 256) * ceil_div(c.d, 256) * 8 >= 256;
   // with a round of 256x256 tiles or more the dx GEMM needs no K splits of
@@ -752,7 +768,7 @@ CeDims ce_dims(const mtp_ce_args *a) {
   return c;
 }
 
-constexpr int kCeParts = 18;     // workspace regions of the CE call
+constexpr int kCeParts = 19;     // workspace regions of the CE call
 
 template <typename T>
 size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
@@ -777,6 +793,7 @@ size_t ce_layout(const mtp_ce_args *a, Carve &c, void **p) {
   p[15] = c.take<float>(acc ? m.slab : 0);
   p[16] = c.take<int32_t>(acc ? m.N : 0);
   p[17] = c.take<int32_t>(acc ? a->D : 0);
+  p[18] = c.take<T>(sizeof(T) == 2 ? (size_t)m.d * m.ldT : 0);   // x_hat^T (bf16 runs)
   return c.off;
 }
 
@@ -799,6 +816,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
   float *dxs = (float *)p[11];
   float *dg_part = (float *)p[12];
   LogitT<T> *zbuf = (LogitT<T> *)p[13];
+  T *xhatT = (T *)p[18];
   float *skws = sizeof(T) == 2 ? (float *)p[14] : nullptr;
   const bool want_acc = a->pred || a->correct || a->accuracy;
   float *rowmax = want_acc ? (float *)p[15] : nullptr;
@@ -818,6 +836,8 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
       MTP_STAGE(MTP_STAGE_OUT_NORM);
       MTP_TRY(launch_out_norm<T>(h, a->g_out, xhat, r, a->labels + (long)k * N, lab, a->device_error, N, d, V,
                                  a->eps, s));
+      if constexpr (sizeof(T) == 2)
+        if (m.big) MTP_TRY(launch_transpose_bf16(reinterpret_cast<const bf16_t *>(xhat), N, d, xhatT, m.ldT, s));
     }
     {
       // the backward scale depends on the labels only: known before any slab
@@ -832,10 +852,18 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         const int32_t *ls = lab + r0;
         {
           MTP_STAGE(MTP_STAGE_CE_FWD);
-          st = pick<T>(m.big, [&](auto cfg) {
-            return gemm_ce_fwd_cfg<T, decltype(cfg)>(xhat + r0 * d, (const T *)a->W_out, ls, part, target + r0,
-                                                      zbuf, nr, V, d, skws, s);
-          });
+          if constexpr (sizeof(T) == 2) {
+            // the transposed tile on 256 x 256 tiles; small problems keep the row tile
+            if (m.big)
+              st = gemm_ce_fwd_t_cfg<T, Big>(xhatT + r0, m.ldT, (const T *)a->W_out, ls, part, target + r0, zbuf,
+                                             nr, V, d, skws, s);
+            else
+              st = gemm_ce_fwd_cfg<T, Small>(xhat + r0 * d, (const T *)a->W_out, ls, part, target + r0, zbuf, nr,
+                                             V, d, skws, s);
+          } else {
+            st = gemm_ce_fwd_cfg<T, Small>(xhat + r0 * d, (const T *)a->W_out, ls, part, target + r0, zbuf, nr, V,
+                                           d, skws, s);
+          }
         }
         if (st) return st;
         {
@@ -846,7 +874,7 @@ int ce_run(const mtp_ce_args *a, hipStream_t s) {
         }
         {
           MTP_STAGE(MTP_STAGE_CE_GRAD);
-          MTP_TRY((launch_ce_dz<T, LogitT<T>>(zbuf, part, m.nt, m.big ? Big::BN : Small::BN, lse + r0, ls,
+          MTP_TRY((launch_ce_dz<T, LogitT<T>>(zbuf, part, m.nt, m.big ? Big::BM : Small::BM, lse + r0, ls,
                                               dz + (r0 - g0) * V, rowmax, want_acc ? pred + r0 : nullptr, nr,
                                               V, s)));
         }
