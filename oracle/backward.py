@@ -126,25 +126,18 @@ def attention_backward(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarr
     return dq, dk, dv
 
 
-def module_backward(h_prev: np.ndarray, tokens: np.ndarray, segment_ids: np.ndarray, depth: int,
-                    w: Dict[str, np.ndarray], E: np.ndarray, n_heads: int, head_dim: int, eps: float,
-                    rope_theta: float, dh: np.ndarray, model: Model = EXACT):
-    """Gradients of one module (M7.6 0x03/0x03C forward) given dL/dh^(k) = dh
-    [B*T, d] at its output.  Returns dict(dh_prev [B*T, d], dE [V, d],
-    and one entry per parameter name in PARAMS)."""
-    B, T = segment_ids.shape
+def block_backward(act: Dict[str, np.ndarray], segment_ids: np.ndarray, w: Dict[str, np.ndarray], n_heads: int,
+                   head_dim: int, eps: float, rope_theta: float, dh: np.ndarray, model: Model = EXACT):
+    """Reverse of the block a = u + Attn(Norm_a(u)), h = a + FFN(Norm_f(a))
+    given dL/dh = dh, from the forward's stored activations ``act`` (u_in,
+    x_a, q, k, v after RoPE, o, a, y, gsw).  Returns dict(du_in = dL/du and the
+    gradients of g_a, Wqkv, Wo, g_f, Wgate, Wup, Wdown)."""
+    B, T = np.asarray(segment_ids).shape
     N = B * T
     A_w = n_heads * head_dim
     st = model.store
-    W = {n: np.asarray(w[n], np.float64) for n in PARAMS}
-    _, act = module_forward(h_prev, tokens, segment_ids, depth, w, E, n_heads, head_dim, eps,
-                            rope_theta, model, keep=True)
-    h_prev = np.asarray(h_prev, np.float64)
-    idx = np.minimum(np.arange(T) + depth, T - 1)
-    shifted = np.clip(np.asarray(tokens)[:, idx], 0, E.shape[0] - 1).reshape(N)
-    e = np.asarray(E, np.float64)[shifted]
+    W = {n: np.asarray(w[n], np.float64) for n in ("g_a", "Wqkv", "Wo", "g_f", "Wgate", "Wup", "Wdown")}
     out: Dict[str, np.ndarray] = {}
-
     # h = a + gsw Wd^T
     g = st(np.asarray(dh, np.float64))
     out["Wdown"] = g.T @ act["gsw"]
@@ -183,8 +176,34 @@ def module_backward(h_prev: np.ndarray, tokens: np.ndarray, segment_ids: np.ndar
     out["Wqkv"] = dqkv.T @ act["x_a"]
     dxa = dqkv @ W["Wqkv"]
     # x_a = RMSNorm_{g_a}(u); the residual passes da to u
-    du_norm, out["g_a"] = rmsnorm_backward(act["u"], W["g_a"], eps, dxa)
-    du = da + du_norm
+    du_norm, out["g_a"] = rmsnorm_backward(act["u_in"], W["g_a"], eps, dxa)
+    out["du_in"] = da + du_norm
+    return out
+
+
+def module_backward(h_prev: np.ndarray, tokens: np.ndarray, segment_ids: np.ndarray, depth: int,
+                    w: Dict[str, np.ndarray], E: np.ndarray, n_heads: int, head_dim: int, eps: float,
+                    rope_theta: float, dh: np.ndarray, model: Model = EXACT):
+    """Gradients of one module (M7.6 0x03/0x03C forward) given dL/dh^(k) = dh
+    [B*T, d] at its output.  Returns dict(dh_prev [B*T, d], dE [V, d],
+    and one entry per parameter name in PARAMS)."""
+    B, T = segment_ids.shape
+    N = B * T
+    A_w = n_heads * head_dim
+    st = model.store
+    W = {n: np.asarray(w[n], np.float64) for n in PARAMS}
+    _, act = module_forward(h_prev, tokens, segment_ids, depth, w, E, n_heads, head_dim, eps,
+                            rope_theta, model, keep=True)
+    h_prev = np.asarray(h_prev, np.float64)
+    idx = np.minimum(np.arange(T) + depth, T - 1)
+    shifted = np.clip(np.asarray(tokens)[:, idx], 0, E.shape[0] - 1).reshape(N)
+    e = np.asarray(E, np.float64)[shifted]
+    out: Dict[str, np.ndarray] = {}
+
+    act = dict(act, u_in=act["u"])
+    r = block_backward(act, segment_ids, w, n_heads, head_dim, eps, rope_theta, dh, model)
+    du = r.pop("du_in")
+    out.update(r)
     # u = M [h_bar; e_bar]
     dub = st(du)
     out["M"] = dub.T @ act["c"]
