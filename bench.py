@@ -318,6 +318,52 @@ def bench_backward(torch, _lib, cfg, inp, chain_out, ce_out, per, cache, reps=5)
             "stages": stages, "flops_basis": "algorithmic reverse-pass FLOPs (recompute not credited) / call time"}
 
 
+def bench_horizons(torch, _lib, cfg, inp, K=2, reps=3):
+    """mtp_horizon_heads at the workload's width: K independent horizon heads
+    (a Transformer block each, then the shared head), forward and backward one
+    head after another on the step's trunk state h^(0).  Algorithmic work per
+    head: the block's forward (6 d A + 2 A d + 6 d f per row, 4 A per attention
+    pair), its backward (twice that), and the head CE's 6 d V per labelled row."""
+    dev = inp["h0"].device
+    g = torch.Generator(device=dev).manual_seed(777)
+    d, A, f = cfg.d, cfg.A_w, cfg.ffn
+
+    def normal(shape, sigma, mean=0.0, dtype=torch.bfloat16):
+        return (torch.randn(shape, generator=g, device=dev) * sigma + mean).to(dtype)
+
+    blocks = [dict(g_a=normal((d,), 0.1, 1.0, torch.float32), g_f=normal((d,), 0.1, 1.0, torch.float32),
+                   Wqkv=normal((3 * A, d), cfg.sigma_w), Wo=normal((d, A), cfg.sigma_w),
+                   Wgate=normal((f, d), cfg.sigma_w), Wup=normal((f, d), cfg.sigma_w),
+                   Wdown=normal((d, f), cfg.sigma_w)) for _ in range(K)]
+    cache = {}
+    run = lambda out=None: _lib.horizon_heads(inp["tokens"], inp["segment_ids"], inp["h0"], blocks, inp["W_out"],
+                                              inp["g_out"], n_heads=cfg.n_heads, head_dim=cfg.head_dim, lam=cfg.lam,
+                                              eps=cfg.eps, rope_theta=cfg.rope_theta, out=out, cache=cache)
+    out = run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        run(out)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    seg = inp["segment_ids"].cpu().numpy()
+    rs = run_starts(seg)
+    pos = np.arange(cfg.T)[None, :]
+    active = seg >= 0
+    pairs = float(((pos - rs + 1) * active).sum())
+    N = cfg.N
+    block = (6.0 * d * A + 2.0 * A * d + 6.0 * d * f) * N + 4.0 * A * pairs
+    labelled = out["counts"].cpu().numpy().astype(np.float64)
+    alg = K * 3.0 * block + float(labelled.sum()) * 6.0 * d * cfg.V
+    tf = alg / (ms * 1e-3) / 1e12
+    del blocks, out, cache
+    return {"K": K, "ms": round(ms, 4), "algorithmic_tflop": round(alg / 1e12, 3), "achieved": round(tf, 1),
+            "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "flops_basis": "per head: block forward + backward (3x the forward) + head CE 6 d V per labelled row"}
+
+
 def bench_verify(torch, _lib, synth, reps=20):
     """mtp_verify on the retained-module verify workload (256 requests,
     V = 129280, gamma = 1..4): kernel time from HIP events around its
@@ -503,6 +549,11 @@ def main():
         for k, v in sorted(backward["stages"].items(), key=lambda kv: -kv[1]["ms"]):
             print(f"    {k:14s} {v['ms']:9.3f} ms", file=sys.stderr)
 
+    horizons = bench_horizons(torch, _lib, cfg, inp)
+    if args.stages:
+        print(f"  horizon heads K={horizons['K']}: {horizons['ms']:.3f} ms, {horizons['achieved']:.0f} TFLOP/s "
+              f"({100 * horizons['frac']:.1f}% of peak)", file=sys.stderr)
+
     propose = bench_propose(torch, _lib, cfg, inp)
     if args.stages:
         print(f"  propose R={propose['R']} cached={propose['cached_slots']}: {propose['ms']:.3f} ms, "
@@ -541,6 +592,7 @@ def main():
         "stages": stages,
         "verify": verify,
         "chain_backward": backward,
+        "horizon_heads": horizons,
         "propose": propose,
         "cpu_baseline": cpu,
     }

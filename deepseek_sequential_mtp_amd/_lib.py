@@ -23,7 +23,9 @@ EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propos
            "mtp_chain_workspace_size", "mtp_ce_workspace_size", "mtp_verify_workspace_size",
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
            "mtp_profile_count", "mtp_verify_noalloc", "mtp_chain_backward",
-           "mtp_chain_backward_workspace_size", "mtp_profile_all")
+           "mtp_chain_backward_workspace_size", "mtp_profile_all", "mtp_horizon_heads",
+           "mtp_horizon_heads_workspace_size")
+BLOCK_FIELDS = ("g_a", "g_f", "Wqkv", "Wo", "Wgate", "Wup", "Wdown")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
           "VERIFY", "BWD_RECOMPUTE", "BWD_MLP", "BWD_ATTN_PROJ", "BWD_ATTN", "BWD_QKV", "BWD_EH")
@@ -48,7 +50,7 @@ class ChainArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 7     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 8     # the struct layouts below mirror include/mtp.h at this version
 
 
 class DepthGrads(C.Structure):
@@ -66,7 +68,27 @@ class ChainBwdArgs(C.Structure):
                 ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
 
 
-C_STRUCT_NAMES = {"DepthGrads": "mtp_depth_grads", "ChainBwdArgs": "mtp_chain_bwd_args"}
+class BlockWeights(C.Structure):
+    _fields_ = [("g_attn", vp), ("g_ffn", vp), ("Wqkv", vp), ("Wo", vp), ("Wgate", vp), ("Wup", vp), ("Wdown", vp)]
+
+
+class BlockGrads(C.Structure):
+    _fields_ = [("g_attn", vp), ("g_ffn", vp), ("Wqkv", vp), ("Wo", vp), ("Wgate", vp), ("Wup", vp), ("Wdown", vp)]
+
+
+class HorizonArgs(C.Structure):
+    _fields_ = [("B", C.c_int), ("T", C.c_int), ("d", C.c_int), ("n_heads", C.c_int), ("head_dim", C.c_int),
+                ("ffn", C.c_int), ("V", C.c_int), ("K", C.c_int), ("dtype", C.c_int), ("eps", C.c_float),
+                ("rope_theta", C.c_float), ("lambda_", C.c_float), ("tokens", vp), ("segment_ids", vp),
+                ("h", vp), ("w", C.POINTER(BlockWeights)), ("W_out", vp), ("g_out", vp), ("loss", vp),
+                ("counts", vp), ("loss_total", vp), ("dh", vp), ("dW_out", vp), ("dg_out", vp),
+                ("dw", C.POINTER(BlockGrads)), ("accumulate", C.c_int), ("device_error", vp),
+                ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+
+
+C_STRUCT_NAMES = {"DepthGrads": "mtp_depth_grads", "ChainBwdArgs": "mtp_chain_bwd_args",
+                  "BlockWeights": "mtp_block_weights", "BlockGrads": "mtp_block_grads",
+                  "HorizonArgs": "mtp_horizon_args"}
 
 
 class CeArgs(C.Structure):
@@ -118,6 +140,9 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib = C.CDLL(path)
         lib.mtp_chain_forward.argtypes = [C.POINTER(ChainArgs), vp]
         lib.mtp_chain_backward.argtypes = [C.POINTER(ChainBwdArgs), vp]
+        lib.mtp_horizon_heads.argtypes = [C.POINTER(HorizonArgs), vp]
+        lib.mtp_horizon_heads_workspace_size.argtypes = [C.POINTER(HorizonArgs)]
+        lib.mtp_horizon_heads_workspace_size.restype = C.c_size_t
         lib.mtp_chain_backward_workspace_size.argtypes = [C.POINTER(ChainBwdArgs)]
         lib.mtp_chain_backward_workspace_size.restype = C.c_size_t
         lib.mtp_head_ce_fwd_bwd.argtypes = [C.POINTER(CeArgs), vp]
@@ -269,6 +294,49 @@ def chain_backward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Te
     a.workspace, a.workspace_bytes = _p(ws), ws.numel()
     _check(lib.mtp_chain_backward(C.byref(a), _stream(stream)))
     out["_keep"] = (warr, garr, hp, dhp, ws)
+    return out
+
+
+def horizon_heads(tokens: torch.Tensor, segment_ids: torch.Tensor, h: torch.Tensor,
+                  blocks: Sequence[Dict[str, torch.Tensor]], W_out: torch.Tensor, g_out: torch.Tensor, *,
+                  n_heads: int, head_dim: int, lam: float, eps: float = 1e-6, rope_theta: float = 10000.0,
+                  accumulate: bool = False, out: Optional[Dict] = None, cache: Optional[Dict] = None,
+                  stream=None) -> Dict:
+    """mtp_horizon_heads.  h [B*T,d] trunk state; blocks: K dicts with g_a, g_f, Wqkv, Wo, Wgate, Wup, Wdown.
+    Returns dict(loss [K], counts [K], loss_total [1], dh f32 [B*T,d], dW_out, dg_out,
+    dw = K dicts of f32 block gradients, device_error)."""
+    B, T = tokens.shape
+    V, d = W_out.shape
+    K = len(blocks)
+    ffn = blocks[0]["Wgate"].shape[0]
+    dev = h.device
+    if out is None:
+        out = dict(loss=torch.empty(K, dtype=torch.float32, device=dev),
+                   counts=torch.empty(K, dtype=torch.int32, device=dev),
+                   loss_total=torch.empty(1, dtype=torch.float32, device=dev),
+                   dh=torch.empty((B * T, d), dtype=torch.float32, device=dev),
+                   dW_out=torch.empty((V, d), dtype=torch.float32, device=dev),
+                   dg_out=torch.empty((d,), dtype=torch.float32, device=dev),
+                   dw=[{n: torch.empty(b[n].shape, dtype=torch.float32, device=dev) for n in BLOCK_FIELDS}
+                       for b in blocks],
+                   device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    warr = (BlockWeights * K)()
+    garr = (BlockGrads * K)()
+    for k, (b, g) in enumerate(zip(blocks, out["dw"])):
+        warr[k] = BlockWeights(*[_p(b[n]) for n in BLOCK_FIELDS])
+        garr[k] = BlockGrads(*[_p(g[n]) for n in BLOCK_FIELDS])
+    a = HorizonArgs(B, T, d, n_heads, head_dim, ffn, V, K, _dtype_code(h), eps, rope_theta, lam, _p(tokens),
+                    _p(segment_ids), _p(h), warr, _p(W_out), _p(g_out), _p(out["loss"]), _p(out["counts"]),
+                    _p(out["loss_total"]), _p(out["dh"]), _p(out["dW_out"]), _p(out["dg_out"]), garr,
+                    1 if accumulate else 0, _p(out["device_error"]), None, 0)
+    lib = load()
+    nbytes = lib.mtp_horizon_heads_workspace_size(C.byref(a))
+    if nbytes == 0:
+        _check(lib.mtp_horizon_heads(C.byref(a), _stream(stream)))
+    ws = _workspace(nbytes, dev, cache, "horizon_ws")
+    a.workspace, a.workspace_bytes = _p(ws), ws.numel()
+    _check(lib.mtp_horizon_heads(C.byref(a), _stream(stream)))
+    out["_keep"] = (warr, garr, ws)
     return out
 
 

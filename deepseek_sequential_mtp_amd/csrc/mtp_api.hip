@@ -580,6 +580,71 @@ size_t chain_bwd_layout(const mtp_chain_bwd_args *a, Carve &c, void **p) {
   return c.off;
 }
 
+// One Transformer block's reverse (bf16): buffers, weights and gradients.
+struct BlockBufs {
+  bf16_t *xa, *qkv, *o, *y, *gsw;       // stored activations (x_a, q|k|v after RoPE, o, y, SwiGLU product)
+  float *lse2, *a;                      // attention log-sum-exps, residual after attention
+  bf16_t *gb, *dgsw, *dgu, *dab, *dO, *dqkv, *dub;
+  float *dy, *da, *Dd, *dxa, *du;
+  float *part, *skws;
+  const int32_t *run_start, *pos;
+  const float2 *rope;                   // NULL: no RoPE
+};
+struct BlockW {
+  const float *g_attn, *g_ffn;
+  const bf16_t *Wqkv, *Wo, *Wgate, *Wup, *Wdown;
+};
+struct BlockG {
+  float *g_attn, *g_ffn, *Wqkv, *Wo, *Wgate, *Wup, *Wdown;
+};
+
+// Reverse of out = a + FFN(Norm_f(a)), a = u + Attn(Norm_a(u)) from the
+// stored activations, given dL/dout = gcur (f32) and its bf16 copy in
+// b.gb: every weight and gain gradient of the block (written, or added
+// with acc) and du = dL/du in b.du (f32) and b.dub (bf16).  The block input
+// u is TU (f32: the module's residual stream; bf16: a trunk state).
+template <typename TU>
+int block_bwd(const BlockBufs &b, const BlockW &w, const BlockG &g, const TU *u, const float *gcur, int acc, int B,
+              int Tl, int d, int H, int hd, int f, float eps, hipStream_t s) {
+  using T = bf16_t;
+  const int A = H * hd, N = B * Tl;
+  int st = 0;
+  float *skws = b.skws;
+  // ---- out = a + gsw W_down^T: the MLP's reverse and Norm_f's
+  {
+    MTP_STAGE(MTP_STAGE_BWD_MLP);
+    if ((st = gemm_nn<T, T>(b.gb, d, w.Wdown, f, b.dgsw, f, N, f, d, 0, skws, s))) return st;
+    if ((st = gemm_swiglu_bwd<T>(b.y, w.Wgate, w.Wup, b.dgsw, b.gsw, b.dgu, N, d, f, skws, s))) return st;
+    if ((st = gemm_tn<T>(b.gb, d, b.gsw, f, g.Wdown, f, d, f, N, acc, skws, s))) return st;
+    if ((st = gemm_nn<T, float>(b.dgu, 2L * f, w.Wgate, d, b.dy, d, N, d, f, 0, skws, s))) return st;
+    if ((st = gemm_nn<T, float>(b.dgu + f, 2L * f, w.Wup, d, b.dy, d, N, d, f, 1, skws, s))) return st;
+    if ((st = gemm_tn<T>(b.dgu, 2L * f, b.y, d, g.Wgate, d, f, d, N, acc, skws, s))) return st;
+    if ((st = gemm_tn<T>(b.dgu + f, 2L * f, b.y, d, g.Wup, d, f, d, N, acc, skws, s))) return st;
+    MTP_TRY(launch_rms_bwd<float>(b.dy, d, b.a, nullptr, w.g_ffn, eps, gcur, nullptr, b.da, b.dab, b.part, g.g_ffn,
+                                  acc, N, d, s));
+  }
+  // ---- a = u + o W_o^T
+  {
+    MTP_STAGE(MTP_STAGE_BWD_ATTN_PROJ);
+    if ((st = gemm_nn<T, T>(b.dab, d, w.Wo, A, b.dO, A, N, A, d, 0, skws, s))) return st;
+    if ((st = gemm_tn<T>(b.dab, d, b.o, A, g.Wo, A, d, A, N, acc, skws, s))) return st;
+  }
+  {
+    MTP_STAGE(MTP_STAGE_BWD_ATTN);
+    MTP_TRY(launch_attention_bwd(b.qkv, b.o, b.dO, b.lse2, b.run_start, b.pos, b.rope, b.Dd, b.dqkv, B, Tl, H, hd,
+                                 s));
+  }
+  // ---- qkv = x_a W_qkv^T, x_a = Norm_a(u)
+  {
+    MTP_STAGE(MTP_STAGE_BWD_QKV);
+    if ((st = gemm_nn<T, float>(b.dqkv, 3L * A, w.Wqkv, d, b.dxa, d, N, d, 3 * A, 0, skws, s))) return st;
+    if ((st = gemm_tn<T>(b.dqkv, 3L * A, b.xa, d, g.Wqkv, d, 3 * A, d, N, acc, skws, s))) return st;
+    MTP_TRY(launch_rms_bwd<TU>(b.dxa, d, u, nullptr, w.g_attn, eps, b.da, nullptr, b.du, b.dub, b.part, g.g_attn,
+                               acc, N, d, s));
+  }
+  return MTP_OK;
+}
+
 __global__ void to_bf16_kernel(const float *__restrict__ x, bf16_t *__restrict__ y, long n4) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
@@ -648,43 +713,19 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
         return st;
       MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
     }
-    // ---- h = a + gsw W_down^T: the MLP's reverse and Norm_f's
-    {
-      MTP_STAGE(MTP_STAGE_BWD_MLP);
-      if (k == D) {
-        const long n4 = (long)N * d / 4;
-        hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, gcur, gb, n4);
-        MTP_TRY(hipGetLastError());
-      }
-      if ((st = gemm_nn<T, T>(gb, d, (const T *)w.Wdown, f, dgsw, f, N, f, d, 0, skws, s))) return st;
-      if ((st = gemm_swiglu_bwd<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, dgsw, gsw, dgu, N, d, f, skws, s)))
-        return st;
-      if ((st = gemm_tn<T>(gb, d, gsw, f, g.Wdown, f, d, f, N, acc, skws, s))) return st;
-      if ((st = gemm_nn<T, float>(dgu, 2L * f, (const T *)w.Wgate, d, dy, d, N, d, f, 0, skws, s))) return st;
-      if ((st = gemm_nn<T, float>(dgu + f, 2L * f, (const T *)w.Wup, d, dy, d, N, d, f, 1, skws, s))) return st;
-      if ((st = gemm_tn<T>(dgu, 2L * f, ybuf, d, g.Wgate, d, f, d, N, acc, skws, s))) return st;
-      if ((st = gemm_tn<T>(dgu + f, 2L * f, ybuf, d, g.Wup, d, f, d, N, acc, skws, s))) return st;
-      MTP_TRY(launch_rms_bwd<float>(dy, d, abuf, nullptr, w.g_ffn, a->eps, gcur, nullptr, da, dab, part, g.g_ffn,
-                                    acc, N, d, s));
-    }
-    // ---- a = u + o W_o^T
-    {
-      MTP_STAGE(MTP_STAGE_BWD_ATTN_PROJ);
-      if ((st = gemm_nn<T, T>(dab, d, (const T *)w.Wo, A, dO, A, N, A, d, 0, skws, s))) return st;
-      if ((st = gemm_tn<T>(dab, d, o, A, g.Wo, A, d, A, N, acc, skws, s))) return st;
+    // ---- the block (MLP, attention, their norms), down to du
+    if (k == D) {
+      const long n4 = (long)N * d / 4;
+      hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, gcur, gb, n4);
+      MTP_TRY(hipGetLastError());
     }
     {
-      MTP_STAGE(MTP_STAGE_BWD_ATTN);
-      MTP_TRY(launch_attention_bwd(qkv, o, dO, lse2, run_start, pos, use_rope ? rope : nullptr, Dd, dqkv, B, Tl, H,
-                                   hd, s));
-    }
-    // ---- qkv = x_a W_qkv^T, x_a = Norm_a(u)
-    {
-      MTP_STAGE(MTP_STAGE_BWD_QKV);
-      if ((st = gemm_nn<T, float>(dqkv, 3L * A, (const T *)w.Wqkv, d, dxa, d, N, d, 3 * A, 0, skws, s))) return st;
-      if ((st = gemm_tn<T>(dqkv, 3L * A, xa, d, g.Wqkv, d, 3 * A, d, N, acc, skws, s))) return st;
-      MTP_TRY(launch_rms_bwd<float>(dxa, d, u, nullptr, w.g_attn, a->eps, da, nullptr, du, dub, part, g.g_attn, acc,
-                                    N, d, s));
+      const BlockBufs bb{xa, qkv, o, ybuf, gsw, lse2, abuf, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, Dd, dxa, du,
+                         part, skws, run_start, pos, use_rope ? rope : nullptr};
+      const BlockW bw{w.g_attn, w.g_ffn, (const T *)w.Wqkv, (const T *)w.Wo, (const T *)w.Wgate, (const T *)w.Wup,
+                      (const T *)w.Wdown};
+      const BlockG bg{g.g_attn, g.g_ffn, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown};
+      if ((st = block_bwd<float>(bb, bw, bg, u, gcur, acc, B, Tl, d, H, hd, f, a->eps, s))) return st;
     }
     // ---- u = M [h_bar; e_bar]: eh_proj, enorm (into dE) and hnorm (the
     // gradient carried to depth k-1, or dh0)
@@ -701,6 +742,218 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
     }
   }
   return MTP_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Independent horizon heads (block heads, sequential per-head schedule)
+// ---------------------------------------------------------------------------
+// labels[n] = x[b, t + k] where t and t + k lie in one run, else -1 (tokens
+// outside [0, V) pass through: the head CE flags and drops them).
+__global__ void horizon_labels_kernel(const int32_t *__restrict__ tokens, const int32_t *__restrict__ seg,
+                                      const int32_t *__restrict__ run_start, int B, int T_len, int k,
+                                      int32_t *__restrict__ labels) {
+  const long n = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (n >= (long)B * T_len) return;
+  const int t = (int)(n % T_len);
+  int lab = -1;
+  if (seg[n] >= 0 && t + k < T_len && run_start[n + k] == run_start[n]) lab = tokens[n + k];
+  labels[n] = lab;
+}
+
+// y = x (first head) or y += x, 4 floats per thread
+__global__ void add_rows_kernel(float *__restrict__ y, const float *__restrict__ x, long n4, int first) {
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  const float4 v = reinterpret_cast<const float4 *>(x)[i];
+  float4 *py = reinterpret_cast<float4 *>(y) + i;
+  if (first) {
+    *py = v;
+  } else {
+    float4 o = *py;
+    o.x += v.x; o.y += v.y; o.z += v.z; o.w += v.w;
+    *py = o;
+  }
+}
+
+// Per-head CE outputs (slot k at index 4 k) -> the caller's arrays; the
+// total objective summed in head order; error flags or-ed.
+__global__ void horizon_finalize_kernel(const float *__restrict__ hl_loss, const int32_t *__restrict__ hl_counts,
+                                        const float *__restrict__ hl_mtp, const int32_t *__restrict__ hl_err,
+                                        const int32_t *__restrict__ rows_err, int K, float *loss, int32_t *counts,
+                                        float *loss_total, int32_t *device_error) {
+  if (threadIdx.x != 0) return;
+  float tot = 0.f;
+  int err = rows_err[0];
+  for (int k = 0; k < K; ++k) {
+    loss[k] = hl_loss[4 * k];
+    counts[k] = hl_counts[4 * k];
+    tot += hl_mtp[4 * k];
+    err |= hl_err[4 * k];
+  }
+  loss_total[0] = tot;
+  if (device_error != nullptr) device_error[0] = err ? 1 : 0;
+}
+
+int check_horizon(const mtp_horizon_args *a) {
+  if (a == nullptr) return MTP_ERR_NULL;
+  if (a->K < 1) return MTP_ERR_DEPTH;
+  mtp_chain_bwd_args c{};
+  c.B = a->B; c.T = a->T; c.d = a->d; c.n_heads = a->n_heads; c.head_dim = a->head_dim; c.ffn = a->ffn;
+  c.V = a->V; c.D = 1; c.dtype = a->dtype; c.eps = a->eps; c.rope_theta = a->rope_theta;
+  const int st = check_chain_bwd(&c);
+  if (st) return st;
+  if (a->V % 8 || a->V >= (1 << 21)) return MTP_ERR_SHAPE;
+  if (!isfinite(a->lambda)) return MTP_ERR_ARG;
+  return MTP_OK;
+}
+
+constexpr int kHorParts = 36;     // workspace regions of the horizon heads
+
+// The head CE arguments of head k (D = 1) over the given workspace.
+mtp_ce_args horizon_ce_args(const mtp_horizon_args *a, void *const *hptr, void *const *dhptr, const int32_t *labels,
+                            float *hl_sum, int32_t *hl_counts, float *hl_loss, float *hl_mtp, int32_t *hl_err, int k,
+                            void *ws, size_t ws_bytes) {
+  mtp_ce_args c{};
+  c.B = a->B; c.T = a->T; c.d = a->d; c.V = a->V; c.D = 1; c.dtype = a->dtype; c.eps = a->eps;
+  c.lambda = a->lambda / (float)a->K;
+  c.reduce = MTP_REDUCE_FIXED;
+  c.denom = 0.0;
+  c.h = hptr;
+  c.labels = labels;
+  c.W_out = a->W_out;
+  c.g_out = a->g_out;
+  c.loss_sum = hl_sum + 4 * k; c.counts = hl_counts + 4 * k; c.loss = hl_loss + 4 * k; c.loss_mtp = hl_mtp + 4 * k;
+  c.lse = nullptr;
+  c.dh = dhptr;
+  c.dW_out = a->dW_out; c.dg_out = a->dg_out;
+  c.accumulate = (k > 0 || a->accumulate) ? 1 : 0;
+  c.device_error = hl_err + 4 * k;
+  c.logit_slab_bytes = 0;
+  c.dh_accumulate = 0;
+  c.pred = nullptr; c.correct = nullptr; c.accuracy = nullptr;
+  c.workspace = ws;
+  c.workspace_bytes = ws_bytes;
+  return c;
+}
+
+size_t horizon_layout(const mtp_horizon_args *a, Carve &c, void **p) {
+  using T = bf16_t;
+  const long N = (long)a->B * a->T;
+  const int d = a->d, A = a->n_heads * a->head_dim, f = a->ffn, H = a->n_heads, K = a->K;
+  p[0] = c.take<int32_t>(N);                      // run_start
+  p[1] = c.take<int32_t>(N);                      // pos
+  p[2] = c.take<int32_t>(a->B);                   // count partials (rows kernel, one depth)
+  p[3] = c.take<int32_t>(a->B);                   // error partials
+  p[4] = c.take<uint8_t>(N);                      // state mask (unused)
+  p[5] = c.take<uint8_t>(N);                      // loss mask (unused)
+  p[6] = c.take<int32_t>(N);                      // chain labels (unused)
+  p[7] = c.take<int32_t>(1);                      // chain count (unused)
+  p[8] = c.take<int32_t>(1);                      // token error flag
+  p[9] = c.take<float2>((size_t)a->T * (a->head_dim / 2));   // RoPE table
+  p[10] = c.take<T>(N * d);                       // x_a
+  p[11] = c.take<T>(N * 3 * (long)A);             // qkv
+  p[12] = c.take<T>(N * (long)A);                 // o
+  p[13] = c.take<float>(N * H);                   // lse2
+  p[14] = c.take<float>(N * d);                   // a
+  p[15] = c.take<T>(N * d);                       // y
+  p[16] = c.take<T>(N * (long)f);                 // silu(gate) * up
+  p[17] = c.take<T>(N * d);                       // the head output u^(k)
+  p[18] = c.take<T>(N * d);                       // dL/du^(k) (bf16)
+  p[19] = c.take<T>(N * (long)f);                 // d(silu(gate) * up)
+  p[20] = c.take<T>(N * 2 * (long)f);             // [d gate | d up]
+  p[21] = c.take<float>(N * d);                   // dy
+  p[22] = c.take<float>(N * d);                   // da
+  p[23] = c.take<T>(N * d);                       // da (bf16)
+  p[24] = c.take<T>(N * (long)A);                 // dO
+  p[25] = c.take<float>(N * H);                   // D = dO . o
+  p[26] = c.take<T>(N * 3 * (long)A);             // dqkv
+  p[27] = c.take<float>(N * d);                   // dx_a
+  p[28] = c.take<float>(N * d);                   // du (the head's share of dh)
+  p[29] = c.take<T>(N * d);                       // du (bf16)
+  p[30] = c.take<int32_t>(N);                     // horizon labels
+  p[31] = c.take<float>(N * d);                   // dL/du^(k) (f32, from the head CE)
+  p[32] = c.take<float>((size_t)dg_row_blocks((int)N) * d);   // gain-gradient partials
+  p[33] = c.take<float>(tail_ws_bytes<Big>() / 4);            // partial tiles of split tail GEMM tiles
+  p[34] = c.take<float>(5 * 4 * (size_t)K);       // per-head CE scalars (sum, counts, loss, objective, error)
+  mtp_ce_args ce = horizon_ce_args(a, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0,
+                                   nullptr, 0);
+  p[35] = c.take<char>(mtp_ce_workspace_size(&ce));            // the head CE's workspace
+  return c.off;
+}
+
+int horizon_run(const mtp_horizon_args *a, hipStream_t s) {
+  using T = bf16_t;
+  void *p[kHorParts];
+  Carve c(a->workspace);
+  const size_t total = horizon_layout(a, c, p);
+  const int B = a->B, Tl = a->T, d = a->d, H = a->n_heads, hd = a->head_dim, f = a->ffn, V = a->V, K = a->K;
+  const int A = H * hd;
+  const int N = B * Tl;
+  int32_t *run_start = (int32_t *)p[0], *pos = (int32_t *)p[1];
+  float2 *rope = (float2 *)p[9];
+  const bool use_rope = a->rope_theta > 0.f;
+  T *xa = (T *)p[10], *qkv = (T *)p[11], *o = (T *)p[12], *ybuf = (T *)p[15], *gsw = (T *)p[16], *out = (T *)p[17];
+  float *lse2 = (float *)p[13], *abuf = (float *)p[14];
+  float *dhk = (float *)p[31];
+  int32_t *hlab = (int32_t *)p[30];
+  float *small = (float *)p[34];
+  float *hl_sum = small, *hl_loss = small + 8 * K, *hl_mtp = small + 12 * K;
+  int32_t *hl_counts = (int32_t *)(small + 4 * K), *hl_err = (int32_t *)(small + 16 * K);
+  const T *h = static_cast<const T *>(a->h);
+  const BlockBufs bb{xa, qkv, o, ybuf, gsw, lse2, abuf, (T *)p[18], (T *)p[19], (T *)p[20], (T *)p[23],
+                     (T *)p[24], (T *)p[26], (T *)p[29], (float *)p[21], (float *)p[22], (float *)p[25],
+                     (float *)p[27], (float *)p[28], (float *)p[32], (float *)p[33], run_start, pos,
+                     use_rope ? rope : nullptr};
+  const size_t ce_bytes = total - (size_t)((char *)p[35] - (char *)a->workspace);
+  const int acc = a->accumulate ? 1 : 0;
+
+  MTP_TRY(launch_rows(a->tokens, a->segment_ids, B, Tl, V, 1, run_start, pos, (uint8_t *)p[4], (uint8_t *)p[5],
+                      (int32_t *)p[6], (int32_t *)p[7], (int32_t *)p[8], (int32_t *)p[2], (int32_t *)p[3], s));
+  if (use_rope) MTP_TRY(rope_table(rope, Tl, hd / 2, a->rope_theta, s));
+  void *hptr[1] = {out};
+  void *dhptr[1] = {dhk};
+  for (int k = 0; k < K; ++k) {
+    const mtp_block_weights &w = a->w[k];
+    const mtp_block_grads &g = a->dw[k];
+    const BlockW bw{w.g_attn, w.g_ffn, (const T *)w.Wqkv, (const T *)w.Wo, (const T *)w.Wgate, (const T *)w.Wup,
+                    (const T *)w.Wdown};
+    const BlockG bg{g.g_attn, g.g_ffn, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown};
+    int st = 0;
+    // ---- head k's block forward: u^(k) = Block_k(h)
+    {
+      MTP_STAGE(MTP_STAGE_BWD_RECOMPUTE);
+      MTP_TRY((launch_rmsnorm<T, T>(h, w.g_attn, xa, nullptr, N, d, a->eps, s)));
+      if ((st = gemm_qkv_rope<T>(xa, bw.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, (float *)p[33], s)))
+        return st;
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, lse2, B, Tl, H, hd, s));
+      if ((st = gemm_nt_store<T, float, T>(o, A, bw.Wo, A, abuf, d, h, d, N, d, A, 1.f, nullptr, 0, (float *)p[33],
+                                           s)))
+        return st;
+      MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
+      if ((st = gemm_swiglu<T>(ybuf, bw.Wgate, bw.Wup, gsw, N, d, f, (float *)p[33], s))) return st;
+      if ((st = gemm_nt_store<T, T, float>(gsw, f, bw.Wdown, f, out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
+                                           (float *)p[33], s)))
+        return st;
+    }
+    // ---- the shared head on u^(k): labels x[t + k + 1] (horizon k + 1), loss and dL/du^(k)
+    hipLaunchKernelGGL(horizon_labels_kernel, dim3((unsigned)((N + 255) / 256)), dim3(256), 0, s, a->tokens,
+                       a->segment_ids, run_start, B, Tl, k + 1, hlab);
+    MTP_TRY(hipGetLastError());
+    const mtp_ce_args ce = horizon_ce_args(a, hptr, dhptr, hlab, hl_sum, hl_counts, hl_loss, hl_mtp, hl_err, k,
+                                           p[35], ce_bytes);
+    if ((st = mtp_head_ce_fwd_bwd(&ce, s))) return st;
+    // ---- head k's block backward; its share of the trunk gradient into dh
+    const long n4 = (long)N * d / 4;
+    hipLaunchKernelGGL(to_bf16_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, dhk, bb.gb, n4);
+    MTP_TRY(hipGetLastError());
+    if ((st = block_bwd<T>(bb, bw, bg, h, dhk, acc, B, Tl, d, H, hd, f, a->eps, s))) return st;
+    hipLaunchKernelGGL(add_rows_kernel, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, s, a->dh, bb.du, n4,
+                       k == 0 ? 1 : 0);
+    MTP_TRY(hipGetLastError());
+  }
+  hipLaunchKernelGGL(horizon_finalize_kernel, dim3(1), dim3(64), 0, s, hl_loss, hl_counts, hl_mtp, hl_err,
+                     (const int32_t *)p[8], K, a->loss, a->counts, a->loss_total, a->device_error);
+  return hipGetLastError() == hipSuccess ? MTP_OK : MTP_ERR_HIP;
 }
 
 int check_ce(const mtp_ce_args *a) {
@@ -1141,6 +1394,36 @@ int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream) {
   if ((st = check_chain_bwd_ptrs(a))) return st;
   if (!a->workspace || a->workspace_bytes < mtp_chain_backward_workspace_size(a)) return MTP_ERR_WORKSPACE;
   return chain_bwd_run(a, static_cast<hipStream_t>(stream));
+}
+
+size_t mtp_horizon_heads_workspace_size(const mtp_horizon_args *a) {
+  if (check_horizon(a) != MTP_OK) return 0;
+  Carve c(nullptr);
+  void *p[kHorParts];
+  return horizon_layout(a, c, p);
+}
+
+int mtp_horizon_heads(const mtp_horizon_args *a, void *stream) {
+  int st = check_horizon(a);
+  if (st) return st;
+  if (!a->tokens || !a->segment_ids || !a->h || !a->w || !a->W_out || !a->g_out || !a->loss || !a->counts ||
+      !a->loss_total || !a->dh || !a->dW_out || !a->dg_out || !a->dw)
+    return MTP_ERR_NULL;
+  for (int k = 0; k < a->K; ++k) {
+    const mtp_block_weights &w = a->w[k];
+    const mtp_block_grads &g = a->dw[k];
+    if (!w.g_attn || !w.g_ffn || !w.Wqkv || !w.Wo || !w.Wgate || !w.Wup || !w.Wdown || !g.g_attn || !g.g_ffn ||
+        !g.Wqkv || !g.Wo || !g.Wgate || !g.Wup || !g.Wdown)
+      return MTP_ERR_NULL;
+    if (!all_al16(w.g_attn, w.g_ffn, w.Wqkv, w.Wo, w.Wgate, w.Wup, w.Wdown) ||
+        !all_al16(g.g_attn, g.g_ffn, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown))
+      return MTP_ERR_ARG;
+  }
+  if (!all_al16(a->tokens, a->segment_ids, a->h, a->W_out, a->g_out, a->dh, a->dW_out, a->dg_out, a->device_error,
+                a->workspace))
+    return MTP_ERR_ARG;
+  if (!a->workspace || a->workspace_bytes < mtp_horizon_heads_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  return horizon_run(a, static_cast<hipStream_t>(stream));
 }
 
 size_t mtp_ce_workspace_size(const mtp_ce_args *a) {

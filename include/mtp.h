@@ -221,6 +221,72 @@ typedef struct {
 } mtp_chain_bwd_args;
 
 /* ------------------------------------------------------------------------
+ * mtp_horizon_heads: K independent horizon heads on one trunk state, each a
+ * Transformer block of its own followed by the shared head, run in the
+ * sequential per-head schedule ([M7.4] 0x02: head k predicts x[t+k] from
+ * the trunk state at t; 0x05B: an independent transformer head per horizon
+ * with a shared vocabulary projection; 0x06A: each head's forward and
+ * backward finish before the next head's, and the trunk receives the sum of
+ * the heads' gradients once).
+ *
+ * Head k (1..K): u^(k) = Block_k(h) -- the block of mtp_chain_forward's
+ * module (pre-norm segment-causal multi-head attention with RoPE at the
+ * position inside the run, then SwiGLU, residual adds), with h as its input
+ * -- then the shared head (Norm_out with g_out, W_out) and the masked CE
+ * against x[b, t+k], labelled where t + k stays inside t's run.  The
+ * objective is (lambda / K) sum_k L^(k), L^(k) = (sum of head k's token
+ * losses) / (B*T).  Per head, in order: the block forward, the head CE
+ * forward and backward (its logits bounded by logit slabs as in
+ * mtp_head_ce_fwd_bwd), the block backward; only one head's activations
+ * and logits are live at a time.
+ *
+ * Inputs : tokens, segment_ids int32 [B,T]; h [B*T, d] (dtype); w [host] K
+ *          block weights; W_out [V, d]; g_out [d] f32.
+ * Outputs: loss f32 [K] (L^(k)), counts int32 [K] (labelled rows),
+ *          loss_total f32 [1] ((lambda / K) sum_k L^(k));
+ *          dh f32 [B*T, d]: the summed gradient at the trunk state (written);
+ *          dW_out f32 [V, d], dg_out f32 [d] and dw [host] K block gradients
+ *          (f32, shapes of mtp_block_weights): written, or added to with
+ *          accumulate = 1;
+ *          device_error int32 [1] (may be NULL): 1 if an active position
+ *          holds a token outside [0, V).
+ * Requirements: as mtp_chain_backward (bf16; head_dim 64 or 128; d <= 8192)
+ * and V % 8 == 0, V < 2^21; K >= 1.
+ * ---------------------------------------------------------------------- */
+typedef struct {
+  const float *g_attn, *g_ffn;         /* [d] f32                              */
+  const void *Wqkv;                    /* [3*H*hd, d]                          */
+  const void *Wo;                      /* [d, H*hd]                            */
+  const void *Wgate, *Wup;             /* [ffn, d]                             */
+  const void *Wdown;                   /* [d, ffn]                             */
+} mtp_block_weights;
+
+typedef struct {
+  float *g_attn, *g_ffn, *Wqkv, *Wo, *Wgate, *Wup, *Wdown;   /* f32, shapes as above */
+} mtp_block_grads;
+
+typedef struct {
+  int B, T, d, n_heads, head_dim, ffn, V, K;
+  mtp_dtype dtype;
+  float eps, rope_theta, lambda;
+  const int32_t *tokens, *segment_ids;
+  const void *h;
+  const mtp_block_weights *w;        /* [host] K entries                       */
+  const void *W_out;
+  const float *g_out;
+  float *loss;                       /* [K]                                    */
+  int32_t *counts;                   /* [K]                                    */
+  float *loss_total;                 /* [1]                                    */
+  float *dh;                         /* [B*T, d]                               */
+  float *dW_out, *dg_out;
+  const mtp_block_grads *dw;         /* [host] K entries                       */
+  int accumulate;
+  int32_t *device_error;             /* optional                               */
+  void *workspace;
+  size_t workspace_bytes;
+} mtp_horizon_args;
+
+/* ------------------------------------------------------------------------
  * mtp_head_ce_fwd_bwd: shared output head Norm_out + W_U, masked CE against
  * the labels of every depth, and the gradients of
  *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
@@ -429,6 +495,7 @@ typedef struct {
 
 int mtp_chain_forward(const mtp_chain_args *a, void *stream);
 int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream);
+int mtp_horizon_heads(const mtp_horizon_args *a, void *stream);
 int mtp_head_ce_fwd_bwd(const mtp_ce_args *a, void *stream);
 int mtp_verify(const mtp_verify_args *a, void *stream);
 
@@ -458,6 +525,7 @@ int mtp_round_commit(const mtp_round_args *a, void *stream);
  * inspected); 0 if the arguments are invalid. */
 size_t mtp_chain_workspace_size(const mtp_chain_args *a);
 size_t mtp_chain_backward_workspace_size(const mtp_chain_bwd_args *a);
+size_t mtp_horizon_heads_workspace_size(const mtp_horizon_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);
 size_t mtp_verify_workspace_size(const mtp_verify_args *a);
 size_t mtp_propose_workspace_size(const mtp_propose_args *a);
@@ -501,7 +569,7 @@ const char *mtp_strerror(int status);
  * struct field added, moved or retyped, a call's meaning changed).  A
  * binding that mirrors the argument structs must refuse a library whose
  * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
-#define MTP_ABI_VERSION 7
+#define MTP_ABI_VERSION 8
 int mtp_abi_version(void);
 
 #ifdef __cplusplus
