@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--ingest-pmc", nargs=3, metavar=("STAGE", "FETCH_CSV", "WRITE_CSV"),
                     help="no GPU: turn two rocprofv3 --pmc counter CSVs (FETCH_SIZE, WRITE_SIZE) of a "
                          "--copy-calibration run into profiles/traffic_<stage>_<workload>.json")
+    ap.add_argument("--pmc-table", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="no GPU: print per-kernel HBM bytes per dispatch (markdown) of the step's and the "
+                         "verify benchmark's kernels from the two counter CSVs of a --copy-calibration run")
     return ap.parse_args()
 
 
@@ -66,39 +69,120 @@ STAGE_KERNELS = {
 }
 COPY_BYTES = 256 << 20          # one direction of the calibration copy
 COPY_KERNEL = r"neg_kernel"
+COPY_REPS = 3
+FIXUP_KERNEL = r"gemm_fixup_kernel"
+# Bandwidth kernels named in the per-kernel traffic table (besides the stages above).
+TABLE_KERNELS = {
+    "DUAL_NORM": r"dual_norm_concat_kernel",
+    "NORM_A_F": r"rmsnorm_kernel",
+    "OUT_NORM": r"out_norm_kernel",
+    "OUT_NORM_BWD": r"out_norm_bwd",
+    "CE_DZ": r"ce_dz_kernel",
+    "GEMM_FIXUP": FIXUP_KERNEL,
+    "VERIFY_LSE": r"verify_lse_kernel",
+    "VERIFY_MASS": r"verify_mass_kernel",
+    "VERIFY_PICK": r"verify_pick_kernel",
+    "VERIFY_TESTS": r"verify_tests_kernel",
+}
+
+
+def _read_counter(path, counter):
+    """{dispatch id: (kernel name, grid size, summed counter value in KiB)}."""
+    import csv
+    rows = {}
+    with open(path) as fh:
+        for r in csv.DictReader(fh):
+            if r["Counter_Name"] != counter:
+                continue
+            key = int(r["Dispatch_Id"])
+            name, grid, val = rows.get(key, (r["Kernel_Name"], int(r.get("Grid_Size", 0) or 0), 0.0))
+            rows[key] = (name, grid, val + float(r["Counter_Value"]))
+    return rows
+
+
+def _phases(rows, path):
+    """Split the dispatches of a --copy-calibration run at the calibration
+    copies: the first COPY_REPS copies follow the timed steps, the next
+    COPY_REPS follow the verify benchmark.  Returns the copy factor (counter
+    bytes per byte copied) and the dispatch ids of the two phases."""
+    import re
+    copies = sorted(i for i, (n, _, _) in rows.items() if re.search(COPY_KERNEL, n))
+    if len(copies) < COPY_REPS:
+        raise SystemExit(f"{path}: fewer than {COPY_REPS} calibration copies")
+    factor = float(np.median([rows[i][2] for i in copies])) * 1024.0 / COPY_BYTES
+    first, last1 = copies[0], copies[COPY_REPS - 1]
+    end2 = copies[2 * COPY_REPS - 1] if len(copies) >= 2 * COPY_REPS else None
+    step = {i for i in rows if i < first}
+    verify = {i for i in rows if end2 is not None and last1 < i < copies[COPY_REPS]}
+    return factor, step, verify
+
+
+def _stage_dispatches(rows, ids, stage):
+    """The stage's dispatches among `ids`: its GEMM launches (the main grid and
+    a split tail) and the fixup kernel that follows a split tail."""
+    import re
+    mine = {i for i in ids if re.search(STAGE_KERNELS[stage], rows[i][0])}
+    mine |= {i for i in ids if re.search(FIXUP_KERNEL, rows[i][0]) and (i - 1) in mine}
+    return mine
 
 
 def ingest_pmc(stage, fetch_csv, write_csv, workload):
-    """Per-launch HBM bytes of `stage`'s kernel from the two counter passes,
-    each scaled by the same counter's reading for the plain copy kernel."""
-    import csv
+    """HBM bytes per step of `stage` over the timed steps (the dispatches
+    before the first calibration copy), from the two counter passes, each
+    scaled by the same counter's reading for the copy kernel.  The number of
+    steps is the output-norm dispatch count over the depth count."""
     import re
+    from deepseek_sequential_mtp_amd import synth
+    D = synth.CHAIN_CONFIGS[workload].D
 
-    def per_dispatch(path, counter):
-        rows = {}
-        with open(path) as fh:
-            for r in csv.DictReader(fh):
-                if r["Counter_Name"] != counter:
-                    continue
-                key = (r["Dispatch_Id"], r["Kernel_Name"])
-                rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
-        kern = [v for (_, n), v in rows.items() if re.search(STAGE_KERNELS[stage], n)]
-        copy = [v for (_, n), v in rows.items() if re.search(COPY_KERNEL, n)]
-        if not kern or not copy:
-            raise SystemExit(f"{path}: no {counter} rows for the stage kernel or the copy kernel")
-        factor = float(np.median(copy)) * 1024.0 / COPY_BYTES     # counter KiB -> bytes, per byte copied
-        return float(np.mean(kern)) * 1024.0 / factor, factor, len(kern)
+    def per_step(path, counter):
+        rows = _read_counter(path, counter)
+        factor, step, _ = _phases(rows, path)
+        n_steps = sum(1 for i in step if re.search(TABLE_KERNELS["OUT_NORM"], rows[i][0])) / D
+        mine = _stage_dispatches(rows, step, stage)
+        if not mine or n_steps < 1:
+            raise SystemExit(f"{path}: no {counter} rows for the stage kernel before the calibration copy")
+        total = sum(rows[i][2] for i in mine) * 1024.0 / factor
+        return total / n_steps, factor, len(mine), n_steps
 
-    fetch, ff, nf = per_dispatch(fetch_csv, "FETCH_SIZE")
-    write, fw, nw = per_dispatch(write_csv, "WRITE_SIZE")
+    fetch, ff, nf, sf = per_step(fetch_csv, "FETCH_SIZE")
+    write, fw, nw, sw = per_step(write_csv, "WRITE_SIZE")
     out = {"stage": stage, "workload": workload, "kernel_regex": STAGE_KERNELS[stage],
-           "fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
-           "bytes_per_launch": fetch + write, "copy_factor_fetch": ff, "copy_factor_write": fw,
-           "launches_counted": [nf, nw], "source_hash": _kernel_hash(stage)}
+           "fetch_bytes_per_step": fetch, "write_bytes_per_step": write, "bytes_per_step": fetch + write,
+           "copy_factor_fetch": ff, "copy_factor_write": fw, "dispatches_counted": [nf, nw], "steps": [sf, sw],
+           "source_hash": _kernel_hash(stage)}
     path = os.path.join(ROOT, "profiles", f"traffic_{stage.lower()}_{workload}.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out))
+
+
+def pmc_table(fetch_csv, write_csv):
+    """Markdown table: mean HBM bytes per dispatch (FETCH_SIZE, WRITE_SIZE,
+    each scaled by the copy kernel's reading) of every named kernel, grouped
+    by phase (timed steps / verify benchmark) and grid size."""
+    import re
+    labels = dict(STAGE_KERNELS)
+    labels.update(TABLE_KERNELS)
+    groups = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _read_counter(path, counter)
+        factor, step, verify = _phases(rows, path)
+        for phase, ids in (("step", step), ("verify", verify)):
+            for i in ids:
+                name, grid, val = rows[i]
+                lab = next((k for k, rx in labels.items() if re.search(rx, name)), None)
+                if lab is None:
+                    continue
+                g = groups.setdefault((phase, lab, grid), {"FETCH_SIZE": [], "WRITE_SIZE": []})
+                g[counter].append(val * 1024.0 / factor)
+    print("| phase | kernel | grid size | dispatches | fetch MB / dispatch | write MB / dispatch |")
+    print("|---|---|---|---|---|---|")
+    for (phase, lab, grid), g in sorted(groups.items()):
+        if not g["FETCH_SIZE"] or not g["WRITE_SIZE"]:
+            continue
+        print(f"| {phase} | {lab} | {grid} | {len(g['FETCH_SIZE'])} | {np.mean(g['FETCH_SIZE']) / 1e6:.2f} | "
+              f"{np.mean(g['WRITE_SIZE']) / 1e6:.2f} |")
 
 
 # ----------------------------------------------------------------------------
@@ -414,6 +498,9 @@ def bench_verify(torch, _lib, synth, reps=20):
 
 def main():
     args = parse()
+    if args.pmc_table:
+        pmc_table(args.pmc_table[0], args.pmc_table[1])
+        return
     if args.ingest_pmc:
         ingest_pmc(args.ingest_pmc[0], args.ingest_pmc[1], args.ingest_pmc[2], args.workload)
         return
@@ -515,8 +602,9 @@ def main():
         try:
             with open(tfile) as fh:
                 tr = json.load(fh)
-            if tr.get("source_hash") == _kernel_hash(dominant):
-                traffic = tr.get("bytes_per_launch")
+            if tr.get("source_hash") == _kernel_hash(dominant) and "bytes_per_step" in tr:
+                # per launch, like `achieved`: the step's bytes over the step's launches
+                traffic = round(tr["bytes_per_step"] / (len(dom_times) / args.steps))
         except (OSError, ValueError):
             traffic = None
 
@@ -527,15 +615,23 @@ def main():
         print(f"  dominant {dominant}: {dom_avg_ms:.3f} ms/launch over {len(dom_times)} launches, "
               f"{dom_step_ms:.3f} ms/step, {achieved:.1f} TFLOP/s ({dom_note})", file=sys.stderr)
 
-    if args.copy_calibration:
+    def calibration_copy():
+        # a plain copy of known size: the reference dispatches that scale the
+        # FETCH_SIZE / WRITE_SIZE counters (and mark the phases of the run)
         src = torch.randn(COPY_BYTES // 4, device=dev)
         dst = torch.empty_like(src)
-        for _ in range(3):
+        for _ in range(COPY_REPS):
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
+        del src, dst
+
+    if args.copy_calibration:
+        calibration_copy()
 
     stages = stage_table(cfg, stage_ms, per)
     verify = bench_verify(torch, _lib, synth)
+    if args.copy_calibration:
+        calibration_copy()
     if args.stages:
         for v in verify:
             print(f"  verify gamma={v['gamma']}: {v['ms']:.3f} ms, {v['achieved']:.0f} GB/s on needed rows "

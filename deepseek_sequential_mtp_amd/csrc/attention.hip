@@ -307,7 +307,7 @@ __global__ __launch_bounds__(kAttnThreads) void attention_kernel(const T *__rest
     const float inv = lt > 0.f ? 1.f / lt : 0.f;
     // base-2 log-sum-exp of the query's scaled scores (for the reverse pass)
     if (lse2_out != nullptr && hl == 0 && qi[nb] < T_len)
-      lse2_out[(rowbase + qi[nb]) * H + h] = m[nb] + __log2f(lt);
+      lse2_out[2 * (rowbase * H + (long)h * T_len + qi[nb])] = m[nb] + __log2f(lt);
     const int qb = wave * kQW + 32 * nb + c32;            // query inside the block
     char *ostage = qb < kQT / 2 ? st0 : st1;
     T *orow = reinterpret_cast<T *>(ostage) + (long)(qb % (kQT / 2)) * HD;

@@ -12,11 +12,16 @@
 // and dq, dk are rotated back through RoPE (the opposite angle at their
 // positions).  q, k are the stored (RoPE'd) values, o the stored output.
 //
+// lse2 and D live side by side per (batch row, head, position): lsed
+// [B, H, T] x float2, so that a tile of consecutive queries reads one
+// contiguous run of them.
+//
 // Two kernels, no atomics (the result does not depend on timing):
 //   dK/dV: a block owns 128 keys of one (batch row, head), four waves of 32;
 //     each wave keeps its keys' K and V fragments in registers and walks the
-//     query tiles that can see them (64 queries per tile, Q and dO staged in
-//     LDS by direct loads, double-buffered).  Per 32 x 32 (query, key) block:
+//     query tiles that can see them (64 queries per tile; Q and dO, and the
+//     tile's (lse2, D) pairs and run starts, staged in LDS by direct loads,
+//     double-buffered).  Per 32 x 32 (query, key) block:
 //     S = Q K^T and dP = dO V^T (queries on MFMA rows, keys on columns, so a
 //     lane holds one key), then dV += P^T dO and dK += dS^T Q with P^T, dS^T
 //     taken straight from those result registers (the MFMA K-slots are the
@@ -48,6 +53,10 @@ struct BwdCfg {
   static constexpr int RPL = 1024 / ROWB;            // rows per 1 KB direct load
   static constexpr int TILE = 64 * ROWB;             // one 64-row tile
   static constexpr int STAGE = 2 * TILE;             // two tiles (Q + dO, or K + V)
+  // dK/dV stage: Q + dO, then one 1 KB direct-load region per wave for the
+  // tile's per-query scalars: (lse2, D) of queries 0-31 and 32-63, run
+  // starts of queries 0-63 (the fourth region is unused)
+  static constexpr int XSTAGE = 2 * TILE + 4 * 1024;
   static constexpr int LOADS = 2 * 64 / RPL / 4;     // load instructions per wave and stage
   static constexpr int SK = HD / 16;                 // MFMA steps over the head dim
   static constexpr int MD = HD / 32;                 // 32-wide head-dim blocks
@@ -117,16 +126,35 @@ __device__ __forceinline__ void load_tile_pair(__amdgpu_buffer_rsrc_t ra, int ld
           valid ? (row0 + qb * C::RPL) * ldx : 0);
   }
 }
+
+// The per-query scalars of the 64-query tile at row0 into the wave's 1 KB
+// region after the two tiles: wave 0 the (lse2, D) pairs of queries
+// row0 .. row0 + 31, wave 1 those of row0 + 32 .. row0 + 63, wave 2 the run
+// starts of all 64 (16 lanes x 16 B each; queries past the row read 0); wave
+// 3 loads nothing (every lane past the resource) so that each wave issues
+// one load per tile.
+template <int HD>
+__device__ __forceinline__ void load_query_scalars(__amdgpu_buffer_rsrc_t rld, __amdgpu_buffer_rsrc_t rrs,
+                                                   int row0, int T_len, bool valid, char *stage, int wave,
+                                                   int lane) {
+  using C = BwdCfg<HD>;
+  const int q0 = row0 + (wave == 1 ? 32 : 0);
+  const bool ok = valid && wave < 3 && q0 < T_len && lane < 16;
+  const int soff = valid && wave < 3 && q0 < T_len ? q0 * (wave == 2 ? 4 : 8) : 0;
+  dma16(wave == 2 ? rrs : rld, stage + 2 * C::TILE + wave * 1024, ok ? (unsigned)(lane * 16) : kOOB, soff);
+}
 }  // namespace
 
-// D[n, h] = dO[n, h, :] . o[n, h, :] in float32.  One block per row; lane
-// groups of HD / 8 lanes hold one head's chunks.
+// D = dO[n, h, :] . o[n, h, :] in float32 into element 1 of the (b, h, t)
+// pair of lsed.  One block per row; lane groups of HD / 8 lanes hold one
+// head's chunks.
 template <int HD>
 __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16_t *__restrict__ dout,
-                                                          const bf16_t *__restrict__ o, float *__restrict__ Dd,
-                                                          int H) {
+                                                          const bf16_t *__restrict__ o, float2 *__restrict__ lsed,
+                                                          int T_len, int H) {
   constexpr int CPH = HD / 8;                        // chunks per head
   const long n = blockIdx.x;
+  const long brow = n / T_len, tpos = n % T_len;
   const int A = H * HD;
   for (int c = threadIdx.x; c < A / 8; c += 256) {
     float a[8], b[8];
@@ -137,19 +165,19 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16_t *__restr
     for (int e = 0; e < 8; ++e) s = fmaf(a[e], b[e], s);
 #pragma unroll
     for (int off = 1; off < CPH; off <<= 1) s += __shfl_xor(s, off);
-    if ((c % CPH) == 0) Dd[n * H + c / CPH] = s;
+    if ((c % CPH) == 0) lsed[(brow * H + c / CPH) * T_len + tpos].y = s;
   }
 }
 
 template <int HD>
 __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
-    const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float *__restrict__ lse2,
-    const float *__restrict__ Dd, const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos,
-    const float2 *__restrict__ rope, bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
+    const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float2 *__restrict__ lsed,
+    const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos, const float2 *__restrict__ rope,
+    bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
   using C = BwdCfg<HD>;
   constexpr int CPR = C::CPR, ROWB = C::ROWB, SK = C::SK, MD = C::MD;
-  __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
-  __shared__ __attribute__((aligned(1024))) char st1[C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char st0[C::XSTAGE];
+  __shared__ __attribute__((aligned(1024))) char st1[C::XSTAGE];
 
   const int A = H * HD;
   const long ld = 3L * A;
@@ -188,8 +216,11 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       make_rsrc(qkv + rowbase * ld + (long)h * HD, (long)(T_len - 1) * ldq_b + ROWB);
   const __amdgpu_buffer_rsrc_t rdo =
       make_rsrc(dout + rowbase * A + (long)h * HD, (long)(T_len - 1) * ldo_b + ROWB);
+  const __amdgpu_buffer_rsrc_t rld = make_rsrc(lsed + ((long)b * H + h) * T_len, (long)T_len * 8);
+  const __amdgpu_buffer_rsrc_t rrs = make_rsrc(run_start + rowbase, (long)T_len * 4);
   auto issue = [&](int it, char *stage) {
     load_tile_pair<HD>(rq, ldq_b, rdo, ldo_b, j0 + it * kBwdQT, it < ntiles, stage, wave, lane);
+    load_query_scalars<HD>(rld, rrs, j0 + it * kBwdQT, T_len, it < ntiles, stage, wave, lane);
   };
 
   f32x16 dK[MD], dV[MD];
@@ -215,17 +246,27 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
         mma32(aq, kreg[st], S, bf16_t{});
         mma32(ad, vreg[st], dP, bf16_t{});
       }
-      // register r: query i0s + 8 (r / 4) + 4 hl + r % 4, key `key`
+      // register r: query i0s + 8 (r / 4) + 4 hl + r % 4, key `key`; the four
+      // queries of r / 4 read their (lse2, D) pairs and run starts from the
+      // stage (one address per lane half: broadcast reads)
       float P[16], dS[16];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int qi = i0s + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool qok = qi < T_len;
-        const long qn = (rowbase + (qok ? qi : 0)) * H + h;
-        const bool vis = kok && qok && key <= qi && key >= run_start[rowbase + (qok ? qi : 0)];
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lse2[qn])) : 0.f;
-        P[r] = p;
-        dS[r] = p * (dP[r] - Dd[qn]);
+      for (int g = 0; g < 4; ++g) {
+        const int ql = 32 * sub + 8 * g + 4 * hl;                // first of the four queries in the tile
+        const float4 *px = reinterpret_cast<const float4 *>(sq + 2 * C::TILE + (ql >> 5) * 1024 + (ql & 31) * 8);
+        const float4 x01 = px[0], x23 = px[1];
+        const int4 rs4 = *reinterpret_cast<const int4 *>(sq + 2 * C::TILE + 2 * 1024 + ql * 4);
+        const float lq[4] = {x01.x, x01.z, x23.x, x23.z}, dq[4] = {x01.y, x01.w, x23.y, x23.w};
+        const int rq4[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int r = 4 * g + e;
+          const int qi = i0s + 8 * g + 4 * hl + e;
+          const bool vis = kok && qi < T_len && key <= qi && key >= rq4[e];
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lq[e])) : 0.f;
+          P[r] = p;
+          dS[r] = p * (dP[r] - dq[e]);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -241,7 +282,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
 
   issue(0, st0);
   issue(1, st1);
-  wait_vm_lds_barrier<C::LOADS>();                 // tile 0 landed
+  wait_vm_lds_barrier<C::LOADS + 1>();             // tile 0 landed
   int it = 0;
   for (; it + 1 < ntiles; it += 2) {
     tile(it, st0);
@@ -299,9 +340,9 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
 
 template <int HD>
 __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
-    const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float *__restrict__ lse2,
-    const float *__restrict__ Dd, const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos,
-    const float2 *__restrict__ rope, bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
+    const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float2 *__restrict__ lsed,
+    const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos, const float2 *__restrict__ rope,
+    bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
   using C = BwdCfg<HD>;
   constexpr int CPR = C::CPR, ROWB = C::ROWB, SK = C::SK, MD = C::MD;
   __shared__ __attribute__((aligned(1024))) char st0[C::STAGE];
@@ -334,8 +375,8 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
       doreg[s] = qok ? reinterpret_cast<const uint4 *>(dp)[2 * s + hl] : make_uint4(0, 0, 0, 0);
     }
   }
-  const long qn = (rowbase + (qok ? qi : 0)) * H + h;
-  const float l2 = lse2[qn], Dq = Dd[qn];
+  const float2 lq = lsed[((long)b * H + h) * T_len + (qok ? qi : 0)];
+  const float l2 = lq.x, Dq = lq.y;
   const int rsq = run_start[rowbase + (qok ? qi : 0)];
 
   const int qlast = min(q0 + kBwdQueries, T_len) - 1;
@@ -446,27 +487,28 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
 }
 
 template <int HD>
-static hipError_t attn_bwd_launch(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, const float *lse2,
-                                  const int32_t *rs, const int32_t *pos, const float2 *rope, float *Dd,
-                                  bf16_t *dqkv, int B, int T_len, int H, hipStream_t s) {
+static hipError_t attn_bwd_launch(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, float2 *lsed,
+                                  const int32_t *rs, const int32_t *pos, const float2 *rope, bf16_t *dqkv, int B,
+                                  int T_len, int H, hipStream_t s) {
   const float scale = 1.f / sqrtf((float)HD);
   const float c2 = kLog2e * scale;
-  hipLaunchKernelGGL((attn_bwd_dot_kernel<HD>), dim3((unsigned)((long)B * T_len)), dim3(256), 0, s, dout, o, Dd, H);
+  hipLaunchKernelGGL((attn_bwd_dot_kernel<HD>), dim3((unsigned)((long)B * T_len)), dim3(256), 0, s, dout, o, lsed,
+                     T_len, H);
   const long nk = (long)(T_len + kBwdKeys - 1) / kBwdKeys * H * B;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HD>), dim3((unsigned)nk), dim3(kBwdThreads), 0, s, qkv, dout, lse2, Dd,
-                     rs, pos, rope, dqkv, B, T_len, H, c2, scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HD>), dim3((unsigned)nk), dim3(kBwdThreads), 0, s, qkv, dout, lsed, rs,
+                     pos, rope, dqkv, B, T_len, H, c2, scale);
   const long nq = (long)(T_len + kBwdQueries - 1) / kBwdQueries * H * B;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<HD>), dim3((unsigned)nq), dim3(kBwdThreads), 0, s, qkv, dout, lse2, Dd,
-                     rs, pos, rope, dqkv, B, T_len, H, c2, scale);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<HD>), dim3((unsigned)nq), dim3(kBwdThreads), 0, s, qkv, dout, lsed, rs,
+                     pos, rope, dqkv, B, T_len, H, c2, scale);
   return hipGetLastError();
 }
 
-hipError_t launch_attention_bwd(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, const float *lse2,
-                                const int32_t *run_start, const int32_t *pos, const float2 *rope, float *Dd,
-                                bf16_t *dqkv, int B, int T_len, int H, int hd, hipStream_t s) {
+hipError_t launch_attention_bwd(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, float2 *lsed,
+                                const int32_t *run_start, const int32_t *pos, const float2 *rope, bf16_t *dqkv,
+                                int B, int T_len, int H, int hd, hipStream_t s) {
   switch (hd) {
-    case 64: return attn_bwd_launch<64>(qkv, o, dout, lse2, run_start, pos, rope, Dd, dqkv, B, T_len, H, s);
-    case 128: return attn_bwd_launch<128>(qkv, o, dout, lse2, run_start, pos, rope, Dd, dqkv, B, T_len, H, s);
+    case 64: return attn_bwd_launch<64>(qkv, o, dout, lsed, run_start, pos, rope, dqkv, B, T_len, H, s);
+    case 128: return attn_bwd_launch<128>(qkv, o, dout, lsed, run_start, pos, rope, dqkv, B, T_len, H, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -54,14 +54,17 @@ hipError_t launch_embed_grad(const int32_t *key, const int32_t *val, int32_t *ke
                              void *sort_tmp, size_t sort_bytes, int N, int V, const float *de, int d, float *dE,
                              hipStream_t s);
 // attention reverse: dqkv [B*T, 3A] (dq, dk after the inverse RoPE; dv) from
-// qkv, o, dO [B*T, A], the forward's lse2 [B*T, H]; Dd [B*T, H] scratch
-hipError_t launch_attention_bwd(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, const float *lse2,
-                                const int32_t *run_start, const int32_t *pos, const float2 *rope, float *Dd,
-                                bf16_t *dqkv, int B, int T_len, int H, int hd, hipStream_t s);
+// qkv, o, dO [B*T, A] and the per-query pairs lsed [B, H, T] x float2 whose
+// first element the forward wrote (lse2); the second receives D = dO . o
+hipError_t launch_attention_bwd(const bf16_t *qkv, const bf16_t *o, const bf16_t *dout, float2 *lsed,
+                                const int32_t *run_start, const int32_t *pos, const float2 *rope, bf16_t *dqkv,
+                                int B, int T_len, int H, int hd, hipStream_t s);
 
 // attention
-// lse2 (may be NULL): [B*T, H] base-2 log-sum-exp of each query's scores
-// scaled by log2(e)/sqrt(hd), for the reverse pass
+// lse2 (may be NULL): per (batch row, head, position) pairs of floats,
+// [B, H, T, 2]; element 0 of each pair receives the base-2 log-sum-exp of the
+// query's scores scaled by log2(e)/sqrt(hd), for the reverse pass (element 1
+// is the reverse pass's)
 template <typename T>
 hipError_t launch_attention(const T *qkv, T *out, const int32_t *run_start, float *lse2, int B, int T_len,
                             int H, int hd, hipStream_t s);

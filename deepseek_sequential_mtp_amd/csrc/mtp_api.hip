@@ -552,7 +552,7 @@ size_t chain_bwd_layout(const mtp_chain_bwd_args *a, Carve &c, void **p) {
   p[12] = c.take<T>(N * d);                       // x_a
   p[13] = c.take<T>(N * 3 * (long)A);             // qkv
   p[14] = c.take<T>(N * (long)A);                 // o
-  p[15] = c.take<float>(N * H);                   // lse2
+  p[15] = c.take<float2>(N * H);                  // (lse2, D) per (batch row, head, position)
   p[16] = c.take<float>(N * d);                   // a
   p[17] = c.take<T>(N * d);                       // y
   p[18] = c.take<T>(N * (long)f);                 // silu(gate) * up
@@ -564,7 +564,7 @@ size_t chain_bwd_layout(const mtp_chain_bwd_args *a, Carve &c, void **p) {
   p[24] = c.take<float>(N * d);                   // da
   p[25] = c.take<T>(N * d);                       // da (bf16)
   p[26] = c.take<T>(N * (long)A);                 // dO
-  p[27] = c.take<float>(N * H);                   // D = dO . o
+  p[27] = c.take<char>(0);                        // (D lives beside lse2)
   p[28] = c.take<T>(N * 3 * (long)A);             // dqkv
   p[29] = c.take<float>(N * d);                   // dx_a
   p[30] = c.take<float>(N * d);                   // du
@@ -583,9 +583,10 @@ size_t chain_bwd_layout(const mtp_chain_bwd_args *a, Carve &c, void **p) {
 // One Transformer block's reverse (bf16): buffers, weights and gradients.
 struct BlockBufs {
   bf16_t *xa, *qkv, *o, *y, *gsw;       // stored activations (x_a, q|k|v after RoPE, o, y, SwiGLU product)
-  float *lse2, *a;                      // attention log-sum-exps, residual after attention
+  float2 *lsed;                         // (lse2, D) pairs [B, H, T]: attention log-sum-exps and dO . o
+  float *a;                             // residual after attention
   bf16_t *gb, *dgsw, *dgu, *dab, *dO, *dqkv, *dub;
-  float *dy, *da, *Dd, *dxa, *du;
+  float *dy, *da, *dxa, *du;
   float *part, *skws;
   const int32_t *run_start, *pos;
   const float2 *rope;                   // NULL: no RoPE
@@ -631,8 +632,7 @@ int block_bwd(const BlockBufs &b, const BlockW &w, const BlockG &g, const TU *u,
   }
   {
     MTP_STAGE(MTP_STAGE_BWD_ATTN);
-    MTP_TRY(launch_attention_bwd(b.qkv, b.o, b.dO, b.lse2, b.run_start, b.pos, b.rope, b.Dd, b.dqkv, B, Tl, H, hd,
-                                 s));
+    MTP_TRY(launch_attention_bwd(b.qkv, b.o, b.dO, b.lsed, b.run_start, b.pos, b.rope, b.dqkv, B, Tl, H, hd, s));
   }
   // ---- qkv = x_a W_qkv^T, x_a = Norm_a(u)
   {
@@ -665,12 +665,12 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
   float2 *rope = (float2 *)p[9];
   T *cbuf = (T *)p[10], *xa = (T *)p[12], *qkv = (T *)p[13], *o = (T *)p[14], *ybuf = (T *)p[17];
   T *gsw = (T *)p[18];
-  float *u = (float *)p[11], *lse2 = (float *)p[15], *abuf = (float *)p[16];
+  float *u = (float *)p[11], *abuf = (float *)p[16];
+  float2 *lsed = (float2 *)p[15];
   float *gbuf = (float *)p[19];
   T *gb = (T *)p[20], *dgsw = (T *)p[21], *dgu = (T *)p[22];
   float *dy = (float *)p[23], *da = (float *)p[24];
   T *dab = (T *)p[25], *dO = (T *)p[26];
-  float *Dd = (float *)p[27];
   T *dqkv = (T *)p[28];
   float *dxa = (float *)p[29], *du = (float *)p[30];
   T *dub = (T *)p[31];
@@ -707,7 +707,7 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
       MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
       if ((st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, skws, s)))
         return st;
-      MTP_TRY(launch_attention<T>(qkv, o, run_start, lse2, B, Tl, H, hd, s));
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, (float *)lsed, B, Tl, H, hd, s));
       if ((st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0,
                                                skws, s)))
         return st;
@@ -720,7 +720,7 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
       MTP_TRY(hipGetLastError());
     }
     {
-      const BlockBufs bb{xa, qkv, o, ybuf, gsw, lse2, abuf, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, Dd, dxa, du,
+      const BlockBufs bb{xa, qkv, o, ybuf, gsw, lsed, abuf, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, dxa, du,
                          part, skws, run_start, pos, use_rope ? rope : nullptr};
       const BlockW bw{w.g_attn, w.g_ffn, (const T *)w.Wqkv, (const T *)w.Wo, (const T *)w.Wgate, (const T *)w.Wup,
                       (const T *)w.Wdown};
@@ -853,7 +853,7 @@ size_t horizon_layout(const mtp_horizon_args *a, Carve &c, void **p) {
   p[10] = c.take<T>(N * d);                       // x_a
   p[11] = c.take<T>(N * 3 * (long)A);             // qkv
   p[12] = c.take<T>(N * (long)A);                 // o
-  p[13] = c.take<float>(N * H);                   // lse2
+  p[13] = c.take<float2>(N * H);                  // (lse2, D) per (batch row, head, position)
   p[14] = c.take<float>(N * d);                   // a
   p[15] = c.take<T>(N * d);                       // y
   p[16] = c.take<T>(N * (long)f);                 // silu(gate) * up
@@ -865,7 +865,7 @@ size_t horizon_layout(const mtp_horizon_args *a, Carve &c, void **p) {
   p[22] = c.take<float>(N * d);                   // da
   p[23] = c.take<T>(N * d);                       // da (bf16)
   p[24] = c.take<T>(N * (long)A);                 // dO
-  p[25] = c.take<float>(N * H);                   // D = dO . o
+  p[25] = c.take<char>(0);                        // (D lives beside lse2)
   p[26] = c.take<T>(N * 3 * (long)A);             // dqkv
   p[27] = c.take<float>(N * d);                   // dx_a
   p[28] = c.take<float>(N * d);                   // du (the head's share of dh)
@@ -893,17 +893,17 @@ int horizon_run(const mtp_horizon_args *a, hipStream_t s) {
   float2 *rope = (float2 *)p[9];
   const bool use_rope = a->rope_theta > 0.f;
   T *xa = (T *)p[10], *qkv = (T *)p[11], *o = (T *)p[12], *ybuf = (T *)p[15], *gsw = (T *)p[16], *out = (T *)p[17];
-  float *lse2 = (float *)p[13], *abuf = (float *)p[14];
+  float2 *lsed = (float2 *)p[13];
+  float *abuf = (float *)p[14];
   float *dhk = (float *)p[31];
   int32_t *hlab = (int32_t *)p[30];
   float *small = (float *)p[34];
   float *hl_sum = small, *hl_loss = small + 8 * K, *hl_mtp = small + 12 * K;
   int32_t *hl_counts = (int32_t *)(small + 4 * K), *hl_err = (int32_t *)(small + 16 * K);
   const T *h = static_cast<const T *>(a->h);
-  const BlockBufs bb{xa, qkv, o, ybuf, gsw, lse2, abuf, (T *)p[18], (T *)p[19], (T *)p[20], (T *)p[23],
-                     (T *)p[24], (T *)p[26], (T *)p[29], (float *)p[21], (float *)p[22], (float *)p[25],
-                     (float *)p[27], (float *)p[28], (float *)p[32], (float *)p[33], run_start, pos,
-                     use_rope ? rope : nullptr};
+  const BlockBufs bb{xa, qkv, o, ybuf, gsw, lsed, abuf, (T *)p[18], (T *)p[19], (T *)p[20], (T *)p[23],
+                     (T *)p[24], (T *)p[26], (T *)p[29], (float *)p[21], (float *)p[22], (float *)p[27],
+                     (float *)p[28], (float *)p[32], (float *)p[33], run_start, pos, use_rope ? rope : nullptr};
   const size_t ce_bytes = total - (size_t)((char *)p[35] - (char *)a->workspace);
   const int acc = a->accumulate ? 1 : 0;
 
@@ -925,7 +925,7 @@ int horizon_run(const mtp_horizon_args *a, hipStream_t s) {
       MTP_TRY((launch_rmsnorm<T, T>(h, w.g_attn, xa, nullptr, N, d, a->eps, s)));
       if ((st = gemm_qkv_rope<T>(xa, bw.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, (float *)p[33], s)))
         return st;
-      MTP_TRY(launch_attention<T>(qkv, o, run_start, lse2, B, Tl, H, hd, s));
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, (float *)lsed, B, Tl, H, hd, s));
       if ((st = gemm_nt_store<T, float, T>(o, A, bw.Wo, A, abuf, d, h, d, N, d, A, 1.f, nullptr, 0, (float *)p[33],
                                            s)))
         return st;
