@@ -249,23 +249,38 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       // register r: query i0s + 8 (r / 4) + 4 hl + r % 4, key `key`; the four
       // queries of r / 4 read their (lse2, D) pairs and run starts from the
       // stage (one address per lane half: broadcast reads)
+      // The block is fully visible when every query follows every key and
+      // the last query's run starts at or before the first key (run starts
+      // never decrease): then no mask arithmetic (wave-uniform branch).
+      const int rs_last = __builtin_amdgcn_readfirstlane(
+          *reinterpret_cast<const int *>(sq + 2 * C::TILE + 2 * 1024 + (32 * sub + 31) * 4));
+      const bool full = i0s >= kw0 + 31 && i0s + 31 < T_len && kw0 + 31 < T_len && rs_last <= kw0;
       float P[16], dS[16];
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int ql = 32 * sub + 8 * g + 4 * hl;                // first of the four queries in the tile
         const float4 *px = reinterpret_cast<const float4 *>(sq + 2 * C::TILE + (ql >> 5) * 1024 + (ql & 31) * 8);
         const float4 x01 = px[0], x23 = px[1];
-        const int4 rs4 = *reinterpret_cast<const int4 *>(sq + 2 * C::TILE + 2 * 1024 + ql * 4);
         const float lq[4] = {x01.x, x01.z, x23.x, x23.z}, dq[4] = {x01.y, x01.w, x23.y, x23.w};
-        const int rq4[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
+        if (full) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int r = 4 * g + e;
-          const int qi = i0s + 8 * g + 4 * hl + e;
-          const bool vis = kok && qi < T_len && key <= qi && key >= rq4[e];
-          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lq[e])) : 0.f;
-          P[r] = p;
-          dS[r] = p * (dP[r] - dq[e]);
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            P[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lq[e]));
+            dS[r] = P[r] * (dP[r] - dq[e]);
+          }
+        } else {
+          const int4 rs4 = *reinterpret_cast<const int4 *>(sq + 2 * C::TILE + 2 * 1024 + ql * 4);
+          const int rq4[4] = {rs4.x, rs4.y, rs4.z, rs4.w};
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int r = 4 * g + e;
+            const int qi = i0s + 8 * g + 4 * hl + e;
+            const bool vis = kok && qi < T_len && key <= qi && key >= rq4[e];
+            const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -lq[e])) : 0.f;
+            P[r] = p;
+            dS[r] = p * (dP[r] - dq[e]);
+          }
         }
       }
 #pragma unroll
@@ -338,8 +353,10 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   }
 }
 
+// Two waves per SIMD (at most 256 registers): the second wave hides the
+// first's waits.
 template <int HD>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dq_kernel(
     const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float2 *__restrict__ lsed,
     const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos, const float2 *__restrict__ rope,
     bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
@@ -384,6 +401,7 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
   const int ntiles = (qlast - kbeg) / kBwdKT + 1;
   const int wq_hi = min(qw0 + 32, T_len) - 1;
   const int w_rs = qw0 < T_len ? run_start[rowbase + qw0] : 0;
+  const int w_rs_hi = qw0 < T_len ? run_start[rowbase + wq_hi] : 0;    // the wave's largest run start
 
   const __amdgpu_buffer_rsrc_t rk =
       make_rsrc(qkv + rowbase * ld + A + (long)h * HD, (long)(T_len - 1) * ldq_b + ROWB);
@@ -413,14 +431,24 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dq_kernel(
         mma32(tile_frag<CPR>(sk, 32 * mb + c32, 2 * st + hl), qreg[st], S, bf16_t{});
         mma32(tile_frag<CPR>(sv, 32 * mb + c32, 2 * st + hl), doreg[st], dP, bf16_t{});
       }
-      // register r: key k0 + 32 mb + 8 (r / 4) + 4 hl + r % 4, query qi
+      // register r: key k0 + 32 mb + 8 (r / 4) + 4 hl + r % 4, query qi.  The
+      // block is fully visible to the wave when its last key precedes the
+      // wave's first query, its first key is at or after the wave's largest
+      // run start, and all 32 queries exist (wave-uniform branch).
+      const int kb0 = k0 + 32 * mb;
+      const bool full = kb0 + 31 <= qw0 && kb0 >= w_rs_hi && qw0 + 31 < T_len;
       float dS[16];
+      if (full) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kj = k0 + 32 * mb + 8 * (r >> 2) + 4 * hl + (r & 3);
-        const bool vis = qok && kj <= qi && kj >= rsq;
-        const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2)) : 0.f;
-        dS[r] = p * (dP[r] - Dq);
+        for (int r = 0; r < 16; ++r) dS[r] = __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2)) * (dP[r] - Dq);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kj = kb0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+          const bool vis = qok && kj <= qi && kj >= rsq;
+          const float p = vis ? __builtin_amdgcn_exp2f(fmaf(S[r], c2, -l2)) : 0.f;
+          dS[r] = p * (dP[r] - Dq);
+        }
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {

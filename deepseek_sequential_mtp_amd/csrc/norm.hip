@@ -2,7 +2,9 @@
 // the block pre-norms, the shared output norm and its backward.
 //
 // RMSNorm_g(z) = g * z / sqrt(mean(z^2) + eps) (M7.6 0x03C); statistics in
-// float32.  One 256-thread block per row, 16-byte chunk accesses.
+// float32.  One 256-thread block per row, 16-byte chunk accesses.  Rows of
+// up to 8 chunks per thread (d <= 8192 for f32 input) are held in registers
+// between the sum of squares and the scaling, so each row is read once.
 #include "kernels.hpp"
 
 namespace mtp {
@@ -45,10 +47,84 @@ __device__ void row_scale_store(const TI *row, const float *g, float s, TO *out,
     for (int e = 0; e < E; ++e) store_elem(out, (long)c * E + e, g[c * E + e] * v[e] * s);
   }
 }
+
+// One row's chunks: CPT > 0 holds chunk threadIdx.x + k * kNormThreads in
+// register k (zeros past the row); CPT == 0 reads the row again for each pass.
+template <typename TI, int CPT>
+struct RowCache {
+  static constexpr int E = Elem<TI>::kPerChunk;
+  uint4 c[CPT > 0 ? CPT : 1];
+  const TI *row;
+  int d;
+  __device__ __forceinline__ RowCache(const TI *r, int d_) : row(r), d(d_) {
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int idx = threadIdx.x + k * kNormThreads;
+        c[k] = idx < d / E ? reinterpret_cast<const uint4 *>(row)[idx] : make_uint4(0, 0, 0, 0);
+      }
+    }
+  }
+  __device__ __forceinline__ float sumsq() const {
+    if constexpr (CPT > 0) {
+      float acc = 0.f;
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        float v[E];
+        chunk_to_f32(c[k], v, TI{});
+#pragma unroll
+        for (int e = 0; e < E; ++e) acc += v[e] * v[e];
+      }
+      return acc;
+    } else {
+      return row_sumsq(row, d);
+    }
+  }
+  // out = g * row * s, one vector store per chunk
+  template <typename TO>
+  __device__ __forceinline__ void scale_store(const float *g, float s, TO *out) const {
+    if constexpr (CPT > 0) {
+#pragma unroll
+      for (int k = 0; k < CPT; ++k) {
+        const int idx = threadIdx.x + k * kNormThreads;
+        if (idx >= d / E) break;
+        float v[E];
+        chunk_to_f32(c[k], v, TI{});
+#pragma unroll
+        for (int q = 0; q < E / 4; ++q) {
+          const float4 gq = reinterpret_cast<const float4 *>(g)[idx * (E / 4) + q];
+          const float w[4] = {gq.x * v[4 * q] * s, gq.y * v[4 * q + 1] * s, gq.z * v[4 * q + 2] * s,
+                              gq.w * v[4 * q + 3] * s};
+          store4(out + (long)idx * E + 4 * q, w);
+        }
+      }
+    } else {
+      row_scale_store(row, g, s, out, d);
+    }
+  }
+};
+
+// Chunks per thread for a row of d elements of T: 1, 2, 4 or 8, or 0 (too
+// long to hold: two reads).
+template <typename T>
+inline int row_cpt(int d) {
+  const int c = (d / Elem<T>::kPerChunk + kNormThreads - 1) / kNormThreads;
+  return c <= 1 ? 1 : c <= 2 ? 2 : c <= 4 ? 4 : c <= 8 ? 8 : 0;
+}
+template <typename T, class F>
+inline void with_cpt(int d, F &&f) {
+  switch (row_cpt<T>(d)) {
+    case 1: f(std::integral_constant<int, 1>{}); break;
+    case 2: f(std::integral_constant<int, 2>{}); break;
+    case 4: f(std::integral_constant<int, 4>{}); break;
+    case 8: f(std::integral_constant<int, 8>{}); break;
+    default: f(std::integral_constant<int, 0>{}); break;
+  }
+}
 }  // namespace
 
 // c[n] = [ g_h * h[n] * s_h ; g_e * E[x(b, i+k)] * s_e ]  (he order)
-template <typename T>
+template <typename T, int CPT>
 __global__ __launch_bounds__(kNormThreads) void dual_norm_concat_kernel(
     const T *__restrict__ h, const T *__restrict__ E, const int32_t *__restrict__ tokens,
     const float *__restrict__ g_h, const float *__restrict__ g_e, T *__restrict__ c, int T_len, int d,
@@ -60,42 +136,42 @@ __global__ __launch_bounds__(kNormThreads) void dual_norm_concat_kernel(
   ti = ti < T_len ? ti : T_len - 1;              // rows with no x_(i+k): any valid id
   int tok = tokens[(long)b * T_len + ti];
   tok = tok < 0 ? 0 : (tok >= V ? V - 1 : tok);
-  const T *hr = h + n * d;
-  const T *er = E + (long)tok * d;
-  const float sh_h = block_sum(row_sumsq(hr, d), sh);
-  const float sh_e = block_sum(row_sumsq(er, d), sh);
+  const RowCache<T, CPT> hr(h + n * d, d);
+  const RowCache<T, CPT> er(E + (long)tok * d, d);
+  const float sh_h = block_sum(hr.sumsq(), sh);
+  const float sh_e = block_sum(er.sumsq(), sh);
   const float s_h = rsqrtf(sh_h / d + eps);
   const float s_e = rsqrtf(sh_e / d + eps);
   T *cr = c + n * 2 * (long)d;
-  row_scale_store(hr, g_h, s_h, cr, d);
-  row_scale_store(er, g_e, s_e, cr + d, d);
+  hr.scale_store(g_h, s_h, cr);
+  er.scale_store(g_e, s_e, cr + d);
 }
 
 // out[n] = g * z[n] / rms(z[n]); optionally r[n] = 1 / rms.
-template <typename TI, typename TO>
+template <typename TI, typename TO, int CPT>
 __global__ __launch_bounds__(kNormThreads) void rmsnorm_kernel(const TI *__restrict__ z,
                                                               const float *__restrict__ g,
                                                               TO *__restrict__ out, float *__restrict__ r,
                                                               int d, float eps) {
   __shared__ float sh[kNormThreads / 64];
   const long n = blockIdx.x;
-  const TI *zr = z + n * d;
-  const float s = rsqrtf(block_sum(row_sumsq(zr, d), sh) / d + eps);
+  const RowCache<TI, CPT> zr(z + n * d, d);
+  const float s = rsqrtf(block_sum(zr.sumsq(), sh) / d + eps);
   if (r != nullptr && threadIdx.x == 0) r[n] = s;
-  row_scale_store(zr, g, s, out + n * d, d);
+  zr.scale_store(g, s, out + n * d);
 }
 
 // Shared output norm for one depth plus label sanitising: labels outside
 // [-1, V) become -1 and raise the error flag.
-template <typename T>
+template <typename T, int CPT>
 __global__ __launch_bounds__(kNormThreads) void out_norm_kernel(
     const T *__restrict__ h, const float *__restrict__ g, T *__restrict__ xhat, float *__restrict__ r,
     const int32_t *__restrict__ labels_in, int32_t *__restrict__ labels_out, int32_t *__restrict__ err,
     int d, int V, float eps) {
   __shared__ float sh[kNormThreads / 64];
   const long n = blockIdx.x;
-  const T *hr = h + n * d;
-  const float s = rsqrtf(block_sum(row_sumsq(hr, d), sh) / d + eps);
+  const RowCache<T, CPT> hr(h + n * d, d);
+  const float s = rsqrtf(block_sum(hr.sumsq(), sh) / d + eps);
   if (threadIdx.x == 0) {
     r[n] = s;
     int lab = labels_in[n];
@@ -105,7 +181,7 @@ __global__ __launch_bounds__(kNormThreads) void out_norm_kernel(
     }
     labels_out[n] = lab;
   }
-  row_scale_store(hr, g, s, xhat + n * d, d);
+  hr.scale_store(g, s, xhat + n * d);
 }
 
 // RMSNorm backward through the output norm:
@@ -270,22 +346,29 @@ template <typename T>
 hipError_t launch_dual_norm_concat(const T *h, const T *E, const int32_t *tokens, const float *g_h,
                                    const float *g_e, T *c, int B, int T_len, int d, int V, int depth,
                                    float eps, hipStream_t s) {
-  hipLaunchKernelGGL(dual_norm_concat_kernel<T>, dim3(B * T_len), dim3(kNormThreads), 0, s, h, E, tokens,
-                     g_h, g_e, c, T_len, d, V, depth, eps);
+  with_cpt<T>(d, [&](auto cpt) {
+    hipLaunchKernelGGL((dual_norm_concat_kernel<T, decltype(cpt)::value>), dim3(B * T_len), dim3(kNormThreads), 0,
+                       s, h, E, tokens, g_h, g_e, c, T_len, d, V, depth, eps);
+  });
   return hipGetLastError();
 }
 template <typename TI, typename TO>
 hipError_t launch_rmsnorm(const TI *z, const float *g, TO *out, float *r, long rows, int d, float eps,
                           hipStream_t s) {
-  hipLaunchKernelGGL((rmsnorm_kernel<TI, TO>), dim3(rows), dim3(kNormThreads), 0, s, z, g, out, r, d, eps);
+  with_cpt<TI>(d, [&](auto cpt) {
+    hipLaunchKernelGGL((rmsnorm_kernel<TI, TO, decltype(cpt)::value>), dim3(rows), dim3(kNormThreads), 0, s, z, g,
+                       out, r, d, eps);
+  });
   return hipGetLastError();
 }
 template <typename T>
 hipError_t launch_out_norm(const T *h, const float *g, T *xhat, float *r, const int32_t *labels_in,
                            int32_t *labels_out, int32_t *err, long rows, int d, int V, float eps,
                            hipStream_t s) {
-  hipLaunchKernelGGL(out_norm_kernel<T>, dim3(rows), dim3(kNormThreads), 0, s, h, g, xhat, r, labels_in,
-                     labels_out, err, d, V, eps);
+  with_cpt<T>(d, [&](auto cpt) {
+    hipLaunchKernelGGL((out_norm_kernel<T, decltype(cpt)::value>), dim3(rows), dim3(kNormThreads), 0, s, h, g, xhat,
+                       r, labels_in, labels_out, err, d, V, eps);
+  });
   return hipGetLastError();
 }
 template <typename T>

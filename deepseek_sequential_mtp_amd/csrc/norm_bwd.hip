@@ -7,6 +7,8 @@
 // RMSNorm_g(z) = g z r, r = 1 / sqrt(mean(z^2) + eps), x_n = z r:
 //   dz = r (g dy - x_n mean(x_n g dy)),   dg = sum over rows of dy x_n.
 #include <rocprim/device/device_radix_sort.hpp>
+#include <rocprim/device/device_run_length_encode.hpp>
+#include <rocprim/device/device_scan.hpp>
 
 #include "kernels.hpp"
 
@@ -155,27 +157,63 @@ __global__ void shifted_rows_kernel(const int32_t *__restrict__ tokens, const ui
   val[n] = (int32_t)n;
 }
 
-// dE[t] += sum of de over the rows whose shifted token is t, in ascending
-// row order (the stable sort keeps it): the block at sorted position p
-// starts a run of equal keys; it sums the run for its column range.
-__global__ __launch_bounds__(kThreads) void embed_grad_kernel(const int32_t *__restrict__ keys,
-                                                             const int32_t *__restrict__ rows, int N,
-                                                             const float *__restrict__ de, int d, int V,
-                                                             float *__restrict__ dE) {
-  const int p = blockIdx.x;
-  const int k = keys[p];
-  if (k >= V || (p > 0 && keys[p - 1] == k)) return;
+// dE[t] += sum of de over the rows whose shifted token is t.  The sorted
+// (key, row) pairs form one run per distinct key (the stable sort keeps the
+// rows ascending); run r holds counts[r] rows from offsets[r].  A fixed grid
+// walks the runs; the block's kEmbWaves waves share a run's rows, wave w
+// taking positions 4 (w + kEmbWaves i) + u, u = 0..3, into accumulator u,
+// and the partial sums are added in wave order, so the result does not
+// depend on timing (no atomics).  Lane l of grid column y owns the 16-byte
+// chunk 64 y + l of the row.  Zipf-distributed tokens give a few long runs
+// (the most frequent token appears in thousands of rows), which all the
+// block's waves split instead of one thread walking them.
+constexpr int kEmbWaves = 16;
+__global__ __launch_bounds__(64 * kEmbWaves) void embed_grad_kernel(
+    const int32_t *__restrict__ unique, const uint32_t *__restrict__ counts, const uint32_t *__restrict__ offsets,
+    const uint32_t *__restrict__ nruns, const int32_t *__restrict__ rows, const float *__restrict__ de, int d,
+    int V, float *__restrict__ dE) {
+  __shared__ float4 part[kEmbWaves][64];
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int nch = d >> 2;
-  for (int c = blockIdx.y * kThreads + threadIdx.x; c < nch; c += gridDim.y * kThreads) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int q = p; q < N && keys[q] == k; ++q) {
-      const float4 v = ld4(de + (long)rows[q] * d, c);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  const int c = blockIdx.y * 64 + lane;
+  const bool cok = c < nch;
+  const int R = (int)nruns[0];
+  for (int r = blockIdx.x; r < R; r += gridDim.x) {
+    const int k = unique[r];
+    if (k >= V) continue;                       // the rows without a gathered embedding
+    const int off = (int)offsets[r], len = (int)counts[r];
+    float4 acc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int q0 = 4 * w; q0 < len; q0 += 4 * kEmbWaves) {
+      float4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        v[u] = q0 + u < len && cok ? ld4(de + (long)rows[off + q0 + u] * d, c) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        acc[u].x += v[u].x; acc[u].y += v[u].y; acc[u].z += v[u].z; acc[u].w += v[u].w;
+      }
     }
-    float4 *dst = reinterpret_cast<float4 *>(dE + (long)k * d) + c;
-    float4 o = *dst;
-    o.x += acc.x; o.y += acc.y; o.z += acc.z; o.w += acc.w;
-    *dst = o;
+    float4 t = acc[0];
+#pragma unroll
+    for (int u = 1; u < 4; ++u) { t.x += acc[u].x; t.y += acc[u].y; t.z += acc[u].z; t.w += acc[u].w; }
+    part[w][lane] = t;
+    __syncthreads();
+    if (w == 0 && cok) {
+      float4 sum = part[0][lane];
+#pragma unroll
+      for (int i = 1; i < kEmbWaves; ++i) {
+        const float4 x = part[i][lane];
+        sum.x += x.x; sum.y += x.y; sum.z += x.z; sum.w += x.w;
+      }
+      float4 *dst = reinterpret_cast<float4 *>(dE + (long)k * d) + c;
+      float4 o = *dst;
+      o.x += sum.x; o.y += sum.y; o.z += sum.z; o.w += sum.w;
+      *dst = o;
+    }
+    __syncthreads();
   }
 }
 
@@ -185,13 +223,31 @@ static unsigned key_bits(int V) {
   return b;
 }
 
-size_t embed_grad_sort_bytes(int N, int V) {
-  size_t bytes = 0;
-  if (rocprim::radix_sort_pairs(nullptr, bytes, (const int32_t *)nullptr, (int32_t *)nullptr,
+// Scratch of launch_embed_grad: the library routines' temporary storage (the
+// largest of the sort's, the run-length encoding's and the scan's), then the
+// runs' keys, counts and offsets (N each) and the run count.
+namespace {
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
+size_t embed_tmp_bytes(int N, int V) {
+  size_t sort_b = 0, rle_b = 0, scan_b = 0;
+  if (rocprim::radix_sort_pairs(nullptr, sort_b, (const int32_t *)nullptr, (int32_t *)nullptr,
                                 (const int32_t *)nullptr, (int32_t *)nullptr, (size_t)N, 0u, key_bits(V)) !=
       hipSuccess)
     return 0;
-  return bytes;
+  if (rocprim::run_length_encode(nullptr, rle_b, (const int32_t *)nullptr, (unsigned)N, (int32_t *)nullptr,
+                                 (uint32_t *)nullptr, (uint32_t *)nullptr) != hipSuccess)
+    return 0;
+  if (rocprim::exclusive_scan(nullptr, scan_b, (const uint32_t *)nullptr, (uint32_t *)nullptr, 0u, (size_t)N,
+                              rocprim::plus<uint32_t>()) != hipSuccess)
+    return 0;
+  return align256(std::max(sort_b, std::max(rle_b, scan_b)));
+}
+}  // namespace
+
+size_t embed_grad_sort_bytes(int N, int V) {
+  const size_t tmp = embed_tmp_bytes(N, V);
+  if (tmp == 0) return 0;
+  return tmp + 3 * align256((size_t)N * 4) + 256;
 }
 
 hipError_t launch_shifted_rows(const int32_t *tokens, const uint8_t *state, int B, int T_len, int V, int depth,
@@ -205,12 +261,29 @@ hipError_t launch_shifted_rows(const int32_t *tokens, const uint8_t *state, int 
 hipError_t launch_embed_grad(const int32_t *key, const int32_t *val, int32_t *key_sorted, int32_t *val_sorted,
                              void *sort_tmp, size_t sort_bytes, int N, int V, const float *de, int d, float *dE,
                              hipStream_t s) {
-  size_t bytes = sort_bytes;
+  const size_t tmp = embed_tmp_bytes(N, V);
+  if (tmp == 0 || sort_bytes < embed_grad_sort_bytes(N, V)) return hipErrorInvalidValue;
+  char *base = static_cast<char *>(sort_tmp);
+  int32_t *unique = reinterpret_cast<int32_t *>(base + tmp);
+  uint32_t *counts = reinterpret_cast<uint32_t *>(base + tmp + align256((size_t)N * 4));
+  uint32_t *offsets = reinterpret_cast<uint32_t *>(base + tmp + 2 * align256((size_t)N * 4));
+  uint32_t *nruns = reinterpret_cast<uint32_t *>(base + tmp + 3 * align256((size_t)N * 4));
+  size_t bytes = tmp;
   hipError_t e = rocprim::radix_sort_pairs(sort_tmp, bytes, key, key_sorted, val, val_sorted, (size_t)N, 0u,
                                            key_bits(V), s);
   if (e != hipSuccess) return e;
-  const int ny = ((d >> 2) + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(embed_grad_kernel, dim3(N, ny), dim3(kThreads), 0, s, key_sorted, val_sorted, N, de, d, V, dE);
+  bytes = tmp;
+  e = rocprim::run_length_encode(sort_tmp, bytes, (const int32_t *)key_sorted, (unsigned)N, unique, counts, nruns, s);
+  if (e != hipSuccess) return e;
+  bytes = tmp;
+  // runs past nruns hold stale counts; their offsets are never read
+  e = rocprim::exclusive_scan(sort_tmp, bytes, (const uint32_t *)counts, offsets, 0u, (size_t)N,
+                              rocprim::plus<uint32_t>(), s);
+  if (e != hipSuccess) return e;
+  const int ny = ((d >> 2) + 63) / 64;
+  const int gx = N < 1024 ? N : 1024;
+  hipLaunchKernelGGL(embed_grad_kernel, dim3(gx, ny), dim3(64 * kEmbWaves), 0, s, unique, counts, offsets, nruns,
+                     val_sorted, de, d, V, dE);
   return hipGetLastError();
 }
 
