@@ -272,3 +272,98 @@ def test_verify_noalloc_refuses_beyond_its_scratch_on_the_host(lib):
     assert lib.mtp_verify_noalloc(None, None) == -1
     a.R = 0
     assert lib.mtp_verify_noalloc(C.byref(a), None) == -2
+
+
+FAKE = 0x7f0000000000          # 16-byte aligned, never dereferenced: these calls return before any launch
+
+
+def _bwd_args(**kw):
+    a = _lib.ChainBwdArgs()
+    a.B, a.T, a.d, a.n_heads, a.head_dim, a.ffn, a.V, a.D = 2, 64, 256, 2, 128, 688, 1000, 2
+    a.dtype, a.eps, a.rope_theta = _lib.MTP_BF16, 1e-6, 1e4
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _fill_bwd_pointers(a, D):
+    w = (_lib.DepthWeights * D)()
+    g = (_lib.DepthGrads * D)()
+    for k in range(D):
+        for name, _ in _lib.DepthWeights._fields_:
+            setattr(w[k], name, FAKE)
+        for name, _ in _lib.DepthGrads._fields_:
+            setattr(g[k], name, FAKE)
+    h = (C.c_void_p * D)(*([FAKE] * D))
+    dh = (C.c_void_p * D)(*([FAKE] * D))
+    for name in ("tokens", "segment_ids", "h0", "embed", "dh0", "dE"):
+        setattr(a, name, FAKE)
+    a.w, a.dw, a.h, a.dh = w, g, h, dh
+    return (w, g, h, dh)                    # keep the arrays alive
+
+
+def test_chain_backward_host_errors(lib):
+    run = lambda a: lib.mtp_chain_backward(C.byref(a), None)
+    assert lib.mtp_chain_backward(None, None) == -1
+    assert run(_bwd_args(D=0)) == -3
+    assert run(_bwd_args(dtype=_lib.MTP_F32, ffn=172, d=64, head_dim=16, n_heads=4)) == -8   # bf16 only
+    assert run(_bwd_args(head_dim=32, n_heads=8)) == -8                                     # head width 64 or 128
+    assert run(_bwd_args(d=8200, ffn=688)) == -8                                            # rows up to 8192
+    assert run(_bwd_args(eps=-1.0)) == -6
+    assert run(_bwd_args()) == -1                                                           # pointers missing
+    a = _bwd_args()
+    keep = _fill_bwd_pointers(a, a.D)
+    a.dh[0] = None                                # the head's gradient of depth 1 is required
+    assert run(a) == -1
+    a.dh[0] = FAKE
+    a.w[1].Wo = FAKE + 8                          # misaligned weight
+    assert run(a) == -6
+    a.w[1].Wo = FAKE
+    need = lib.mtp_chain_backward_workspace_size(C.byref(a))
+    assert need > 0
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert run(a) == -5                           # workspace too small
+    a.workspace = None
+    assert run(a) == -5
+    del keep
+    # the workspace grows with the rows and does not depend on the pointers
+    assert lib.mtp_chain_backward_workspace_size(C.byref(_bwd_args(T=128))) > need
+    assert lib.mtp_chain_backward_workspace_size(C.byref(_bwd_args(D=0))) == 0
+
+
+def test_horizon_heads_host_errors(lib):
+    def args(**kw):
+        a = _lib.HorizonArgs()
+        a.B, a.T, a.d, a.n_heads, a.head_dim, a.ffn, a.V, a.K = 2, 64, 256, 2, 128, 688, 1000, 2
+        a.dtype, a.eps, a.rope_theta, a.lambda_ = _lib.MTP_BF16, 1e-6, 1e4, 0.1
+        for k, v in kw.items():
+            setattr(a, k, v)
+        return a
+    run = lambda a: lib.mtp_horizon_heads(C.byref(a), None)
+    assert lib.mtp_horizon_heads(None, None) == -1
+    assert run(args(K=0)) == -3
+    assert run(args(V=1004)) == -2                       # V a multiple of 8
+    assert run(args(head_dim=32, n_heads=8)) == -8
+    assert run(args(lambda_=float("nan"))) == -6
+    assert run(args()) == -1
+    a = args()
+    w = (_lib.BlockWeights * 2)()
+    g = (_lib.BlockGrads * 2)()
+    for k in range(2):
+        for name, _ in _lib.BlockWeights._fields_:
+            setattr(w[k], name, FAKE)
+        for name, _ in _lib.BlockGrads._fields_:
+            setattr(g[k], name, FAKE)
+    for name in ("tokens", "segment_ids", "h", "W_out", "g_out", "loss", "counts", "loss_total", "dh", "dW_out",
+                 "dg_out"):
+        setattr(a, name, FAKE)
+    a.w, a.dw = w, g
+    a.dw[1].Wgate = None
+    assert run(a) == -1
+    a.dw[1].Wgate = FAKE + 4
+    assert run(a) == -6
+    a.dw[1].Wgate = FAKE
+    need = lib.mtp_horizon_heads_workspace_size(C.byref(a))
+    assert need > 0
+    a.workspace, a.workspace_bytes = FAKE, need - 1
+    assert run(a) == -5
