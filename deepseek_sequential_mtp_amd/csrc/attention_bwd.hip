@@ -209,8 +209,17 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   }
   // query tiles from j0 while their first query's window can reach the
   // block's keys (window starts never decrease along a row)
+  // (a binary search over the tile starts: run starts never decrease along a
+  // row, so the tiles that qualify are a prefix; the first always does)
   int ntiles = 0;
-  for (int i0 = j0; i0 < T_len && run_start[rowbase + i0] <= jlast; i0 += kBwdQT) ++ntiles;
+  {
+    int hi = (T_len - j0 + kBwdQT - 1) / kBwdQT;     // tiles starting inside the row
+    while (ntiles < hi) {
+      const int mid = (ntiles + hi) >> 1;
+      if (run_start[rowbase + j0 + mid * kBwdQT] <= jlast) ntiles = mid + 1;
+      else hi = mid;
+    }
+  }
 
   const __amdgpu_buffer_rsrc_t rq =
       make_rsrc(qkv + rowbase * ld + (long)h * HD, (long)(T_len - 1) * ldq_b + ROWB);
@@ -235,7 +244,10 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
       const int i0s = i0 + 32 * sub;
-      if (!(kw0 < T_len && i0s < T_len && i0s + 31 >= kw0 && run_start[rowbase + i0s] <= kw0 + 31)) continue;
+      // the sub-tile's first run start, from the tile's staged run starts
+      const int rs_first = __builtin_amdgcn_readfirstlane(
+          *reinterpret_cast<const int *>(sq + 2 * C::TILE + 2 * 1024 + (32 * sub) * 4));
+      if (!(kw0 < T_len && i0s < T_len && i0s + 31 >= kw0 && rs_first <= kw0 + 31)) continue;
       f32x16 S, dP;
 #pragma unroll
       for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
