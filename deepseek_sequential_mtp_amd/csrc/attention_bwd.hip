@@ -16,8 +16,11 @@
 // [B, H, T] x float2, so that a tile of consecutive queries reads one
 // contiguous run of them.
 //
-// Two kernels, no atomics (the result does not depend on timing):
-//   dK/dV: a block owns 128 keys of one (batch row, head), four waves of 32;
+// Three passes, no atomics (the result does not depend on timing):
+//   dV and dK (one kernel template, two launches: each pass keeps only its
+//   own accumulators, so that two waves fit each SIMD; the scores are
+//   computed in both): a block owns 128 keys of one (batch row, head), four
+//   waves of 32;
 //     each wave keeps its keys' K and V fragments in registers and walks the
 //     query tiles that can see them (64 queries per tile; Q and dO, and the
 //     tile's (lse2, D) pairs and run starts, staged in LDS by direct loads,
@@ -169,8 +172,8 @@ __global__ __launch_bounds__(256) void attn_bwd_dot_kernel(const bf16_t *__restr
   }
 }
 
-template <int HD>
-__global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
+template <int HD, bool DK>
+__global__ __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(2))) void attn_bwd_dkdv_kernel(
     const bf16_t *__restrict__ qkv, const bf16_t *__restrict__ dout, const float2 *__restrict__ lsed,
     const int32_t *__restrict__ run_start, const int32_t *__restrict__ pos, const float2 *__restrict__ rope,
     bf16_t *__restrict__ dqkv, int B, int T_len, int H, float c2, float scale) {
@@ -197,14 +200,15 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   const int key = kw0 + c32;                         // this lane's key (result column)
   const bool kok = key < T_len;
 
-  // the wave's K and V fragments (MFMA B operands: column = key, K = head dim)
-  uint4 kreg[SK], vreg[SK];
+  // the wave's K (and, for dK, V) fragments (MFMA B operands: column = key,
+  // K = head dim)
+  uint4 kreg[SK], vreg[DK ? SK : 1];
   {
     const bf16_t *kp = qkv + (rowbase + (kok ? key : 0)) * ld + A + (long)h * HD;
 #pragma unroll
     for (int s = 0; s < SK; ++s) {
       kreg[s] = kok ? reinterpret_cast<const uint4 *>(kp)[2 * s + hl] : make_uint4(0, 0, 0, 0);
-      vreg[s] = kok ? reinterpret_cast<const uint4 *>(kp + A)[2 * s + hl] : make_uint4(0, 0, 0, 0);
+      if constexpr (DK) vreg[s] = kok ? reinterpret_cast<const uint4 *>(kp + A)[2 * s + hl] : make_uint4(0, 0, 0, 0);
     }
   }
   // query tiles from j0 while their first query's window can reach the
@@ -232,11 +236,11 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
     load_query_scalars<HD>(rld, rrs, j0 + it * kBwdQT, T_len, it < ntiles, stage, wave, lane);
   };
 
-  f32x16 dK[MD], dV[MD];
+  f32x16 acc[MD];                                    // dK or dV of the wave's keys
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dK[md][r] = dV[md][r] = 0.f;
+    for (int r = 0; r < 16; ++r) acc[md][r] = 0.f;
 
   auto tile = [&](int it, const char *sq) {
     const char *sdo = sq + C::TILE;
@@ -253,10 +257,8 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       for (int r = 0; r < 16; ++r) S[r] = dP[r] = 0.f;
 #pragma unroll
       for (int st = 0; st < SK; ++st) {
-        const uint4 aq = tile_frag<CPR>(sq, 32 * sub + c32, 2 * st + hl);
-        const uint4 ad = tile_frag<CPR>(sdo, 32 * sub + c32, 2 * st + hl);
-        mma32(aq, kreg[st], S, bf16_t{});
-        mma32(ad, vreg[st], dP, bf16_t{});
+        mma32(tile_frag<CPR>(sq, 32 * sub + c32, 2 * st + hl), kreg[st], S, bf16_t{});
+        if constexpr (DK) mma32(tile_frag<CPR>(sdo, 32 * sub + c32, 2 * st + hl), vreg[st], dP, bf16_t{});
       }
       // register r: query i0s + 8 (r / 4) + 4 hl + r % 4, key `key`; the four
       // queries of r / 4 read their (lse2, D) pairs and run starts from the
@@ -297,11 +299,14 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
       }
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint4 pa = pack8(P + 8 * j), sa = pack8(dS + 8 * j);
+        if constexpr (DK) {
+          const uint4 sa = pack8(dS + 8 * j);
 #pragma unroll
-        for (int md = 0; md < MD; ++md) {
-          mma32(pa, tile_tr<CPR>(sdo, 32 * sub, j, md, lane), dV[md], bf16_t{});
-          mma32(sa, tile_tr<CPR>(sq, 32 * sub, j, md, lane), dK[md], bf16_t{});
+          for (int md = 0; md < MD; ++md) mma32(sa, tile_tr<CPR>(sq, 32 * sub, j, md, lane), acc[md], bf16_t{});
+        } else {
+          const uint4 pa = pack8(P + 8 * j);
+#pragma unroll
+          for (int md = 0; md < MD; ++md) mma32(pa, tile_tr<CPR>(sdo, 32 * sub, j, md, lane), acc[md], bf16_t{});
         }
       }
     }
@@ -325,43 +330,43 @@ __global__ __launch_bounds__(kBwdThreads) void attn_bwd_dkdv_kernel(
   // dK: scale, then back through RoPE at each key's position.  Register r of
   // block md holds key kw0 + 8 (r / 4) + 4 hl + r % 4, head-dim 32 md + c32;
   // the rotation partner of block md < MD / 2 is block md + MD / 2.
+  if constexpr (DK) {
 #pragma unroll
-  for (int md = 0; md < MD; ++md)
+    for (int md = 0; md < MD; ++md)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) dK[md][r] *= scale;
-  if (rope != nullptr) {
-    constexpr int HALF = HD / 2;
+      for (int r = 0; r < 16; ++r) acc[md][r] *= scale;
+    if (rope != nullptr) {
+      constexpr int HALF = HD / 2;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int kr = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
-      const int p = kr < T_len ? pos[rowbase + kr] : 0;
+      for (int r = 0; r < 16; ++r) {
+        const int kr = kw0 + 8 * (r >> 2) + 4 * hl + (r & 3);
+        const int p = kr < T_len ? pos[rowbase + kr] : 0;
 #pragma unroll
-      for (int md = 0; md < MD / 2; ++md) {
-        const float2 cs = rope[(long)p * HALF + 32 * md + c32];
-        const float d1 = dK[md][r], d2 = dK[md + MD / 2][r];
-        dK[md][r] = d1 * cs.x + d2 * cs.y;
-        dK[md + MD / 2][r] = d2 * cs.x - d1 * cs.y;
+        for (int md = 0; md < MD / 2; ++md) {
+          const float2 cs = rope[(long)p * HALF + 32 * md + c32];
+          const float d1 = acc[md][r], d2 = acc[md + MD / 2][r];
+          acc[md][r] = d1 * cs.x + d2 * cs.y;
+          acc[md + MD / 2][r] = d2 * cs.x - d1 * cs.y;
+        }
       }
     }
   }
-  // stage [key][head dim] in LDS (dK in st0, dV in st1), then 16-byte stores
+  // stage [key][head dim] in LDS, then 16-byte stores into the dk (or dv) columns
 #pragma unroll
   for (int md = 0; md < MD; ++md)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int kl = 32 * wave + 8 * (r >> 2) + 4 * hl + (r & 3);
       const int dd = 32 * md + c32;
-      reinterpret_cast<bf16_t *>(st0 + kl * ROWB)[dd].bits = f32_to_bf16(dK[md][r]);
-      reinterpret_cast<bf16_t *>(st1 + kl * ROWB)[dd].bits = f32_to_bf16(dV[md][r]);
+      reinterpret_cast<bf16_t *>(st0 + kl * ROWB)[dd].bits = f32_to_bf16(acc[md][r]);
     }
   __syncthreads();
   for (int cidx = t; cidx < kBwdKeys * CPR; cidx += kBwdThreads) {
     const int kl = cidx / CPR, ch = cidx % CPR;
     const int kr = j0 + kl;
     if (kr >= T_len) continue;
-    bf16_t *dst = dqkv + (rowbase + kr) * ld + (long)h * HD + ch * 8;
-    *reinterpret_cast<uint4 *>(dst + A) = *reinterpret_cast<const uint4 *>(st0 + kl * ROWB + ch * 16);
-    *reinterpret_cast<uint4 *>(dst + 2L * A) = *reinterpret_cast<const uint4 *>(st1 + kl * ROWB + ch * 16);
+    bf16_t *dst = dqkv + (rowbase + kr) * ld + (DK ? A : 2L * A) + (long)h * HD + ch * 8;
+    *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(st0 + kl * ROWB + ch * 16);
   }
 }
 
@@ -535,8 +540,10 @@ static hipError_t attn_bwd_launch(const bf16_t *qkv, const bf16_t *o, const bf16
   hipLaunchKernelGGL((attn_bwd_dot_kernel<HD>), dim3((unsigned)((long)B * T_len)), dim3(256), 0, s, dout, o, lsed,
                      T_len, H);
   const long nk = (long)(T_len + kBwdKeys - 1) / kBwdKeys * H * B;
-  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HD>), dim3((unsigned)nk), dim3(kBwdThreads), 0, s, qkv, dout, lsed, rs,
-                     pos, rope, dqkv, B, T_len, H, c2, scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HD, false>), dim3((unsigned)nk), dim3(kBwdThreads), 0, s, qkv, dout, lsed,
+                     rs, pos, rope, dqkv, B, T_len, H, c2, scale);
+  hipLaunchKernelGGL((attn_bwd_dkdv_kernel<HD, true>), dim3((unsigned)nk), dim3(kBwdThreads), 0, s, qkv, dout, lsed,
+                     rs, pos, rope, dqkv, B, T_len, H, c2, scale);
   const long nq = (long)(T_len + kBwdQueries - 1) / kBwdQueries * H * B;
   hipLaunchKernelGGL((attn_bwd_dq_kernel<HD>), dim3((unsigned)nq), dim3(kBwdThreads), 0, s, qkv, dout, lsed, rs,
                      pos, rope, dqkv, B, T_len, H, c2, scale);
