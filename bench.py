@@ -360,46 +360,61 @@ def bench_propose(torch, _lib, cfg, inp, R=64, prefix=2048, reps=10):
 def bench_backward(torch, _lib, cfg, inp, chain_out, ce_out, per, cache, reps=5):
     """mtp_chain_backward after the timed step (its chain outputs and the head
     CE's dh): the gradient of L_MTP through every module to h^(0), E and the
-    per-depth weights.  Algorithmic work credits the products of the reverse
-    pass once: the data and weight gradients of every chain GEMM (twice the
-    forward's FLOPs) and 8 A per attention pair (dV, dP, dQ, dK); the
-    module's forward recompute is executed but not credited."""
+    per-depth weights, timed with the forward's saved activations (`ms`) and
+    with each depth's forward recomputed (`ms_recompute`).  Algorithmic work
+    credits the products of the reverse pass once: the data and weight
+    gradients of every chain GEMM (twice the forward's FLOPs) and 8 A per
+    attention pair (dV, dP, dQ, dK)."""
     dev = inp["h0"].device
     out = dict(dh0=torch.empty((cfg.N, cfg.d), dtype=torch.float32, device=dev),
                dE=torch.zeros((cfg.V, cfg.d), dtype=torch.float32, device=dev),
                dw=[{n: torch.empty(w[n].shape, dtype=torch.float32, device=dev) for n in _lib.GRAD_FIELDS}
                    for w in inp["depths"]],
                device_error=torch.empty(1, dtype=torch.int32, device=dev))
+    # the same forward again with its activations kept (untimed)
+    kept = _lib.chain_forward(inp["tokens"], inp["segment_ids"], inp["h0"], inp["E"], inp["depths"],
+                              n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps, rope_theta=cfg.rope_theta,
+                              save=True)
 
-    def run():
+    def run(saved):
         _lib.chain_backward(inp["tokens"], inp["segment_ids"], inp["h0"], inp["E"], inp["depths"], chain_out["h"],
                             ce_out["dh"], n_heads=cfg.n_heads, head_dim=cfg.head_dim, eps=cfg.eps,
-                            rope_theta=cfg.rope_theta, out=out, cache=cache)
+                            rope_theta=cfg.rope_theta, out=out, cache=cache, saved=saved)
 
-    run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    timer = _lib.AllStageTimer(64 * reps)
-    with timer:
-        e0.record()
-        for _ in range(reps):
-            run()
-        e1.record()
+    def timed(saved):
+        run(saved)
         torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / reps
-    stages = {k: {"ms": round(float(np.sum(v)) / reps, 4)} for k, v in timer.by_stage().items()}
-    fwd_gemm = sum(p[k] for p in per for k in ("EH_PROJ", "QKV", "O_PROJ", "GATE_UP", "DOWN"))
-    attn_pairs_flops = sum(p["ATTN"] for p in per)          # 4 A P
-    alg = 2.0 * fwd_gemm + 2.0 * attn_pairs_flops
-    # executed: the recompute (the forward, 4 A per pair), then dK/dV (S, dP,
-    # dV, dK) and dQ (S, dP, dQ): 4 + 14 = 18 A per pair
-    executed = 3.0 * fwd_gemm + 4.5 * attn_pairs_flops
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        timer = _lib.AllStageTimer(64 * reps)
+        with timer:
+            e0.record()
+            for _ in range(reps):
+                run(saved)
+            e1.record()
+            torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / reps
+        return ms, {k: {"ms": round(float(np.sum(v)) / reps, 4)} for k, v in timer.by_stage().items()}
+
+    ms, stages = timed(kept["saved"])
+    ms_re, stages_re = timed(None)
+    g = lambda *ks: sum(p[k] for p in per for k in ks)
+    fwd_gemm = g("EH_PROJ", "QKV", "O_PROJ", "GATE_UP", "DOWN")
+    attn = g("ATTN")                                        # 4 A per pair
+    alg = 2.0 * fwd_gemm + 2.0 * attn
+    # executed: the gate/up product again inside the MLP reverse, and the
+    # attention reverse's dV pass (S, dV), dK pass (S, dP, dK) and dQ pass
+    # (S, dP, dQ): 16 A per pair; the recompute adds eh_proj, QKV, O-proj
+    # and the attention forward
+    executed = 2.0 * fwd_gemm + g("GATE_UP") + 4.0 * attn
+    executed_re = executed + g("EH_PROJ", "QKV", "O_PROJ") + attn
     tf = alg / (ms * 1e-3) / 1e12
-    del out
-    return {"ms": round(ms, 4), "algorithmic_tflop": round(alg / 1e12, 3),
-            "executed_tflop": round(executed / 1e12, 3), "achieved": round(tf, 1), "unit": "TFLOP/s",
-            "frac": round(tf / PEAK_BF16_TFLOPS, 4), "tokens_per_s": round(cfg.N / (ms * 1e-3), 1),
-            "stages": stages, "flops_basis": "algorithmic reverse-pass FLOPs (recompute not credited) / call time"}
+    del out, kept
+    return {"ms": round(ms, 4), "ms_recompute": round(ms_re, 4), "algorithmic_tflop": round(alg / 1e12, 3),
+            "executed_tflop": round(executed / 1e12, 3), "executed_tflop_recompute": round(executed_re / 1e12, 3),
+            "achieved": round(tf, 1), "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "frac_recompute": round(alg / (ms_re * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "tokens_per_s": round(cfg.N / (ms * 1e-3), 1), "stages": stages, "stages_recompute": stages_re,
+            "flops_basis": "algorithmic reverse-pass FLOPs / call time (saved activations; recompute beside it)"}
 
 
 def bench_horizons(torch, _lib, cfg, inp, K=2, reps=3):
@@ -640,8 +655,9 @@ def main():
 
     backward = bench_backward(torch, _lib, cfg, inp, chain_out, ce_out, per, cache)
     if args.stages:
-        print(f"  chain backward: {backward['ms']:.3f} ms, {backward['achieved']:.0f} TFLOP/s algorithmic "
-              f"({100 * backward['frac']:.1f}% of peak)", file=sys.stderr)
+        print(f"  chain backward: {backward['ms']:.3f} ms with saved activations, {backward['achieved']:.0f} TFLOP/s "
+              f"algorithmic ({100 * backward['frac']:.1f}% of peak); {backward['ms_recompute']:.3f} ms recomputing "
+              f"each depth's forward", file=sys.stderr)
         for k, v in sorted(backward["stages"].items(), key=lambda kv: -kv[1]["ms"]):
             print(f"    {k:14s} {v['ms']:9.3f} ms", file=sys.stderr)
 

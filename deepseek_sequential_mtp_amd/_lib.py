@@ -24,7 +24,7 @@ EXPORTS = ("mtp_chain_forward", "mtp_head_ce_fwd_bwd", "mtp_verify", "mtp_propos
            "mtp_propose_workspace_size", "mtp_strerror", "mtp_abi_version", "mtp_profile_stage",
            "mtp_profile_count", "mtp_verify_noalloc", "mtp_chain_backward",
            "mtp_chain_backward_workspace_size", "mtp_profile_all", "mtp_horizon_heads",
-           "mtp_horizon_heads_workspace_size")
+           "mtp_horizon_heads_workspace_size", "mtp_chain_saved_bytes")
 BLOCK_FIELDS = ("g_a", "g_f", "Wqkv", "Wo", "Wgate", "Wup", "Wdown")
 STAGES = ("ROWS", "DUAL_NORM", "EH_PROJ", "NORM_A", "QKV", "ATTN", "O_PROJ", "NORM_F", "GATE_UP",
           "DOWN", "OUT_NORM", "CE_FWD", "CE_REDUCE", "CE_GRAD", "CE_DX", "CE_NORM_BWD", "CE_DW",
@@ -47,10 +47,11 @@ class ChainArgs(C.Structure):
                 ("tokens", vp), ("segment_ids", vp), ("h0", vp), ("embed", vp),
                 ("w", C.POINTER(DepthWeights)), ("h_out", C.POINTER(vp)),
                 ("state_mask", vp), ("loss_mask", vp), ("labels", vp), ("counts", vp),
-                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t),
+                ("saved", vp), ("saved_bytes", C.c_size_t)]
 
 
-ABI_VERSION = 8     # the struct layouts below mirror include/mtp.h at this version
+ABI_VERSION = 9     # the struct layouts below mirror include/mtp.h at this version
 
 
 class DepthGrads(C.Structure):
@@ -65,7 +66,8 @@ class ChainBwdArgs(C.Structure):
                 ("tokens", vp), ("segment_ids", vp), ("h0", vp), ("embed", vp),
                 ("w", C.POINTER(DepthWeights)), ("h", C.POINTER(vp)), ("dh", C.POINTER(vp)),
                 ("dh0", vp), ("dE", vp), ("dw", C.POINTER(DepthGrads)), ("accumulate", C.c_int),
-                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t)]
+                ("device_error", vp), ("workspace", vp), ("workspace_bytes", C.c_size_t),
+                ("saved", vp), ("saved_bytes", C.c_size_t)]
 
 
 class BlockWeights(C.Structure):
@@ -154,6 +156,8 @@ def load(path: str = LIB_PATH) -> C.CDLL:
         lib.mtp_propose_workspace_size.restype = C.c_size_t
         lib.mtp_chain_workspace_size.argtypes = [C.POINTER(ChainArgs)]
         lib.mtp_chain_workspace_size.restype = C.c_size_t
+        lib.mtp_chain_saved_bytes.argtypes = [C.POINTER(ChainArgs)]
+        lib.mtp_chain_saved_bytes.restype = C.c_size_t
         lib.mtp_ce_workspace_size.argtypes = [C.POINTER(CeArgs)]
         lib.mtp_ce_workspace_size.restype = C.c_size_t
         lib.mtp_verify_workspace_size.argtypes = [C.POINTER(VerifyArgs)]
@@ -212,10 +216,13 @@ def _workspace(nbytes: int, device, cache: Optional[Dict] = None, key: str = "ws
 def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Tensor,
                   embed: torch.Tensor, depths: Sequence[Dict[str, torch.Tensor]], *, n_heads: int,
                   head_dim: int, eps: float = 1e-6, rope_theta: float = 10000.0,
-                  out: Optional[Dict] = None, cache: Optional[Dict] = None, stream=None) -> Dict:
+                  out: Optional[Dict] = None, cache: Optional[Dict] = None, save: bool = False,
+                  stream=None) -> Dict:
     """mtp_chain_forward.  tokens/segment_ids int32 [B,T]; h0 [B*T,d]; embed [V,d];
     depths: D dicts with g_h, g_e, M, g_a, Wqkv, Wo, g_f, Wgate, Wup, Wdown.
-    Returns dict(h=[D x [B*T,d]], state_mask, loss_mask, labels, counts, device_error)."""
+    Returns dict(h=[D x [B*T,d]], state_mask, loss_mask, labels, counts, device_error), and with
+    save=True also ``saved`` (uint8, the activations chain_backward can take instead of
+    recomputing them; allocated unless ``out`` already holds one)."""
     B, T = tokens.shape
     V, d = embed.shape
     D = len(depths)
@@ -237,8 +244,15 @@ def chain_forward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Ten
     a = ChainArgs(B, T, d, n_heads, head_dim, ffn, V, D, _dtype_code(h0), eps, rope_theta,
                   _p(tokens), _p(segment_ids), _p(h0), _p(embed), ws_arr, hout,
                   _p(out["state_mask"]), _p(out["loss_mask"]), _p(out["labels"]), _p(out["counts"]),
-                  _p(out["device_error"]), None, 0)
+                  _p(out["device_error"]), None, 0, None, 0)
     lib = load()
+    if save:
+        need = lib.mtp_chain_saved_bytes(C.byref(a))
+        if need == 0:
+            raise ValueError("saved activations need a valid bf16 chain")
+        if out.get("saved") is None or out["saved"].numel() < need:
+            out["saved"] = torch.empty(need, dtype=torch.uint8, device=dev)
+        a.saved, a.saved_bytes = _p(out["saved"]), out["saved"].numel()
     nbytes = lib.mtp_chain_workspace_size(C.byref(a))
     if nbytes == 0:
         _check(lib.mtp_chain_forward(C.byref(a), _stream(stream)))   # raises the shape error
@@ -261,10 +275,11 @@ def chain_backward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Te
                    depths: Sequence[Dict[str, torch.Tensor]], hs: Sequence[torch.Tensor],
                    dh: Sequence[torch.Tensor], *, n_heads: int, head_dim: int, eps: float = 1e-6,
                    rope_theta: float = 10000.0, accumulate: bool = False, out: Optional[Dict] = None,
-                   cache: Optional[Dict] = None, stream=None) -> Dict:
+                   cache: Optional[Dict] = None, saved: Optional[torch.Tensor] = None, stream=None) -> Dict:
     """mtp_chain_backward.  hs: h^(1..D) from chain_forward; dh: D f32 tensors [B*T,d] (the
     head's gradients).  Returns dict(dh0 f32 [B*T,d], dE f32 [V,d] (added to; zeros when
-    ``out`` is not given), dw = D dicts of f32 gradients keyed like the weights, device_error)."""
+    ``out`` is not given), dw = D dicts of f32 gradients keyed like the weights, device_error).
+    saved: chain_forward(save=True)'s ``saved`` for the same inputs (skips the recompute)."""
     B, T = tokens.shape
     V, d = embed.shape
     D = len(depths)
@@ -285,7 +300,8 @@ def chain_backward(tokens: torch.Tensor, segment_ids: torch.Tensor, h0: torch.Te
     dhp = (vp * D)(*[x.data_ptr() for x in dh])
     a = ChainBwdArgs(B, T, d, n_heads, head_dim, ffn, V, D, _dtype_code(h0), eps, rope_theta, _p(tokens),
                      _p(segment_ids), _p(h0), _p(embed), warr, hp, dhp, _p(out["dh0"]), _p(out["dE"]), garr,
-                     1 if accumulate else 0, _p(out["device_error"]), None, 0)
+                     1 if accumulate else 0, _p(out["device_error"]), None, 0,
+                     _p(saved) if saved is not None else None, saved.numel() if saved is not None else 0)
     lib = load()
     nbytes = lib.mtp_chain_backward_workspace_size(C.byref(a))
     if nbytes == 0:

@@ -353,6 +353,40 @@ int check_chain_ptrs(const mtp_chain_args *a) {
 
 constexpr int kChainParts = 14;  // workspace regions of the chain call
 
+// ---------------------------------------------------------------------------
+// Saved activations (bf16 chain, optional): per depth, the activations of
+// the forward that the reverse pass reads, so that it need not recompute
+// them.  Depth k's record starts at k * saved_depth_bytes(...).
+// ---------------------------------------------------------------------------
+struct SavedDepth {
+  bf16_t *c, *xa, *qkv, *o, *y;
+  float *u, *a;
+  float2 *lsed;
+};
+inline size_t saved_depth_layout(long N, int d, int A, int H, Carve &c, SavedDepth &r) {
+  r.c = c.take<bf16_t>(N * 2 * d);
+  r.u = c.take<float>(N * d);
+  r.xa = c.take<bf16_t>(N * d);
+  r.qkv = c.take<bf16_t>(N * 3 * (long)A);
+  r.o = c.take<bf16_t>(N * (long)A);
+  r.lsed = c.take<float2>(N * H);
+  r.a = c.take<float>(N * d);
+  r.y = c.take<bf16_t>(N * d);
+  c.take<char>(0);                                  // the record ends aligned
+  return c.off;
+}
+inline size_t saved_depth_bytes(long N, int d, int A, int H) {
+  Carve c(nullptr);
+  SavedDepth r;
+  return saved_depth_layout(N, d, A, H, c, r);
+}
+inline SavedDepth saved_depth(const void *base, int k, long N, int d, int A, int H) {
+  Carve c(static_cast<char *>(const_cast<void *>(base)) + (size_t)k * saved_depth_bytes(N, d, A, H));
+  SavedDepth r;
+  saved_depth_layout(N, d, A, H, c, r);
+  return r;
+}
+
 template <typename T>
 size_t chain_layout(const mtp_chain_args *a, Carve &c, void **parts) {
   const long N = (long)a->B * a->T;
@@ -400,10 +434,18 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
 
   const T *h_prev = static_cast<const T *>(a->h0);
   const T *E = static_cast<const T *>(a->embed);
+  float *lse2 = nullptr;                           // kept only with saved activations
   for (int k = 1; k <= a->D; ++k) {
     const mtp_depth_weights &w = a->w[k - 1];
     T *h_out = static_cast<T *>(a->h_out[k - 1]);
     int st = 0;
+    if constexpr (std::is_same_v<T, bf16_t>) {
+      if (a->saved != nullptr) {
+        const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H);
+        cbuf = sd.c; u = sd.u; xa = sd.xa; qkv = sd.qkv; o = sd.o; abuf = sd.a; ybuf = sd.y;
+        lse2 = (float *)sd.lsed;
+      }
+    }
     {
       MTP_STAGE(MTP_STAGE_DUAL_NORM);
       MTP_TRY(launch_dual_norm_concat<T>(h_prev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
@@ -425,7 +467,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     if (st) return st;
     {
       MTP_STAGE(MTP_STAGE_ATTN);
-      MTP_TRY(launch_attention<T>(qkv, o, run_start, nullptr, B, Tl, H, hd, s));
+      MTP_TRY(launch_attention<T>(qkv, o, run_start, lse2, B, Tl, H, hd, s));
     }
     {
       MTP_STAGE(MTP_STAGE_O_PROJ);
@@ -699,21 +741,28 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
     const uint8_t *st_k = state + (long)(k - 1) * N;
     const float *gcur = k == D ? a->dh[D - 1] : gbuf;
     int st = 0;
-    // ---- the module's forward again (as chain_run), keeping lse2
-    {
+    // this depth's forward activations: the caller's saved record, or the
+    // module's forward run again here (as chain_run), keeping lse2
+    T *cbk = cbuf, *xak = xa, *qkvk = qkv, *ok = o, *yk = ybuf;
+    float *uk = u, *ak = abuf;
+    float2 *lsk = lsed;
+    if (a->saved != nullptr) {
+      const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H);
+      cbk = sd.c; xak = sd.xa; qkvk = sd.qkv; ok = sd.o; yk = sd.y; uk = sd.u; ak = sd.a; lsk = sd.lsed;
+    } else {
       MTP_STAGE(MTP_STAGE_BWD_RECOMPUTE);
-      MTP_TRY(launch_dual_norm_concat<T>(hprev, E, a->tokens, w.g_h, w.g_e, cbuf, B, Tl, d, V, k, a->eps, s));
-      if ((st = gemm_nt_store<T, float, float>(cbuf, 2L * d, (const T *)w.M, 2L * d, u, d, nullptr, 0, N, d, 2 * d,
+      MTP_TRY(launch_dual_norm_concat<T>(hprev, E, a->tokens, w.g_h, w.g_e, cbk, B, Tl, d, V, k, a->eps, s));
+      if ((st = gemm_nt_store<T, float, float>(cbk, 2L * d, (const T *)w.M, 2L * d, uk, d, nullptr, 0, N, d, 2 * d,
                                                1.f, nullptr, 0, skws, s)))
         return st;
-      MTP_TRY((launch_rmsnorm<float, T>(u, w.g_attn, xa, nullptr, N, d, a->eps, s)));
-      if ((st = gemm_qkv_rope<T>(xa, (const T *)w.Wqkv, qkv, pos, use_rope ? rope : nullptr, N, d, A, hd, skws, s)))
+      MTP_TRY((launch_rmsnorm<float, T>(uk, w.g_attn, xak, nullptr, N, d, a->eps, s)));
+      if ((st = gemm_qkv_rope<T>(xak, (const T *)w.Wqkv, qkvk, pos, use_rope ? rope : nullptr, N, d, A, hd, skws, s)))
         return st;
-      MTP_TRY(launch_attention<T>(qkv, o, run_start, (float *)lsed, B, Tl, H, hd, s));
-      if ((st = gemm_nt_store<T, float, float>(o, A, (const T *)w.Wo, A, abuf, d, u, d, N, d, A, 1.f, nullptr, 0,
+      MTP_TRY(launch_attention<T>(qkvk, ok, run_start, (float *)lsk, B, Tl, H, hd, s));
+      if ((st = gemm_nt_store<T, float, float>(ok, A, (const T *)w.Wo, A, ak, d, uk, d, N, d, A, 1.f, nullptr, 0,
                                                skws, s)))
         return st;
-      MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
+      MTP_TRY((launch_rmsnorm<float, T>(ak, w.g_ffn, yk, nullptr, N, d, a->eps, s)));
     }
     // ---- the block (MLP, attention, their norms), down to du
     if (k == D) {
@@ -722,19 +771,19 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
       MTP_TRY(hipGetLastError());
     }
     {
-      const BlockBufs bb{xa, qkv, o, ybuf, gsw, lsed, abuf, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, dxa, du,
+      const BlockBufs bb{xak, qkvk, ok, yk, gsw, lsk, ak, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, dxa, du,
                          part, skws, run_start, pos, use_rope ? rope : nullptr};
       const BlockW bw{w.g_attn, w.g_ffn, (const T *)w.Wqkv, (const T *)w.Wo, (const T *)w.Wgate, (const T *)w.Wup,
                       (const T *)w.Wdown};
       const BlockG bg{g.g_attn, g.g_ffn, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown};
-      if ((st = block_bwd<float>(bb, bw, bg, u, gcur, acc, B, Tl, d, H, hd, f, a->eps, s))) return st;
+      if ((st = block_bwd<float>(bb, bw, bg, uk, gcur, acc, B, Tl, d, H, hd, f, a->eps, s))) return st;
     }
     // ---- u = M [h_bar; e_bar]: eh_proj, enorm (into dE) and hnorm (the
     // gradient carried to depth k-1, or dh0)
     {
       MTP_STAGE(MTP_STAGE_BWD_EH);
       if ((st = gemm_nn<T, float>(dub, d, (const T *)w.M, 2L * d, dc, 2L * d, N, 2 * d, d, 0, skws, s))) return st;
-      if ((st = gemm_tn<T>(dub, d, cbuf, 2L * d, g.M, 2L * d, d, 2 * d, N, acc, skws, s))) return st;
+      if ((st = gemm_tn<T>(dub, d, cbk, 2L * d, g.M, 2L * d, d, 2 * d, N, acc, skws, s))) return st;
       MTP_TRY(launch_shifted_rows(a->tokens, st_k, B, Tl, V, k, tok, key, val, s));
       MTP_TRY(launch_rms_bwd<T>(dc + d, 2L * d, E, tok, w.g_e, a->eps, nullptr, st_k, de, nullptr, part, g.g_e, acc,
                                 N, d, s));
@@ -1374,11 +1423,21 @@ size_t mtp_chain_workspace_size(const mtp_chain_args *a) {
   return a->dtype == MTP_BF16 ? chain_layout<bf16_t>(a, c, p) : chain_layout<float>(a, c, p);
 }
 
+size_t mtp_chain_saved_bytes(const mtp_chain_args *a) {
+  if (check_chain(a) != MTP_OK || a->dtype != MTP_BF16) return 0;
+  return (size_t)a->D * saved_depth_bytes((long)a->B * a->T, a->d, a->n_heads * a->head_dim, a->n_heads);
+}
+
 int mtp_chain_forward(const mtp_chain_args *a, void *stream) {
   int st = check_chain(a);
   if (st) return st;
   if ((st = check_chain_ptrs(a))) return st;
   if (!a->workspace || a->workspace_bytes < mtp_chain_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  if (a->saved != nullptr) {
+    if (a->dtype != MTP_BF16) return MTP_ERR_UNSUPPORTED;
+    if (!al16(a->saved)) return MTP_ERR_ARG;
+    if (a->saved_bytes < mtp_chain_saved_bytes(a)) return MTP_ERR_WORKSPACE;
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   return a->dtype == MTP_BF16 ? chain_run<bf16_t>(a, s) : chain_run<float>(a, s);
 }
@@ -1395,6 +1454,12 @@ int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream) {
   if (st) return st;
   if ((st = check_chain_bwd_ptrs(a))) return st;
   if (!a->workspace || a->workspace_bytes < mtp_chain_backward_workspace_size(a)) return MTP_ERR_WORKSPACE;
+  if (a->saved != nullptr) {
+    if (!al16(a->saved)) return MTP_ERR_ARG;
+    if (a->saved_bytes < (size_t)a->D * saved_depth_bytes((long)a->B * a->T, a->d, a->n_heads * a->head_dim,
+                                                           a->n_heads))
+      return MTP_ERR_WORKSPACE;
+  }
   return chain_bwd_run(a, static_cast<hipStream_t>(stream));
 }
 

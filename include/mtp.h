@@ -134,6 +134,15 @@ typedef struct {
  *   (other widths return MTP_ERR_UNSUPPORTED); B*T <= 2^30; one batch row's
  *   [q | k | v] activation, T * 3 * n_heads * head_dim elements, must span
  *   less than 2 GiB (else MTP_ERR_UNSUPPORTED).
+ * Saved activations (optional, bf16 only): with saved != NULL the call also
+ * keeps, per depth, the activations mtp_chain_backward would otherwise
+ * recompute (the concat, the residual streams, the normed inputs, q|k|v
+ * after RoPE, the attention output and its per-query log-sum-exps) in
+ * saved, which must hold mtp_chain_saved_bytes(a) bytes (else
+ * MTP_ERR_WORKSPACE; MTP_F32 with saved returns MTP_ERR_UNSUPPORTED).  The
+ * layout is internal to the library; the buffer is caller-owned and is
+ * handed to mtp_chain_backward for the same shapes and inputs.  h_out and
+ * every other output are the same with or without it.
  * ---------------------------------------------------------------------- */
 typedef struct {
   int B, T, d, n_heads, head_dim, ffn, V, D;
@@ -150,6 +159,8 @@ typedef struct {
   int32_t *device_error;
   void *workspace;
   size_t workspace_bytes;
+  void *saved;                       /* optional: per-depth activations kept  */
+  size_t saved_bytes;                /* for mtp_chain_backward                */
 } mtp_chain_args;
 
 /* ------------------------------------------------------------------------
@@ -190,6 +201,11 @@ typedef struct {
  *          mtp_depth_weights): written, or added to with accumulate = 1;
  *          device_error int32 [1] (may be NULL): 1 if an active position
  *          holds a token outside [0, V), else 0.
+ * Saved activations (optional): saved != NULL must be the buffer that
+ * mtp_chain_forward filled for the same shapes, tokens, segment ids, h0,
+ * embedding and weights (saved_bytes >= mtp_chain_saved_bytes of those
+ * shapes, else MTP_ERR_WORKSPACE); the recompute is then skipped and the
+ * results are bitwise the same as with saved = NULL.
  * Requirements: as mtp_chain_forward, and: dtype MTP_BF16 (MTP_F32 returns
  * MTP_ERR_UNSUPPORTED), head_dim 64 or 128, d <= 8192.
  * ---------------------------------------------------------------------- */
@@ -218,6 +234,8 @@ typedef struct {
   int32_t *device_error;             /* optional                               */
   void *workspace;
   size_t workspace_bytes;
+  const void *saved;                 /* optional: mtp_chain_forward's saved   */
+  size_t saved_bytes;                /* activations                           */
 } mtp_chain_bwd_args;
 
 /* ------------------------------------------------------------------------
@@ -525,6 +543,11 @@ int mtp_round_commit(const mtp_round_args *a, void *stream);
  * inspected); 0 if the arguments are invalid. */
 size_t mtp_chain_workspace_size(const mtp_chain_args *a);
 size_t mtp_chain_backward_workspace_size(const mtp_chain_bwd_args *a);
+/* Bytes of the optional saved-activation buffer of mtp_chain_forward /
+ * mtp_chain_backward for these shapes (about 2 d x 2 + d x 4 + d x 2 +
+ * 3 A x 2 + A x 2 + 8 H + d x 4 + d x 2 bytes per row and depth, A =
+ * n_heads * head_dim); 0 if the arguments are invalid or not bf16. */
+size_t mtp_chain_saved_bytes(const mtp_chain_args *a);
 size_t mtp_horizon_heads_workspace_size(const mtp_horizon_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);
 size_t mtp_verify_workspace_size(const mtp_verify_args *a);
@@ -569,7 +592,7 @@ const char *mtp_strerror(int status);
  * struct field added, moved or retyped, a call's meaning changed).  A
  * binding that mirrors the argument structs must refuse a library whose
  * mtp_abi_version() differs from the MTP_ABI_VERSION it was written for. */
-#define MTP_ABI_VERSION 8
+#define MTP_ABI_VERSION 9
 int mtp_abi_version(void);
 
 #ifdef __cplusplus

@@ -367,3 +367,51 @@ def test_horizon_heads_host_errors(lib):
     assert need > 0
     a.workspace, a.workspace_bytes = FAKE, need - 1
     assert run(a) == -5
+
+
+def test_saved_activation_sizes_and_errors(lib):
+    a = _chain_args(dtype=_lib.MTP_BF16, d=256, ffn=688, n_heads=2, head_dim=128, V=1000, T=64, D=2)
+    per = lib.mtp_chain_saved_bytes(C.byref(a)) // 2
+    N, d, A, H = 2 * 64, 256, 256, 2
+    # c, u, x_a, q|k|v, o, (lse2, D) pairs, a, y: each region 256-byte aligned
+    exact = N * (2 * d * 2 + d * 4 + d * 2 + 3 * A * 2 + A * 2 + H * 8 + d * 4 + d * 2)
+    assert exact <= per < exact + 8 * 256
+    assert lib.mtp_chain_saved_bytes(C.byref(_chain_args())) == 0            # f32: no saving
+    assert lib.mtp_chain_saved_bytes(C.byref(_chain_args(D=0))) == 0
+    # forward: every pointer set (never dereferenced), workspace large enough
+    ws = lib.mtp_chain_workspace_size(C.byref(a))
+    w = (_lib.DepthWeights * 2)()
+    for k in range(2):
+        for name, _ in _lib.DepthWeights._fields_:
+            setattr(w[k], name, FAKE)
+    hout = (C.c_void_p * 2)(FAKE, FAKE)
+    for name in ("tokens", "segment_ids", "h0", "embed", "state_mask", "loss_mask", "labels", "counts",
+                 "device_error"):
+        setattr(a, name, FAKE)
+    a.w, a.h_out, a.workspace, a.workspace_bytes = w, hout, FAKE, ws
+    run = lambda x: lib.mtp_chain_forward(C.byref(x), None)
+    a.saved, a.saved_bytes = FAKE, 2 * per - 1
+    assert run(a) == -5                                                      # saved buffer too small
+    a.saved, a.saved_bytes = FAKE + 8, 2 * per
+    assert run(a) == -6                                                      # misaligned
+    f = _chain_args()
+    for name in ("tokens", "segment_ids", "h0", "embed", "state_mask", "loss_mask", "labels", "counts",
+                 "device_error"):
+        setattr(f, name, FAKE)
+    wf = (_lib.DepthWeights * 1)()
+    for name, _ in _lib.DepthWeights._fields_:
+        setattr(wf[0], name, FAKE)
+    hf = (C.c_void_p * 1)(FAKE)
+    f.w, f.h_out, f.workspace = wf, hf, FAKE
+    f.workspace_bytes = lib.mtp_chain_workspace_size(C.byref(f))
+    f.saved, f.saved_bytes = FAKE, 1 << 30
+    assert run(f) == -8                                                      # f32 chain keeps nothing
+    # backward: a saved buffer smaller than the forward's is refused
+    b = _bwd_args()
+    keep = _fill_bwd_pointers(b, b.D)
+    b.workspace, b.workspace_bytes = FAKE, lib.mtp_chain_backward_workspace_size(C.byref(b))
+    b.saved, b.saved_bytes = FAKE, 1024
+    assert lib.mtp_chain_backward(C.byref(b), None) == -5
+    b.saved = FAKE + 4
+    assert lib.mtp_chain_backward(C.byref(b), None) == -6
+    del keep
