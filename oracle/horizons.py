@@ -115,8 +115,9 @@ def block_forward(h: np.ndarray, segment_ids: np.ndarray, w, n_heads: int, head_
 
 def block_heads(h: np.ndarray, tokens: np.ndarray, segment_ids: np.ndarray, blocks, W_out: np.ndarray,
                 g_out: np.ndarray, n_heads: int, head_dim: int, eps: float, rope_theta: float, lam: float,
-                model: Model = EXACT, grads: bool = True):
-    """K = len(blocks) horizons, head k = the shared head on Block_k(h).
+                model: Model = EXACT, grads: bool = True, denom: float = None):
+    """K = len(blocks) horizons, head k = the shared head on Block_k(h);
+    denom: the fixed denominator (default B*T of these rows).
     Returns the head CE's outputs (loss, loss_mtp, counts, dW_out, dg_out)
     and, with grads, dh_trunk = sum over heads of dL/dh through head k and
     ``blocks_grad`` = per-head dicts of block-parameter gradients."""
@@ -127,7 +128,7 @@ def block_heads(h: np.ndarray, tokens: np.ndarray, segment_ids: np.ndarray, bloc
         u, act = block_forward(h, segment_ids, w, n_heads, head_dim, eps, rope_theta, model, keep=True)
         outs.append(u)
         acts.append(act)
-    out = head.head_ce(outs, labels, W_out, g_out, eps, lam, "fixed", None, model, grads=grads)
+    out = head.head_ce(outs, labels, W_out, g_out, eps, lam, "fixed", denom, model, grads=grads)
     out["labels"] = labels
     if grads:
         dh = np.zeros_like(np.asarray(h, np.float64))
