@@ -676,13 +676,6 @@ __global__ __launch_bounds__(Cfg::NT) void gemm_fixup_kernel(Epi epi, TileSched 
                           lds2);
 }
 
-// Raster group: group_m > 0 groups that many row tiles (clamped to [1, mt]);
-// group_m < 0 groups -group_m column tiles (clamped to [1, nt]).
-inline int clamp_group(int group_m, int mt, int nt) {
-  if (group_m < 0) return -(-group_m > nt ? nt : -group_m);
-  return group_m < 1 ? 1 : (group_m > mt ? mt : group_m);
-}
-
 // Host-side launch helpers.  launch_gemm: every tile, K split k_splits ways,
 // each split through the epilogue.
 template <typename T, class Cfg, class LA, class LB, class Epi>
@@ -691,7 +684,7 @@ inline hipError_t launch_gemm(const LA &la, const LB &lb, const Epi &epi, int M,
   TileSched ts;
   ts.mt = (M + Cfg::BM - 1) / Cfg::BM;
   ts.nt = (N + Cfg::BN - 1) / Cfg::BN;
-  ts.group_m = clamp_group(group_m, ts.mt, ts.nt);
+  ts.group_m = group_m < 1 ? 1 : (group_m > ts.mt ? ts.mt : group_m);
   ts.k_splits = k_splits < 1 ? 1 : k_splits;
   ts.tile0 = 0;
   ts.ntiles = ts.mt * ts.nt;
@@ -738,7 +731,7 @@ inline hipError_t launch_gemm_balanced(const LA &la, const LB &lb, const Epi &ep
   TileSched ts;
   ts.mt = (M + Cfg::BM - 1) / Cfg::BM;
   ts.nt = (N + Cfg::BN - 1) / Cfg::BN;
-  ts.group_m = clamp_group(group_m, ts.mt, ts.nt);
+  ts.group_m = group_m < 1 ? 1 : (group_m > ts.mt ? ts.mt : group_m);
   const long ntiles = (long)ts.mt * ts.nt;
   if (ntiles <= 0) return hipSuccess;
   const long R = ntiles % kGemmSlots;

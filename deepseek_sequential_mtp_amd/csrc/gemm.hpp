@@ -297,17 +297,6 @@ struct DmaMNMajor {
 // logical range in column-groups of `group_m` row tiles.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void tile_coords(int logical, int mt, int nt, int group_m, int &tm, int &tn) {
-  if (group_m < 0) {            // groups of -group_m column tiles instead (the roles of M and N swapped)
-    const int gn = -group_m;
-    const int per_group = gn * mt;
-    const int g = logical / per_group;
-    const int first = g * gn;
-    const int gsz = min(nt - first, gn);
-    const int in = logical - g * per_group;
-    tn = first + in % gsz;
-    tm = in / gsz;
-    return;
-  }
   const int per_group = group_m * nt;
   const int g = logical / per_group;
   const int first = g * group_m;

@@ -234,10 +234,9 @@ int gemm_ce_fwd_cfg(const T *xhat, const T *W, const int *lab, float2 *part, flo
 
 // Transposed tile (bf16): z^T = W_out x_hat^T with W_out the pair-row A
 // operand and x_hat^T [d, ldT] the MN-major B operand (whole 128-byte lines
-// for both).  Raster: groups of 8 token tiles; inside a group the 8 token
-// tiles of one vocabulary tile run next to each other, so W_out is read once
-// per group, and an XCD's 32 tiles in flight (4 vocabulary x 8 token tiles)
-// read 12 operand tiles.
+// for both).  Raster: groups of 4 vocabulary tiles, the 4 tiles of a group
+// running next to each other for each token tile, so that an XCD's 32 tiles
+// in flight are 4 vocabulary x 8 token tiles and read 12 operand tiles.
 template <typename T, class Cfg>
 int gemm_ce_fwd_t_cfg(const T *xhatT, long ldT, const T *W, const int *lab, float2 *part, float *target,
                       _Float16 *z, int rows, int V, int d, float *skws, hipStream_t s) {
@@ -245,7 +244,7 @@ int gemm_ce_fwd_t_cfg(const T *xhatT, long ldT, const T *W, const int *lab, floa
   EpiCEFwdT epi{lab, part, target, z, V, V, rows, nt};
   PA<T, Cfg> la{W, (long)d, V, d};
   MB_<T, Cfg> lb{xhatT, ldT, rows, d};
-  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, V, rows, d, -8, skws, s)));
+  MTP_TRY((run_gemm<T, Cfg>(la, lb, epi, V, rows, d, 4, skws, s)));
   return MTP_OK;
 }
 
