@@ -1038,7 +1038,7 @@ int check_ce_ptrs(const mtp_ce_args *a) {
 
 struct CeDims {
   long N, ldT; int d, V, nt, splits; bool big, big_dx;
-  long slab;          // rows per fp32 logit slab
+  long slab;          // rows per logit slab (logits kept as LogitT)
   long group;         // rows per dz buffer: a whole number of slabs (or all N rows)
 };
 
@@ -1051,11 +1051,14 @@ CeDims ce_dims(const mtp_ce_args *a) {
   c.d = a->d;
   c.V = a->V;
   const size_t budget = a->logit_slab_bytes ? a->logit_slab_bytes : kDefaultLogitSlab;
-  long r = (long)(budget / ((size_t)c.V * sizeof(float)));
+  // a slab keeps its logits as LogitT (fp16 offsets for bf16 runs): the more
+  // rows a slab holds, the fewer times the forward GEMM streams W_out from
+  // HBM and the fewer partly filled rounds of tiles it runs
+  long r = (long)(budget / ((size_t)c.V * sizeof(LogitT<T>)));
   if (r >= 256) r -= r % 256;
   c.slab = r < 1 ? 1 : (r > c.N ? c.N : r);
-  // dz is stored in T: the same byte budget holds sizeof(float) / sizeof(T)
-  // slabs of it, and the dx_hat / dW_out GEMMs run once per group of slabs
+  // dz is stored in T (as wide as LogitT): the dx_hat / dW_out GEMMs run once
+  // per group of G rows with G * V * sizeof(T) within the same budget
   long g = (long)(budget / ((size_t)c.V * sizeof(T)));
   g -= g % c.slab;
   c.group = g < c.slab ? c.slab : (g > c.N ? c.N : g);

@@ -310,15 +310,16 @@ typedef struct {
  *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
  * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  The logits are never held for
  * the whole batch: rows are processed in slabs of R rows with
- * R * V * 4 <= logit_slab_bytes (R rounded down to a multiple of 256 when it
- * is at least 256, and at least 1).  Per slab the forward GEMM reduces each
+ * R * V * w <= logit_slab_bytes, w the width of a kept logit (4 bytes for
+ * f32, 2 for bf16; R rounded down to a multiple of 256 when it is at least
+ * 256, and at least 1).  Per slab the forward GEMM reduces each
  * vocabulary tile to an online (max, sum-exp) partial per row and keeps the
  * slab's logits (f32: as fp32; bf16: as fp16 offsets from the row's maximum
  * over its 256-wide vocabulary tile, which are <= 0); the partials give the
  * row's log-sum-exp and softmax - onehot is formed from the kept logits,
  * stored in dtype.  That gradient is
  * kept for a group of G rows, G * V * sizeof(dtype) <= logit_slab_bytes (a
- * whole number of slabs, at least one; two for bf16), and the dx_hat and
+ * whole number of slabs, at least one), and the dx_hat and
  * dW_out GEMMs run once per group.  The logit and gradient buffers are
  * bounded by the slab and the group, not by B*T (the per-row buffers, such
  * as x_hat [B*T, d], do grow with B*T).
@@ -348,8 +349,8 @@ typedef struct {
  *          offsets, so values within 2^-25 of the row maximum tie with it).
  * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
  *          MTP_REDUCE_VALID_MEAN (denom ignored).
- * logit_slab_bytes: bound on the fp32 logit slab and on the gradient group
- *          (0 selects 1 GiB).
+ * logit_slab_bytes: bound on the kept logits of a slab and on the gradient
+ *          group (0 selects 1 GiB: 4096 rows at V = 129280 in bf16).
  * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0;
  * V < 2^21.  Labels outside [-1, V) are treated as -1 and set device_error
  * (may be NULL).

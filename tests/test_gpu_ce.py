@@ -57,7 +57,7 @@ def _case(cfg, reduce="fixed", denom=0.0, label_rows=None, accumulate=False, see
                    accuracy=torch.empty(cfg.D, device="cuda"))
     res = _lib.head_ce_fwd_bwd(hs, lab_t, W, g, lam=cfg.lam, eps=cfg.eps, reduce=reduce, denom=denom,
                                accumulate=accumulate, want_lse=True, want_accuracy=want_accuracy, out=out,
-                               logit_slab_bytes=slab_rows * cfg.V * 4)
+                               logit_slab_bytes=slab_rows * cfg.V * (2 if cfg.dtype == "bf16" else 4))
     torch.cuda.synchronize()
     ref = ohead.head_ce(inp["h"], labels, inp["W_out"], inp["g_out"], cfg.eps, cfg.lam, reduce,
                         denom if denom > 0 else None, model)
@@ -138,9 +138,9 @@ def test_ce_tiny_f32(slab_rows):
 @pytest.mark.parametrize("reduce,slab_rows", [("fixed", 0), ("valid_mean", 0), ("fixed", 80),
                                               ("valid_mean", 128)])
 def test_ce_bf16_ragged_two_depths(reduce, slab_rows):
-    # bf16 dz holds two logit slabs of rows, so the dx / dW GEMMs run per
-    # group of two slabs.  slab_rows=128: 600 rows in groups 256, 256, 88;
-    # slab_rows=80: groups 160 x 3 and 120 (slabs 80 + 40); two depths
+    # the dx / dW GEMMs run once per logit slab (dz and the kept logits are
+    # both 2 bytes wide).  slab_rows=128: 600 rows in slabs 128 x 4 and 88;
+    # slab_rows=80: slabs 80 x 7 and 40; two depths
     cfg = synth.scaled(synth.D1, name="ce_ragged", B=2, T=300, d=256, V=1000, D=2, seg_lo=20,
                        seg_hi=200, sigma_w=0.05)
     res, ref, labels = _case(cfg, reduce=reduce, slab_rows=slab_rows)
@@ -159,8 +159,8 @@ def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
                                             (0, 1024, 20480)])
 def test_ce_bf16_big_tiles(slab_rows, d, V):
     # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each, balanced
-    # schedule); slab_rows=256 runs the 1024 rows as four slabs in two dz
-    # groups; d=1056 gives the forward GEMM an odd number of 32-element K
+    # schedule); slab_rows=256 runs the 1024 rows as four slabs, each its
+    # own dz group; d=1056 gives the forward GEMM an odd number of 32-element K
     # slices (a half-filled last pair of 128-byte A rows); V=20480 makes 320
     # tiles: one whole round of 256, the other 64 split over K into partial
     # tiles that the fixup pass sums

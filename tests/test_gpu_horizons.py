@@ -39,7 +39,8 @@ def test_independent_horizons_on_one_trunk_state(dtype, K, slab_rows):
           f"{(labels >= 0).sum(axis=1).tolist()}", flush=True)
     res = _lib.head_ce_fwd_bwd([h_dev] * K, tdev(labels.reshape(K, cfg.B, cfg.T).astype(np.int32), torch.int32),
                                tdev(inp["W_out"], tdt), tdev(inp["g_out"], torch.float32), lam=cfg.lam,
-                               eps=cfg.eps, dh_accumulate=True, out=out, logit_slab_bytes=slab_rows * cfg.V * 4)
+                               eps=cfg.eps, dh_accumulate=True, out=out,
+                               logit_slab_bytes=slab_rows * cfg.V * (2 if dtype == "bf16" else 4))
     torch.cuda.synchronize()
     ref = horizons.independent_heads(h, inp["tokens"], inp["segment_ids"], K, inp["W_out"], inp["g_out"],
                                      cfg.eps, cfg.lam, model)
