@@ -442,9 +442,12 @@ struct EpiCEFwd {
 // max m_t and s_t = sum exp(z - m_t) over its valid vocabulary rows go to
 // part[token * nt + tile_m] (float2), the target logit to target[token] when
 // the label falls in this tile, and the fp16 offsets z - m_t to zout[token, v]
-// (4 consecutive ids per 8-byte store).  A lane holds one token column and 16
-// vocabulary rows per block; the 32 rows of a block pair live in lanes l and
-// l ^ 32, and the WGM row waves meet through LDS (2 x WGM x BN floats).
+// (staged through LDS per column block, then 16-byte stores along each token's
+// row; direct 8-byte stores from the accumulators took twice as long).  A
+// tile whose vocabulary rows all lie below M skips the row checks.  A lane
+// holds one token column and 16 vocabulary rows per block; the 32 rows of a
+// block pair live in lanes l and l ^ 32, and the WGM row waves meet through
+// LDS (2 x WGM x BN floats).
 // Requires BN * V * 2 < 2^31 and V % 4 == 0 (checked by the caller).
 // ---------------------------------------------------------------------------
 struct EpiCEFwdT {
@@ -460,15 +463,24 @@ struct EpiCEFwdT {
     const long cols = ntok - n0 < Cfg::BN ? ntok - n0 : Cfg::BN;
     const __amdgpu_buffer_rsrc_t rl = make_rsrc(labels + n0, cols * 4L);
     const __amdgpu_buffer_rsrc_t rt = make_rsrc(target + n0, cols * 4L);
+    // a tile whose vocabulary rows all lie below M needs no row checks
+    const bool full = m0 + Cfg::BM <= M;
     // 1) column max over this wave's rows
 #pragma unroll
     for (int j = 0; j < Cfg::NB; ++j) {
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < Cfg::MB; ++i)
+        for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          mx = m0 + acc_row<Cfg>(wm, i, r, lane) < M ? fmaxf(mx, acc[i][j][r]) : mx;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc[i][j][r]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            mx = m0 + acc_row<Cfg>(wm, i, r, lane) < M ? fmaxf(mx, acc[i][j][r]) : mx;
+      }
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       if (hl == 0) redm[wm * Cfg::BN + acc_col<Cfg>(wn, j, lane)] = mx;
     }
@@ -487,15 +499,27 @@ struct EpiCEFwdT {
       // the label's row relative to this wave's first row, if it is one of this lane's
       const int rel = (col < cols ? lab0 : -1) - (m0 + wm * Cfg::WM);
       float sum = 0.f, tv = 0.f;
+      if (full) {
 #pragma unroll
-      for (int i = 0; i < Cfg::MB; ++i)
+        for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int vr = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
-          const float z = acc[i][j][r];
-          sum += m0 + wm * Cfg::WM + vr < M ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
-          tv = vr == rel ? z : tv;
-        }
+          for (int r = 0; r < 16; ++r) {
+            const int vr = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float z = acc[i][j][r];
+            sum += __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm));
+            tv = vr == rel ? z : tv;
+          }
+      } else {
+#pragma unroll
+        for (int i = 0; i < Cfg::MB; ++i)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int vr = i * 32 + 8 * (r >> 2) + 4 * hl + (r & 3);
+            const float z = acc[i][j][r];
+            sum += m0 + wm * Cfg::WM + vr < M ? __builtin_amdgcn_exp2f(fmaf(z, kLog2e, nm)) : 0.f;
+            tv = vr == rel ? z : tv;
+          }
+      }
       const bool has = rel >= 0 && rel < Cfg::WM && ((rel >> 2) & 1) == hl;
       if (__builtin_amdgcn_ballot_w64(has) != 0) buf_store_elem(rt, has ? (unsigned)(col * 4) : kOOB, tv, float{});
       sum += __shfl_xor(sum, 32);
