@@ -601,9 +601,21 @@ __device__ __forceinline__ void gemm_segment(const LA &la, const LB &lb, int m0,
     __shared__ __attribute__((aligned(1024))) char st0[Cfg::LDS_STAGE], st1[Cfg::LDS_STAGE],    \
         st2[Cfg::LDS_STAGE], st3[Cfg::LDS_STAGE];                                               \
     r0[0] = st0; r0[1] = st1; r0[2] = st2; r0[3] = st3;                                         \
-    if constexpr (Cfg::NS == 5) {                                                               \
+    if constexpr (Cfg::NS >= 5) {                                                               \
       __shared__ __attribute__((aligned(1024))) char st4[Cfg::LDS_STAGE];                       \
-      r0[Cfg::NS - 1] = st4;                                                                    \
+      r0[4] = st4;                                                                              \
+    }                                                                                           \
+    if constexpr (Cfg::NS >= 6) {                                                               \
+      __shared__ __attribute__((aligned(1024))) char st5[Cfg::LDS_STAGE];                       \
+      r0[5] = st5;                                                                              \
+    }                                                                                           \
+    if constexpr (Cfg::NS >= 7) {                                                               \
+      __shared__ __attribute__((aligned(1024))) char st6[Cfg::LDS_STAGE];                       \
+      r0[6] = st6;                                                                              \
+    }                                                                                           \
+    if constexpr (Cfg::NS >= 8) {                                                               \
+      __shared__ __attribute__((aligned(1024))) char st7[Cfg::LDS_STAGE];                       \
+      r0[7] = st7;                                                                              \
     }                                                                                           \
   }
 

@@ -32,7 +32,7 @@ struct Tile {
   static constexpr int MB = WM / 32, NB = WN / 32;    // 32x32 blocks per wave
   static constexpr int ROWB = 64;                     // bytes per operand row and stage
   static constexpr int NS = NS_;                      // LDS stages
-  static_assert(NS == 4 || NS == 5, "stage count");
+  static_assert(NS >= 4 && NS <= 8, "stage count");
   static constexpr int LDS_STAGE = (BM + BN) * ROWB;  // bytes per stage
 };
 

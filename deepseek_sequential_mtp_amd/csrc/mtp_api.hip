@@ -108,6 +108,13 @@ struct StageScope {
 // ---------------------------------------------------------------------------
 using Big = Tile<256, 256, 4, 2>;
 using Small = Tile<128, 128>;
+// GEMMs of a few rows (the proposer's R <= 64 requests) stream the weights:
+// a 64-row tile wastes no MFMA work on absent rows, its 80 KB of LDS lets two
+// blocks share a compute unit, and each block keeps three 16 KB weight slices
+// in flight (the 256x256 tile streamed the vocabulary head at 3.8 TB/s, this
+// one at 4.8 TB/s; QKV 3.3 -> 4.3 TB/s, gate/up 2.8 -> 3.5 TB/s, where 192
+// and 144 tiles leave part of the chip idle; a 64x128 tile was slower).
+using Few = Tile<64, 256, 2, 2, 4>;
 
 // Operand loaders for a tile shape: K-major / MN-major A (BM rows) and B (BN rows).
 template <typename T, class Cfg> using KA = DmaKMajor<T, Cfg::BM, Cfg::NT>;
@@ -149,6 +156,12 @@ int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc
                   hipStream_t s) {
   EpiStore<OutT, ResT> epi{C, ldc, M, N, alpha, alpha_dev, R, ldr, accumulate, 0};
   if constexpr (sizeof(T) == 2) {
+    if (M <= Few::BM) {
+      PA<T, Few> la{A, lda, M, K};
+      KB<T, Few> lb{Bm, ldb, N, K};
+      MTP_TRY((launch_gemm<T, Few>(la, lb, epi, M, N, K, 8, 1, s)));
+      return MTP_OK;
+    }
     if (use_big(M, N)) {
       PA<T, Big> la{A, lda, M, K};
       KB<T, Big> lb{Bm, ldb, N, K};
@@ -180,6 +193,12 @@ int gemm_qkv_rope(const T *xa, const T *W, T *qkv, const int *pos, const float2 
                   int hd, float *skws, hipStream_t s) {
   // The wave's column range (WN) must cover whole heads for HALF >= 32.
   if constexpr (sizeof(T) == 2) {
+    if (M <= Few::BM) switch (hd) {
+      case 32: return gemm_qkv_rope_cfg<T, 16, Few>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+      case 64: return gemm_qkv_rope_cfg<T, 32, Few>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+      case 128: return gemm_qkv_rope_cfg<T, 64, Few>(xa, W, qkv, pos, rope, M, d, A, skws, s);
+      default: return MTP_ERR_UNSUPPORTED;
+    }
     switch (hd) {
       case 32: return gemm_qkv_rope_cfg<T, 16, Big>(xa, W, qkv, pos, rope, M, d, A, skws, s);
       case 64: return gemm_qkv_rope_cfg<T, 32, Big>(xa, W, qkv, pos, rope, M, d, A, skws, s);
@@ -197,6 +216,13 @@ int gemm_qkv_rope(const T *xa, const T *W, T *qkv, const int *pos, const float2 
 template <typename T>
 int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, float *skws, hipStream_t s) {
   if constexpr (sizeof(T) == 2) {
+    if (M <= Few::BM) {
+      EpiSwiGLU<T> epi{out, (long)f, M, f};
+      PA<T, Few> la{y, (long)d, M, d};
+      DmaKMajorSwiGLU<T, Few> lb{Wg, Wu, (long)d, f, d};
+      MTP_TRY((launch_gemm<T, Few>(la, lb, epi, M, 2 * ceil_div(f, Few::BN / 2) * (Few::BN / 2), d, 8, 1, s)));
+      return MTP_OK;
+    }
     if (use_big(M, 2L * f)) {
       EpiSwiGLU<T> epi{out, (long)f, M, f};
       PA<T, Big> la{y, (long)d, M, d};
@@ -1269,8 +1295,9 @@ int check_propose_ptrs(const mtp_propose_args *a) {
 // enough blocks to stream the weights with most compute units, at least 8 K
 // slices of 32 per split.
 constexpr int kMaxSplits = 16;
+template <class Cfg>
 inline int few_row_splits(int M, int N, int K) {
-  const long tiles = (long)ceil_div(M, Small::BM) * ceil_div(N, Small::BN);
+  const long tiles = (long)ceil_div(M, Cfg::BM) * ceil_div(N, Cfg::BN);
   long sp = 512 / (tiles > 0 ? tiles : 1);
   const long by_k = K / (32 * 8);
   sp = sp < by_k ? sp : by_k;
@@ -1283,7 +1310,9 @@ inline int few_row_splits(int M, int N, int K) {
 template <typename T, typename TO>
 int gemm_few_rows(const T *A, long lda, const T *Bm, long ldb, float *part, TO *out, const float *res, int M, int N,
                   int K, hipStream_t s) {
-  const int sp = few_row_splits(M, N, K);
+  // (the 128x128 tile: with K splits it fills the chip; the 64-row tile
+  // measured slower here)
+  const int sp = few_row_splits<Small>(M, N, K);
   EpiStore<float, float> epi{part, (long)N, M, N, 1.f, nullptr, nullptr, 0, 0, (long)M * N};
   PA<T, Small> la{A, lda, M, K};
   KB<T, Small> lb{Bm, ldb, N, K};
