@@ -86,6 +86,53 @@ def module_rows(h_rows: np.ndarray, tok_rows: Sequence[int], w: Dict[str, np.nda
     return out, ks, vs
 
 
+def step_from_cache(h: np.ndarray, tok: int, p: int, k_cache: np.ndarray, v_cache: np.ndarray,
+                    w: Dict[str, np.ndarray], E: np.ndarray, W_out: np.ndarray, g_out: np.ndarray,
+                    n_heads: int, head_dim: int, eps: float, theta: float, tau: float, u: float,
+                    model: Model = EXACT):
+    """The step at slot p (0x09A: the module serves from its own cache) with
+    the keys and values of slots 0..p-1 given as stored rows (k after RoPE),
+    not recomputed from earlier module inputs: the row (h, tok) is normalised
+    and projected as in module_rows, its query attends to the given slots and
+    to its own key and value, and the block and the head follow.  Returns
+    dict(h, logits, token, margin, k, v) with k, v this slot's stored key and
+    value rows.  Weights may be passed in float64 to skip the conversions."""
+    st = model.store
+    A = n_heads * head_dim
+    f64 = lambda a: np.asarray(a, np.float64)
+    hb = rmsnorm(f64(h)[None, :], w["g_h"], eps)
+    eb = rmsnorm(f64(E[int(tok)])[None, :], w["g_e"], eps)
+    c = st(np.concatenate([hb, eb], axis=1))
+    u_row = (c @ f64(w["M"]).T)[0]
+    xa = st(rmsnorm(u_row[None, :], w["g_a"], eps))
+    qkv = f64(w["Wqkv"]) @ xa[0]
+    q = np.zeros(A)
+    k = np.zeros(A)
+    for hh in range(n_heads):
+        sl = slice(hh * head_dim, (hh + 1) * head_dim)
+        q[sl] = st(rope(qkv[None, None, sl], np.array([p]), theta)[0, 0])
+        k[sl] = st(rope(qkv[None, None, A + hh * head_dim: A + (hh + 1) * head_dim], np.array([p]), theta)[0, 0])
+    v = st(qkv[2 * A:])
+    keys = np.concatenate([f64(k_cache[:p]), k[None, :]], axis=0)     # slots 0..p
+    vals = np.concatenate([f64(v_cache[:p]), v[None, :]], axis=0)
+    o = np.zeros(A)
+    for hh in range(n_heads):
+        sl = slice(hh * head_dim, (hh + 1) * head_dim)
+        sc = keys[:, sl] @ q[sl] / np.sqrt(head_dim)
+        pr = np.exp(sc - sc.max())
+        pr /= pr.sum()
+        o[sl] = pr @ vals[:, sl]
+    o = st(o)
+    a = u_row + f64(w["Wo"]) @ o
+    y = st(rmsnorm(a[None, :], w["g_f"], eps))[0]
+    gsw = st(silu(f64(w["Wgate"]) @ y) * (f64(w["Wup"]) @ y))
+    h_out = st(a + f64(w["Wdown"]) @ gsw)
+    z = head_logits(h_out, W_out, g_out, eps, model)
+    p_soft, _ = softmax64(z, tau)
+    token, margin = inverse_cdf(p_soft, u)
+    return dict(h=h_out, logits=z, token=token, margin=margin, k=k, v=v)
+
+
 def head_logits(h: np.ndarray, W_out: np.ndarray, g_out: np.ndarray, eps: float, model: Model = EXACT):
     """Stored logits store(W_out store(RMSNorm_{g_out}(h))) of one row."""
     st = model.store

@@ -99,3 +99,50 @@ def test_rollout_feeds_back_state_and_token():
     bad = propose.propose_step(np.array(rows_h), rows_t[:-1] + [cfg.V], w, inp["E"], inp["W_out"],
                                inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4, 1.0, 0.5)
     assert bad["status"] == propose.BAD_TOKEN
+
+
+@pytest.mark.parametrize("model", [EXACT, BF16])
+def test_step_from_the_cache_of_its_own_rows(model):
+    """Given the keys and values that module_rows stores for slots 0..p-1,
+    the step from the cache reproduces the step that recomputes them (a
+    second implementation: one row, vectorised attention), and the key and
+    value it stores for slot p are module_rows' row p."""
+    cfg, inp = _tiny(3)
+    w = inp["depths"][0]
+    toks = inp["tokens"][0]
+    tau, u = 0.9, 0.37
+    for p in (0, 1, 6, cfg.T - 2):
+        h_rows = inp["h0"][:p + 1]
+        h, ks, vs = propose.module_rows(h_rows, toks[1:p + 2], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps,
+                                        1e4, model)
+        ref = propose.propose_step(h_rows, toks[1:p + 2], w, inp["E"], inp["W_out"], inp["g_out"], cfg.n_heads,
+                                   cfg.head_dim, cfg.eps, 1e4, tau, u, model)
+        got = propose.step_from_cache(h_rows[p], toks[p + 1], p, ks[:p], vs[:p], w, inp["E"], inp["W_out"],
+                                      inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4, tau, u, model)
+        tol = dict(rtol=1e-11, atol=1e-12) if model is EXACT else dict(rtol=0, atol=0.05)
+        np.testing.assert_allclose(got["h"], ref["h"], **tol)
+        np.testing.assert_allclose(got["logits"], ref["logits"], **tol)
+        np.testing.assert_allclose(got["k"], ks[p], **tol)
+        np.testing.assert_allclose(got["v"], vs[p], **tol)
+        if model is EXACT:
+            assert got["token"] == ref["token"]
+
+
+def test_step_from_the_cache_reads_the_cache():
+    """Changing one cached value row moves the output; changing a cached row
+    past p does not."""
+    cfg, inp = _tiny(4)
+    w = inp["depths"][0]
+    toks = inp["tokens"][0]
+    p = 5
+    h_rows = inp["h0"][:p + 1]
+    _, ks, vs = propose.module_rows(h_rows, toks[1:p + 2], w, inp["E"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4)
+    args = (w, inp["E"], inp["W_out"], inp["g_out"], cfg.n_heads, cfg.head_dim, cfg.eps, 1e4, 1.0, 0.5)
+    base = propose.step_from_cache(h_rows[p], toks[p + 1], p, ks, vs, *args)
+    v2 = vs.copy()
+    v2[2] += 1.0
+    moved = propose.step_from_cache(h_rows[p], toks[p + 1], p, ks, v2, *args)
+    assert np.max(np.abs(moved["h"] - base["h"])) > 1e-3
+    v3 = np.concatenate([vs, np.ones((3, vs.shape[1]))])
+    same = propose.step_from_cache(h_rows[p], toks[p + 1], p, ks, v3, *args)
+    np.testing.assert_array_equal(same["h"], base["h"])
