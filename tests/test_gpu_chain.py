@@ -82,6 +82,17 @@ def test_chain_bf16_ragged(hd):
     _check(cfg, inp, out, BF16, 2e-2)
 
 
+@pytest.mark.parametrize("hd", [128, 64])
+def test_chain_bf16_few_rows(hd):
+    # at most 64 rows (B * T = 2 x 29): every GEMM of the chain runs on the
+    # 64-row tile (its ragged row tail, three vocabulary-sized operands of
+    # 256-wide column tiles plus a ragged one); two depths
+    cfg = synth.scaled(synth.D1, name=f"few_rows_hd{hd}", B=2, T=29, d=256, n_heads=256 // hd, head_dim=hd,
+                       ffn=688, V=1000, D=2, seg_lo=5, seg_hi=20, sigma_w=0.05)
+    inp, out = _run(cfg)
+    _check(cfg, inp, out, BF16, 2e-2)
+
+
 def test_chain_bf16_padding_and_token_error():
     cfg = synth.scaled(synth.D1, name="padded", B=2, T=130, d=128, n_heads=1, head_dim=128,
                        ffn=256, V=512, D=1, seg_lo=10, seg_hi=60, sigma_w=0.05)

@@ -78,6 +78,17 @@ def test_chain_backward_bf16_ragged(hd):
     _check(cfg, inp, bw)
 
 
+def test_chain_backward_bf16_few_rows():
+    # at most 64 rows: the forward's GEMMs and the head's small GEMMs run on
+    # the 64-row tile; two depths
+    cfg = synth.scaled(synth.D1, name="bwd_few_rows", B=2, T=29, d=256, n_heads=2, head_dim=128, ffn=688,
+                       V=1000, D=2, seg_lo=5, seg_hi=20, sigma_w=0.05)
+    inp = synth.make_chain_inputs(cfg)
+    print(f"[chain-bwd] {cfg.name} B={cfg.B} T={cfg.T}", flush=True)
+    _, _, bw = _gpu_pipeline(cfg, inp)
+    _check(cfg, inp, bw)
+
+
 def test_chain_backward_bf16_depth3_padding_no_rope():
     cfg = synth.scaled(synth.D1, name="bwd_d3_pad", B=2, T=200, d=128, n_heads=1, head_dim=128, ffn=256, V=512,
                        D=3, seg_lo=10, seg_hi=90, sigma_w=0.05, rope_theta=0.0)
