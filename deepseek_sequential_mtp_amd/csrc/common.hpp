@@ -178,6 +178,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int ntiles) {
   const int x = bid & 7, j = bid >> 3;
   return x < r ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
+// Reverse of SwiGLU at one element: from the gate pre-activation g, the up
+// pre-activation u and the incoming gradient dgs of silu(g) u, the product
+// sw = silu(g) u, dg = dgs u silu'(g) with silu'(g) = sig(g) (1 + g (1 -
+// sig(g))), and du = dgs silu(g).
+__device__ __forceinline__ void swiglu_bwd_elem(float g, float u, float dgs, float &sw, float &dg, float &du) {
+  const float sig = __fdividef(1.f, 1.f + __expf(-g));
+  const float sl = g * sig;
+  sw = sl * u;
+  dg = dgs * u * sig * (1.f + g * (1.f - sig));
+  du = dgs * sl;
+}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 

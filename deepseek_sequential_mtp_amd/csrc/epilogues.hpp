@@ -233,6 +233,7 @@ struct EpiRope {
 template <typename OutT>
 struct EpiSwiGLU {
   OutT *C; long ldc; int M, f;
+  float *pre;   // optional: the pre-activations, gate at [row, feat] and up at [row, f + feat] (f32)
   template <class Cfg>
   __device__ __forceinline__ void apply(f32x16 (&acc)[Cfg::MB][Cfg::NB], int m0, int n0, int wm,
                                         int wn, int lane, int, char *, char *) const {
@@ -240,6 +241,8 @@ struct EpiSwiGLU {
     const int tile_n = n0 / Cfg::BN;
     const long rows = M - m0 < Cfg::BM ? M - m0 : Cfg::BM;
     const __amdgpu_buffer_rsrc_t rc = make_rsrc(C + (long)m0 * ldc, rows * ldc * (long)sizeof(OutT));
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(pre != nullptr ? pre + (long)m0 * 2 * f : nullptr, pre != nullptr ? rows * 2L * f * 4 : 0);
 #pragma unroll
     for (int i = 0; i < Cfg::MB; ++i)
 #pragma unroll
@@ -248,6 +251,14 @@ struct EpiSwiGLU {
         const bool fok = feat < f;
         const bool odd = lane & 1;
         const unsigned pc = (unsigned)((feat & ~1) * sizeof(OutT));
+        if (pre != nullptr) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const long row = acc_row<Cfg>(wm, i, r, lane);
+            buf_store_elem(rp, fok ? (unsigned)((row * 2 * f + feat) * 4) : kOOB, acc[i][j][r], float{});
+            buf_store_elem(rp, fok ? (unsigned)((row * 2 * f + f + feat) * 4) : kOOB, acc[i][j + NBh][r], float{});
+          }
+        }
         float v[16];
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -273,6 +284,9 @@ struct EpiSwiGLU {
 //   dgu[row, feat]       = dgsw u silu'(g),  silu'(g) = sig(g) (1 + g (1 - sig(g)))
 //   dgu[row, f + feat]   = dgsw silu(g)
 // All three in bf16 (dgu feeds the dy and dW_gate / dW_up products).
+// swiglu_bwd_elem (common.hpp) is the per-element arithmetic, shared with
+// the kernel that reads saved pre-activations instead (the same values, bit
+// for bit).
 // ---------------------------------------------------------------------------
 template <typename OutT>
 struct EpiSwiGLUBwd {
@@ -300,12 +314,7 @@ struct EpiSwiGLUBwd {
           const int row = acc_row<Cfg>(wm, i, r, lane);
           const float dg_in =
               buf_load_elem(rin, fok ? (unsigned)(((long)row * ldg + feat) * sizeof(OutT)) : kOOB, OutT{});
-          const float g = acc[i][j][r], u = acc[i][j + NBh][r];
-          const float sig = __fdividef(1.f, 1.f + __expf(-g));
-          const float sl = g * sig;
-          vs[r] = sl * u;
-          vg[r] = dg_in * u * sig * (1.f + g * (1.f - sig));
-          vu[r] = dg_in * sl;
+          swiglu_bwd_elem(acc[i][j][r], acc[i][j + NBh][r], dg_in, vs[r], vg[r], vu[r]);
         }
         const unsigned pc = (unsigned)((feat & ~1) * sizeof(OutT));
 #pragma unroll

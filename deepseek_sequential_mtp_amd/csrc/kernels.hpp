@@ -48,6 +48,11 @@ hipError_t launch_rms_bwd(const float *dy, long ldy, const TZ *z, const int32_t 
 // elsewhere) and row indices
 hipError_t launch_shifted_rows(const int32_t *tokens, const uint8_t *state, int B, int T_len, int V, int depth,
                                int32_t *tok, int32_t *key, int32_t *val, hipStream_t s);
+// reverse of SwiGLU from saved pre-activations pre [N, 2f] f32 (gate | up):
+// gsw = silu(gate) up [N, f] and dgu = [d gate | d up] [N, 2f] (bf16), from
+// dgsw [N, f] (bf16); f % 4 == 0
+hipError_t launch_swiglu_bwd(const float *pre, const bf16_t *dgsw, bf16_t *gsw, bf16_t *dgu, long N, int f,
+                             hipStream_t s);
 // dE[t] += sum of de rows whose key is t (stable sort by key, then one sum per run)
 size_t embed_grad_sort_bytes(int N, int V);
 hipError_t launch_embed_grad(const int32_t *key, const int32_t *val, int32_t *key_sorted, int32_t *val_sorted,

@@ -214,17 +214,18 @@ int gemm_qkv_rope(const T *xa, const T *W, T *qkv, const int *pos, const float2 
 }
 
 template <typename T>
-int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, float *skws, hipStream_t s) {
+int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int f, float *skws, hipStream_t s,
+                float *pre = nullptr) {
   if constexpr (sizeof(T) == 2) {
     if (M <= Few::BM) {
-      EpiSwiGLU<T> epi{out, (long)f, M, f};
+      EpiSwiGLU<T> epi{out, (long)f, M, f, pre};
       PA<T, Few> la{y, (long)d, M, d};
       DmaKMajorSwiGLU<T, Few> lb{Wg, Wu, (long)d, f, d};
       MTP_TRY((launch_gemm<T, Few>(la, lb, epi, M, 2 * ceil_div(f, Few::BN / 2) * (Few::BN / 2), d, 8, 1, s)));
       return MTP_OK;
     }
     if (use_big(M, 2L * f)) {
-      EpiSwiGLU<T> epi{out, (long)f, M, f};
+      EpiSwiGLU<T> epi{out, (long)f, M, f, pre};
       PA<T, Big> la{y, (long)d, M, d};
       DmaKMajorSwiGLU<T, Big> lb{Wg, Wu, (long)d, f, d};
       MTP_TRY((run_gemm<T, Big>(la, lb, epi, M, 2 * ceil_div(f, Big::BN / 2) * (Big::BN / 2), d, 8, skws, s)));
@@ -232,7 +233,7 @@ int gemm_swiglu(const T *y, const T *Wg, const T *Wu, T *out, int M, int d, int 
     }
   }
   {
-    EpiSwiGLU<T> epi{out, (long)f, M, f};
+    EpiSwiGLU<T> epi{out, (long)f, M, f, pre};
     PA<T, Small> la{y, (long)d, M, d};
     DmaKMajorSwiGLU<T, Small> lb{Wg, Wu, (long)d, f, d};
     MTP_TRY((launch_gemm<T, Small>(la, lb, epi, M, 2 * ceil_div(f, Small::BN / 2) * (Small::BN / 2), d, 8,
@@ -386,9 +387,10 @@ constexpr int kChainParts = 14;  // workspace regions of the chain call
 struct SavedDepth {
   bf16_t *c, *xa, *qkv, *o, *y;
   float *u, *a;
+  float *gu;                                        // gate | up before SwiGLU [N, 2 ffn]
   float2 *lsed;
 };
-inline size_t saved_depth_layout(long N, int d, int A, int H, Carve &c, SavedDepth &r) {
+inline size_t saved_depth_layout(long N, int d, int A, int H, int f, Carve &c, SavedDepth &r) {
   r.c = c.take<bf16_t>(N * 2 * d);
   r.u = c.take<float>(N * d);
   r.xa = c.take<bf16_t>(N * d);
@@ -397,18 +399,19 @@ inline size_t saved_depth_layout(long N, int d, int A, int H, Carve &c, SavedDep
   r.lsed = c.take<float2>(N * H);
   r.a = c.take<float>(N * d);
   r.y = c.take<bf16_t>(N * d);
+  r.gu = c.take<float>(N * 2 * (long)f);
   c.take<char>(0);                                  // the record ends aligned
   return c.off;
 }
-inline size_t saved_depth_bytes(long N, int d, int A, int H) {
+inline size_t saved_depth_bytes(long N, int d, int A, int H, int f) {
   Carve c(nullptr);
   SavedDepth r;
-  return saved_depth_layout(N, d, A, H, c, r);
+  return saved_depth_layout(N, d, A, H, f, c, r);
 }
-inline SavedDepth saved_depth(const void *base, int k, long N, int d, int A, int H) {
-  Carve c(static_cast<char *>(const_cast<void *>(base)) + (size_t)k * saved_depth_bytes(N, d, A, H));
+inline SavedDepth saved_depth(const void *base, int k, long N, int d, int A, int H, int f) {
+  Carve c(static_cast<char *>(const_cast<void *>(base)) + (size_t)k * saved_depth_bytes(N, d, A, H, f));
   SavedDepth r;
-  saved_depth_layout(N, d, A, H, c, r);
+  saved_depth_layout(N, d, A, H, f, c, r);
   return r;
 }
 
@@ -460,15 +463,17 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
   const T *h_prev = static_cast<const T *>(a->h0);
   const T *E = static_cast<const T *>(a->embed);
   float *lse2 = nullptr;                           // kept only with saved activations
+  float *pre = nullptr;                            // gate | up before SwiGLU, likewise
   for (int k = 1; k <= a->D; ++k) {
     const mtp_depth_weights &w = a->w[k - 1];
     T *h_out = static_cast<T *>(a->h_out[k - 1]);
     int st = 0;
     if constexpr (std::is_same_v<T, bf16_t>) {
       if (a->saved != nullptr) {
-        const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H);
+        const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H, f);
         cbuf = sd.c; u = sd.u; xa = sd.xa; qkv = sd.qkv; o = sd.o; abuf = sd.a; ybuf = sd.y;
         lse2 = (float *)sd.lsed;
+        pre = sd.gu;
       }
     }
     {
@@ -506,7 +511,7 @@ int chain_run(const mtp_chain_args *a, hipStream_t s) {
     }
     {
       MTP_STAGE(MTP_STAGE_GATE_UP);
-      st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, skws, s);
+      st = gemm_swiglu<T>(ybuf, (const T *)w.Wgate, (const T *)w.Wup, gsw, N, d, f, skws, s, pre);
     }
     if (st) return st;
     {
@@ -659,6 +664,7 @@ struct BlockBufs {
   float *part, *skws;
   const int32_t *run_start, *pos;
   const float2 *rope;                   // NULL: no RoPE
+  const float *gu;                      // gate | up before SwiGLU [N, 2f] f32, or NULL: recomputed
 };
 struct BlockW {
   const float *g_attn, *g_ffn;
@@ -684,7 +690,10 @@ int block_bwd(const BlockBufs &b, const BlockW &w, const BlockG &g, const TU *u,
   {
     MTP_STAGE(MTP_STAGE_BWD_MLP);
     if ((st = gemm_nn<T, T>(b.gb, d, w.Wdown, f, b.dgsw, f, N, f, d, 0, skws, s))) return st;
-    if ((st = gemm_swiglu_bwd<T>(b.y, w.Wgate, w.Wup, b.dgsw, b.gsw, b.dgu, N, d, f, skws, s))) return st;
+    // with the forward's pre-activations kept, their reverse is elementwise;
+    // else the gate/up product runs again with the reverse as its epilogue
+    if (b.gu != nullptr) MTP_TRY(launch_swiglu_bwd(b.gu, b.dgsw, b.gsw, b.dgu, N, f, s));
+    else if ((st = gemm_swiglu_bwd<T>(b.y, w.Wgate, w.Wup, b.dgsw, b.gsw, b.dgu, N, d, f, skws, s))) return st;
     if ((st = gemm_tn<T>(b.gb, d, b.gsw, f, g.Wdown, f, d, f, N, acc, skws, s))) return st;
     if ((st = gemm_nn<T, float>(b.dgu, 2L * f, w.Wgate, d, b.dy, d, N, d, f, 0, skws, s))) return st;
     if ((st = gemm_nn<T, float>(b.dgu + f, 2L * f, w.Wup, d, b.dy, d, N, d, f, 1, skws, s))) return st;
@@ -770,10 +779,12 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
     // module's forward run again here (as chain_run), keeping lse2
     T *cbk = cbuf, *xak = xa, *qkvk = qkv, *ok = o, *yk = ybuf;
     float *uk = u, *ak = abuf;
+    const float *guk = nullptr;
     float2 *lsk = lsed;
     if (a->saved != nullptr) {
-      const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H);
+      const SavedDepth sd = saved_depth(a->saved, k - 1, N, d, A, H, f);
       cbk = sd.c; xak = sd.xa; qkvk = sd.qkv; ok = sd.o; yk = sd.y; uk = sd.u; ak = sd.a; lsk = sd.lsed;
+      guk = sd.gu;
     } else {
       MTP_STAGE(MTP_STAGE_BWD_RECOMPUTE);
       MTP_TRY(launch_dual_norm_concat<T>(hprev, E, a->tokens, w.g_h, w.g_e, cbk, B, Tl, d, V, k, a->eps, s));
@@ -797,7 +808,7 @@ int chain_bwd_run(const mtp_chain_bwd_args *a, hipStream_t s) {
     }
     {
       const BlockBufs bb{xak, qkvk, ok, yk, gsw, lsk, ak, gb, dgsw, dgu, dab, dO, dqkv, dub, dy, da, dxa, du,
-                         part, skws, run_start, pos, use_rope ? rope : nullptr};
+                         part, skws, run_start, pos, use_rope ? rope : nullptr, guk};
       const BlockW bw{w.g_attn, w.g_ffn, (const T *)w.Wqkv, (const T *)w.Wo, (const T *)w.Wgate, (const T *)w.Wup,
                       (const T *)w.Wdown};
       const BlockG bg{g.g_attn, g.g_ffn, g.Wqkv, g.Wo, g.Wgate, g.Wup, g.Wdown};
@@ -941,7 +952,7 @@ size_t horizon_layout(const mtp_horizon_args *a, Carve &c, void **p) {
   p[22] = c.take<float>(N * d);                   // da
   p[23] = c.take<T>(N * d);                       // da (bf16)
   p[24] = c.take<T>(N * (long)A);                 // dO
-  p[25] = c.take<char>(0);                        // (D lives beside lse2)
+  p[25] = c.take<float>(N * 2 * (long)f);         // gate | up before SwiGLU (f32), for the reverse
   p[26] = c.take<T>(N * 3 * (long)A);             // dqkv
   p[27] = c.take<float>(N * d);                   // dx_a
   p[28] = c.take<float>(N * d);                   // du (the head's share of dh)
@@ -979,7 +990,8 @@ int horizon_run(const mtp_horizon_args *a, hipStream_t s) {
   const T *h = static_cast<const T *>(a->h);
   const BlockBufs bb{xa, qkv, o, ybuf, gsw, lsed, abuf, (T *)p[18], (T *)p[19], (T *)p[20], (T *)p[23],
                      (T *)p[24], (T *)p[26], (T *)p[29], (float *)p[21], (float *)p[22], (float *)p[27],
-                     (float *)p[28], (float *)p[32], (float *)p[33], run_start, pos, use_rope ? rope : nullptr};
+                     (float *)p[28], (float *)p[32], (float *)p[33], run_start, pos, use_rope ? rope : nullptr,
+                     (const float *)p[25]};
   const size_t ce_bytes = total - (size_t)((char *)p[35] - (char *)a->workspace);
   const int acc = a->accumulate ? 1 : 0;
 
@@ -1006,7 +1018,7 @@ int horizon_run(const mtp_horizon_args *a, hipStream_t s) {
                                            s)))
         return st;
       MTP_TRY((launch_rmsnorm<float, T>(abuf, w.g_ffn, ybuf, nullptr, N, d, a->eps, s)));
-      if ((st = gemm_swiglu<T>(ybuf, bw.Wgate, bw.Wup, gsw, N, d, f, (float *)p[33], s))) return st;
+      if ((st = gemm_swiglu<T>(ybuf, bw.Wgate, bw.Wup, gsw, N, d, f, (float *)p[33], s, (float *)p[25]))) return st;
       if ((st = gemm_nt_store<T, T, float>(gsw, f, bw.Wdown, f, out, d, abuf, d, N, d, f, 1.f, nullptr, 0,
                                            (float *)p[33], s)))
         return st;
@@ -1456,7 +1468,7 @@ size_t mtp_chain_workspace_size(const mtp_chain_args *a) {
 
 size_t mtp_chain_saved_bytes(const mtp_chain_args *a) {
   if (check_chain(a) != MTP_OK || a->dtype != MTP_BF16) return 0;
-  return (size_t)a->D * saved_depth_bytes((long)a->B * a->T, a->d, a->n_heads * a->head_dim, a->n_heads);
+  return (size_t)a->D * saved_depth_bytes((long)a->B * a->T, a->d, a->n_heads * a->head_dim, a->n_heads, a->ffn);
 }
 
 int mtp_chain_forward(const mtp_chain_args *a, void *stream) {
@@ -1488,7 +1500,7 @@ int mtp_chain_backward(const mtp_chain_bwd_args *a, void *stream) {
   if (a->saved != nullptr) {
     if (!al16(a->saved)) return MTP_ERR_ARG;
     if (a->saved_bytes < (size_t)a->D * saved_depth_bytes((long)a->B * a->T, a->d, a->n_heads * a->head_dim,
-                                                           a->n_heads))
+                                                           a->n_heads, a->ffn))
       return MTP_ERR_WORKSPACE;
   }
   return chain_bwd_run(a, static_cast<hipStream_t>(stream));

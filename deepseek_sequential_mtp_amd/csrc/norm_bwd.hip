@@ -287,4 +287,39 @@ hipError_t launch_embed_grad(const int32_t *key, const int32_t *val, int32_t *ke
   return hipGetLastError();
 }
 
+// Reverse of SwiGLU from saved pre-activations (the recompute GEMM's
+// epilogue without the GEMM): pre [N, 2f] f32 (gate | up) and dgsw [N, f]
+// bf16 give gsw = silu(gate) up [N, f] and dgu = [d gate | d up] [N, 2f], in
+// bf16.  One thread per row and 4 features (f % 4 == 0).
+__global__ void swiglu_bwd_kernel(const float *__restrict__ pre, const bf16_t *__restrict__ dgsw,
+                                  bf16_t *__restrict__ gsw, bf16_t *__restrict__ dgu, long N, int f) {
+  const int f4 = f >> 2;
+  const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= N * f4) return;
+  const long row = i / f4;
+  const int j = 4 * (int)(i - row * f4);
+  const float4 g = *reinterpret_cast<const float4 *>(pre + row * 2 * f + j);
+  const float4 u = *reinterpret_cast<const float4 *>(pre + row * 2 * f + f + j);
+  const uint2 dw = *reinterpret_cast<const uint2 *>(dgsw + row * f + j);
+  const float gv[4] = {g.x, g.y, g.z, g.w}, uv[4] = {u.x, u.y, u.z, u.w};
+  const float dv[4] = {bf16_lo_f32(dw.x), bf16_hi_f32(dw.x), bf16_lo_f32(dw.y), bf16_hi_f32(dw.y)};
+  float sw[4], dg[4], du[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) swiglu_bwd_elem(gv[e], uv[e], dv[e], sw[e], dg[e], du[e]);
+  *reinterpret_cast<uint2 *>(gsw + row * f + j) = make_uint2(pack_bf16x2(sw[0], sw[1]), pack_bf16x2(sw[2], sw[3]));
+  *reinterpret_cast<uint2 *>(dgu + row * 2 * f + j) = make_uint2(pack_bf16x2(dg[0], dg[1]), pack_bf16x2(dg[2], dg[3]));
+  *reinterpret_cast<uint2 *>(dgu + row * 2 * f + f + j) =
+      make_uint2(pack_bf16x2(du[0], du[1]), pack_bf16x2(du[2], du[3]));
+}
+
+hipError_t launch_swiglu_bwd(const float *pre, const bf16_t *dgsw, bf16_t *gsw, bf16_t *dgu, long N, int f,
+                             hipStream_t s) {
+  if (f % 4 != 0) return hipErrorInvalidValue;
+  const long n = N * (f / 4);
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(swiglu_bwd_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, pre, dgsw, gsw, dgu, N,
+                     f);
+  return hipGetLastError();
+}
+
 }  // namespace mtp

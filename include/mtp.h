@@ -137,7 +137,8 @@ typedef struct {
  * Saved activations (optional, bf16 only): with saved != NULL the call also
  * keeps, per depth, the activations mtp_chain_backward would otherwise
  * recompute (the concat, the residual streams, the normed inputs, q|k|v
- * after RoPE, the attention output and its per-query log-sum-exps) in
+ * after RoPE, the attention output and its per-query log-sum-exps, and the
+ * gate and up projections before SwiGLU, in f32) in
  * saved, which must hold mtp_chain_saved_bytes(a) bytes (else
  * MTP_ERR_WORKSPACE; MTP_F32 with saved returns MTP_ERR_UNSUPPORTED).  The
  * layout is internal to the library; the buffer is caller-owned and is
@@ -204,8 +205,9 @@ typedef struct {
  * Saved activations (optional): saved != NULL must be the buffer that
  * mtp_chain_forward filled for the same shapes, tokens, segment ids, h0,
  * embedding and weights (saved_bytes >= mtp_chain_saved_bytes of those
- * shapes, else MTP_ERR_WORKSPACE); the recompute is then skipped and the
- * results are bitwise the same as with saved = NULL.
+ * shapes, else MTP_ERR_WORKSPACE); the recompute is then skipped (the
+ * gate/up product too: the reverse of SwiGLU reads the kept projections)
+ * and the results are bitwise the same as with saved = NULL.
  * Requirements: as mtp_chain_forward, and: dtype MTP_BF16 (MTP_F32 returns
  * MTP_ERR_UNSUPPORTED), head_dim 64 or 128, d <= 8192.
  * ---------------------------------------------------------------------- */
@@ -546,8 +548,9 @@ size_t mtp_chain_workspace_size(const mtp_chain_args *a);
 size_t mtp_chain_backward_workspace_size(const mtp_chain_bwd_args *a);
 /* Bytes of the optional saved-activation buffer of mtp_chain_forward /
  * mtp_chain_backward for these shapes (about 2 d x 2 + d x 4 + d x 2 +
- * 3 A x 2 + A x 2 + 8 H + d x 4 + d x 2 bytes per row and depth, A =
- * n_heads * head_dim); 0 if the arguments are invalid or not bf16. */
+ * 3 A x 2 + A x 2 + 8 H + d x 4 + d x 2 + 2 ffn x 4 bytes per row and
+ * depth, A = n_heads * head_dim); 0 if the arguments are invalid or not
+ * bf16. */
 size_t mtp_chain_saved_bytes(const mtp_chain_args *a);
 size_t mtp_horizon_heads_workspace_size(const mtp_horizon_args *a);
 size_t mtp_ce_workspace_size(const mtp_ce_args *a);

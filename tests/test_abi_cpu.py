@@ -372,10 +372,10 @@ def test_horizon_heads_host_errors(lib):
 def test_saved_activation_sizes_and_errors(lib):
     a = _chain_args(dtype=_lib.MTP_BF16, d=256, ffn=688, n_heads=2, head_dim=128, V=1000, T=64, D=2)
     per = lib.mtp_chain_saved_bytes(C.byref(a)) // 2
-    N, d, A, H = 2 * 64, 256, 256, 2
-    # c, u, x_a, q|k|v, o, (lse2, D) pairs, a, y: each region 256-byte aligned
-    exact = N * (2 * d * 2 + d * 4 + d * 2 + 3 * A * 2 + A * 2 + H * 8 + d * 4 + d * 2)
-    assert exact <= per < exact + 8 * 256
+    N, d, A, H, f = 2 * 64, 256, 256, 2, 688
+    # c, u, x_a, q|k|v, o, (lse2, D) pairs, a, y, gate|up (f32): each region 256-byte aligned
+    exact = N * (2 * d * 2 + d * 4 + d * 2 + 3 * A * 2 + A * 2 + H * 8 + d * 4 + d * 2 + 2 * f * 4)
+    assert exact <= per < exact + 9 * 256
     assert lib.mtp_chain_saved_bytes(C.byref(_chain_args())) == 0            # f32: no saving
     assert lib.mtp_chain_saved_bytes(C.byref(_chain_args(D=0))) == 0
     # forward: every pointer set (never dereferenced), workspace large enough
