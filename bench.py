@@ -78,6 +78,7 @@ TABLE_KERNELS = {
     "OUT_NORM": r"out_norm_kernel",
     "OUT_NORM_BWD": r"out_norm_bwd",
     "CE_DZ": r"ce_dz_kernel",
+    "EH_O_DOWN": r"gemm_kernel.*DmaKMajor128<[^>]*>, mtp::DmaKMajor<[^>]*>, mtp::EpiStore<",
     "GEMM_FIXUP": FIXUP_KERNEL,
     "VERIFY_LSE": r"verify_lse_kernel",
     "VERIFY_MASS": r"verify_mass_kernel",
