@@ -726,10 +726,12 @@ def main():
 
 def _kernel_hash(stage: str) -> str:
     """Hash of the sources the stage's kernel is compiled from (the GEMM
-    templates, or the attention kernel), so that a stored traffic figure is
-    dropped once that kernel changes."""
+    templates and the host code that picks their tiles, slabs and splits, or
+    the attention kernel), so that a stored traffic figure is dropped once
+    that kernel or its launch changes."""
     import hashlib
-    files = ["common.hpp", "attention.hip"] if stage == "ATTN" else ["common.hpp", "gemm.hpp", "epilogues.hpp"]
+    files = (["common.hpp", "attention.hip"] if stage == "ATTN"
+             else ["common.hpp", "gemm.hpp", "epilogues.hpp", "mtp_api.hip"])
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "deepseek_sequential_mtp_amd", "csrc")
     for name in files:

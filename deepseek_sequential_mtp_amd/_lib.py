@@ -364,7 +364,7 @@ def head_ce_fwd_bwd(hs: Sequence[torch.Tensor], labels: torch.Tensor, W_out: tor
                     cache: Optional[Dict] = None, stream=None) -> Dict:
     """mtp_head_ce_fwd_bwd.  hs: D tensors [B*T,d]; labels int32 [D,B,T].  logit_slab_bytes
     bounds the kept logits of a slab (fp16 for bf16, fp32 for f32) and the dz row group
-    (0: the library default).
+    (0: the library default, 1 GiB with at most half of the rows per slab).
     Returns dict(loss_sum, counts, loss, loss_mtp, lse, dh, dW_out, dg_out, device_error,
     pred, correct, accuracy); the last three (top-1 accuracy by depth) only with
     want_accuracy (or when ``out`` holds them)."""

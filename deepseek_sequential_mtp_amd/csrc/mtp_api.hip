@@ -1093,6 +1093,14 @@ CeDims ce_dims(const mtp_ce_args *a) {
   // rows a slab holds, the fewer times the forward GEMM streams W_out from
   // HBM and the fewer partly filled rounds of tiles it runs
   long r = (long)(budget / ((size_t)c.V * sizeof(LogitT<T>)));
+  if (a->logit_slab_bytes == 0 && c.N > 1) {
+    // under the default bound a slab never keeps the logits of the whole
+    // batch: at most half of its rows (rounded up to a multiple of 256 from
+    // 256 rows on, which stays below the row count)
+    long half = (c.N + 1) / 2;
+    if (half >= 256) half = (half + 255) / 256 * 256;
+    r = r < half ? r : half;
+  }
   if (r >= 256) r -= r % 256;
   c.slab = r < 1 ? 1 : (r > c.N ? c.N : r);
   // dz is stored in T (as wide as LogitT): the dx_hat / dW_out GEMMs run once

@@ -310,11 +310,13 @@ typedef struct {
  * mtp_head_ce_fwd_bwd: shared output head Norm_out + W_U, masked CE against
  * the labels of every depth, and the gradients of
  *   L_MTP = (lambda / D) * sum_k L^(k),  L^(k) = loss_sum[k] / denom_k
- * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  The logits are never held for
- * the whole batch: rows are processed in slabs of R rows with
- * R * V * w <= logit_slab_bytes, w the width of a kept logit (4 bytes for
- * f32, 2 for bf16; R rounded down to a multiple of 256 when it is at least
- * 256, and at least 1).  Per slab the forward GEMM reduces each
+ * ([M7.6] 0x03, 0x04B, 0x05, 0x05A, 0x05B).  Rows are processed in slabs
+ * of R rows with R * V * w <= logit_slab_bytes, w the width of a kept logit
+ * (4 bytes for f32, 2 for bf16; R rounded down to a multiple of 256 when it
+ * is at least 256, and at least 1).  Under the default bound R is also at
+ * most half of the B*T rows (rounded up to a multiple of 256 from 256 rows
+ * on), so the logits of the whole batch are never held at once; an explicit
+ * bound is taken as given.  Per slab the forward GEMM reduces each
  * vocabulary tile to an online (max, sum-exp) partial per row and keeps the
  * slab's logits (f32: as fp32; bf16: as fp16 offsets from the row's maximum
  * over its 256-wide vocabulary tile, which are <= 0); the partials give the
@@ -352,7 +354,9 @@ typedef struct {
  * reduce: MTP_REDUCE_FIXED with denom > 0 (0 selects B*T), or
  *          MTP_REDUCE_VALID_MEAN (denom ignored).
  * logit_slab_bytes: bound on the kept logits of a slab and on the gradient
- *          group (0 selects 1 GiB: 4096 rows at V = 129280 in bf16).
+ *          group (0 selects 1 GiB with at most half of the rows per slab:
+ *          2048-row slabs and one 4096-row group at B*T = 4096,
+ *          V = 129280 in bf16).
  * Requirements: bf16: d % 8 == 0, V % 8 == 0; f32: d % 4 == 0, V % 4 == 0;
  * V < 2^21.  Labels outside [-1, V) are treated as -1 and set device_error
  * (may be NULL).

@@ -155,11 +155,12 @@ def test_ce_bf16_accumulate_and_custom_denom(slab_rows):
     _assert(cfg, res, ref, labels, accumulate=True)
 
 
-@pytest.mark.parametrize("slab_rows,d,V", [(0, 1024, 16384), (256, 1024, 16384), (0, 1056, 16384),
-                                            (0, 1024, 20480)])
+@pytest.mark.parametrize("slab_rows,d,V", [(1024, 1024, 16384), (256, 1024, 16384), (1024, 1056, 16384),
+                                            (1024, 1024, 20480)])
 def test_ce_bf16_big_tiles(slab_rows, d, V):
     # 256x256 tiles in the forward and dW GEMMs (>= 256 tiles each, balanced
-    # schedule); slab_rows=256 runs the 1024 rows as four slabs, each its
+    # schedule) when one slab holds all 1024 rows (an explicit bound: the
+    # default one keeps at most half of the rows); slab_rows=256 runs the 1024 rows as four slabs, each its
     # own dz group; d=1056 gives the forward GEMM an odd number of 32-element K
     # slices (a half-filled last pair of 128-byte A rows); V=20480 makes 320
     # tiles: one whole round of 256, the other 64 split over K into partial
@@ -209,7 +210,7 @@ def test_ce_accuracy_exact_ties_take_the_lowest_id(dtype, V):
     assert np.all(pred[m] < V // 2)
 
 
-@pytest.mark.parametrize("slab_rows", [0, 256])
+@pytest.mark.parametrize("slab_rows", [1024, 256])
 def test_ce_bf16_big_tiles_accuracy(slab_rows):
     cfg = synth.scaled(synth.D1, name="ce_big_acc", B=1, T=1024, d=1024, V=16384, D=1, seg_lo=100,
                        seg_hi=700, sigma_w=0.02)
@@ -219,15 +220,16 @@ def test_ce_bf16_big_tiles_accuracy(slab_rows):
 
 
 def test_ce_bf16_more_rows_than_one_grid_dimension():
-    # 70000 rows in one logit slab: the softmax-gradient pass strides its rows
-    # over a grid dimension of at most 65535 blocks; labels on 256 sampled rows
-    # (160 of them beyond row 65535) keep the oracle cheap
+    # 70000 rows in one logit slab (an explicit bound of 70144 rows): the
+    # softmax-gradient pass strides its rows over a grid dimension of at most
+    # 65535 blocks; labels on 256 sampled rows (160 of them beyond row 65535)
+    # keep the oracle cheap
     cfg = synth.scaled(synth.D1, name="ce_tall", B=1, T=70000, d=64, V=256, D=1, seg_lo=2000,
                        seg_hi=9000, sigma_w=0.05)
     rng = np.random.default_rng(4)
     rows = np.concatenate([rng.choice(65536, 96, replace=False),
                            65536 + rng.choice(70000 - 65536, 160, replace=False)])
-    res, ref, labels = _case(cfg, label_rows=rows, want_accuracy=True)
+    res, ref, labels = _case(cfg, label_rows=rows, want_accuracy=True, slab_rows=70144)
     assert int((labels[0, 65536:] >= 0).sum()) > 100
     _assert(cfg, res, ref, labels)
 
