@@ -49,9 +49,9 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restric
 // depth's scale lambda / (D * denom) is applied by the consuming GEMMs).
 // The logits are either fp32 (ZT = float) or fp16 offsets z - m_t from the
 // row max of their vocabulary tile (ZT = _Float16; m_t is the first member of
-// part[row * nt + col / tile_cols]).  V is a multiple of 4 and of the tile
-// width's divisors used here: each thread handles 4 consecutive columns of
-// one tile.
+// part[row * nt + col / tile_cols]).  Each thread handles W consecutive
+// columns of one tile, 16 bytes of kept logits (W = 8 fp16 offsets or 4
+// fp32 logits; V is a multiple of W and the tile width of 8).
 // With pred, the same pass finds each labelled row's argmax: a column is a
 // maximum when its logit equals the row maximum rowmax (fp16 offsets: its
 // tile's maximum is the row's and its offset is 0); atomicMin keeps the
@@ -62,6 +62,7 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
                                                     const int32_t *__restrict__ labels, T *__restrict__ dz,
                                                     const float *__restrict__ rowmax, int32_t *__restrict__ pred,
                                                     int V, int N) {
+  constexpr int W = 16 / (int)sizeof(ZT);
   // column blocks on x, rows on y (a row stride covers N > 65535)
   for (long row = blockIdx.y; row < N; row += gridDim.y) {
     const int lab = labels[row];
@@ -69,36 +70,44 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
     const float rmax = (pred != nullptr && lab >= 0) ? rowmax[row] : 0.f;
     const ZT *zr = z + row * V;
     T *dr = dz + row * V;
-    for (int c4 = blockIdx.x * 256 + threadIdx.x; c4 < V / 4; c4 += gridDim.x * 256) {
-      float g[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int cw = blockIdx.x * 256 + threadIdx.x; cw < V / W; cw += gridDim.x * 256) {
+      float g[W];
+#pragma unroll
+      for (int e = 0; e < W; ++e) g[e] = 0.f;
       if (lab >= 0) {
-        float zz[4];
+        float zz[W];
         float off = nl;
         float top = rmax;            // the value a maximal column holds
         if constexpr (sizeof(ZT) == 4) {
-          const float4 v = reinterpret_cast<const float4 *>(zr)[c4];
+          const float4 v = reinterpret_cast<const float4 *>(zr)[cw];
           zz[0] = v.x; zz[1] = v.y; zz[2] = v.z; zz[3] = v.w;
         } else {
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-          const h4 v = reinterpret_cast<const h4 *>(zr)[c4];
-          zz[0] = (float)v[0]; zz[1] = (float)v[1]; zz[2] = (float)v[2]; zz[3] = (float)v[3];
-          const float mt = part[row * nt + (4 * c4) / tile_cols].x;
+          typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+          const h8 v = reinterpret_cast<const h8 *>(zr)[cw];
+#pragma unroll
+          for (int e = 0; e < W; ++e) zz[e] = (float)v[e];
+          const float mt = part[row * nt + (W * cw) / tile_cols].x;
           off = fmaf(mt, kLog2e, nl);
           top = mt == rmax ? 0.f : 1.f;  // offsets are <= 0: 1 matches none
         }
         if (pred != nullptr) {
           int first = -1;
 #pragma unroll
-          for (int e = 3; e >= 0; --e) first = zz[e] == top ? 4 * c4 + e : first;
+          for (int e = W - 1; e >= 0; --e) first = zz[e] == top ? W * cw + e : first;
           if (first >= 0) atomicMin(pred + row, first);
         }
         // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
         // (probabilities below 2^-126 flush to zero)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, off)) - (4 * c4 + e == lab ? 1.f : 0.f);
+        for (int e = 0; e < W; ++e)
+          g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, off)) - (W * cw + e == lab ? 1.f : 0.f);
       }
-      store4(dr + 4 * c4, g);
+      if constexpr (sizeof(T) == 2 && W == 8) {
+        reinterpret_cast<uint4 *>(dr)[cw] = f32_to_chunk(g, T{});
+      } else {
+#pragma unroll
+        for (int q = 0; q < W; q += 4) store4(dr + W * cw + q, *reinterpret_cast<const float(*)[4]>(g + q));
+      }
     }
   }
 }
@@ -149,7 +158,7 @@ hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, 
                         const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,
                         hipStream_t s) {
   if (N == 0) return hipSuccess;
-  const int bx = min((V / 4 + 1023) / 1024, 65535);
+  const int bx = min((V / (16 / (int)sizeof(ZT)) + 1023) / 1024, 65535);
   hipLaunchKernelGGL((ce_dz_kernel<T, ZT>), dim3(bx, min(N, 65535)), dim3(256), 0, s, z, part, nt, tile_cols,
                      lse, labels, dz, rowmax, pred, V, N);
   return hipGetLastError();
