@@ -593,7 +593,7 @@ __device__ __forceinline__ void gemm_segment(const LA &la, const LB &lb, int m0,
 }
 
 // LDS of one GEMM block: the pair-row layout (3 A regions of BM x 128 bytes,
-// 4 B stages of BN x 64 bytes) or NS stages of (BM + BN) x 64 bytes.  An
+// 4 B stages of BNL x 64 bytes) or NS stages of (BM + BN) x 64 bytes.  An
 // epilogue may use the first two regions as scratch once the main loop has
 // returned.
 #define MTP_GEMM_LDS(Cfg, LA)                                                                   \
@@ -602,8 +602,8 @@ __device__ __forceinline__ void gemm_segment(const LA &la, const LB &lb, int m0,
   if constexpr (PairRows<LA>::value) {                                                          \
     __shared__ __attribute__((aligned(1024))) char a0[Cfg::BM * 128], a1[Cfg::BM * 128],        \
         a2[Cfg::BM * 128];                                                                      \
-    __shared__ __attribute__((aligned(1024))) char b0[Cfg::BN * 64], b1[Cfg::BN * 64],          \
-        b2[Cfg::BN * 64], b3[Cfg::BN * 64];                                                     \
+    __shared__ __attribute__((aligned(1024))) char b0[Cfg::BNL * 64], b1[Cfg::BNL * 64],        \
+        b2[Cfg::BNL * 64], b3[Cfg::BNL * 64];                                                   \
     r0[0] = a0; r0[1] = a1; r0[2] = a2;                                                         \
     r1[0] = b0; r1[1] = b1; r1[2] = b2; r1[3] = b3;                                             \
   } else {                                                                                      \

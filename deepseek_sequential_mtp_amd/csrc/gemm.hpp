@@ -23,9 +23,10 @@
 
 namespace mtp {
 
-template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2, int NS_ = 4>
+template <int BM_, int BN_, int WGM_ = 2, int WGN_ = 2, int NS_ = 4, int BNL_ = BN_>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_;
+  static constexpr int BNL = BNL_;                    // B rows held in LDS (>= BN)
   static constexpr int WGM = WGM_, WGN = WGN_;       // waves along M and N
   static constexpr int NT = 64 * WGM * WGN;           // threads per workgroup
   static constexpr int WM = BM / WGM, WN = BN / WGN;  // per-wave tile
@@ -33,7 +34,8 @@ struct Tile {
   static constexpr int ROWB = 64;                     // bytes per operand row and stage
   static constexpr int NS = NS_;                      // LDS stages
   static_assert(NS >= 4 && NS <= 8, "stage count");
-  static constexpr int LDS_STAGE = (BM + BN) * ROWB;  // bytes per stage
+  static_assert(BNL >= BN, "LDS holds every B row of the tile");
+  static constexpr int LDS_STAGE = (BM + BNL) * ROWB; // bytes per stage
 };
 
 // ---------------------------------------------------------------------------
@@ -103,8 +105,12 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t rs, char *lds_dst, 
 // 16 tile rows; lane L fills physical chunk L & 3 of row L >> 2 and fetches
 // the logical chunk the swizzle places there, (L & 3) ^ (L >> 4) (the block's
 // first row is a multiple of 16, so the swizzle term depends on L only).
-template <typename T, int ROWS, int NT>
+// With CAP < ROWS the tile has CAP rows in a ROWS-row LDS layout: the load
+// blocks past CAP get out-of-range lane offsets (no memory traffic, zeros in
+// LDS), so every wave still issues the same number of loads.
+template <typename T, int ROWS, int NT, int CAP = ROWS>
 struct DmaKMajor {
+  static_assert(CAP <= ROWS && CAP % 16 == 0, "row cap");
   static constexpr int E = Elem<T>::kPerChunk;
   static constexpr int NBLK = ROWS / 16, WAVES = NT / 64, PER_WAVE = NBLK / WAVES;
   static_assert(NBLK % WAVES == 0, "blocks per wave");
@@ -119,7 +125,7 @@ struct DmaKMajor {
   __device__ __forceinline__ void issue(int row0, int k0, char *region) const {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const long nrow = rows - row0 < ROWS ? rows - row0 : ROWS;
+    const long nrow = rows - row0 < CAP ? rows - row0 : CAP;
     const __amdgpu_buffer_rsrc_t rs = make_rsrc(base + (long)row0 * ld, nrow * ld * (long)sizeof(T));
     const int ldb = (int)(ld * sizeof(T));
     const int c = (lane & 3) ^ (lane >> 4);
@@ -127,7 +133,8 @@ struct DmaKMajor {
 #pragma unroll
     for (int i = 0; i < PER_WAVE; ++i) {
       const int q = wave * PER_WAVE + i;
-      dma16(rs, region + q * 1024, voff, 16 * q * ldb + k0 * (int)sizeof(T));
+      dma16(rs, region + q * 1024, (CAP == ROWS || 16 * q < CAP) ? voff : kOOB,
+            16 * q * ldb + k0 * (int)sizeof(T));
     }
   }
 };

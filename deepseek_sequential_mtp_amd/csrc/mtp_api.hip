@@ -115,6 +115,13 @@ using Small = Tile<128, 128>;
 // one at 4.8 TB/s; QKV 3.3 -> 4.3 TB/s, gate/up 2.8 -> 3.5 TB/s, where 192
 // and 144 tiles leave part of the chip idle; a 64x128 tile was slower).
 using Few = Tile<64, 256, 2, 2, 4>;
+// A 256 x 224 tile (eight waves of 32 x 224 each; B staged in the 256-row
+// layout, its last 32 rows empty) for NT GEMMs whose 256 x 256 tiles would
+// leave the last round partly idle: at M 4096, N 7168 (eh_proj, O-proj, down
+// at V3 width) 448 tiles of 256 x 256 take two rounds, 512 tiles of 256 x 224
+// two rounds of 7/8 the work.
+using Wide = Tile<256, 224, 8, 1, 4, 256>;
+template <typename T> using KBW = DmaKMajor<T, Wide::BNL, Wide::NT, Wide::BN>;
 
 // Operand loaders for a tile shape: K-major / MN-major A (BM rows) and B (BN rows).
 template <typename T, class Cfg> using KA = DmaKMajor<T, Cfg::BM, Cfg::NT>;
@@ -140,6 +147,14 @@ inline bool use_big(long M, long N) { return (long)ceil_div(M, 256) * ceil_div(N
 // faster balanced).
 constexpr long kBalancedRounds = 4;
 constexpr int kBalancedK = 65536;
+// The 256 x 224 tile replaces a plain (unbalanced) 256 x 256 launch when its
+// rounds of 7/8-size tiles take at most 95% of the 256 x 256 rounds.
+inline bool use_wide(long M, long N, long K) {
+  const long big = (long)ceil_div(M, 256) * ceil_div(N, 256);
+  if (big >= kBalancedRounds * kGemmSlots || K >= kBalancedK) return false;
+  const long wide = (long)ceil_div(M, 256) * ceil_div(N, 224);
+  return 0.875 * (double)ceil_div(wide, kGemmSlots) <= 0.95 * (double)ceil_div(big, kGemmSlots);
+}
 template <typename T, class Cfg, class LA, class LB, class Epi>
 hipError_t run_gemm(const LA &la, const LB &lb, const Epi &epi, int M, int N, int K, int group_m, float *skws,
                     hipStream_t s) {
@@ -163,6 +178,12 @@ int gemm_nt_store(const T *A, long lda, const T *Bm, long ldb, OutT *C, long ldc
       return MTP_OK;
     }
     if (use_big(M, N)) {
+      if (use_wide(M, N, K)) {
+        PA<T, Wide> la{A, lda, M, K};
+        KBW<T> lb{Bm, ldb, N, K};
+        MTP_TRY((launch_gemm<T, Wide>(la, lb, epi, M, N, K, 8, 1, s)));
+        return MTP_OK;
+      }
       PA<T, Big> la{A, lda, M, K};
       KB<T, Big> lb{Bm, ldb, N, K};
       MTP_TRY((run_gemm<T, Big>(la, lb, epi, M, N, K, 8, skws, s)));

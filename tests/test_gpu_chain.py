@@ -130,3 +130,16 @@ def test_chain_rope_off_and_deterministic():
                               n_heads=2, head_dim=64, eps=cfg.eps, rope_theta=0.0)
     torch.cuda.synchronize()
     assert torch.equal(out["h"][0], out2["h"][0])
+
+
+def test_chain_bf16_wide_tile_ragged():
+    # 4000 rows x d 7000: the three NT GEMMs with d outputs (eh_proj, O-proj,
+    # down) take the 256 x 224 tile (512 tiles where 256 x 256 would make 448,
+    # a partly idle second round), with a ragged last row tile (4000 = 15 x 256
+    # + 160) and a ragged last column tile (7000 = 31 x 224 + 56).  Weights at
+    # the V3-width scale (sigma 0.006), where |h| stays near the workloads'
+    # magnitudes that the bf16 rule is calibrated on
+    cfg = synth.scaled(synth.D1, name="wide_tile", B=1, T=4000, d=7000, n_heads=2, head_dim=128,
+                       ffn=512, V=512, D=1, seg_lo=64, seg_hi=1024, sigma_w=0.006)
+    inp, out = _run(cfg)
+    _check(cfg, inp, out, BF16, 2e-2)
