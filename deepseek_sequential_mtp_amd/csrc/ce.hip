@@ -56,6 +56,8 @@ __global__ __launch_bounds__(256) void ce_combine_kernel(const float2 *__restric
 // maximum when its logit equals the row maximum rowmax (fp16 offsets: its
 // tile's maximum is the row's and its offset is 0); atomicMin keeps the
 // lowest such column.
+constexpr int kDzChunksPerThread = 4;
+
 template <typename T, typename ZT>
 __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, const float2 *__restrict__ part,
                                                     int nt, int tile_cols, const float *__restrict__ lse,
@@ -63,50 +65,68 @@ __global__ __launch_bounds__(256) void ce_dz_kernel(const ZT *__restrict__ z, co
                                                     const float *__restrict__ rowmax, int32_t *__restrict__ pred,
                                                     int V, int N) {
   constexpr int W = 16 / (int)sizeof(ZT);
-  // column blocks on x, rows on y (a row stride covers N > 65535)
+  constexpr int U = kDzChunksPerThread;
+  // column blocks on x, rows on y (a row stride covers N > 65535); a thread
+  // takes U chunks 256 apart, all loaded before any is used, so that U 16-byte
+  // loads per thread are in flight
   for (long row = blockIdx.y; row < N; row += gridDim.y) {
     const int lab = labels[row];
     const float nl = -lse[row] * kLog2e;
     const float rmax = (pred != nullptr && lab >= 0) ? rowmax[row] : 0.f;
     const ZT *zr = z + row * V;
     T *dr = dz + row * V;
-    for (int cw = blockIdx.x * 256 + threadIdx.x; cw < V / W; cw += gridDim.x * 256) {
-      float g[W];
-#pragma unroll
-      for (int e = 0; e < W; ++e) g[e] = 0.f;
+    for (int cw0 = blockIdx.x * 256 * U + threadIdx.x; cw0 < V / W; cw0 += gridDim.x * 256 * U) {
+      float zz[U][W];
       if (lab >= 0) {
-        float zz[W];
-        float off = nl;
-        float top = rmax;            // the value a maximal column holds
-        if constexpr (sizeof(ZT) == 4) {
-          const float4 v = reinterpret_cast<const float4 *>(zr)[cw];
-          zz[0] = v.x; zz[1] = v.y; zz[2] = v.z; zz[3] = v.w;
-        } else {
-          typedef _Float16 h8 __attribute__((ext_vector_type(8)));
-          const h8 v = reinterpret_cast<const h8 *>(zr)[cw];
 #pragma unroll
-          for (int e = 0; e < W; ++e) zz[e] = (float)v[e];
-          const float mt = part[row * nt + (W * cw) / tile_cols].x;
-          off = fmaf(mt, kLog2e, nl);
-          top = mt == rmax ? 0.f : 1.f;  // offsets are <= 0: 1 matches none
+        for (int u = 0; u < U; ++u) {
+          const int cw = cw0 + 256 * u;
+          if (cw < V / W) {
+            if constexpr (sizeof(ZT) == 4) {
+              const float4 v = reinterpret_cast<const float4 *>(zr)[cw];
+              zz[u][0] = v.x; zz[u][1] = v.y; zz[u][2] = v.z; zz[u][3] = v.w;
+            } else {
+              typedef _Float16 h8 __attribute__((ext_vector_type(8)));
+              const h8 v = reinterpret_cast<const h8 *>(zr)[cw];
+#pragma unroll
+              for (int e = 0; e < W; ++e) zz[u][e] = (float)v[e];
+            }
+          }
         }
-        if (pred != nullptr) {
-          int first = -1;
-#pragma unroll
-          for (int e = W - 1; e >= 0; --e) first = zz[e] == top ? W * cw + e : first;
-          if (first >= 0) atomicMin(pred + row, first);
-        }
-        // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
-        // (probabilities below 2^-126 flush to zero)
-#pragma unroll
-        for (int e = 0; e < W; ++e)
-          g[e] = __builtin_amdgcn_exp2f(fmaf(zz[e], kLog2e, off)) - (W * cw + e == lab ? 1.f : 0.f);
       }
-      if constexpr (sizeof(T) == 2 && W == 8) {
-        reinterpret_cast<uint4 *>(dr)[cw] = f32_to_chunk(g, T{});
-      } else {
 #pragma unroll
-        for (int q = 0; q < W; q += 4) store4(dr + W * cw + q, *reinterpret_cast<const float(*)[4]>(g + q));
+      for (int u = 0; u < U; ++u) {
+        const int cw = cw0 + 256 * u;
+        if (cw >= V / W) break;
+        float g[W];
+#pragma unroll
+        for (int e = 0; e < W; ++e) g[e] = 0.f;
+        if (lab >= 0) {
+          float off = nl;
+          float top = rmax;            // the value a maximal column holds
+          if constexpr (sizeof(ZT) == 2) {
+            const float mt = part[row * nt + (W * cw) / tile_cols].x;
+            off = fmaf(mt, kLog2e, nl);
+            top = mt == rmax ? 0.f : 1.f;  // offsets are <= 0: 1 matches none
+          }
+          if (pred != nullptr) {
+            int first = -1;
+#pragma unroll
+            for (int e = W - 1; e >= 0; --e) first = zz[u][e] == top ? W * cw + e : first;
+            if (first >= 0) atomicMin(pred + row, first);
+          }
+          // softmax = 2^(z log2 e - lse log2 e): one FMA and the hardware exp2
+          // (probabilities below 2^-126 flush to zero)
+#pragma unroll
+          for (int e = 0; e < W; ++e)
+            g[e] = __builtin_amdgcn_exp2f(fmaf(zz[u][e], kLog2e, off)) - (W * cw + e == lab ? 1.f : 0.f);
+        }
+        if constexpr (sizeof(T) == 2 && W == 8) {
+          reinterpret_cast<uint4 *>(dr)[cw] = f32_to_chunk(g, T{});
+        } else {
+#pragma unroll
+          for (int q = 0; q < W; q += 4) store4(dr + W * cw + q, *reinterpret_cast<const float(*)[4]>(g + q));
+        }
       }
     }
   }
@@ -158,7 +178,8 @@ hipError_t launch_ce_dz(const ZT *z, const float2 *part, int nt, int tile_cols, 
                         const int32_t *labels, T *dz, const float *rowmax, int32_t *pred, int N, int V,
                         hipStream_t s) {
   if (N == 0) return hipSuccess;
-  const int bx = min((V / (16 / (int)sizeof(ZT)) + 1023) / 1024, 65535);
+  const int per_block = 256 * kDzChunksPerThread;
+  const int bx = min((V / (16 / (int)sizeof(ZT)) + per_block - 1) / per_block, 65535);
   hipLaunchKernelGGL((ce_dz_kernel<T, ZT>), dim3(bx, min(N, 65535)), dim3(256), 0, s, z, part, nt, tile_cols,
                      lse, labels, dz, rowmax, pred, V, N);
   return hipGetLastError();
