@@ -124,6 +124,24 @@ __device__ __forceinline__ double exp_tang(double x, const double *tab) {
   return ldexp(tab[ki & 255] * p, ki >> 8);
 }
 
+// exp_tang for the log-sum-exp loop, whose arguments the caller keeps at or
+// above -700 (so the power of two 2^m, m >= -1011, stays a normal number):
+// the scaling is an integer add to the exponent field of the table value,
+// which gives the same bits as ldexp of the product (a power-of-two scaling
+// of a normal number is exact either way).  NaN and +inf arguments give NaN.
+__device__ __forceinline__ double exp_tang_ge700(double x, const double *tab) {
+  const double t = fma(x, kInvLn2_256, kRoundShift);
+  const double k = t - kRoundShift;
+  const int ki = __double2loint(t);
+  const double r = fma(-k, kLn2_256, x);
+  double p = fma(r, 1.0 / 6.0, 0.5);
+  p = fma(r, p, 1.0);
+  p = fma(r, p, 1.0);
+  const double e = tab[ki & 255];
+  const double es = __hiloint2double(__double2hiint(e) + ((ki >> 8) << 20), __double2loint(e));
+  return es * p;
+}
+
 // 1 if any of the chunk's logits is NaN or +inf (bf16: from the raw bits).
 template <typename T, int E>
 __device__ __forceinline__ int chunk_bad(const T *p, const float (&v)[E]) {
@@ -191,20 +209,35 @@ __global__ __launch_bounds__(kVThreads) void verify_lse_kernel(const T *zt, cons
   // z / tau > max(z) / tau for finite z: the max is taken on raw logits
   // (tau > 0 keeps the order), the finiteness test once per chunk; NaN and
   // +inf poison the row, -inf contributes exp(-inf) = 0
+  // A NaN or +inf logit needs no test of its own once the lane has a finite
+  // running max: it turns the lane's sum into NaN (exp_tang_ge700 of NaN, or
+  // of +inf - inf once the running max is +inf), which the merge below flags.  Arguments are kept
+  // at or above -700 by clamping the logit in float before the conversion
+  // (lo: the logit whose argument is -700 at this max); the comparison keeps
+  // NaN, and a clamped term is below e^-700 of the max's term.
+  float lo = -INFINITY;
   auto consume = [&](const float (&v)[E]) {
     float cm = v[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) cm = fmaxf(cm, v[e]);
-    bad |= chunk_bad<T, E>(nullptr, v);
     cm *= inv_tau;
     if (cm > m) {
       if (m != -INFINITY) s *= exp_tang((double)m - (double)cm, tab);
       m = cm;
+      lo = (float)((-700.0 + (double)m) * (double)tau);
     }
-    const double nm = m == -INFINITY ? 0.0 : -(double)m;
+    if (m == -INFINITY) {
+      // no finite logit yet: this chunk holds only -inf (nothing to add) or NaN
+      bad |= chunk_bad<T, E>(nullptr, v);
+      return;
+    }
+    const double nm = -(double)m;
     double cs = 0.0;
 #pragma unroll
-    for (int e = 0; e < E; ++e) cs += exp_tang(fma((double)v[e], dtau, nm), tab);
+    for (int e = 0; e < E; ++e) {
+      const float vc = v[e] < lo ? lo : v[e];
+      cs += exp_tang_ge700(fma((double)vc, dtau, nm), tab);
+    }
     s += cs;
   };
   // four chunks in flight per lane, then their arithmetic
@@ -223,6 +256,7 @@ __global__ __launch_bounds__(kVThreads) void verify_lse_kernel(const T *zt, cons
     consume(v);
   }
   // merge the lanes' (max, sum) pairs
+  bad |= (isnan(s) || m == INFINITY) ? 1 : 0;
   float mx = warp_max(m);
   for (int o = 32; o > 0; o >>= 1) bad |= __shfl_xor(bad, o);
   if (lane == 0) { shm[w] = mx; shb[w] = bad; }
