@@ -224,7 +224,9 @@ __global__ __launch_bounds__(kVThreads) void verify_lse_kernel(const T *zt, cons
     if (cm > m) {
       if (m != -INFINITY) s *= exp_tang((double)m - (double)cm, tab);
       m = cm;
-      lo = (float)((-700.0 + (double)m) * (double)tau);
+      // below -FLT_MAX every finite logit already meets the bound; -inf is
+      // then lifted to -FLT_MAX, which meets it too
+      lo = (float)fmax((-700.0 + (double)m) * (double)tau, -3.4028234663852886e38);
     }
     if (m == -INFINITY) {
       // no finite logit yet: this chunk holds only -inf (nothing to add) or NaN
