@@ -100,6 +100,34 @@ def test_verify_float32_logits_and_statuses():
     assert list(g["status"][:6]) == [0, 1, 2, 5, 5, 3]
 
 
+def test_verify_extreme_logits_and_temperature():
+    # float32 logits spread over most of the float range with a temperature of
+    # 1e36, so z / temperature lies within +-300 and the log-sum-exp loop's
+    # float clamp of the logits (bounded at -FLT_MAX) is exercised at its
+    # limits; -inf logits contribute nothing; decisions match the oracle's
+    R, G, V = 16, 2, 256
+    tau = 1e36
+    rng = np.random.default_rng(11)
+    zt = (rng.uniform(-1.0, 1.0, (R, G + 1, V)) * 3.0e38).astype(np.float32)
+    zd = (zt[:, :G].astype(np.float64) * 0.9 + rng.uniform(-1.0, 1.0, (R, G, V)) * 2.0e37).astype(np.float32)
+    zt[:, :, 3] = -np.inf
+    zd[:, :, 7] = -np.inf
+    q = ov.draft_probs(zd, tau)
+    y = synth.sample_from_probs(rng, q)
+    ua = rng.random((R, G), dtype=np.float32)
+    us = rng.random((R, G + 1), dtype=np.float32)
+    res = _lib.verify(tdev(zt, torch.float32), tdev(zd, torch.float32), tdev(y.astype(np.int32), torch.int32),
+                      tdev(ua, torch.float32), tdev(us, torch.float32), temperature=tau)
+    torch.cuda.synchronize()
+    g = {k: to_np(v) for k, v in res.items() if k != "_keep" and v is not None}
+    for r in range(R):
+        o = ov.verify_request(zt[r], zd[r], y[r], ua[r], us[r], tau)
+        if min(o["accept_margin"], o["sample_margin"]) < TIE:
+            continue
+        assert (g["status"][r], g["accepted_len"][r], g["next_token"][r]) == (o["status"], o["A"], o["token"]), r
+    assert (g["status"] == 0).all()
+
+
 def test_verify_single_token_invariant_on_grid():
     """The explainer page's example through the GPU: y enumerated with weight
     q(y), uniforms on a midpoint grid; emitted-token law = p."""
